@@ -1,0 +1,278 @@
+"""Benchmark of the single-GPU Atom datapath on one MI355X.
+
+One step = one pass of the whole datapath over one batch of synthetic inputs, all
+resident in HBM before timing starts, every consumer call notified (producer-side
+plr_notify, then the consumer waits on its per-chunk flags):
+  1. reduce    W=8 contributions of [8192, 7168] bf16, N(0, 0.5)  -> one [8192, 7168] share
+  2. allgather W=8 sources of 64 MiB random bits                  -> 512 MiB, packed by rank
+  3. alltoall  W=8 sources of 8 x 8 MiB tiles                     -> 512 MiB, out[d][s] = in[s][d]
+  4. alltoallv W=8 x 4096 rows of 7168 bf16, Zipf(1.1) destinations -> 32768 packed rows
+`value` is the step's algorithmic HBM bytes (bytes read + bytes written) divided by
+the wall-clock time of a step, in GB/s. Decode-size latency (W=8 x [T, 7168] bf16,
+T in 1/8/32/64) is reported beside it as p50/p90 microseconds of the reduce kernel,
+notify off and on.
+
+Prints one JSON line. Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import statistics
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "achieved HBM GB/s (W=8 bf16 reduce, layout copy) + p50 µs at decode size"
+PEAK_HBM_GBS = 8000.0
+W = 8
+R3, C3 = 8192, 7168                 # reduce share [rows, cols] bf16
+B4 = 64 << 20                       # bytes per copy source
+R5, RB5 = 4096, 7168 * 2            # rows per source, row bytes
+DECODE_T = (1, 8, 32, 64)
+
+# algorithmic bytes per launch (bytes read + bytes written)
+BYTES = {
+    "reduce": (W + 1) * R3 * C3 * 2,
+    "allgather": 2 * W * B4,
+    "alltoall": 2 * W * B4,
+    "alltoallv": 2 * W * R5 * RB5 + W * R5 * 4,
+}
+KERNEL_NAMES = {"reduce": "k_reduce_direct", "allgather": "k_copy_direct",
+                "alltoall": "k_copy_direct", "alltoallv": "k_copy_v_scatter"}
+CSRC = os.path.join(ROOT, "reduce_atom_amd", "csrc")
+
+
+def source_hash() -> str:
+    h = hashlib.sha256()
+    for name in sorted(os.listdir(CSRC)):
+        with open(os.path.join(CSRC, name), "rb") as f:
+            h.update(name.encode() + f.read())
+    return h.hexdigest()[:16]
+
+
+def counters_traffic(op: str):
+    """HBM bytes per launch from a committed rocprofv3 counter summary, if it was
+    taken on the current kernel sources; else None."""
+    path = os.path.join(ROOT, "profiles", f"{op}_counters.txt")
+    if not os.path.exists(path):
+        return None
+    kv = {}
+    with open(path) as f:
+        for line in f:
+            if ":" in line and not line.startswith("#"):
+                k, v = line.split(":", 1)
+                kv[k.strip()] = v.strip()
+    if kv.get("source_hash") != source_hash():
+        return None
+    try:
+        return float(kv["traffic_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def make_inputs(torch, synth, seed, dev):
+    x = {}
+    x["r_src"] = [synth.normal_t(seed, 3, w, R3 * C3, 0.5, device=dev) for w in range(W)]
+    x["r_dst"] = torch.empty(R3 * C3, dtype=torch.bfloat16, device=dev)
+    x["c_src"] = [synth.bits_t(seed, 4, s, B4, device=dev) for s in range(W)]
+    x["ag_dst"] = torch.empty(W * B4, dtype=torch.uint8, device=dev)
+    x["a2a_dst"] = torch.empty(W * B4, dtype=torch.uint8, device=dev)
+    p = synth.zipf_weights(1.1, W)
+    x["v_src"] = [synth.bits_t(seed, 6, s, R5 * RB5, device=dev) for s in range(W)]
+    x["v_dest"] = [synth.categorical_t(seed, 5, s, R5, p, device=dev) for s in range(W)]
+    x["v_dst"] = torch.empty(W * R5 * RB5, dtype=torch.uint8, device=dev)
+    x["v_counts"] = torch.empty(W * W, dtype=torch.int64, device=dev)
+    x["v_offsets"] = torch.empty(W * W, dtype=torch.int64, device=dev)
+    return x
+
+
+def run_bench(args):
+    import torch
+
+    import reduce_atom_amd as plr
+    import synth
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    x = make_inputs(torch, synth, args.seed, dev)
+    L = {
+        "reduce": plr.plr_layout_create("reduce", "bf16", W, R3 * C3 * 2, "packed", "packed"),
+        "allgather": plr.plr_layout_create("copy", "bf16", W, B4, "packed", "packed"),
+        "alltoall": plr.plr_layout_create("copy", "bf16", W, B4, "scattered", "transposed"),
+    }
+    ws = {k: torch.zeros(l.workspace_bytes, dtype=torch.uint8, device=dev) for k, l in L.items()}
+    scratch = torch.empty(plr.plr_copy_v_scratch_bytes(W, [R5] * W), dtype=torch.uint8, device=dev)
+
+    def op(name):
+        if name == "reduce":
+            plr.plr_reduce(L[name], x["r_src"], x["r_dst"], ws[name])
+        elif name == "allgather":
+            plr.plr_copy(L[name], x["c_src"], x["ag_dst"], ws[name])
+        elif name == "alltoall":
+            plr.plr_copy(L[name], x["c_src"], x["a2a_dst"], ws[name])
+        else:
+            plr.plr_copy_v(x["v_src"], [R5] * W, x["v_dest"], RB5, x["v_dst"], x["v_counts"],
+                           x["v_offsets"], scratch)
+
+    ops = ["reduce", "allgather", "alltoall", "alltoallv"]
+
+    def step(events=None):
+        for name in ops:
+            if name in L:
+                plr.plr_notify(L[name], -1, ws[name])
+            if events is not None:
+                events[name][0].record()
+            op(name)
+            if events is not None:
+                events[name][1].record()
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    ev = [{n: (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for n in ops}
+          for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for k in range(args.steps):
+        step(ev[k])
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    for name, l in L.items():
+        rc = plr.plr_check(l, ws[name])
+        if rc != plr.PLR_OK:
+            raise RuntimeError(f"{name}: device error {plr.plr_strerror(rc)}")
+    ms_per_step = (t1 - t0) * 1e3 / args.steps
+    per_op_us = {n: statistics.mean(e[n][0].elapsed_time(e[n][1]) for e in ev) * 1e3 for n in ops}
+    step_bytes = sum(BYTES.values())
+    value = step_bytes / (ms_per_step * 1e-3) / 1e9
+
+    # roofline of the dominant single-kernel op (alltoallv is two kernels)
+    single = ["reduce", "allgather", "alltoall"]
+    dom = max(single, key=lambda n: per_op_us[n])
+    achieved = BYTES[dom] / (per_op_us[dom] * 1e-6) / 1e9
+    roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": counters_traffic(dom),
+                "kernel": KERNEL_NAMES[dom], "op": dom, "algorithmic_bytes": BYTES[dom],
+                "avg_us": round(per_op_us[dom], 2)}
+    per_op = {n: {"avg_us": round(per_op_us[n], 2),
+                  "GB/s": round(BYTES[n] / (per_op_us[n] * 1e-6) / 1e9, 1),
+                  "frac": round(BYTES[n] / (per_op_us[n] * 1e-6) / 1e9 / PEAK_HBM_GBS, 4)}
+              for n in ops}
+    del x, ws, scratch
+    torch.cuda.empty_cache()
+    decode = run_decode(args, torch, plr, synth, dev) if not args.no_decode else None
+    return value, ms_per_step, roofline, per_op, decode
+
+
+def run_decode(args, torch, plr, synth, dev):
+    out = {}
+    for T in DECODE_T:
+        n = T * 7168
+        srcs = [synth.normal_t(args.seed, 2, w, n, 1.0, device=dev) for w in range(W)]
+        dst = torch.empty(n, dtype=torch.bfloat16, device=dev)
+        res = {}
+        for mode in ("notify_off", "notify_on"):
+            L = plr.plr_layout_create("reduce", "bf16", W, 2 * n, "packed", "packed")
+            ws = torch.zeros(L.workspace_bytes, dtype=torch.uint8, device=dev) if mode == "notify_on" else None
+
+            def once():
+                if ws is not None:
+                    plr.plr_notify(L, -1, ws)
+                plr.plr_reduce(L, srcs, dst, ws)
+
+            for _ in range(args.decode_warmup):
+                once()
+            evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                   for _ in range(args.decode_iters)]
+            torch.cuda.synchronize()
+            for a, b in evs:
+                if ws is not None:
+                    plr.plr_notify(L, -1, ws)
+                a.record()
+                plr.plr_reduce(L, srcs, dst, ws)
+                b.record()
+            torch.cuda.synchronize()
+            us = sorted(a.elapsed_time(b) * 1e3 for a, b in evs)
+            if ws is not None and plr.plr_check(L, ws) != plr.PLR_OK:
+                raise RuntimeError("decode: device error")
+            res[mode] = {"p50_us": round(us[len(us) // 2], 2), "p90_us": round(us[int(len(us) * 0.9)], 2)}
+        res["GB/s_at_p50"] = round((W + 1) * n * 2 / (res["notify_off"]["p50_us"] * 1e-6) / 1e9, 1)
+        out[f"T={T}"] = res
+    return out
+
+
+def run_cpu_baseline(args):
+    """The oracle, as it stands, on a bounded sample of the same step (a fraction of
+    every op's data), on this host's CPU, single-threaded."""
+    import numpy as np
+    import torch
+
+    import oracle
+    import synth
+
+    f = args.cpu_fraction
+    rr = max(1, int(R3 * f))
+    red = [synth.normal_t(args.seed, 3, w, rr * C3, 0.5).view(torch.int16).numpy().view(np.uint16)
+           for w in range(W)]
+    bb = max(16 * W, int(B4 * f) // (16 * W) * (16 * W))
+    cps = [synth.bits_np(args.seed, 4, s, bb) for s in range(W)]
+    rv = max(1, int(R5 * f))
+    p = synth.zipf_weights(1.1, W)
+    vs = [synth.bits_np(args.seed, 6, s, rv * RB5) for s in range(W)]
+    vd = [synth.categorical_np(args.seed, 5, s, rv, p) for s in range(W)]
+    sample_bytes = ((W + 1) * rr * C3 * 2 + 2 * (2 * W * bb) + 2 * W * rv * RB5 + W * rv * 4)
+    times = []
+    for _ in range(args.cpu_reps):
+        t = time.perf_counter()
+        oracle.reduce("bf16", red)
+        oracle.copy_layout("packed", "packed", cps)
+        oracle.copy_layout("scattered", "transposed", cps)
+        oracle.copy_v(vs, vd, RB5)
+        times.append(time.perf_counter() - t)
+    tmed = statistics.median(times)
+    return {"value": round(sample_bytes / tmed / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "sample": (f"fraction {f} of every op of one step: reduce {rr} of {R3} rows, "
+                       f"allgather/alltoall {bb} of {B4} bytes per source, alltoallv {rv} of {R5} rows "
+                       f"per source; median of {args.cpu_reps} runs of {tmed:.2f} s"),
+            "seconds": round(tmed, 3)}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--decode-iters", type=int, default=1000)
+    ap.add_argument("--decode-warmup", type=int, default=100)
+    ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-fraction", type=float, default=0.125)
+    ap.add_argument("--cpu-reps", type=int, default=3)
+    args = ap.parse_args()
+    if args.gpus != 1:
+        sys.exit(f"bench.py runs on one GPU only (got --gpus {args.gpus}): this datapath holds the W "
+                 "contributions of one GPU's share in that GPU's memory and uses no second GPU.")
+
+    value, ms, roofline, per_op, decode = run_bench(args)
+    cpu = None if args.no_cpu_baseline else run_cpu_baseline(args)
+    line = {
+        "metric": METRIC, "value": round(value, 1), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms, 4), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": "notified datapath step, W=8: reduce 8x[8192,7168] bf16 N(0,0.5); "
+                               "allgather 8x64MiB; alltoall 8x(8x8MiB); alltoallv 8x4096 rows x "
+                               "7168 bf16, Zipf(1.1) destinations",
+                   "world": W, "notify": True, "seed": args.seed, "step_bytes": sum(BYTES.values())},
+        "roofline": roofline, "cpu_baseline": cpu, "per_op": per_op, "decode_reduce_us": decode,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

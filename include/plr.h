@@ -1,0 +1,227 @@
+/*
+ * plr.h - C ABI of the single-GPU Atom datapath for gfx950 (AMD Instinct MI355X).
+ *
+ * The method is the datapath layer ("Atom") of Purlin (Aimuyo, Gandhi, Kozyrakis,
+ * "Purlin: Separating Orchestration from the Datapath of Collectives"): two data
+ * movement primitives, copy and reduce (abstract; section 3.3 "The Atom"), driven
+ * by a collective specification that names an input layout, an output layout and
+ * the copy or reduce operation (section 3.1 "Layouts"), and coordinated chunk by
+ * chunk by Stage, Notify And Consume (section 3.2 "SNAC").
+ *
+ * This library runs one GPU's share of that work with the W contributions of the
+ * W ranks held as W separate buffers in the same GPU's memory:
+ *   - plr_reduce: elementwise sum of W contributions into one share
+ *     (a ReduceScatter or AllReduce share), in source order 0..W-1;
+ *   - plr_copy:   the layout copies of AllGather, AllToAll and the gather half
+ *     of a composed AllReduce;
+ *   - plr_copy_v: the variable-length AllToAll (MoE dispatch) packing.
+ *
+ * Conventions shared by every call
+ *   - Pointers named "device" are HIP device pointers; "host" ones are host memory.
+ *   - The caller owns every device buffer (sources, destination, counts, offsets,
+ *     workspace, scratch). The library never allocates device memory; it owns only
+ *     the host-side plr_layout object.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the null stream). Calls that
+ *     take a stream are asynchronous on it; plr_check is the only call that waits.
+ *   - Alignment: every device address and every byte count must be a multiple of 16
+ *     (the Atom's vector width; the reference implementation asks 16 bytes on all
+ *     but its newest target, README "Using Purlin", Python note). Violations return
+ *     PLR_EALIGN before anything is launched.
+ *   - Errors are returned as int codes (PLR_OK = 0). Nothing aborts, and no C++
+ *     exception crosses this ABI. Argument errors are detected on the host before
+ *     any launch; on error the output buffers are untouched. PLR_EHIP reports a
+ *     failed HIP launch (plr_last_hip_error gives the HIP code). A device-side
+ *     notification timeout is sticky in the workspace and surfaces through plr_check.
+ *   - Calls are not thread-safe on one plr_layout (its epoch advances per call);
+ *     distinct layouts may be used from distinct threads.
+ */
+#ifndef PLR_H
+#define PLR_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define PLR_MAX_WORLD 16
+
+/* ---- error codes ---- */
+enum {
+  PLR_OK = 0,
+  PLR_EINVAL = 1,        /* bad argument: NULL, out of range, aliasing, bad layout pair */
+  PLR_EALIGN = 2,        /* an address or byte count is not a multiple of 16 */
+  PLR_EUNSUPPORTED = 3,  /* W > 16, a non-deterministic reduction mode, too many explicit segments */
+  PLR_EHIP = 4,          /* a HIP runtime call or kernel launch failed */
+  PLR_ETIMEOUT = 5       /* device side: a chunk's notification did not arrive in time */
+};
+
+/* ---- element types (the reduction accumulates in binary32 for all of them) ---- */
+typedef enum { PLR_BF16 = 0, PLR_F16 = 1, PLR_F32 = 2 } plr_dtype;
+
+/* ---- the operation a collective applies between its layouts (section 3.1) ---- */
+typedef enum { PLR_OP_REDUCE = 0, PLR_OP_COPY = 1 } plr_op;
+
+/* ---- layout kinds (section 3.1 "Layouts") ----
+ * PACKED:     a rank's region is one contiguous block of bytes_per_src bytes.
+ * SCATTERED:  a rank's region is W equal slices of bytes_per_src / W bytes;
+ *             slice j belongs to rank j.
+ * TRANSPOSED: a W x W grid of such slices in which output slice (d, s) is
+ *             input slice (s, d).
+ * Supported (in_kind, out_kind) pairs:
+ *   reduce  PACKED    -> PACKED     the whole contribution is reduced (share = bytes_per_src)
+ *   reduce  SCATTERED -> PACKED     rank `rank` reduces slice `rank` of every source
+ *   copy    PACKED    -> PACKED     AllGather: source s lands at byte s * bytes_per_src
+ *   copy    SCATTERED -> TRANSPOSED AllToAll: slice d of source s lands at slice d*W + s
+ *   copy    SCATTERED -> SCATTERED  gather half of AllReduce: slice s of source s lands
+ *                                   at slice s of the output
+ */
+typedef enum { PLR_PACKED = 0, PLR_SCATTERED = 1, PLR_TRANSPOSED = 2 } plr_layout_kind;
+
+/* ---- datapath choice (section 3.3: the Atom's pipeline stages data through
+ * workgroup-local memory; on gfx950 it can also go straight through registers) ---- */
+enum { PLR_PATH_POLICY = 0, PLR_PATH_DIRECT = 1, PLR_PATH_LDS = 2 };
+
+/* ---- reduction mode (README "Deterministic Reduction"): only the deterministic,
+ * source-ordered reduction exists here. ---- */
+enum { PLR_MODE_DETERMINISTIC = 0 };
+
+/* A collective specification plus optional launch policy overrides.
+ * Zero-initialise it, then fill the fields; every zero policy field means
+ * "use the built-in gfx950 policy" (section 4.2 "Codesign Policies and Tuning":
+ * chunk sizes, workgroup counts and pipeline depths are tuned per collective and
+ * per GPU, and callers may supply their own). */
+typedef struct {
+  plr_op op;
+  plr_dtype dtype;            /* element type; copies move bytes and ignore it */
+  int world;                  /* W, number of sources, 1..16 */
+  int rank;                   /* the share reduced by a SCATTERED reduce, 0..W-1 */
+  size_t bytes_per_src;       /* bytes of each source buffer (multiple of 16, of 16*W if scattered) */
+  plr_layout_kind in_kind, out_kind;
+  /* Optional explicit byte offsets (multiples of 16) overriding the derived ones.
+   * reduce: in_offsets[w] is where the share starts inside source w (W entries);
+   *         out_offsets must be NULL.
+   * copy:   one entry per segment in the derived segment order (source-major:
+   *         W segments for AllGather / AllReduce gather, W*W for AllToAll with
+   *         segment s*W + d); at most 64 segments; output segments must not overlap.
+   * The arrays are copied at creation; the caller keeps ownership. */
+  const size_t* in_offsets;
+  const size_t* out_offsets;
+  int mode;                   /* PLR_MODE_DETERMINISTIC (0); anything else: PLR_EUNSUPPORTED */
+  /* policy overrides (0 = built-in policy) */
+  size_t chunk_bytes;         /* per-source bytes per chunk: the notification granule */
+  int workgroups;             /* grid size */
+  int block;                  /* threads per workgroup: 64, 128, 256 or 512 */
+  int unroll;                 /* 16-byte vectors per lane per pipeline step: 1, 2 or 4 */
+  int stages;                 /* LDS pipeline depth, 1..4 (PLR_PATH_LDS only) */
+  int datapath;               /* PLR_PATH_POLICY, PLR_PATH_DIRECT or PLR_PATH_LDS */
+  uint64_t spin_limit;        /* polls of a chunk flag before PLR_ETIMEOUT; 0 = default (about a second) */
+} plr_layout_desc;
+
+typedef struct plr_layout plr_layout; /* opaque, host only */
+
+/* Compile a collective specification into a segment and chunk table
+ * (sections 3.1 "Layouts" and 3.2 "SNAC": dependencies are derived from the
+ * layouts). Host only: touches no device and allocates no device memory.
+ * On success *out owns a new layout (free it with plr_layout_destroy) and the
+ * layout's epoch is 0. Errors: PLR_EINVAL, PLR_EALIGN, PLR_EUNSUPPORTED. */
+int plr_layout_create(const plr_layout_desc* desc, plr_layout** out);
+
+/* Free a layout (NULL is accepted). */
+void plr_layout_destroy(plr_layout* L);
+
+/* Bytes of workspace a notified call needs: a 256-byte header (error word) followed
+ * by the chunk flags, uint64_t flags[W][nchunks]. The caller allocates it in device
+ * memory, ZEROED, once; it is never reset between calls (the epoch only grows,
+ * section 4.3 "Epoch Bookkeeping"). One workspace belongs to one layout. */
+size_t plr_layout_workspace_bytes(const plr_layout* L);
+
+/* Bytes the call writes into dst: the share for a reduce, the whole output for a copy. */
+size_t plr_layout_dst_bytes(const plr_layout* L);
+
+/* Number of chunks (the notification granules) and of copy segments. */
+int plr_layout_nchunks(const plr_layout* L);
+int plr_layout_nsegments(const plr_layout* L);
+
+/* Segment k of the compiled table, in bytes: the source index, the offset read in
+ * that source, the offset written in dst, and the length. For a reduce there are W
+ * segments (one per source, all with dst_off 0). Returns PLR_EINVAL if k is out of range. */
+int plr_layout_segment(const plr_layout* L, int k, int* src, size_t* src_off,
+                       size_t* dst_off, size_t* len);
+
+/* The resolved launch policy (after the built-in table and the overrides). */
+int plr_layout_policy(const plr_layout* L, size_t* chunk_bytes, int* workgroups, int* block,
+                      int* unroll, int* stages, int* datapath);
+
+/* Current epoch E of the layout: the last notified call consumed flags >= E. */
+uint64_t plr_layout_epoch(const plr_layout* L);
+
+/* Reduce (section 3.3 "The Atom", SCORE): for every element i of the share,
+ *   dst[i] = round(((x_0[i] + x_1[i]) + ...) + x_{W-1}[i])
+ * with x_w the share inside srcs[w], binary32 accumulation starting from x_0, and
+ * one round-to-nearest-even into the element type at the end. Each output element
+ * is produced by one lane, sources in order, so the result is bitwise repeatable.
+ *   srcs      host array of W device pointers (source w = rank w), each bytes_per_src bytes
+ *   dst       device, plr_layout_dst_bytes(L) bytes; must not overlap any source share
+ *   workspace device workspace of plr_layout_workspace_bytes(L), or NULL. When given,
+ *             every chunk waits for flags[w][c] >= E+1 for all w (notify, section 3.2),
+ *             and E advances by one after the launch.
+ * Errors: PLR_EINVAL (NULL layout/pointer, wrong op, aliasing), PLR_EALIGN, PLR_EHIP. */
+int plr_reduce(plr_layout* L, const void* const* srcs, void* dst, void* workspace, void* stream);
+
+/* Copy (section 3.1 "Layouts", section 3.3 "The Atom"): moves every segment of the
+ * layout's table, bytes only (NaN payloads and any bit pattern are preserved).
+ *   srcs      host array of W device pointers, each bytes_per_src bytes
+ *   dst       device, plr_layout_dst_bytes(L) bytes; must not overlap any source
+ *   workspace as for plr_reduce; a chunk of a segment waits only for its own
+ *             source's flag.
+ * Errors: as plr_reduce. */
+int plr_copy(plr_layout* L, const void* const* srcs, void* dst, void* workspace, void* stream);
+
+/* Variable-length AllToAll packing (appendix C.4 "Variable-Length Collectives";
+ * section 4: partition sizes at run time, prefix sums). Source s has rows_per_src[s]
+ * rows of row_bytes bytes; row i goes to destination dest_of_row[s][i] in [0, W).
+ *   counts[s*W + d]  (device, int64, W*W)  rows of source s bound for d
+ *   offsets[d*W + s] (device, int64, W*W)  first output row of block (d, s):
+ *                    destinations in order, and sources in order inside one
+ *   dst (device, sum(rows) * row_bytes)    row i of source s lands at row
+ *                    offsets[d*W + s] + (rows i' < i of source s bound for d)
+ *   scratch (device, plr_copy_v_scratch_bytes bytes, contents need no init)
+ *   srcs, dest_of_row: host arrays of W device pointers; rows_per_src: host array.
+ * A destination id outside [0, W) is a caller error: its row is skipped and its
+ * counts and offsets are undefined.
+ * Errors: PLR_EINVAL, PLR_EALIGN (row_bytes, srcs, dst), PLR_EUNSUPPORTED (W > 16), PLR_EHIP. */
+int plr_copy_v(int world, const void* const* srcs, const int64_t* rows_per_src,
+               const int32_t* const* dest_of_row, size_t row_bytes, void* dst,
+               int64_t* counts, int64_t* offsets, void* scratch, void* stream);
+
+/* Scratch bytes plr_copy_v needs for these row counts (host only). */
+size_t plr_copy_v_scratch_bytes(int world, const int64_t* rows_per_src);
+
+/* Producer side of notify (section 3.2 "SNAC"; section 4.3: the epoch supplies the
+ * notification value): release-stores E+1 into every chunk flag of source `src`
+ * (or of all sources if src == -1), after all work already queued on `stream`.
+ * The next plr_reduce / plr_copy on L consumes epoch E+1.
+ * Errors: PLR_EINVAL (src out of range, NULL workspace), PLR_EALIGN, PLR_EHIP. */
+int plr_notify(plr_layout* L, int src, void* workspace, void* stream);
+
+/* Wait for `stream`, then read and clear the workspace's sticky device error.
+ * Returns PLR_OK, PLR_ETIMEOUT (some chunk's flag never reached its epoch; that
+ * call's output is undefined), or PLR_EHIP / PLR_EINVAL for the check itself. */
+int plr_check(plr_layout* L, void* workspace, void* stream);
+
+/* Static text for an error code. */
+const char* plr_strerror(int code);
+
+/* The HIP error code of the last PLR_EHIP on this thread (0 if none). */
+int plr_last_hip_error(void);
+
+/* Library version string. */
+const char* plr_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PLR_H */

@@ -1,0 +1,257 @@
+"""Python binding of libplr.so: the single-GPU Atom datapath (copy and reduce) for gfx950.
+
+Argument marshalling only: every step of the datapath runs in the library's HIP
+kernels. The functions carry the C ABI's names (include/plr.h) and take torch
+tensors (device memory) or raw integer device addresses. torch supplies memory and
+streams; nothing here computes.
+
+Importing this package loads ``libplr.so`` from this directory and raises
+ImportError if it has not been built (``python -m reduce_atom_amd._build``): there
+is no fallback path.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libplr.so")
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError(f"{LIB_PATH} is missing: build it with `python -m reduce_atom_amd._build`")
+
+_lib = ctypes.CDLL(LIB_PATH)
+
+# ---- constants (include/plr.h) ----
+PLR_OK, PLR_EINVAL, PLR_EALIGN, PLR_EUNSUPPORTED, PLR_EHIP, PLR_ETIMEOUT = range(6)
+PLR_BF16, PLR_F16, PLR_F32 = 0, 1, 2
+PLR_OP_REDUCE, PLR_OP_COPY = 0, 1
+PLR_PACKED, PLR_SCATTERED, PLR_TRANSPOSED = 0, 1, 2
+PLR_PATH_POLICY, PLR_PATH_DIRECT, PLR_PATH_LDS = 0, 1, 2
+PLR_MODE_DETERMINISTIC = 0
+PLR_MAX_WORLD = 16
+
+DTYPE_CODES = {"bf16": PLR_BF16, "f16": PLR_F16, "f32": PLR_F32}
+KIND_CODES = {"packed": PLR_PACKED, "scattered": PLR_SCATTERED, "transposed": PLR_TRANSPOSED}
+OP_CODES = {"reduce": PLR_OP_REDUCE, "copy": PLR_OP_COPY}
+
+_c = ctypes
+_vp, _sz, _i, _u64, _i64p = _c.c_void_p, _c.c_size_t, _c.c_int, _c.c_uint64, _c.POINTER(_c.c_int64)
+
+
+class plr_layout_desc(_c.Structure):
+    _fields_ = [
+        ("op", _i), ("dtype", _i), ("world", _i), ("rank", _i),
+        ("bytes_per_src", _sz),
+        ("in_kind", _i), ("out_kind", _i),
+        ("in_offsets", _c.POINTER(_sz)), ("out_offsets", _c.POINTER(_sz)),
+        ("mode", _i),
+        ("chunk_bytes", _sz),
+        ("workgroups", _i), ("block", _i), ("unroll", _i), ("stages", _i), ("datapath", _i),
+        ("spin_limit", _u64),
+    ]
+
+
+_lib.plr_layout_create.argtypes = [_c.POINTER(plr_layout_desc), _c.POINTER(_vp)]
+_lib.plr_layout_create.restype = _i
+_lib.plr_layout_destroy.argtypes = [_vp]
+_lib.plr_layout_destroy.restype = None
+for _n in ("plr_layout_workspace_bytes", "plr_layout_dst_bytes"):
+    getattr(_lib, _n).argtypes = [_vp]
+    getattr(_lib, _n).restype = _sz
+for _n in ("plr_layout_nchunks", "plr_layout_nsegments"):
+    getattr(_lib, _n).argtypes = [_vp]
+    getattr(_lib, _n).restype = _i
+_lib.plr_layout_epoch.argtypes = [_vp]
+_lib.plr_layout_epoch.restype = _u64
+_lib.plr_layout_segment.argtypes = [_vp, _i, _c.POINTER(_i), _c.POINTER(_sz), _c.POINTER(_sz),
+                                    _c.POINTER(_sz)]
+_lib.plr_layout_segment.restype = _i
+_lib.plr_layout_policy.argtypes = [_vp, _c.POINTER(_sz)] + [_c.POINTER(_i)] * 5
+_lib.plr_layout_policy.restype = _i
+_lib.plr_reduce.argtypes = [_vp, _c.POINTER(_vp), _vp, _vp, _vp]
+_lib.plr_reduce.restype = _i
+_lib.plr_copy.argtypes = [_vp, _c.POINTER(_vp), _vp, _vp, _vp]
+_lib.plr_copy.restype = _i
+_lib.plr_copy_v.argtypes = [_i, _c.POINTER(_vp), _i64p, _c.POINTER(_vp), _sz, _vp, _vp, _vp, _vp, _vp]
+_lib.plr_copy_v.restype = _i
+_lib.plr_copy_v_scratch_bytes.argtypes = [_i, _i64p]
+_lib.plr_copy_v_scratch_bytes.restype = _sz
+_lib.plr_notify.argtypes = [_vp, _i, _vp, _vp]
+_lib.plr_notify.restype = _i
+_lib.plr_check.argtypes = [_vp, _vp, _vp]
+_lib.plr_check.restype = _i
+_lib.plr_strerror.argtypes = [_i]
+_lib.plr_strerror.restype = _c.c_char_p
+_lib.plr_last_hip_error.argtypes = []
+_lib.plr_last_hip_error.restype = _i
+_lib.plr_version.argtypes = []
+_lib.plr_version.restype = _c.c_char_p
+
+EXPORTS = [
+    "plr_layout_create", "plr_layout_destroy", "plr_layout_workspace_bytes", "plr_layout_dst_bytes",
+    "plr_layout_nchunks", "plr_layout_nsegments", "plr_layout_segment", "plr_layout_policy",
+    "plr_layout_epoch", "plr_reduce", "plr_copy", "plr_copy_v", "plr_copy_v_scratch_bytes",
+    "plr_notify", "plr_check", "plr_strerror", "plr_last_hip_error", "plr_version",
+]
+
+
+class PlrError(RuntimeError):
+    def __init__(self, code: int, where: str):
+        self.code = code
+        msg = plr_strerror(code)
+        if code == PLR_EHIP:
+            msg += f" (hip error {_lib.plr_last_hip_error()})"
+        super().__init__(f"{where}: {msg} [{code}]")
+
+
+def _ok(rc: int, where: str) -> None:
+    if rc != PLR_OK:
+        raise PlrError(rc, where)
+
+
+def plr_strerror(code: int) -> str:
+    return _lib.plr_strerror(code).decode()
+
+
+def plr_version() -> str:
+    return _lib.plr_version().decode()
+
+
+def _addr(x) -> int | None:
+    """Device address of a tensor (contiguous, on a GPU) or a raw integer address."""
+    if x is None:
+        return None
+    if isinstance(x, int):
+        return x
+    if not x.is_cuda:
+        raise ValueError("device tensor expected")
+    if not x.is_contiguous():
+        raise ValueError("contiguous tensor expected")
+    return x.data_ptr()
+
+
+def _stream(stream) -> int | None:
+    if stream is None:
+        import torch
+
+        return torch.cuda.current_stream().cuda_stream if torch.cuda.is_available() else None
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+def _ptrs(xs):
+    return (_vp * len(xs))(*[_addr(x) for x in xs])
+
+
+class Layout:
+    """A compiled collective specification (host object owning a plr_layout*)."""
+
+    def __init__(self, handle: int):
+        self._h = _vp(handle)
+
+    @property
+    def handle(self):
+        return self._h
+
+    def __del__(self):
+        h = getattr(self, "_h", None)
+        if h is not None and h.value:
+            _lib.plr_layout_destroy(h)
+            self._h = None
+
+    @property
+    def workspace_bytes(self) -> int:
+        return _lib.plr_layout_workspace_bytes(self._h)
+
+    @property
+    def dst_bytes(self) -> int:
+        return _lib.plr_layout_dst_bytes(self._h)
+
+    @property
+    def nchunks(self) -> int:
+        return _lib.plr_layout_nchunks(self._h)
+
+    @property
+    def epoch(self) -> int:
+        return _lib.plr_layout_epoch(self._h)
+
+    def segments(self):
+        out = []
+        for k in range(_lib.plr_layout_nsegments(self._h)):
+            s, so, do, ln = _i(), _sz(), _sz(), _sz()
+            _ok(_lib.plr_layout_segment(self._h, k, _c.byref(s), _c.byref(so), _c.byref(do),
+                                        _c.byref(ln)), "plr_layout_segment")
+            out.append((s.value, so.value, do.value, ln.value))
+        return out
+
+    def policy(self) -> dict:
+        cb, wg, bl, un, st, dp = _sz(), _i(), _i(), _i(), _i(), _i()
+        _ok(_lib.plr_layout_policy(self._h, _c.byref(cb), _c.byref(wg), _c.byref(bl), _c.byref(un),
+                                   _c.byref(st), _c.byref(dp)), "plr_layout_policy")
+        return dict(chunk_bytes=cb.value, workgroups=wg.value, block=bl.value, unroll=un.value,
+                    stages=st.value, datapath=dp.value)
+
+
+def plr_layout_create(op, dtype, world, bytes_per_src, in_kind, out_kind, rank=0,
+                      in_offsets=None, out_offsets=None, mode=PLR_MODE_DETERMINISTIC,
+                      chunk_bytes=0, workgroups=0, block=0, unroll=0, stages=0, datapath=0,
+                      spin_limit=0) -> Layout:
+    """Compile a layout. op/dtype/kinds accept the C enum values or their names."""
+    d = plr_layout_desc()
+    d.op = OP_CODES.get(op, op)
+    d.dtype = DTYPE_CODES.get(dtype, dtype)
+    d.world, d.rank, d.bytes_per_src = world, rank, bytes_per_src
+    d.in_kind = KIND_CODES.get(in_kind, in_kind)
+    d.out_kind = KIND_CODES.get(out_kind, out_kind)
+    keep = []
+    if in_offsets is not None:
+        a = (_sz * len(in_offsets))(*in_offsets)
+        keep.append(a)
+        d.in_offsets = _c.cast(a, _c.POINTER(_sz))
+    if out_offsets is not None:
+        a = (_sz * len(out_offsets))(*out_offsets)
+        keep.append(a)
+        d.out_offsets = _c.cast(a, _c.POINTER(_sz))
+    d.mode, d.chunk_bytes, d.workgroups = mode, chunk_bytes, workgroups
+    d.block, d.unroll, d.stages, d.datapath, d.spin_limit = block, unroll, stages, datapath, spin_limit
+    h = _vp()
+    _ok(_lib.plr_layout_create(_c.byref(d), _c.byref(h)), "plr_layout_create")
+    return Layout(h.value)
+
+
+def plr_layout_destroy(layout: Layout) -> None:
+    layout.__del__()
+
+
+def plr_reduce(layout: Layout, srcs, dst, workspace=None, stream=None) -> None:
+    _ok(_lib.plr_reduce(layout.handle, _ptrs(srcs), _addr(dst), _addr(workspace), _stream(stream)),
+        "plr_reduce")
+
+
+def plr_copy(layout: Layout, srcs, dst, workspace=None, stream=None) -> None:
+    _ok(_lib.plr_copy(layout.handle, _ptrs(srcs), _addr(dst), _addr(workspace), _stream(stream)),
+        "plr_copy")
+
+
+def plr_copy_v_scratch_bytes(world: int, rows_per_src) -> int:
+    rows = (_c.c_int64 * world)(*rows_per_src)
+    return _lib.plr_copy_v_scratch_bytes(world, rows)
+
+
+def plr_copy_v(srcs, rows_per_src, dest_of_row, row_bytes, dst, counts, offsets, scratch,
+               stream=None) -> None:
+    W = len(srcs)
+    rows = (_c.c_int64 * W)(*rows_per_src)
+    _ok(_lib.plr_copy_v(W, _ptrs(srcs), rows, _ptrs(dest_of_row), row_bytes, _addr(dst),
+                        _addr(counts), _addr(offsets), _addr(scratch), _stream(stream)), "plr_copy_v")
+
+
+def plr_notify(layout: Layout, src: int, workspace, stream=None) -> None:
+    _ok(_lib.plr_notify(layout.handle, src, _addr(workspace), _stream(stream)), "plr_notify")
+
+
+def plr_check(layout: Layout, workspace, stream=None) -> int:
+    """Returns the sticky device error code (PLR_OK or PLR_ETIMEOUT) and clears it."""
+    return _lib.plr_check(layout.handle, _addr(workspace), _stream(stream))

@@ -1,0 +1,239 @@
+// C ABI entry points: validation, kernel argument marshalling, launch, epoch advance.
+// Every step of the datapath runs in the HIP kernels; this file only checks
+// arguments on the host and fills the kernel argument blocks.
+#include <hip/hip_runtime_api.h>
+
+#include <algorithm>
+#include <atomic>
+
+#include "kernels.h"
+#include "layout.h"
+
+using namespace plr;
+
+namespace {
+
+thread_local int g_last_hip = 0;
+
+int hip_fail(hipError_t e) {
+  g_last_hip = (int)e;
+  return PLR_EHIP;
+}
+
+bool a16(const void* p) { return ((uintptr_t)p & 15) == 0; }
+
+bool overlaps(uintptr_t a0, uint64_t alen, uintptr_t b0, uint64_t blen) {
+  return alen && blen && a0 < b0 + blen && b0 < a0 + alen;
+}
+
+// Compute units of the current device, cached per device id.
+std::atomic<int> g_cu_cache[64];
+
+int cu_count() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  int v = g_cu_cache[dev].load(std::memory_order_relaxed);
+  if (v > 0) return v;
+  int n = 0;
+  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+    n = 256;
+  g_cu_cache[dev].store(n, std::memory_order_relaxed);
+  return n;
+}
+
+uint32_t grid_for(const plr_layout* L) {
+  if (L->workgroups > 0) return (uint32_t)L->workgroups;
+  uint64_t g = L->nchunks;
+  if (L->wg_per_cu > 0) g = std::min<uint64_t>(g, (uint64_t)cu_count() * L->wg_per_cu);
+  return (uint32_t)std::max<uint64_t>(g, 1);
+}
+
+Launch launch_of(const plr_layout* L) {
+  return Launch{grid_for(L), (uint32_t)L->block, L->unroll, L->stages, L->datapath};
+}
+
+// Common checks of plr_reduce / plr_copy. Fills the notification block.
+int check_call(const plr_layout* L, plr_op op, const void* const* srcs, const void* dst,
+               void* workspace, Notify* nt) {
+  if (!L || L->op != op || !srcs || !dst) return PLR_EINVAL;
+  if (!a16(dst)) return PLR_EALIGN;
+  for (int w = 0; w < L->world; ++w) {
+    if (!srcs[w]) return PLR_EINVAL;
+    if (!a16(srcs[w])) return PLR_EALIGN;
+  }
+  // the output must not overlap anything the call reads
+  for (const auto& s : L->segs)
+    if (overlaps((uintptr_t)dst, L->dst_bytes, (uintptr_t)srcs[s.src] + s.src_off, s.len))
+      return PLR_EINVAL;
+  nt->flags = nullptr;
+  nt->err = nullptr;
+  nt->epoch = L->epoch + 1;
+  nt->spin_limit = L->spin_limit;
+  if (workspace) {
+    if (!a16(workspace)) return PLR_EALIGN;
+    nt->err = static_cast<uint64_t*>(workspace);
+    nt->flags = reinterpret_cast<const uint64_t*>(static_cast<char*>(workspace) + kWorkspaceHeader);
+  }
+  return PLR_OK;
+}
+
+}  // namespace
+
+extern "C" int plr_reduce(plr_layout* L, const void* const* srcs, void* dst, void* workspace,
+                          void* stream) {
+  Notify nt;
+  int rc = check_call(L, PLR_OP_REDUCE, srcs, dst, workspace, &nt);
+  if (rc) return rc;
+  if (L->nchunks) {
+    ReduceArgs a{};
+    for (int w = 0; w < L->world; ++w)
+      a.src[w] = reinterpret_cast<const u32x4*>(static_cast<const char*>(srcs[w]) + L->segs[w].src_off);
+    a.dst = static_cast<u32x4*>(dst);
+    a.nvec = L->seg_len / 16;
+    a.chunk_vecs = L->chunk_bytes / 16;
+    a.nchunks = L->nchunks;
+    a.world = (uint32_t)L->world;
+    a.nt = nt;
+    hipError_t e = launch_reduce(a, L->dtype, launch_of(L), static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return hip_fail(e);
+  }
+  if (workspace) L->epoch = nt.epoch;
+  return PLR_OK;
+}
+
+extern "C" int plr_copy(plr_layout* L, const void* const* srcs, void* dst, void* workspace,
+                        void* stream) {
+  Notify nt;
+  int rc = check_call(L, PLR_OP_COPY, srcs, dst, workspace, &nt);
+  if (rc) return rc;
+  if (L->nchunks) {
+    CopyArgs a{};
+    for (int w = 0; w < L->world; ++w) a.src[w] = static_cast<const uint8_t*>(srcs[w]);
+    a.dst = static_cast<uint8_t*>(dst);
+    a.seg_len = L->seg_len;
+    a.chunk_bytes = L->chunk_bytes;
+    a.chunks_per_seg = L->chunks_per_seg;
+    a.nseg = (uint32_t)L->segs.size();
+    a.nchunks = L->nchunks;
+    a.world = (uint32_t)L->world;
+    a.nt = nt;
+    if (L->table_fits) {
+      a.mode = kCopyTable;
+      for (size_t k = 0; k < L->segs.size(); ++k) {
+        a.seg_src[k] = (uint32_t)L->segs[k].src;
+        a.seg_src_off[k] = L->segs[k].src_off;
+        a.seg_dst_off[k] = L->segs[k].dst_off;
+      }
+    } else {  // only derived AllToAll tables exceed the kernarg table
+      a.mode = kCopyTransposed;
+      a.slice = L->seg_len;
+    }
+    hipError_t e = launch_copy(a, launch_of(L), static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return hip_fail(e);
+  }
+  if (workspace) L->epoch = nt.epoch;
+  return PLR_OK;
+}
+
+extern "C" size_t plr_copy_v_scratch_bytes(int world, const int64_t* rows_per_src) {
+  if (world < 1 || world > PLR_MAX_WORLD || !rows_per_src) return 0;
+  uint64_t total = 0;
+  for (int s = 0; s < world; ++s) total += rows_per_src[s] > 0 ? (uint64_t)rows_per_src[s] : 0;
+  const uint64_t bytes = total * sizeof(int32_t);
+  return (size_t)std::max<uint64_t>(256, (bytes + 255) & ~255ull);
+}
+
+extern "C" int plr_copy_v(int world, const void* const* srcs, const int64_t* rows_per_src,
+                          const int32_t* const* dest_of_row, size_t row_bytes, void* dst,
+                          int64_t* counts, int64_t* offsets, void* scratch, void* stream) {
+  if (world < 1) return PLR_EINVAL;
+  if (world > PLR_MAX_WORLD) return PLR_EUNSUPPORTED;
+  if (!srcs || !rows_per_src || !dest_of_row || !counts || !offsets || !scratch) return PLR_EINVAL;
+  if (row_bytes == 0) return PLR_EINVAL;
+  if (row_bytes % 16) return PLR_EALIGN;
+  if (((uintptr_t)counts & 7) || ((uintptr_t)offsets & 7) || !a16(scratch)) return PLR_EALIGN;
+  CopyVArgs a{};
+  a.row_start[0] = 0;
+  for (int s = 0; s < world; ++s) {
+    if (rows_per_src[s] < 0) return PLR_EINVAL;
+    if (rows_per_src[s] > 0) {
+      if (!srcs[s] || !dest_of_row[s] || !dst) return PLR_EINVAL;
+      if (!a16(srcs[s])) return PLR_EALIGN;
+      if ((uintptr_t)dest_of_row[s] & 3) return PLR_EALIGN;
+    }
+    a.src[s] = static_cast<const uint8_t*>(srcs[s]);
+    a.dest[s] = dest_of_row[s];
+    a.row_start[s + 1] = a.row_start[s] + rows_per_src[s];
+  }
+  const int64_t total = a.row_start[world];
+  for (int s = world + 1; s <= PLR_MAX_WORLD; ++s) a.row_start[s] = total;
+  if (total > 0x7FFFFFFF) return PLR_EUNSUPPORTED;  // ranks are int32
+  if (total > 0) {
+    if (!a16(dst)) return PLR_EALIGN;
+    const uint64_t out_bytes = (uint64_t)total * row_bytes;
+    for (int s = 0; s < world; ++s)
+      if (overlaps((uintptr_t)dst, out_bytes, (uintptr_t)srcs[s], (uint64_t)rows_per_src[s] * row_bytes))
+        return PLR_EINVAL;
+  }
+  a.dst = static_cast<uint8_t*>(dst);
+  a.counts = counts;
+  a.offsets = offsets;
+  a.rank = static_cast<int32_t*>(scratch);
+  a.row_bytes = row_bytes;
+  a.world = (uint32_t)world;
+  const uint64_t waves_needed = ((uint64_t)total + 3) / 4;
+  const uint32_t grid =
+      (uint32_t)std::max<uint64_t>(1, std::min<uint64_t>(waves_needed, (uint64_t)cu_count() * 8));
+  hipError_t e = launch_copy_v(a, grid, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e);
+  return PLR_OK;
+}
+
+extern "C" int plr_notify(plr_layout* L, int src, void* workspace, void* stream) {
+  if (!L || !workspace) return PLR_EINVAL;
+  if (src < -1 || src >= L->world) return PLR_EINVAL;
+  if (!a16(workspace)) return PLR_EALIGN;
+  if (L->nchunks == 0) return PLR_OK;
+  NotifyArgs a{};
+  uint64_t* flags = reinterpret_cast<uint64_t*>(static_cast<char*>(workspace) + kWorkspaceHeader);
+  a.flags = src < 0 ? flags : flags + (uint64_t)src * L->nchunks;
+  a.nflags = src < 0 ? (uint64_t)L->world * L->nchunks : L->nchunks;
+  a.epoch = L->epoch + 1;
+  hipError_t e = launch_notify(a, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e);
+  return PLR_OK;
+}
+
+extern "C" int plr_check(plr_layout* L, void* workspace, void* stream) {
+  if (!L || !workspace) return PLR_EINVAL;
+  if (!a16(workspace)) return PLR_EALIGN;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  uint64_t v = 0;
+  hipError_t e = hipMemcpyAsync(&v, workspace, sizeof(v), hipMemcpyDeviceToHost, s);
+  if (e == hipSuccess) e = hipStreamSynchronize(s);
+  if (e != hipSuccess) return hip_fail(e);
+  if (v != 0) {
+    const uint64_t zero = 0;
+    e = hipMemcpyAsync(workspace, &zero, sizeof(zero), hipMemcpyHostToDevice, s);
+    if (e == hipSuccess) e = hipStreamSynchronize(s);
+    if (e != hipSuccess) return hip_fail(e);
+    return v == PLR_ETIMEOUT ? PLR_ETIMEOUT : PLR_EINVAL;
+  }
+  return PLR_OK;
+}
+
+extern "C" const char* plr_strerror(int code) {
+  switch (code) {
+    case PLR_OK: return "success";
+    case PLR_EINVAL: return "invalid argument";
+    case PLR_EALIGN: return "address or byte count not a multiple of 16";
+    case PLR_EUNSUPPORTED: return "unsupported configuration";
+    case PLR_EHIP: return "HIP runtime error";
+    case PLR_ETIMEOUT: return "chunk notification timed out";
+    default: return "unknown error";
+  }
+}
+
+extern "C" int plr_last_hip_error(void) { return g_last_hip; }
+
+extern "C" const char* plr_version(void) { return "plr 0.1.0 gfx950"; }

@@ -1,0 +1,143 @@
+// Device helpers shared by the kernels: 16-byte vector access, element conversions,
+// and the consumer side of chunk notification.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "kernels.h"
+
+namespace plr {
+
+__device__ __forceinline__ u32x4 ld16(const u32x4* p) { return __builtin_nontemporal_load(p); }
+__device__ __forceinline__ u32x4 ld16_cached(const u32x4* p) { return *p; }
+__device__ __forceinline__ void st16(u32x4* p, u32x4 v) { __builtin_nontemporal_store(v, p); }
+
+// ---- element types inside one 16-byte vector ----
+// Element j of a vector is at bits [16j, 16j+16) of the little-endian 128-bit word
+// (32j for fp32). Widening is exact; narrowing is one round-to-nearest-even.
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+template <int DT>
+struct Elems;
+
+template <>
+struct Elems<PLR_BF16> {
+  static constexpr int N = 8;
+  __device__ static __forceinline__ void widen(u32x4 v, float* f) {
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      f[2 * k] = __uint_as_float(v[k] << 16);
+      f[2 * k + 1] = __uint_as_float(v[k] & 0xFFFF0000u);
+    }
+  }
+  __device__ static __forceinline__ u32x4 narrow(const float* f) {
+    u32x4 r;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      bf16x2 b = __builtin_convertvector((f32x2){f[2 * k], f[2 * k + 1]}, bf16x2);
+      r[k] = __builtin_bit_cast(uint32_t, b);
+    }
+    return r;
+  }
+};
+
+template <>
+struct Elems<PLR_F16> {
+  static constexpr int N = 8;
+  // Scalar conversions with explicit bit packing: v_cvt_f32_f16 widens exactly and
+  // v_cvt_f16_f32 rounds to nearest even (denormals kept, the kernels' float mode).
+  __device__ static __forceinline__ void widen(u32x4 v, float* f) {
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      f[2 * k] = (float)__builtin_bit_cast(_Float16, (uint16_t)(v[k] & 0xFFFFu));
+      f[2 * k + 1] = (float)__builtin_bit_cast(_Float16, (uint16_t)(v[k] >> 16));
+    }
+  }
+  __device__ static __forceinline__ u32x4 narrow(const float* f) {
+    u32x4 r;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const uint32_t lo = __builtin_bit_cast(uint16_t, (_Float16)f[2 * k]);
+      const uint32_t hi = __builtin_bit_cast(uint16_t, (_Float16)f[2 * k + 1]);
+      r[k] = lo | (hi << 16);
+    }
+    return r;
+  }
+};
+
+template <>
+struct Elems<PLR_F32> {
+  static constexpr int N = 4;
+  __device__ static __forceinline__ void widen(u32x4 v, float* f) {
+#pragma unroll
+    for (int k = 0; k < 4; ++k) f[k] = __uint_as_float(v[k]);
+  }
+  __device__ static __forceinline__ u32x4 narrow(const float* f) {
+    u32x4 r;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) r[k] = __float_as_uint(f[k]);
+    return r;
+  }
+};
+
+// SCORE combine (section 3.3): one lane owns the vector's elements and adds the W
+// sources into a binary32 accumulator in source order, starting from source 0.
+template <int DT, int W>
+__device__ __forceinline__ u32x4 combine(const u32x4* x) {
+  constexpr int N = Elems<DT>::N;
+  float acc[N];
+  Elems<DT>::widen(x[0], acc);
+#pragma unroll
+  for (int w = 1; w < W; ++w) {
+    float t[N];
+    Elems<DT>::widen(x[w], t);
+#pragma unroll
+    for (int j = 0; j < N; ++j) acc[j] = acc[j] + t[j];
+  }
+  return Elems<DT>::narrow(acc);
+}
+
+// ---- consumer side of notify (section 3.2) ----
+// Lanes 0..n-1 of the calling wave each poll one flag (first + lane*stride) until it
+// reaches nt.epoch, with a bounded number of polls. Returns true when every flag
+// arrived; the acquire fence then orders the wave's later loads after the producer's
+// release. On a timeout one lane records PLR_ETIMEOUT in the sticky error word;
+// if another wave already recorded an error the wave gives up too. All lanes of the
+// wave must call this together.
+__device__ __forceinline__ bool wait_flags(const Notify& nt, const uint64_t* first, uint64_t stride,
+                                           int n) {
+  const int lane = __lane_id();
+  int bad = 0;
+  if (lane < n) {
+    const uint64_t* f = first + (uint64_t)lane * stride;
+    uint64_t polls = 0;
+    while (__hip_atomic_load(f, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < nt.epoch) {
+      if (++polls >= nt.spin_limit) {
+        bad = 1;
+        break;
+      }
+      if ((polls & 63) == 0 &&
+          __hip_atomic_load(nt.err, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0) {
+        bad = 2;
+        break;
+      }
+      __builtin_amdgcn_s_sleep(2);
+    }
+  }
+  const uint64_t timed_out = __ballot(bad == 1);
+  const uint64_t failed = __ballot(bad != 0);
+  if (failed) {
+    if (timed_out && lane == __builtin_ctzll(timed_out)) {
+      uint64_t expect = 0;
+      __hip_atomic_compare_exchange_strong(nt.err, &expect, (uint64_t)PLR_ETIMEOUT, __ATOMIC_RELAXED,
+                                           __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    return false;
+  }
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+  return true;
+}
+
+}  // namespace plr

@@ -1,0 +1,97 @@
+// Kernel argument blocks and launchers shared by the host library and the HIP kernels.
+// Every struct is passed by value as the kernel argument (kernarg segment), so the
+// kernels read layout tables and pointers through the scalar cache.
+#pragma once
+
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#include "plr.h"
+
+namespace plr {
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));  // one 16-byte vector
+
+constexpr int kMaxTableSegs = 64;   // explicit segment table carried in kernarg
+constexpr size_t kWorkspaceHeader = 256;
+constexpr uint64_t kDefaultSpinLimit = 1ull << 20;
+
+// Datapath variants of one launch.
+struct Launch {
+  uint32_t grid;
+  uint32_t block;
+  int unroll;
+  int stages;
+  int datapath;  // PLR_PATH_DIRECT or PLR_PATH_LDS
+};
+
+// Notification state of one consuming launch (section 3.2, SNAC "notify").
+struct Notify {
+  const uint64_t* flags;  // [W][nchunks], or nullptr when the call is not notified
+  uint64_t* err;          // sticky error word (workspace header), or nullptr
+  uint64_t epoch;         // a chunk may be consumed once its flags are >= epoch
+  uint64_t spin_limit;    // polls before giving up with PLR_ETIMEOUT
+};
+
+struct ReduceArgs {
+  const u32x4* src[PLR_MAX_WORLD];  // start of the share inside each source
+  u32x4* dst;
+  uint64_t nvec;        // 16-byte vectors in the share
+  uint64_t chunk_vecs;  // vectors per chunk
+  uint32_t nchunks;
+  uint32_t world;
+  Notify nt;
+};
+
+// Copy segments: all segments of one layout have the same length (seg_len bytes).
+// Segment k reads source seg_src[k] at seg_src_off[k] and writes dst at seg_dst_off[k].
+// Layouts with more than kMaxTableSegs segments (AllToAll with W > 8) use the
+// transposed formula instead of the table: k = s*W + d, src_off = d*slice,
+// dst_off = (d*W + s)*slice.
+enum CopyMode : uint32_t { kCopyTable = 0, kCopyTransposed = 1 };
+
+struct CopyArgs {
+  const uint8_t* src[PLR_MAX_WORLD];
+  uint8_t* dst;
+  uint64_t seg_len;
+  uint64_t chunk_bytes;
+  uint32_t chunks_per_seg;
+  uint32_t nseg;
+  uint32_t nchunks;
+  uint32_t world;
+  uint32_t mode;
+  uint32_t pad;
+  uint64_t slice;  // kCopyTransposed: bytes per slice
+  Notify nt;
+  uint32_t seg_src[kMaxTableSegs];
+  uint64_t seg_src_off[kMaxTableSegs];
+  uint64_t seg_dst_off[kMaxTableSegs];
+};
+
+struct CopyVArgs {
+  const uint8_t* src[PLR_MAX_WORLD];
+  const int32_t* dest[PLR_MAX_WORLD];
+  int64_t row_start[PLR_MAX_WORLD + 1];  // prefix of rows_per_src
+  uint8_t* dst;
+  int64_t* counts;   // [s][d]
+  int64_t* offsets;  // [d][s]
+  int32_t* rank;     // scratch: rank of each row inside its (source, destination) block
+  uint64_t row_bytes;
+  uint32_t world;
+  uint32_t pad;
+};
+
+struct NotifyArgs {
+  uint64_t* flags;
+  uint64_t nflags;  // flags to store, starting at `flags`
+  uint64_t epoch;
+};
+
+// Launchers (defined next to their kernels). Return a hipError_t.
+hipError_t launch_reduce(const ReduceArgs& a, int dtype, const Launch& l, hipStream_t s);
+hipError_t launch_copy(const CopyArgs& a, const Launch& l, hipStream_t s);
+hipError_t launch_copy_v(const CopyVArgs& a, uint32_t scatter_grid, hipStream_t s);
+hipError_t launch_notify(const NotifyArgs& a, hipStream_t s);
+
+}  // namespace plr

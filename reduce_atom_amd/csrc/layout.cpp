@@ -1,0 +1,223 @@
+// Layout compile (host only): a collective specification becomes a segment table, a
+// chunk count and a resolved launch policy.
+//
+// Purlin paper, section 3.1 "Layouts": a collective is a naming of an input and an
+// output layout plus copy or reduce; the kinds are packed, scattered and transposed.
+// Section 3.2 "SNAC" derives the rank dependencies from the layouts: here that is the
+// table saying which (source, offset) feeds which output range. Section 4.2 "Codesign
+// Policies and Tuning": chunk sizes, workgroup counts and pipeline depths come from a
+// per-GPU table that callers may override.
+#include "layout.h"
+
+#include <algorithm>
+#include <new>
+
+#include "kernels.h"
+
+namespace plr {
+
+size_t elem_bytes(plr_dtype t) { return t == PLR_F32 ? 4 : 2; }
+
+// gfx950 policy table. Two regimes, as on the pages (latency-bound decode versus
+// throughput-bound prefill): small shares launch one short pipeline step per
+// workgroup on as many compute units as it takes, so every load is in flight at
+// once; large shares use 64 KiB chunks per source and a grid of a few workgroups
+// per compute unit striding over the chunks.
+static void default_policy(plr_layout* L) {
+  L->stages = 2;
+  L->datapath = PLR_PATH_DIRECT;
+  L->workgroups = 0;
+  if (L->op == PLR_OP_REDUCE) {
+    if (L->seg_len <= (2u << 20)) {  // latency regime
+      L->block = 64;
+      L->unroll = 1;
+      L->chunk_bytes = (uint64_t)L->block * 16 * L->unroll;
+      L->wg_per_cu = 0;  // one workgroup per chunk
+    } else {
+      L->block = 256;
+      L->unroll = 2;
+      L->chunk_bytes = 64u << 10;
+      L->wg_per_cu = 8;
+    }
+  } else {
+    L->block = 256;
+    L->unroll = 4;
+    L->chunk_bytes = 64u << 10;
+    L->wg_per_cu = 8;
+  }
+}
+
+}  // namespace plr
+
+using namespace plr;
+
+static bool aligned16(uint64_t x) { return (x & 15) == 0; }
+
+extern "C" int plr_layout_create(const plr_layout_desc* d, plr_layout** out) {
+  if (!d || !out) return PLR_EINVAL;
+  *out = nullptr;
+  if (d->world < 1) return PLR_EINVAL;
+  if (d->world > PLR_MAX_WORLD) return PLR_EUNSUPPORTED;
+  if (d->mode != PLR_MODE_DETERMINISTIC) return PLR_EUNSUPPORTED;
+  if (d->op != PLR_OP_REDUCE && d->op != PLR_OP_COPY) return PLR_EINVAL;
+  if (d->dtype != PLR_BF16 && d->dtype != PLR_F16 && d->dtype != PLR_F32) return PLR_EINVAL;
+  if (d->in_kind < PLR_PACKED || d->in_kind > PLR_TRANSPOSED) return PLR_EINVAL;
+  if (d->out_kind < PLR_PACKED || d->out_kind > PLR_TRANSPOSED) return PLR_EINVAL;
+  if (!aligned16(d->bytes_per_src)) return PLR_EALIGN;
+
+  plr_layout* L = new (std::nothrow) plr_layout();
+  if (!L) return PLR_EINVAL;
+  L->op = d->op;
+  L->dtype = d->dtype;
+  L->world = d->world;
+  L->rank = d->rank;
+  L->bytes_per_src = d->bytes_per_src;
+  L->in_kind = d->in_kind;
+  L->out_kind = d->out_kind;
+  L->epoch = 0;
+
+  const int W = d->world;
+  const uint64_t B = d->bytes_per_src;
+  auto fail = [&](int code) {
+    delete L;
+    return code;
+  };
+
+  if (d->op == PLR_OP_REDUCE) {
+    if (d->out_kind != PLR_PACKED || d->out_offsets) return fail(PLR_EINVAL);
+    uint64_t share, off;
+    if (d->in_kind == PLR_PACKED) {
+      share = B;
+      off = 0;
+    } else if (d->in_kind == PLR_SCATTERED) {
+      if (d->rank < 0 || d->rank >= W) return fail(PLR_EINVAL);
+      if (B % (16ull * W)) return fail(PLR_EALIGN);
+      share = B / W;
+      off = (uint64_t)d->rank * share;
+    } else {
+      return fail(PLR_EINVAL);
+    }
+    for (int w = 0; w < W; ++w) {
+      const uint64_t o = d->in_offsets ? d->in_offsets[w] : off;
+      if (!aligned16(o)) return fail(PLR_EALIGN);
+      L->segs.push_back({w, o, 0, share});
+    }
+    L->seg_len = share;
+    L->dst_bytes = share;
+  } else {
+    if (d->in_kind == PLR_PACKED && d->out_kind == PLR_PACKED) {  // AllGather
+      for (int s = 0; s < W; ++s) L->segs.push_back({s, 0, (uint64_t)s * B, B});
+      L->seg_len = B;
+    } else if (d->in_kind == PLR_SCATTERED &&
+               (d->out_kind == PLR_TRANSPOSED || d->out_kind == PLR_SCATTERED)) {
+      if (B % (16ull * W)) return fail(PLR_EALIGN);
+      const uint64_t t = B / W;
+      if (d->out_kind == PLR_TRANSPOSED) {  // AllToAll: out slice (d, s) = in slice (s, d)
+        for (int s = 0; s < W; ++s)
+          for (int dd = 0; dd < W; ++dd)
+            L->segs.push_back({s, (uint64_t)dd * t, ((uint64_t)dd * W + s) * t, t});
+      } else {  // gather half of AllReduce: out slice s = slice s of source s
+        for (int s = 0; s < W; ++s) L->segs.push_back({s, (uint64_t)s * t, (uint64_t)s * t, t});
+      }
+      L->seg_len = t;
+    } else {
+      return fail(PLR_EINVAL);
+    }
+    const size_t nseg = L->segs.size();
+    if ((d->in_offsets || d->out_offsets) && nseg > (size_t)kMaxTableSegs)
+      return fail(PLR_EUNSUPPORTED);
+    for (size_t k = 0; k < nseg; ++k) {
+      if (d->in_offsets) L->segs[k].src_off = d->in_offsets[k];
+      if (d->out_offsets) L->segs[k].dst_off = d->out_offsets[k];
+      if (!aligned16(L->segs[k].src_off) || !aligned16(L->segs[k].dst_off)) return fail(PLR_EALIGN);
+    }
+    // output segments must not overlap (two writers of one byte would race)
+    std::vector<std::pair<uint64_t, uint64_t>> iv;
+    for (auto& s : L->segs) iv.push_back({s.dst_off, s.dst_off + s.len});
+    std::sort(iv.begin(), iv.end());
+    L->dst_bytes = 0;
+    for (size_t k = 0; k < iv.size(); ++k) {
+      if (k && iv[k].first < iv[k - 1].second) return fail(PLR_EINVAL);
+      L->dst_bytes = std::max<uint64_t>(L->dst_bytes, iv[k].second);
+    }
+    L->table_fits = nseg <= (size_t)kMaxTableSegs;
+  }
+
+  // policy: built-in table, then the caller's overrides
+  default_policy(L);
+  if (d->chunk_bytes) {
+    if (!aligned16(d->chunk_bytes)) return fail(PLR_EALIGN);
+    L->chunk_bytes = d->chunk_bytes;
+  }
+  if (d->workgroups < 0) return fail(PLR_EINVAL);
+  if (d->workgroups) L->workgroups = d->workgroups;
+  if (d->block) {
+    if (d->block != 64 && d->block != 128 && d->block != 256 && d->block != 512) return fail(PLR_EINVAL);
+    L->block = d->block;
+  }
+  if (d->unroll) {
+    if (d->unroll != 1 && d->unroll != 2 && d->unroll != 4) return fail(PLR_EINVAL);
+    L->unroll = d->unroll;
+  }
+  if (d->stages) {
+    if (d->stages < 1 || d->stages > 4) return fail(PLR_EINVAL);
+    L->stages = d->stages;
+  }
+  if (d->datapath) {
+    if (d->datapath != PLR_PATH_DIRECT && d->datapath != PLR_PATH_LDS) return fail(PLR_EINVAL);
+    if (d->datapath == PLR_PATH_LDS) return fail(PLR_EUNSUPPORTED);
+    L->datapath = d->datapath;
+  }
+  L->spin_limit = d->spin_limit ? d->spin_limit : kDefaultSpinLimit;
+
+  // chunk table
+  if (L->seg_len == 0) {
+    L->chunks_per_seg = 0;
+    L->nchunks = 0;
+  } else {
+    const uint64_t cb = std::min<uint64_t>(L->chunk_bytes, L->seg_len);
+    L->chunk_bytes = cb;
+    const uint64_t cps = (L->seg_len + cb - 1) / cb;
+    const uint64_t n = L->op == PLR_OP_REDUCE ? cps : cps * L->segs.size();
+    if (n > 0xFFFFFFFFull) return fail(PLR_EUNSUPPORTED);
+    L->chunks_per_seg = (uint32_t)cps;
+    L->nchunks = (uint32_t)n;
+  }
+  *out = L;
+  return PLR_OK;
+}
+
+extern "C" void plr_layout_destroy(plr_layout* L) { delete L; }
+
+extern "C" size_t plr_layout_workspace_bytes(const plr_layout* L) {
+  if (!L) return 0;
+  return kWorkspaceHeader + (size_t)L->world * L->nchunks * sizeof(uint64_t);
+}
+
+extern "C" size_t plr_layout_dst_bytes(const plr_layout* L) { return L ? L->dst_bytes : 0; }
+extern "C" int plr_layout_nchunks(const plr_layout* L) { return L ? (int)L->nchunks : -1; }
+extern "C" int plr_layout_nsegments(const plr_layout* L) { return L ? (int)L->segs.size() : -1; }
+extern "C" uint64_t plr_layout_epoch(const plr_layout* L) { return L ? L->epoch : 0; }
+
+extern "C" int plr_layout_segment(const plr_layout* L, int k, int* src, size_t* src_off,
+                                  size_t* dst_off, size_t* len) {
+  if (!L || k < 0 || k >= (int)L->segs.size()) return PLR_EINVAL;
+  const auto& s = L->segs[k];
+  if (src) *src = s.src;
+  if (src_off) *src_off = s.src_off;
+  if (dst_off) *dst_off = s.dst_off;
+  if (len) *len = s.len;
+  return PLR_OK;
+}
+
+extern "C" int plr_layout_policy(const plr_layout* L, size_t* chunk_bytes, int* workgroups,
+                                 int* block, int* unroll, int* stages, int* datapath) {
+  if (!L) return PLR_EINVAL;
+  if (chunk_bytes) *chunk_bytes = L->chunk_bytes;
+  if (workgroups) *workgroups = L->workgroups;
+  if (block) *block = L->block;
+  if (unroll) *unroll = L->unroll;
+  if (stages) *stages = L->stages;
+  if (datapath) *datapath = L->datapath;
+  return PLR_OK;
+}

@@ -1,0 +1,25 @@
+// Producer side of notify (Purlin paper, section 3.2 "SNAC": a stage is announced by
+// a flag; section 4.3 "Epoch Bookkeeping": a monotonic 64-bit epoch supplies the
+// value). One release fence per wave orders everything this stream already did
+// before the flag stores, which are agent-scope atomics so that consumers on any
+// XCD observe them.
+#include "device_common.h"
+
+namespace plr {
+
+__global__ void __launch_bounds__(256) k_notify(const NotifyArgs a) {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+  const uint64_t stride = (uint64_t)gridDim.x * blockDim.x;
+  for (uint64_t i = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x; i < a.nflags; i += stride)
+    __hip_atomic_store(a.flags + i, a.epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+hipError_t launch_notify(const NotifyArgs& a, hipStream_t s) {
+  uint64_t blocks = (a.nflags + 255) / 256;
+  if (blocks < 1) blocks = 1;
+  if (blocks > 256) blocks = 256;
+  hipLaunchKernelGGL(k_notify, dim3((uint32_t)blocks), dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+}  // namespace plr

@@ -1,0 +1,95 @@
+"""Parity of plr_copy_v (HIP, through the C ABI) with the oracle: output rows, counts
+and offsets bitwise."""
+import numpy as np
+import pytest
+import torch
+
+import synth
+from conftest import golden_lines
+from plrtest import to_dev
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def plr():
+    assert torch.cuda.is_available(), "the GPU tests need a GPU"
+    import reduce_atom_amd
+
+    return reduce_atom_amd
+
+
+def _run(plr, srcs_np, dests_np, row_bytes):
+    W = len(srcs_np)
+    rows = [int(d.size) for d in dests_np]
+    srcs = [to_dev(s) for s in srcs_np]
+    dests = [torch.from_numpy(np.ascontiguousarray(d, dtype=np.int32).copy()).cuda()
+             if d.size else torch.zeros(4, dtype=torch.int32, device="cuda") for d in dests_np]
+    total = sum(rows)
+    dst = torch.full((max(total * row_bytes, 16),), 0x77, dtype=torch.uint8, device="cuda")
+    counts = torch.full((W * W,), -1, dtype=torch.int64, device="cuda")
+    offsets = torch.full((W * W,), -1, dtype=torch.int64, device="cuda")
+    scratch = torch.empty(plr.plr_copy_v_scratch_bytes(W, rows), dtype=torch.uint8, device="cuda")
+    plr.plr_copy_v(srcs, rows, dests, row_bytes, dst, counts, offsets, scratch)
+    torch.cuda.synchronize()
+    return (dst.cpu().numpy()[:total * row_bytes], counts.cpu().numpy().reshape(W, W),
+            offsets.cpu().numpy().reshape(W, W))
+
+
+def _check(plr, oracle_mod, srcs, dests, rb):
+    out, c, o = _run(plr, srcs, dests, rb)
+    ref, rc, ro = oracle_mod.copy_v(srcs, dests, rb)
+    assert np.array_equal(c, rc)
+    assert np.array_equal(o, ro)
+    assert np.array_equal(out, ref)
+
+
+def test_golden_small(plr, oracle_mod):
+    lines = list(golden_lines("copy_v_small.txt"))
+    W = int(lines[0].split()[1])
+    dests = [np.array([int(v) for v in l.split()[2:]], np.int32) for l in lines[1:1 + W]]
+    srcs = [synth.bits_np(0, 5, s, d.size * 32) for s, d in enumerate(dests)]
+    out, c, o = _run(plr, srcs, dests, 32)
+    assert np.array_equal(c.reshape(-1), [int(v) for v in lines[1 + W].split()[1:]])
+    assert np.array_equal(o.reshape(-1), [int(v) for v in lines[2 + W].split()[1:]])
+    order = [tuple(int(v) for v in t.split(":")) for t in lines[3 + W].split()[1:]]
+    rows = out.reshape(-1, 32)
+    for k, (s, i) in enumerate(order):
+        assert np.array_equal(rows[k], srcs[s].reshape(-1, 32)[i])
+
+
+@pytest.mark.parametrize("W,rows_each,rb", [(1, 100, 16), (2, 7, 48), (3, 513, 32), (8, 300, 14336),
+                                            (16, 40, 64), (5, 0, 16)])
+def test_random_zipf(plr, oracle_mod, W, rows_each, rb):
+    rows = [rows_each + (s * 7) % 3 if rows_each else (s % 2) * 5 for s in range(W)]
+    p = synth.zipf_weights(1.1, W)
+    dests = [synth.categorical_np(W, 5, s, rows[s], p) for s in range(W)]
+    srcs = [synth.bits_np(W, 6, s, max(rows[s], 1) * rb) for s in range(W)]
+    _check(plr, oracle_mod, srcs, dests, rb)
+
+
+def test_many_tiles_per_source(plr, oracle_mod):
+    """More rows per source than one rank-kernel tile (4096), uneven across sources."""
+    W, rb = 4, 16
+    rows = [10000, 4096, 4097, 1]
+    dests = [synth.categorical_np(9, 5, s, rows[s], synth.zipf_weights(1.1, W)) for s in range(W)]
+    srcs = [synth.bits_np(9, 6, s, rows[s] * rb) for s in range(W)]
+    _check(plr, oracle_mod, srcs, dests, rb)
+
+
+def test_special_destinations(plr, oracle_mod):
+    W, R, rb = 8, 1000, 32
+    srcs = [synth.bits_np(11, 6, s, R * rb) for s in range(W)]
+    _check(plr, oracle_mod, srcs, [np.zeros(R, np.int32)] * W, rb)
+    _check(plr, oracle_mod, srcs, [(np.arange(R) % W).astype(np.int32)] * W, rb)
+    _check(plr, oracle_mod, srcs, [np.full(R, W - 1, np.int32)] * W, rb)
+
+
+def test_config5_moe_dispatch(plr, oracle_mod):
+    """8 sources x 4096 rows of 7168 bf16, destinations from Zipf(1.1) weights; the
+    whole output, counts and offsets."""
+    W, R, rb = 8, 4096, 7168 * 2
+    p = synth.zipf_weights(1.1, W)
+    dests = [synth.categorical_np(0, 5, s, R, p) for s in range(W)]
+    srcs = [synth.bits_np(0, 6, s, R * rb) for s in range(W)]
+    _check(plr, oracle_mod, srcs, dests, rb)

@@ -1,0 +1,90 @@
+"""The notification protocol (stage / notify / consume) on one GPU: a consumer never
+reads a chunk before its flag, a withheld flag ends in PLR_ETIMEOUT (no hang), and
+epochs keep working across many calls without resetting the workspace."""
+import numpy as np
+import pytest
+import torch
+
+import synth
+from plrtest import assert_same, to_dev
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def plr():
+    assert torch.cuda.is_available(), "the GPU tests need a GPU"
+    import reduce_atom_amd
+
+    return reduce_atom_amd
+
+
+def test_many_calls_without_reset(plr, oracle_mod):
+    W, n = 4, 8192
+    srcs_np = [synth.normal_np(1, 2, w, n) for w in range(W)]
+    ref = oracle_mod.reduce("bf16", srcs_np)
+    srcs = [to_dev(s) for s in srcs_np]
+    L = plr.plr_layout_create("reduce", "bf16", W, 2 * n, "packed", "packed", chunk_bytes=2048)
+    ws = torch.zeros(L.workspace_bytes, dtype=torch.uint8, device="cuda")
+    dst = torch.empty(2 * n, dtype=torch.uint8, device="cuda")
+    for i in range(1000):
+        for w in range(W):
+            plr.plr_notify(L, w, ws)
+        plr.plr_reduce(L, srcs, dst, ws)
+    assert plr.plr_check(L, ws) == plr.PLR_OK
+    assert L.epoch == 1000
+    assert_same("bf16", dst.cpu().numpy().view(np.uint16), ref)
+    flags = ws[256:].view(torch.int64).cpu().numpy()
+    assert (flags == 1000).all()
+
+
+@pytest.mark.parametrize("op", ["reduce", "copy"])
+def test_withheld_notify_times_out(plr, op):
+    W, nbytes = 4, 16384
+    srcs = [torch.zeros(nbytes, dtype=torch.uint8, device="cuda") for _ in range(W)]
+    kinds = ("packed", "packed")
+    L = plr.plr_layout_create(op, "bf16", W, nbytes, *kinds, chunk_bytes=4096, spin_limit=2000)
+    ws = torch.zeros(L.workspace_bytes, dtype=torch.uint8, device="cuda")
+    dst = torch.empty(L.dst_bytes, dtype=torch.uint8, device="cuda")
+    for w in range(W - 1):  # the last source never notifies
+        plr.plr_notify(L, w, ws)
+    (plr.plr_reduce if op == "reduce" else plr.plr_copy)(L, srcs, dst, ws)
+    assert plr.plr_check(L, ws) == plr.PLR_ETIMEOUT
+    assert plr.plr_check(L, ws) == plr.PLR_OK  # read-and-clear
+    # the next epoch works once every source notifies
+    plr.plr_notify(L, -1, ws)
+    (plr.plr_reduce if op == "reduce" else plr.plr_copy)(L, srcs, dst, ws)
+    assert plr.plr_check(L, ws) == plr.PLR_OK
+
+
+def test_delayed_producer_on_another_stream(plr, oracle_mod):
+    """The producer writes poison, waits, writes the real data, then notifies, all on its
+    own stream; the consumer is queued first on another stream and must wait for the
+    flags: its output must be the reduction of the real data, never of the poison."""
+    W, n = 8, 1 << 16
+    real_np = [synth.normal_np(2, 2, w, n) for w in range(W)]
+    ref = oracle_mod.reduce("bf16", real_np)
+    real = [to_dev(s) for s in real_np]
+    srcs = [torch.empty_like(r) for r in real]
+    L = plr.plr_layout_create("reduce", "bf16", W, 2 * n, "packed", "packed", chunk_bytes=4096,
+                              workgroups=4, block=64, spin_limit=1 << 22)
+    ws = torch.zeros(L.workspace_bytes, dtype=torch.uint8, device="cuda")
+    dst = torch.empty(2 * n, dtype=torch.uint8, device="cuda")
+    torch.cuda.synchronize()
+    producer = torch.cuda.Stream()
+    consumer = torch.cuda.Stream()
+    with torch.cuda.stream(producer):
+        for s in srcs:
+            s.fill_(0xFF)  # NaN poison
+    producer.synchronize()
+    with torch.cuda.stream(consumer):
+        plr.plr_reduce(L, srcs, dst, ws)  # waits on flags of epoch 1
+    with torch.cuda.stream(producer):
+        if hasattr(torch.cuda, "_sleep"):
+            torch.cuda._sleep(20_000_000)
+        for s, r in zip(srcs, real):
+            s.copy_(r)
+        plr.plr_notify(L, -1, ws)
+    torch.cuda.synchronize()
+    assert plr.plr_check(L, ws, consumer) == plr.PLR_OK
+    assert_same("bf16", dst.cpu().numpy().view(np.uint16), ref)

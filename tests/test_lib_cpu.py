@@ -1,0 +1,174 @@
+"""Host-side checks of the C-ABI library (no GPU needed): it loads, exports every
+symbol include/plr.h declares, its struct layout matches the binding, and the layout
+compiler, policy and argument validation behave as the header states. No call here
+reaches a kernel launch."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+from conftest import ROOT, golden_lines
+
+
+@pytest.fixture(scope="module")
+def plr():
+    so = os.path.join(ROOT, "reduce_atom_amd", "libplr.so")
+    if not os.path.exists(so):
+        from reduce_atom_amd import _build
+
+        _build.build()
+    import reduce_atom_amd
+
+    return reduce_atom_amd
+
+
+def _declared_functions():
+    text = open(os.path.join(ROOT, "include", "plr.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(plr_\w+)\s*\(", text)))
+
+
+def test_exports_every_declared_symbol(plr):
+    names = _declared_functions()
+    assert len(names) >= 18
+    lib = ctypes.CDLL(plr.LIB_PATH)
+    for n in names:
+        assert hasattr(lib, n), n
+    assert sorted(plr.EXPORTS) == names
+    out = subprocess.run(["nm", "-D", "--defined-only", plr.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    exported = set(re.findall(r" T (plr_\w+)", out))
+    assert exported == set(names)
+
+
+def test_desc_struct_layout_matches_c(plr, tmp_path):
+    fields = [f for f, _ in plr.plr_layout_desc._fields_]
+    prog = tmp_path / "abi.c"
+    prog.write_text("#include <stdio.h>\n#include <stddef.h>\n#include \"plr.h\"\nint main(void){\n"
+                    "printf(\"%zu\\n\", sizeof(plr_layout_desc));\n"
+                    + "".join(f"printf(\"%zu\\n\", offsetof(plr_layout_desc, {f}));\n" for f in fields)
+                    + "return 0;}\n")
+    exe = tmp_path / "abi"
+    subprocess.run(["gcc", "-I", os.path.join(ROOT, "include"), str(prog), "-o", str(exe)], check=True)
+    got = [int(x) for x in subprocess.run([str(exe)], capture_output=True, text=True).stdout.split()]
+    assert got[0] == ctypes.sizeof(plr.plr_layout_desc)
+    assert got[1:] == [getattr(plr.plr_layout_desc, f).offset for f in fields]
+
+
+def test_segments_match_golden(plr):
+    for line in golden_lines("layout_segments.txt"):
+        ik, ok, *segs = line.split()
+        want = sorted(tuple(int(v) for v in s.split(":")) for s in segs)
+        L = plr.plr_layout_create("copy", "bf16", 2, 32, ik, ok)
+        assert sorted(L.segments()) == want, line
+
+
+@pytest.mark.parametrize("W", [1, 2, 3, 8, 9, 16])
+@pytest.mark.parametrize("pair", [("packed", "packed"), ("scattered", "transposed"),
+                                  ("scattered", "scattered")])
+def test_segments_match_oracle_reading(plr, oracle_mod, W, pair):
+    B = 16 * W * 5
+    L = plr.plr_layout_create("copy", "bf16", W, B, *pair)
+    ref, total = oracle_mod.copy_segments(pair[0], pair[1], W, B)
+    assert sorted(L.segments()) == sorted(ref)
+    assert L.dst_bytes == total
+
+
+@pytest.mark.parametrize("W,rank", [(1, 0), (4, 0), (4, 3), (8, 5)])
+def test_reduce_share_segments(plr, oracle_mod, W, rank):
+    B = 16 * W * 7
+    L = plr.plr_layout_create("reduce", "bf16", W, B, "scattered", "packed", rank=rank)
+    offs, n = oracle_mod.reduce_share("scattered", W, rank, B // 2)
+    assert L.segments() == [(w, offs[w] * 2, 0, n * 2) for w in range(W)]
+    assert L.dst_bytes == n * 2
+    P = plr.plr_layout_create("reduce", "f32", W, B, "packed", "packed")
+    assert P.segments() == [(w, 0, 0, B) for w in range(W)]
+
+
+def test_chunks_and_workspace(plr):
+    L = plr.plr_layout_create("reduce", "bf16", 8, 8192 * 7168 * 2, "packed", "packed")
+    pol = L.policy()
+    n = -(-8192 * 7168 * 2 // pol["chunk_bytes"])
+    assert L.nchunks == n
+    assert L.workspace_bytes == 256 + 8 * n * 8
+    C = plr.plr_layout_create("copy", "bf16", 8, 64 << 20, "scattered", "transposed", chunk_bytes=1 << 20)
+    assert C.nchunks == 64 * 8 and C.workspace_bytes == 256 + 8 * 512 * 8
+    R = plr.plr_layout_create("copy", "bf16", 3, 48 * 3, "packed", "packed", chunk_bytes=32)
+    assert R.nchunks == 3 * 5  # 144-byte segments in 32-byte chunks: ragged last chunk
+    E = plr.plr_layout_create("reduce", "bf16", 4, 0, "packed", "packed")
+    assert E.nchunks == 0 and E.dst_bytes == 0
+
+
+def test_policy_overrides(plr):
+    L = plr.plr_layout_create("reduce", "f16", 4, 1 << 24, "packed", "packed", chunk_bytes=4096,
+                              workgroups=33, block=128, unroll=4, datapath=plr.PLR_PATH_DIRECT)
+    assert L.policy() == dict(chunk_bytes=4096, workgroups=33, block=128, unroll=4, stages=2,
+                              datapath=plr.PLR_PATH_DIRECT)
+
+
+def _code(fn, *a, **k):
+    try:
+        fn(*a, **k)
+    except Exception as e:  # noqa: BLE001
+        return getattr(e, "code", None)
+    return 0
+
+
+def test_layout_errors(plr):
+    E = plr.PlrError
+    mk = plr.plr_layout_create
+    assert _code(mk, "reduce", "bf16", 0, 64, "packed", "packed") == plr.PLR_EINVAL
+    assert _code(mk, "reduce", "bf16", 17, 64, "packed", "packed") == plr.PLR_EUNSUPPORTED
+    assert _code(mk, "reduce", "bf16", 2, 40, "packed", "packed") == plr.PLR_EALIGN
+    assert _code(mk, "reduce", "bf16", 3, 16 * 4, "scattered", "packed") == plr.PLR_EALIGN
+    assert _code(mk, "reduce", "bf16", 3, 16 * 3, "scattered", "packed", rank=3) == plr.PLR_EINVAL
+    assert _code(mk, "reduce", "bf16", 2, 64, "packed", "transposed") == plr.PLR_EINVAL
+    assert _code(mk, "copy", "bf16", 2, 64, "packed", "transposed") == plr.PLR_EINVAL
+    assert _code(mk, "copy", "bf16", 2, 64, "transposed", "packed") == plr.PLR_EINVAL
+    assert _code(mk, "reduce", "bf16", 2, 64, "packed", "packed", mode=1) == plr.PLR_EUNSUPPORTED
+    assert _code(mk, "reduce", "bf16", 2, 64, "packed", "packed", in_offsets=[0, 8]) == plr.PLR_EALIGN
+    assert _code(mk, "reduce", "bf16", 2, 64, "packed", "packed", out_offsets=[0]) == plr.PLR_EINVAL
+    assert _code(mk, "copy", "bf16", 2, 64, "packed", "packed", out_offsets=[0, 32]) == plr.PLR_EINVAL
+    assert _code(mk, "copy", "bf16", 2, 64, "packed", "packed", out_offsets=[64, 0]) == 0
+    assert _code(mk, "copy", "bf16", 9, 16 * 9, "scattered", "transposed",
+                 in_offsets=list(range(0, 16 * 81, 16))) == plr.PLR_EUNSUPPORTED
+    assert _code(mk, "copy", "bf16", 2, 64, "packed", "packed", chunk_bytes=24) == plr.PLR_EALIGN
+    assert _code(mk, "copy", "bf16", 2, 64, "packed", "packed", block=100) == plr.PLR_EINVAL
+    assert _code(mk, "copy", "bf16", 2, 64, "packed", "packed", unroll=3) == plr.PLR_EINVAL
+    assert issubclass(E, RuntimeError)
+
+
+def test_call_validation_without_device(plr):
+    """Argument errors are caught on the host before any launch (fake addresses)."""
+    L = plr.plr_layout_create("reduce", "bf16", 2, 4096, "packed", "packed")
+    A, B, D = 1 << 40, (1 << 40) + (1 << 20), (1 << 40) + (2 << 20)
+    assert _code(plr.plr_reduce, L, [A, B], D + 8) == plr.PLR_EALIGN
+    assert _code(plr.plr_reduce, L, [A + 4, B], D) == plr.PLR_EALIGN
+    assert _code(plr.plr_reduce, L, [A, B], A + 2048) == plr.PLR_EINVAL  # dst overlaps a source
+    assert _code(plr.plr_reduce, L, [A, B], D, workspace=D + (1 << 20) + 8) == plr.PLR_EALIGN
+    assert _code(plr.plr_copy, L, [A, B], D) == plr.PLR_EINVAL  # wrong op
+    C = plr.plr_layout_create("copy", "bf16", 2, 4096, "packed", "packed")
+    assert _code(plr.plr_copy, C, [A, B], A + 4096 - 16) == plr.PLR_EINVAL
+    assert _code(plr.plr_notify, C, 2, D) == plr.PLR_EINVAL
+    assert _code(plr.plr_notify, C, 0, D + 8) == plr.PLR_EALIGN
+    cv = plr.plr_copy_v
+    assert _code(cv, [A], [4], [D], 24, B, D, D, D) == plr.PLR_EALIGN
+    assert _code(cv, [A] * 17, [1] * 17, [D] * 17, 16, B, D, D, D) == plr.PLR_EUNSUPPORTED
+    assert _code(cv, [A + 8], [4], [D], 16, B, D, D, D) == plr.PLR_EALIGN
+    assert _code(cv, [A], [4], [D], 16, A + 16, D, D, D) == plr.PLR_EINVAL  # dst overlaps source
+    assert _code(cv, [A], [-1], [D], 16, B, D, D, D) == plr.PLR_EINVAL
+
+
+def test_scratch_bytes(plr):
+    assert plr.plr_copy_v_scratch_bytes(8, [4096] * 8) == 8 * 4096 * 4
+    assert plr.plr_copy_v_scratch_bytes(2, [1, 2]) == 256
+    assert plr.plr_copy_v_scratch_bytes(0, []) == 0
+
+
+def test_strerror(plr):
+    for code in range(6):
+        assert plr.plr_strerror(code)
+    assert "timed out" in plr.plr_strerror(plr.PLR_ETIMEOUT)
+    assert plr.plr_version().startswith("plr")
