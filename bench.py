@@ -75,6 +75,104 @@ def counters_traffic(op: str):
         return None
 
 
+def summarize_trace(path: str) -> str:
+    """Per-kernel, per-launch-shape durations from a rocprofv3 kernel-trace CSV."""
+    import collections
+    import csv
+
+    groups = collections.defaultdict(list)
+    with open(path) as f:
+        for r in csv.DictReader(f):
+            name = r["Kernel_Name"]
+            if "plr::" not in name and "direct_copy_kernel" not in name:
+                continue
+            short = name.split("(")[0].replace("void ", "")[:60]
+            key = (short, int(r["Grid_Size_X"]), int(r["Workgroup_Size_X"]))
+            groups[key].append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1000.0)
+    lines = [f"{'kernel':60s} {'grid_threads':>12s} {'wg':>4s} {'calls':>6s} {'avg_us':>9s} "
+             f"{'p50_us':>8s} {'p90_us':>8s} {'min_us':>8s}"]
+    for (k, grid, wg), v in sorted(groups.items()):
+        v.sort()
+        lines.append(f"{k:60s} {grid:12d} {wg:4d} {len(v):6d} {statistics.mean(v):9.2f} "
+                     f"{v[len(v) // 2]:8.2f} {v[int(len(v) * 0.9)]:8.2f} {v[0]:8.2f}")
+    return "\n".join(lines)
+
+
+def summarize_counters(path: str) -> str:
+    """Per-kernel, per-launch-shape mean counter values from a rocprofv3 counter CSV."""
+    import collections
+    import csv
+
+    groups = collections.defaultdict(list)
+    with open(path) as f:
+        for r in csv.DictReader(f):
+            name = r["Kernel_Name"]
+            if "plr::" not in name and "direct_copy_kernel" not in name:
+                continue
+            short = name.split("(")[0].replace("void ", "")[:60]
+            key = (short, int(r["Grid_Size"] if "Grid_Size" in r else r["Grid_Size_X"]), r["Counter_Name"])
+            groups[key].append(float(r["Counter_Value"]))
+    lines = [f"{'kernel':60s} {'grid_threads':>12s} {'counter':>12s} {'dispatches':>10s} {'mean':>16s}"]
+    for (k, grid, c), v in sorted(groups.items()):
+        lines.append(f"{k:60s} {grid:12d} {c:>12s} {len(v):10d} {statistics.mean(v):16.1f}")
+    return "\n".join(lines)
+
+
+COUNTER_CMD = ("rocprofv3 --pmc {c} -f csv -d <dir> -o b -- python3 bench.py --steps 3 --warmup 1 "
+               "--no-decode --no-cpu-baseline")
+CALIB_CMD = "rocprofv3 --pmc {c} -f csv -d <dir> -o c -- python3 bench.py --calibrate"
+# counters are taken per kernel; allgather and alltoall share the copy kernel and
+# move the same bytes, so their dispatches are averaged together
+OP_KERNELS = {"reduce": ("plr::k_reduce_direct", None), "allgather": ("plr::k_copy_direct", None),
+              "alltoall": ("plr::k_copy_direct", None), "alltoallv": ("plr::k_copy_v_scatter", None)}
+
+
+def _mean_counter(path, name_part, grid=None):
+    import csv
+
+    vals = []
+    with open(path) as f:
+        for r in csv.DictReader(f):
+            if name_part in r["Kernel_Name"] and (grid is None or int(r["Grid_Size"]) == grid):
+                vals.append(float(r["Counter_Value"]))
+    if not vals:
+        raise ValueError(f"no dispatch of {name_part} in {path}")
+    return statistics.mean(vals), len(vals)
+
+
+def write_counter_profiles(fetch_csv, write_csv, cal_fetch_csv, cal_write_csv, out_dir):
+    """Turn rocprofv3 FETCH_SIZE / WRITE_SIZE runs into per-op HBM traffic summaries.
+    Both counters are scaled by what they read for the runtime's plain device copy of
+    1 GiB (`__amd_rocclr_copyBuffer`, known to read and write 1 GiB)."""
+    cal_f, _ = _mean_counter(cal_fetch_csv, "__amd_rocclr_copyBuffer")
+    cal_w, _ = _mean_counter(cal_write_csv, "__amd_rocclr_copyBuffer")
+    known_kib = (1 << 30) / 1024
+    sf, sw = known_kib / cal_f, known_kib / cal_w
+    h = source_hash()
+    for op, (kname, _) in OP_KERNELS.items():
+        f_kib, nf = _mean_counter(fetch_csv, kname)
+        w_kib, nw = _mean_counter(write_csv, kname)
+        traffic = (f_kib * sf + w_kib * sw) * 1024
+        path = os.path.join(out_dir, f"{op}_counters.txt")
+        with open(path, "w") as out:
+            out.write(f"# HBM traffic per launch of {kname} ({op}) in the bench step, MI355X\n")
+            out.write(f"# commands: {COUNTER_CMD.format(c='FETCH_SIZE')}\n")
+            out.write(f"#           {COUNTER_CMD.format(c='WRITE_SIZE')}\n")
+            out.write(f"#           {CALIB_CMD.format(c='FETCH_SIZE')}   (and WRITE_SIZE)\n")
+            out.write("# then: python bench.py --counters-profile <fetch.csv> <write.csv> <cal_fetch.csv> "
+                      "<cal_write.csv>\n")
+            out.write(f"kernel: {kname}\n")
+            out.write(f"dispatches_fetch: {nf}\ndispatches_write: {nw}\n")
+            out.write(f"fetch_size_kib_mean: {f_kib:.1f}\nwrite_size_kib_mean: {w_kib:.1f}\n")
+            out.write(f"calibration_copy_fetch_kib: {cal_f:.1f}\ncalibration_copy_write_kib: {cal_w:.1f}\n")
+            out.write(f"fetch_scale: {sf:.5f}\nwrite_scale: {sw:.5f}\n")
+            out.write(f"traffic_bytes_per_launch: {traffic:.0f}\n")
+            out.write(f"algorithmic_bytes_per_launch: {BYTES[op]}\n")
+            out.write(f"traffic_over_algorithmic: {traffic / BYTES[op]:.4f}\n")
+            out.write(f"source_hash: {h}\n")
+        print(path, f"{traffic / BYTES[op]:.4f}")
+
+
 def make_inputs(torch, synth, seed, dev):
     x = {}
     x["r_src"] = [synth.normal_t(seed, 3, w, R3 * C3, 0.5, device=dev) for w in range(W)]
@@ -254,11 +352,41 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-fraction", type=float, default=0.125)
     ap.add_argument("--cpu-reps", type=int, default=3)
+    ap.add_argument("--summarize-trace", metavar="CSV",
+                    help="print per-kernel durations of a rocprofv3 kernel-trace CSV and exit")
+    ap.add_argument("--summarize-counters", metavar="CSV",
+                    help="print per-kernel mean counters of a rocprofv3 counter CSV and exit")
+    ap.add_argument("--counters-profile", nargs=4, metavar="CSV",
+                    help="FETCH_SIZE, WRITE_SIZE, calibration FETCH_SIZE, calibration WRITE_SIZE "
+                         "counter CSVs: write profiles/<op>_counters.txt and exit")
+    ap.add_argument("--calibrate", action="store_true",
+                    help="only run torch's plain device copy of 1 GiB five times (the reference "
+                         "for scaling HBM byte counters)")
     args = ap.parse_args()
     if args.gpus != 1:
         sys.exit(f"bench.py runs on one GPU only (got --gpus {args.gpus}): this datapath holds the W "
                  "contributions of one GPU's share in that GPU's memory and uses no second GPU.")
 
+    if args.summarize_trace:
+        print(summarize_trace(args.summarize_trace))
+        return
+    if args.counters_profile:
+        write_counter_profiles(*args.counters_profile, os.path.join(ROOT, "profiles"))
+        return
+    if args.summarize_counters:
+        print(summarize_counters(args.summarize_counters))
+        return
+    if args.calibrate:
+        import torch
+
+        src = torch.empty(1 << 30, dtype=torch.uint8, device="cuda").fill_(1)
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"calibrate": "torch copy_", "bytes_read": 1 << 30, "bytes_written": 1 << 30,
+                          "launches": 5}), flush=True)
+        return
     value, ms, roofline, per_op, decode = run_bench(args)
     cpu = None if args.no_cpu_baseline else run_cpu_baseline(args)
     line = {

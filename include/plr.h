@@ -110,8 +110,11 @@ typedef struct {
   const size_t* out_offsets;
   int mode;                   /* PLR_MODE_DETERMINISTIC (0); anything else: PLR_EUNSUPPORTED */
   /* policy overrides (0 = built-in policy) */
-  size_t chunk_bytes;         /* per-source bytes per chunk: the notification granule */
-  int workgroups;             /* grid size */
+  size_t tile_bytes;          /* per-source bytes one workgroup consumes per step */
+  size_t chunk_bytes;         /* per-source bytes one flag announces: the notification granule,
+                                 rounded up to a whole number of tiles */
+  int workgroups;             /* grid size; each workgroup then consumes a run of
+                                 ceil(tiles / workgroups) consecutive tiles */
   int block;                  /* threads per workgroup: 64, 128, 256 or 512 */
   int unroll;                 /* 16-byte vectors per lane per pipeline step: 1, 2 or 4 */
   int stages;                 /* LDS pipeline depth, 1..4 (PLR_PATH_LDS only) */
@@ -140,8 +143,10 @@ size_t plr_layout_workspace_bytes(const plr_layout* L);
 /* Bytes the call writes into dst: the share for a reduce, the whole output for a copy. */
 size_t plr_layout_dst_bytes(const plr_layout* L);
 
-/* Number of chunks (the notification granules) and of copy segments. */
+/* Number of chunks (the notification granules), of tiles (workgroup steps) and of
+ * copy segments. */
 int plr_layout_nchunks(const plr_layout* L);
+int plr_layout_ntiles(const plr_layout* L);
 int plr_layout_nsegments(const plr_layout* L);
 
 /* Segment k of the compiled table, in bytes: the source index, the offset read in
@@ -150,9 +155,10 @@ int plr_layout_nsegments(const plr_layout* L);
 int plr_layout_segment(const plr_layout* L, int k, int* src, size_t* src_off,
                        size_t* dst_off, size_t* len);
 
-/* The resolved launch policy (after the built-in table and the overrides). */
-int plr_layout_policy(const plr_layout* L, size_t* chunk_bytes, int* workgroups, int* block,
-                      int* unroll, int* stages, int* datapath);
+/* The resolved launch policy (after the built-in table and the overrides).
+ * workgroups == 0 means one workgroup per tile. Any output pointer may be NULL. */
+int plr_layout_policy(const plr_layout* L, size_t* tile_bytes, size_t* chunk_bytes,
+                      int* workgroups, int* block, int* unroll, int* stages, int* datapath);
 
 /* Current epoch E of the layout: the last notified call consumed flags >= E. */
 uint64_t plr_layout_epoch(const plr_layout* L);

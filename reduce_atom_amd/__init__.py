@@ -6,7 +6,7 @@ tensors (device memory) or raw integer device addresses. torch supplies memory a
 streams; nothing here computes.
 
 Importing this package loads ``libplr.so`` from this directory and raises
-ImportError if it has not been built (``python -m reduce_atom_amd._build``): there
+ImportError if it has not been built (``python reduce_atom_amd/_build.py``): there
 is no fallback path.
 """
 from __future__ import annotations
@@ -18,7 +18,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libplr.so")
 
 if not os.path.exists(LIB_PATH):
-    raise ImportError(f"{LIB_PATH} is missing: build it with `python -m reduce_atom_amd._build`")
+    raise ImportError(f"{LIB_PATH} is missing: build it with `python reduce_atom_amd/_build.py`")
 
 _lib = ctypes.CDLL(LIB_PATH)
 
@@ -46,7 +46,7 @@ class plr_layout_desc(_c.Structure):
         ("in_kind", _i), ("out_kind", _i),
         ("in_offsets", _c.POINTER(_sz)), ("out_offsets", _c.POINTER(_sz)),
         ("mode", _i),
-        ("chunk_bytes", _sz),
+        ("tile_bytes", _sz), ("chunk_bytes", _sz),
         ("workgroups", _i), ("block", _i), ("unroll", _i), ("stages", _i), ("datapath", _i),
         ("spin_limit", _u64),
     ]
@@ -59,7 +59,7 @@ _lib.plr_layout_destroy.restype = None
 for _n in ("plr_layout_workspace_bytes", "plr_layout_dst_bytes"):
     getattr(_lib, _n).argtypes = [_vp]
     getattr(_lib, _n).restype = _sz
-for _n in ("plr_layout_nchunks", "plr_layout_nsegments"):
+for _n in ("plr_layout_nchunks", "plr_layout_ntiles", "plr_layout_nsegments"):
     getattr(_lib, _n).argtypes = [_vp]
     getattr(_lib, _n).restype = _i
 _lib.plr_layout_epoch.argtypes = [_vp]
@@ -67,7 +67,7 @@ _lib.plr_layout_epoch.restype = _u64
 _lib.plr_layout_segment.argtypes = [_vp, _i, _c.POINTER(_i), _c.POINTER(_sz), _c.POINTER(_sz),
                                     _c.POINTER(_sz)]
 _lib.plr_layout_segment.restype = _i
-_lib.plr_layout_policy.argtypes = [_vp, _c.POINTER(_sz)] + [_c.POINTER(_i)] * 5
+_lib.plr_layout_policy.argtypes = [_vp, _c.POINTER(_sz), _c.POINTER(_sz)] + [_c.POINTER(_i)] * 5
 _lib.plr_layout_policy.restype = _i
 _lib.plr_reduce.argtypes = [_vp, _c.POINTER(_vp), _vp, _vp, _vp]
 _lib.plr_reduce.restype = _i
@@ -90,7 +90,7 @@ _lib.plr_version.restype = _c.c_char_p
 
 EXPORTS = [
     "plr_layout_create", "plr_layout_destroy", "plr_layout_workspace_bytes", "plr_layout_dst_bytes",
-    "plr_layout_nchunks", "plr_layout_nsegments", "plr_layout_segment", "plr_layout_policy",
+    "plr_layout_nchunks", "plr_layout_ntiles", "plr_layout_nsegments", "plr_layout_segment", "plr_layout_policy",
     "plr_layout_epoch", "plr_reduce", "plr_copy", "plr_copy_v", "plr_copy_v_scratch_bytes",
     "plr_notify", "plr_check", "plr_strerror", "plr_last_hip_error", "plr_version",
 ]
@@ -155,10 +155,10 @@ class Layout:
     def handle(self):
         return self._h
 
-    def __del__(self):
+    def __del__(self, _destroy=_lib.plr_layout_destroy):
         h = getattr(self, "_h", None)
         if h is not None and h.value:
-            _lib.plr_layout_destroy(h)
+            _destroy(h)
             self._h = None
 
     @property
@@ -186,17 +186,21 @@ class Layout:
             out.append((s.value, so.value, do.value, ln.value))
         return out
 
+    @property
+    def ntiles(self) -> int:
+        return _lib.plr_layout_ntiles(self._h)
+
     def policy(self) -> dict:
-        cb, wg, bl, un, st, dp = _sz(), _i(), _i(), _i(), _i(), _i()
-        _ok(_lib.plr_layout_policy(self._h, _c.byref(cb), _c.byref(wg), _c.byref(bl), _c.byref(un),
-                                   _c.byref(st), _c.byref(dp)), "plr_layout_policy")
-        return dict(chunk_bytes=cb.value, workgroups=wg.value, block=bl.value, unroll=un.value,
-                    stages=st.value, datapath=dp.value)
+        tb, cb, wg, bl, un, st, dp = _sz(), _sz(), _i(), _i(), _i(), _i(), _i()
+        _ok(_lib.plr_layout_policy(self._h, _c.byref(tb), _c.byref(cb), _c.byref(wg), _c.byref(bl),
+                                   _c.byref(un), _c.byref(st), _c.byref(dp)), "plr_layout_policy")
+        return dict(tile_bytes=tb.value, chunk_bytes=cb.value, workgroups=wg.value, block=bl.value,
+                    unroll=un.value, stages=st.value, datapath=dp.value)
 
 
 def plr_layout_create(op, dtype, world, bytes_per_src, in_kind, out_kind, rank=0,
                       in_offsets=None, out_offsets=None, mode=PLR_MODE_DETERMINISTIC,
-                      chunk_bytes=0, workgroups=0, block=0, unroll=0, stages=0, datapath=0,
+                      tile_bytes=0, chunk_bytes=0, workgroups=0, block=0, unroll=0, stages=0, datapath=0,
                       spin_limit=0) -> Layout:
     """Compile a layout. op/dtype/kinds accept the C enum values or their names."""
     d = plr_layout_desc()
@@ -214,7 +218,7 @@ def plr_layout_create(op, dtype, world, bytes_per_src, in_kind, out_kind, rank=0
         a = (_sz * len(out_offsets))(*out_offsets)
         keep.append(a)
         d.out_offsets = _c.cast(a, _c.POINTER(_sz))
-    d.mode, d.chunk_bytes, d.workgroups = mode, chunk_bytes, workgroups
+    d.mode, d.tile_bytes, d.chunk_bytes, d.workgroups = mode, tile_bytes, chunk_bytes, workgroups
     d.block, d.unroll, d.stages, d.datapath, d.spin_limit = block, unroll, stages, datapath, spin_limit
     h = _vp()
     _ok(_lib.plr_layout_create(_c.byref(d), _c.byref(h)), "plr_layout_create")

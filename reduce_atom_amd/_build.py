@@ -2,7 +2,8 @@
 
 Every source is compiled by hipcc (device code for gfx950 only) and linked into one
 shared library exporting the C ABI of include/plr.h. Run as
-``python -m reduce_atom_amd._build`` or through ``__graft_entry__.build()``.
+``python reduce_atom_amd/_build.py`` or through ``__graft_entry__.build()`` (not as
+``-m reduce_atom_amd._build``: importing the package loads the library).
 """
 from __future__ import annotations
 
@@ -23,7 +24,7 @@ ARCH = "gfx950"
 
 COMMON = [
     "-O3", "-std=c++17", "-fPIC", "-Wall", "-Wno-unused-command-line-argument",
-    "-I", os.path.join(ROOT, "include"), "-I", CSRC,
+    "-I", os.path.join(ROOT, "include"),
     "-fno-fast-math", "-ffp-contract=off",
 ]
 # gfx950 device code; packed fp32 instructions are kept out of the device code.
@@ -33,10 +34,10 @@ DEVICE = [f"--offload-arch={ARCH}", "-Xclang", "-target-feature", "-Xclang", "-p
 SOURCES = ["api.cpp", "layout.cpp", "reduce.hip", "copy.hip", "copy_v.hip", "notify.hip"]
 
 
-def _compile(src: str) -> str:
-    path = os.path.join(CSRC, src)
-    obj = os.path.join(BUILD, src + ".o")
-    cmd = [HIPCC, *COMMON]
+def _compile(src: str, build_dir: str = BUILD, defines=(), csrc: str = CSRC) -> str:
+    path = os.path.join(csrc, src)
+    obj = os.path.join(build_dir, src + ".o")
+    cmd = [HIPCC, *COMMON, "-I", csrc, *[f"-D{d}" for d in defines]]
     if src.endswith(".hip"):
         cmd += ["-x", "hip", *DEVICE]
     else:
@@ -48,21 +49,24 @@ def _compile(src: str) -> str:
     return obj
 
 
-def build(jobs: int | None = None, verbose: bool = False) -> str:
-    """Compile and link libplr.so (always rebuilds)."""
-    os.makedirs(BUILD, exist_ok=True)
+def build(jobs: int | None = None, verbose: bool = False, out: str = OUT, defines=(),
+          csrc: str = CSRC) -> str:
+    """Compile and link libplr.so (always rebuilds). `defines` (extra -D macros) and
+    `csrc` (another source directory) are for tuning builds written to another `out`."""
+    build_dir = BUILD if out == OUT else out + ".objs"
+    os.makedirs(build_dir, exist_ok=True)
     jobs = jobs or min(len(SOURCES), os.cpu_count() or 4, 16)
     with cf.ThreadPoolExecutor(jobs) as ex:
-        objs = list(ex.map(_compile, SOURCES))
-    tmp = OUT + ".tmp"
+        objs = list(ex.map(lambda s: _compile(s, build_dir, defines, csrc), SOURCES))
+    tmp = out + ".tmp"
     cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stderr}")
-    os.replace(tmp, OUT)
+    os.replace(tmp, out)
     if verbose:
-        print(f"built {OUT}")
-    return OUT
+        print(f"built {out}")
+    return out
 
 
 def clean() -> None:

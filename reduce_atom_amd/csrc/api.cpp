@@ -41,15 +41,20 @@ int cu_count() {
   return n;
 }
 
-uint32_t grid_for(const plr_layout* L) {
-  if (L->workgroups > 0) return (uint32_t)L->workgroups;
-  uint64_t g = L->nchunks;
-  if (L->wg_per_cu > 0) g = std::min<uint64_t>(g, (uint64_t)cu_count() * L->wg_per_cu);
-  return (uint32_t)std::max<uint64_t>(g, 1);
+// Tiles per workgroup: the policy's run, or what an explicit (or per-compute-unit)
+// workgroup count implies; the grid then covers every tile once.
+uint32_t run_for(const plr_layout* L, bool notified) {
+  uint64_t g = 0;
+  if (L->workgroups > 0) g = (uint64_t)L->workgroups;
+  else if (L->wg_per_cu > 0) g = (uint64_t)cu_count() * L->wg_per_cu;
+  if (g == 0) return (uint32_t)std::max(1, notified ? L->run_notified : L->run);
+  return (uint32_t)std::max<uint64_t>(1, (L->ntiles + g - 1) / g);
 }
 
-Launch launch_of(const plr_layout* L) {
-  return Launch{grid_for(L), (uint32_t)L->block, L->unroll, L->stages, L->datapath};
+Launch launch_of(const plr_layout* L, bool notified) {
+  const uint32_t run = run_for(L, notified);
+  const uint32_t grid = (uint32_t)std::max<uint64_t>(1, ((uint64_t)L->ntiles + run - 1) / run);
+  return Launch{grid, (uint32_t)L->block, L->unroll, L->stages, L->datapath, run};
 }
 
 // Common checks of plr_reduce / plr_copy. Fills the notification block.
@@ -84,17 +89,21 @@ extern "C" int plr_reduce(plr_layout* L, const void* const* srcs, void* dst, voi
   Notify nt;
   int rc = check_call(L, PLR_OP_REDUCE, srcs, dst, workspace, &nt);
   if (rc) return rc;
-  if (L->nchunks) {
+  if (L->ntiles) {
     ReduceArgs a{};
     for (int w = 0; w < L->world; ++w)
       a.src[w] = reinterpret_cast<const u32x4*>(static_cast<const char*>(srcs[w]) + L->segs[w].src_off);
     a.dst = static_cast<u32x4*>(dst);
     a.nvec = L->seg_len / 16;
-    a.chunk_vecs = L->chunk_bytes / 16;
+    a.tile_vecs = L->tile_bytes / 16;
+    a.ntiles = L->ntiles;
+    a.tiles_per_chunk = L->tiles_per_chunk;
     a.nchunks = L->nchunks;
     a.world = (uint32_t)L->world;
     a.nt = nt;
-    hipError_t e = launch_reduce(a, L->dtype, launch_of(L), static_cast<hipStream_t>(stream));
+    const Launch l = launch_of(L, nt.flags != nullptr);
+    a.run = l.run;
+    hipError_t e = launch_reduce(a, L->dtype, l, static_cast<hipStream_t>(stream));
     if (e != hipSuccess) return hip_fail(e);
   }
   if (workspace) L->epoch = nt.epoch;
@@ -106,15 +115,18 @@ extern "C" int plr_copy(plr_layout* L, const void* const* srcs, void* dst, void*
   Notify nt;
   int rc = check_call(L, PLR_OP_COPY, srcs, dst, workspace, &nt);
   if (rc) return rc;
-  if (L->nchunks) {
+  if (L->ntiles) {
     CopyArgs a{};
     for (int w = 0; w < L->world; ++w) a.src[w] = static_cast<const uint8_t*>(srcs[w]);
     a.dst = static_cast<uint8_t*>(dst);
     a.seg_len = L->seg_len;
-    a.chunk_bytes = L->chunk_bytes;
+    a.tile_bytes = L->tile_bytes;
+    a.tiles_per_seg = L->tiles_per_seg;
+    a.ntiles = L->ntiles;
+    a.tiles_per_chunk = L->tiles_per_chunk;
     a.chunks_per_seg = L->chunks_per_seg;
-    a.nseg = (uint32_t)L->segs.size();
     a.nchunks = L->nchunks;
+    a.nseg = (uint32_t)L->segs.size();
     a.world = (uint32_t)L->world;
     a.nt = nt;
     if (L->table_fits) {
@@ -128,7 +140,9 @@ extern "C" int plr_copy(plr_layout* L, const void* const* srcs, void* dst, void*
       a.mode = kCopyTransposed;
       a.slice = L->seg_len;
     }
-    hipError_t e = launch_copy(a, launch_of(L), static_cast<hipStream_t>(stream));
+    const Launch l = launch_of(L, nt.flags != nullptr);
+    a.run = l.run;
+    hipError_t e = launch_copy(a, l, static_cast<hipStream_t>(stream));
     if (e != hipSuccess) return hip_fail(e);
   }
   if (workspace) L->epoch = nt.epoch;
@@ -181,9 +195,8 @@ extern "C" int plr_copy_v(int world, const void* const* srcs, const int64_t* row
   a.rank = static_cast<int32_t*>(scratch);
   a.row_bytes = row_bytes;
   a.world = (uint32_t)world;
-  const uint64_t waves_needed = ((uint64_t)total + 3) / 4;
-  const uint32_t grid =
-      (uint32_t)std::max<uint64_t>(1, std::min<uint64_t>(waves_needed, (uint64_t)cu_count() * 8));
+  // one row per wave: four rows per 256-thread workgroup
+  const uint32_t grid = (uint32_t)std::max<uint64_t>(1, ((uint64_t)total + 3) / 4);
   hipError_t e = launch_copy_v(a, grid, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e);
   return PLR_OK;

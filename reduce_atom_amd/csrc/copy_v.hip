@@ -5,7 +5,7 @@
 // Output rows are packed per destination, in source then row order:
 //   kernel 1 (one workgroup per source): counts[s][d] and, for every row, its rank
 //            among the earlier rows of the same source bound for the same
-//            destination (a workgroup-wide exclusive scan of one-hot counts);
+//            destination (wave ballots plus a workgroup-wide exclusive scan);
 //   kernel 2 (many workgroups): a prologue in every workgroup turns the W*W counts
 //            into offsets[d][s] (an exclusive scan in destination-major order),
 //            then each wave moves whole rows with 16-byte loads and stores to row
@@ -14,13 +14,15 @@
 
 namespace plr {
 
-constexpr int kRankThreads = 256;
-constexpr int kRankRowsPerThread = 16;
-constexpr int kRankTile = kRankThreads * kRankRowsPerThread;
+constexpr int kRankThreads = 1024;
+constexpr int kRankWaves = kRankThreads / 64;
 
+// Kernel 1: one workgroup per source. Rows are taken 1024 at a time in row order,
+// one per thread; a wave ballot per destination gives each row its rank among the
+// earlier lanes bound for the same destination, per-wave totals in LDS give the
+// ranks of earlier waves, and a carry per destination accumulates earlier passes.
 __global__ void __launch_bounds__(kRankThreads) k_copy_v_rank(const CopyVArgs a) {
-  __shared__ int32_t slot[kRankThreads][PLR_MAX_WORLD + 1];
-  __shared__ int32_t wave_tot[kRankThreads / 64][PLR_MAX_WORLD];
+  __shared__ int32_t wave_cnt[kRankWaves][PLR_MAX_WORLD];
   __shared__ int32_t carry[PLR_MAX_WORLD];
 
   const int s = blockIdx.x;
@@ -30,69 +32,46 @@ __global__ void __launch_bounds__(kRankThreads) k_copy_v_rank(const CopyVArgs a)
   const int64_t r0 = a.row_start[s];
   const int64_t rows = a.row_start[s + 1] - r0;
   const int32_t* dest = a.dest[s];
+  const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));  // lanes < this one
 
   if (t < PLR_MAX_WORLD) carry[t] = 0;
   __syncthreads();
 
-  for (int64_t base = 0; base < rows; base += kRankTile) {
-    // this thread's rows: base + t*K .. base + t*K + K-1, in row order
-    int32_t dk[kRankRowsPerThread];
-    const int64_t first = base + (int64_t)t * kRankRowsPerThread;
+  for (int64_t base = 0; base < rows; base += kRankThreads) {
+    const int64_t i = base + t;
+    const int d = (i < rows) ? dest[i] : -1;
+    int in_wave = 0;  // rows of lower lanes in this wave bound for d
 #pragma unroll
-    for (int k = 0; k < kRankRowsPerThread; ++k) dk[k] = (first + k < rows) ? dest[first + k] : -1;
-
-    int cnt[PLR_MAX_WORLD];
-#pragma unroll
-    for (int d = 0; d < PLR_MAX_WORLD; ++d) {
-      int c = 0;
-#pragma unroll
-      for (int k = 0; k < kRankRowsPerThread; ++k) c += (dk[k] == d);
-      cnt[d] = c;
-    }
-    // inclusive scan of every destination's count across the wave
-    int incl[PLR_MAX_WORLD];
-#pragma unroll
-    for (int d = 0; d < PLR_MAX_WORLD; ++d) {
-      int x = cnt[d];
-#pragma unroll
-      for (int o = 1; o < 64; o <<= 1) {
-        const int y = __shfl_up(x, o, 64);
-        if (lane >= o) x += y;
+    for (int dd = 0; dd < PLR_MAX_WORLD; ++dd) {
+      if (dd < W) {
+        const uint64_t m = __ballot(d == dd);
+        if (lane == 0) wave_cnt[wave][dd] = __popcll(m);
+        if (d == dd) in_wave = __popcll(m & below);
       }
-      incl[d] = x;
-    }
-    if (lane == 63) {
-#pragma unroll
-      for (int d = 0; d < PLR_MAX_WORLD; ++d) wave_tot[wave][d] = incl[d];
     }
     __syncthreads();
-#pragma unroll
-    for (int d = 0; d < PLR_MAX_WORLD; ++d) {
-      if (d < W) {
-        int p = carry[d] + incl[d] - cnt[d];
-        for (int w2 = 0; w2 < wave; ++w2) p += wave_tot[w2][d];
-        slot[t][d] = p;
-      }
+    if (d >= 0 && d < W) {
+      int r = carry[d] + in_wave;
+      for (int w2 = 0; w2 < wave; ++w2) r += wave_cnt[w2][d];
+      a.rank[r0 + i] = r;
     }
-    __syncthreads();  // everyone has read carry and wave_tot
+    __syncthreads();  // every thread has read carry and wave_cnt
     if (t < W) {
       int tot = 0;
-      for (int w2 = 0; w2 < kRankThreads / 64; ++w2) tot += wave_tot[w2][t];
+      for (int w2 = 0; w2 < kRankWaves; ++w2) tot += wave_cnt[w2][t];
       carry[t] += tot;
     }
-#pragma unroll
-    for (int k = 0; k < kRankRowsPerThread; ++k) {
-      const int d = dk[k];
-      if (d >= 0 && d < W) a.rank[r0 + first + k] = slot[t][d]++;
-    }
-    __syncthreads();  // before the next tile reuses wave_tot / slot, and carry is final
+    __syncthreads();
   }
   if (t < W) a.counts[s * W + t] = carry[t];
 }
 
 constexpr int kScatterThreads = 256;
-constexpr int kScatterUnroll = 8;
+constexpr int kScatterUnroll = 16;
 
+// Kernel 2: a prologue in every workgroup scans the W*W counts (workgroup 0 also
+// writes them out as offsets); then wave k of the grid moves row k: all of a
+// 14,336-byte row (14 vectors per lane) is in flight at once.
 __global__ void __launch_bounds__(kScatterThreads) k_copy_v_scatter(const CopyVArgs a) {
   __shared__ int64_t cnt[PLR_MAX_WORLD * PLR_MAX_WORLD];
   __shared__ int64_t off[PLR_MAX_WORLD * PLR_MAX_WORLD];
@@ -134,7 +113,7 @@ __global__ void __launch_bounds__(kScatterThreads) k_copy_v_scatter(const CopyVA
 #pragma unroll
       for (int u = 0; u < kScatterUnroll; ++u) {
         const uint64_t v = v0 + (uint64_t)u * 64 + lane;
-        if (v < nvec) x[u] = ld16_cached(src + v);
+        if (v < nvec) x[u] = ld16(src + v);
       }
 #pragma unroll
       for (int u = 0; u < kScatterUnroll; ++u) {

@@ -9,9 +9,28 @@
 
 namespace plr {
 
-__device__ __forceinline__ u32x4 ld16(const u32x4* p) { return __builtin_nontemporal_load(p); }
-__device__ __forceinline__ u32x4 ld16_cached(const u32x4* p) { return *p; }
-__device__ __forceinline__ void st16(u32x4* p, u32x4 v) { __builtin_nontemporal_store(v, p); }
+// Streaming access: every byte is touched once, so loads and stores carry the
+// non-temporal hint unless a build selects otherwise.
+#ifndef PLR_LD_NT
+#define PLR_LD_NT 1
+#endif
+#ifndef PLR_ST_NT
+#define PLR_ST_NT 1
+#endif
+__device__ __forceinline__ u32x4 ld16(const u32x4* p) {
+#if PLR_LD_NT
+  return __builtin_nontemporal_load(p);
+#else
+  return *p;
+#endif
+}
+__device__ __forceinline__ void st16(u32x4* p, u32x4 v) {
+#if PLR_ST_NT
+  __builtin_nontemporal_store(v, p);
+#else
+  *p = v;
+#endif
+}
 
 // ---- element types inside one 16-byte vector ----
 // Element j of a vector is at bits [16j, 16j+16) of the little-endian 128-bit word
@@ -138,6 +157,17 @@ __device__ __forceinline__ bool wait_flags(const Notify& nt, const uint64_t* fir
   }
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
   return true;
+}
+
+// Workgroup form: only wave 0 polls and executes the agent-scope acquire (on a chip
+// with one L2 per XCD that acquire invalidates cached lines, so it is paid once per
+// workgroup and chunk, not once per wave); the workgroup barrier then orders the
+// other waves' loads after it. Returns false on a timeout or an earlier error. Every
+// thread of the workgroup must call this together.
+__device__ __forceinline__ bool wg_wait_flags(const Notify& nt, const uint64_t* first, uint64_t stride,
+                                              int n) {
+  const bool ok = (threadIdx.x >> 6) ? true : wait_flags(nt, first, stride, n);
+  return !__syncthreads_or(!ok);
 }
 
 }  // namespace plr

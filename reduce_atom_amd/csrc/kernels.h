@@ -24,6 +24,7 @@ struct Launch {
   int unroll;
   int stages;
   int datapath;  // PLR_PATH_DIRECT or PLR_PATH_LDS
+  uint32_t run;  // consecutive tiles per workgroup
 };
 
 // Notification state of one consuming launch (section 3.2, SNAC "notify").
@@ -34,13 +35,21 @@ struct Notify {
   uint64_t spin_limit;    // polls before giving up with PLR_ETIMEOUT
 };
 
+// Work division shared by reduce and copy: a workgroup consumes a run of whole
+// consecutive tiles (a tile is the Atom's step), and tiles_per_chunk consecutive
+// tiles of one segment form a chunk, the notification granule whose flags a tile
+// waits for.
 struct ReduceArgs {
   const u32x4* src[PLR_MAX_WORLD];  // start of the share inside each source
   u32x4* dst;
   uint64_t nvec;        // 16-byte vectors in the share
-  uint64_t chunk_vecs;  // vectors per chunk
-  uint32_t nchunks;
+  uint64_t tile_vecs;   // vectors per tile
+  uint32_t ntiles;
+  uint32_t tiles_per_chunk;
+  uint32_t nchunks;     // flags per source
   uint32_t world;
+  uint32_t run;         // consecutive tiles per workgroup
+  uint32_t pad;
   Notify nt;
 };
 
@@ -55,12 +64,16 @@ struct CopyArgs {
   const uint8_t* src[PLR_MAX_WORLD];
   uint8_t* dst;
   uint64_t seg_len;
-  uint64_t chunk_bytes;
+  uint64_t tile_bytes;
+  uint32_t tiles_per_seg;
+  uint32_t ntiles;
+  uint32_t tiles_per_chunk;
   uint32_t chunks_per_seg;
+  uint32_t nchunks;     // flags per source: segment k's chunk j is flag k*chunks_per_seg + j
   uint32_t nseg;
-  uint32_t nchunks;
   uint32_t world;
   uint32_t mode;
+  uint32_t run;    // consecutive tiles per workgroup
   uint32_t pad;
   uint64_t slice;  // kCopyTransposed: bytes per slice
   Notify nt;

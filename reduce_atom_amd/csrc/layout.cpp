@@ -18,32 +18,40 @@ namespace plr {
 
 size_t elem_bytes(plr_dtype t) { return t == PLR_F32 ? 4 : 2; }
 
-// gfx950 policy table. Two regimes, as on the pages (latency-bound decode versus
-// throughput-bound prefill): small shares launch one short pipeline step per
-// workgroup on as many compute units as it takes, so every load is in flight at
-// once; large shares use 64 KiB chunks per source and a grid of a few workgroups
-// per compute unit striding over the chunks.
+// gfx950 policy table (measured on MI355X with 8 x 117 MB bf16 reduces and 512 MiB
+// copies): the best streaming rate comes from one short step per workgroup and a
+// grid that covers every tile, so the dispatcher walks the whole chip through memory
+// front to back; 16-byte non-temporal loads and stores. Tiles: 4 KiB per source for
+// the reduce (one vector per lane per source), 8 KiB for copies. Flags cover 256 KiB
+// chunks (16 KiB for decode-size shares). A notified workgroup pays one agent-scope
+// acquire per chunk it enters, and those acquires invalidate L2 lines, so large
+// notified calls give each workgroup a run of 2 (reduce) or 4 (copy) tiles; decode-size
+// shares (at most 2 MiB) keep one tile per workgroup, where latency rules.
 static void default_policy(plr_layout* L) {
   L->stages = 2;
   L->datapath = PLR_PATH_DIRECT;
   L->workgroups = 0;
+  L->wg_per_cu = 0;
+  L->run = 1;  // one tile per workgroup: the grid covers every tile
+  L->run_notified = L->op == PLR_OP_REDUCE ? 2 : 4;
   if (L->op == PLR_OP_REDUCE) {
-    if (L->seg_len <= (2u << 20)) {  // latency regime
-      L->block = 64;
+    if (L->seg_len <= (2u << 20)) {  // latency regime: every tile in one dispatch wave
+      L->block = 256;
       L->unroll = 1;
-      L->chunk_bytes = (uint64_t)L->block * 16 * L->unroll;
-      L->wg_per_cu = 0;  // one workgroup per chunk
+      L->tile_bytes = 4u << 10;
+      L->chunk_bytes = 16u << 10;
+      L->run_notified = 1;
     } else {
       L->block = 256;
-      L->unroll = 2;
-      L->chunk_bytes = 64u << 10;
-      L->wg_per_cu = 8;
+      L->unroll = 1;
+      L->tile_bytes = 4u << 10;
+      L->chunk_bytes = 256u << 10;
     }
   } else {
     L->block = 256;
-    L->unroll = 4;
-    L->chunk_bytes = 64u << 10;
-    L->wg_per_cu = 8;
+    L->unroll = 2;
+    L->tile_bytes = 8u << 10;
+    L->chunk_bytes = 256u << 10;
   }
 }
 
@@ -145,9 +153,14 @@ extern "C" int plr_layout_create(const plr_layout_desc* d, plr_layout** out) {
 
   // policy: built-in table, then the caller's overrides
   default_policy(L);
+  if (d->tile_bytes) {
+    if (!aligned16(d->tile_bytes)) return fail(PLR_EALIGN);
+    L->tile_bytes = d->tile_bytes;
+  }
   if (d->chunk_bytes) {
     if (!aligned16(d->chunk_bytes)) return fail(PLR_EALIGN);
     L->chunk_bytes = d->chunk_bytes;
+    if (!d->tile_bytes) L->tile_bytes = std::min<uint64_t>(L->tile_bytes, L->chunk_bytes);
   }
   if (d->workgroups < 0) return fail(PLR_EINVAL);
   if (d->workgroups) L->workgroups = d->workgroups;
@@ -170,18 +183,25 @@ extern "C" int plr_layout_create(const plr_layout_desc* d, plr_layout** out) {
   }
   L->spin_limit = d->spin_limit ? d->spin_limit : kDefaultSpinLimit;
 
-  // chunk table
+  // tile and chunk tables; a chunk is a whole number of tiles of one segment
   if (L->seg_len == 0) {
-    L->chunks_per_seg = 0;
-    L->nchunks = 0;
+    L->tiles_per_seg = L->tiles_per_chunk = L->chunks_per_seg = 0;
+    L->ntiles = L->nchunks = 0;
   } else {
-    const uint64_t cb = std::min<uint64_t>(L->chunk_bytes, L->seg_len);
-    L->chunk_bytes = cb;
-    const uint64_t cps = (L->seg_len + cb - 1) / cb;
-    const uint64_t n = L->op == PLR_OP_REDUCE ? cps : cps * L->segs.size();
-    if (n > 0xFFFFFFFFull) return fail(PLR_EUNSUPPORTED);
+    const uint64_t tile = std::min<uint64_t>(L->tile_bytes, L->seg_len);
+    const uint64_t tps = (L->seg_len + tile - 1) / tile;
+    uint64_t tpc = std::max<uint64_t>(1, (L->chunk_bytes + tile - 1) / tile);
+    tpc = std::min<uint64_t>(tpc, tps);
+    const uint64_t cps = (tps + tpc - 1) / tpc;
+    const uint64_t nseg = L->op == PLR_OP_REDUCE ? 1 : L->segs.size();
+    if (tps * nseg > 0x7FFFFFFFull) return fail(PLR_EUNSUPPORTED);
+    L->tile_bytes = tile;
+    L->chunk_bytes = tile * tpc;
+    L->tiles_per_seg = (uint32_t)tps;
+    L->tiles_per_chunk = (uint32_t)tpc;
     L->chunks_per_seg = (uint32_t)cps;
-    L->nchunks = (uint32_t)n;
+    L->ntiles = (uint32_t)(tps * nseg);
+    L->nchunks = (uint32_t)(cps * nseg);
   }
   *out = L;
   return PLR_OK;
@@ -196,6 +216,7 @@ extern "C" size_t plr_layout_workspace_bytes(const plr_layout* L) {
 
 extern "C" size_t plr_layout_dst_bytes(const plr_layout* L) { return L ? L->dst_bytes : 0; }
 extern "C" int plr_layout_nchunks(const plr_layout* L) { return L ? (int)L->nchunks : -1; }
+extern "C" int plr_layout_ntiles(const plr_layout* L) { return L ? (int)L->ntiles : -1; }
 extern "C" int plr_layout_nsegments(const plr_layout* L) { return L ? (int)L->segs.size() : -1; }
 extern "C" uint64_t plr_layout_epoch(const plr_layout* L) { return L ? L->epoch : 0; }
 
@@ -210,9 +231,11 @@ extern "C" int plr_layout_segment(const plr_layout* L, int k, int* src, size_t* 
   return PLR_OK;
 }
 
-extern "C" int plr_layout_policy(const plr_layout* L, size_t* chunk_bytes, int* workgroups,
-                                 int* block, int* unroll, int* stages, int* datapath) {
+extern "C" int plr_layout_policy(const plr_layout* L, size_t* tile_bytes, size_t* chunk_bytes,
+                                 int* workgroups, int* block, int* unroll, int* stages,
+                                 int* datapath) {
   if (!L) return PLR_EINVAL;
+  if (tile_bytes) *tile_bytes = L->tile_bytes;
   if (chunk_bytes) *chunk_bytes = L->chunk_bytes;
   if (workgroups) *workgroups = L->workgroups;
   if (block) *block = L->block;

@@ -30,14 +30,22 @@ struct plr_layout {
   uint64_t dst_bytes;
   bool table_fits;  // copy: the table is carried in the kernel arguments
 
-  // chunking (section 3.2 "SNAC": the notification granule)
-  uint64_t chunk_bytes;      // per source (reduce) / per segment piece (copy)
-  uint32_t chunks_per_seg;   // copy only
-  uint32_t nchunks;
+  // work and notification granules: a tile is what one workgroup consumes per
+  // step; a chunk (a whole number of tiles of one segment) is what one flag per
+  // source announces (section 3.2 "SNAC")
+  uint64_t tile_bytes;       // per source (reduce) / per segment piece (copy)
+  uint64_t chunk_bytes;
+  uint32_t tiles_per_seg;
+  uint32_t tiles_per_chunk;
+  uint32_t chunks_per_seg;
+  uint32_t ntiles;           // reduce: tiles of the share; copy: nseg * tiles_per_seg
+  uint32_t nchunks;          // reduce: chunks of the share; copy: nseg * chunks_per_seg
 
   // resolved policy (section 4.2 "Codesign Policies and Tuning")
-  int workgroups;  // 0 = sized at launch from the device's compute-unit count
-  int wg_per_cu;   // used when workgroups == 0
+  int workgroups;  // explicit grid size, or 0
+  int wg_per_cu;   // grid = compute units * wg_per_cu when workgroups == 0 and this is > 0
+  int run;           // tiles per workgroup when neither of the above is set
+  int run_notified;  // the same for notified calls (each workgroup pays one acquire per chunk)
   int block;
   int unroll;
   int stages;

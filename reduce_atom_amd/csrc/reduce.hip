@@ -7,10 +7,11 @@
 // binary32 accumulator) and `U` such vectors per step, so W*U 16-byte loads are in
 // flight per lane before the first add.
 //
-// Work division: the share is cut into chunks of `chunk_vecs` vectors (the
-// notification granule, section 3.2); a workgroup consumes whole chunks, striding
-// over them by the grid size. When the call is notified, each wave first waits for
-// the chunk's W flags.
+// Work division: the share is cut into tiles of `tile_vecs` vectors, the step one
+// workgroup consumes; tiles_per_chunk consecutive tiles form a chunk, the
+// notification granule (section 3.2). Workgroup b consumes the run of tiles
+// [b*run, (b+1)*run); when the call is notified, the workgroup waits for a chunk's W
+// flags before its first tile of that chunk.
 #include "device_common.h"
 
 namespace plr {
@@ -18,25 +19,33 @@ namespace plr {
 template <int DT, int W, int U>
 __global__ void __launch_bounds__(512) k_reduce_direct(const ReduceArgs a) {
   const uint32_t nthr = blockDim.x;
-  for (uint32_t c = blockIdx.x; c < a.nchunks; c += gridDim.x) {
-    if (a.nt.flags && !wait_flags(a.nt, a.nt.flags + c, a.nchunks, W)) return;
-    const uint64_t v_end = min((uint64_t)(c + 1) * a.chunk_vecs, a.nvec);
-    uint64_t v = (uint64_t)c * a.chunk_vecs + threadIdx.x;
+  uint32_t ready = 0xFFFFFFFFu;  // chunk whose flags this workgroup has already seen
+  const uint32_t t_end = min(a.ntiles, (blockIdx.x + 1) * a.run);
+  for (uint32_t t = blockIdx.x * a.run; t < t_end; ++t) {
+    if (a.nt.flags) {
+      const uint32_t c = t / a.tiles_per_chunk;
+      if (c != ready) {
+        if (!wg_wait_flags(a.nt, a.nt.flags + c, a.nchunks, W)) return;
+        ready = c;
+      }
+    }
+    const uint64_t v_end = min((uint64_t)(t + 1) * a.tile_vecs, a.nvec);
+    uint64_t v = (uint64_t)t * a.tile_vecs + threadIdx.x;
     // full pipeline steps: U vectors per lane, all W*U loads issued before any add
     for (; v + (uint64_t)(U - 1) * nthr < v_end; v += (uint64_t)U * nthr) {
       u32x4 x[U][W];
 #pragma unroll
       for (int u = 0; u < U; ++u)
 #pragma unroll
-        for (int w = 0; w < W; ++w) x[u][w] = ld16_cached(a.src[w] + v + (uint64_t)u * nthr);
+        for (int w = 0; w < W; ++w) x[u][w] = ld16(a.src[w] + v + (uint64_t)u * nthr);
 #pragma unroll
       for (int u = 0; u < U; ++u) st16(a.dst + v + (uint64_t)u * nthr, combine<DT, W>(x[u]));
     }
-    // ragged end of the chunk: one vector at a time
+    // ragged end of the tile: one vector at a time
     for (; v < v_end; v += nthr) {
       u32x4 x[W];
 #pragma unroll
-      for (int w = 0; w < W; ++w) x[w] = ld16_cached(a.src[w] + v);
+      for (int w = 0; w < W; ++w) x[w] = ld16(a.src[w] + v);
       st16(a.dst + v, combine<DT, W>(x));
     }
   }

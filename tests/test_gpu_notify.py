@@ -88,3 +88,30 @@ def test_delayed_producer_on_another_stream(plr, oracle_mod):
     torch.cuda.synchronize()
     assert plr.plr_check(L, ws, consumer) == plr.PLR_OK
     assert_same("bf16", dst.cpu().numpy().view(np.uint16), ref)
+
+
+@pytest.mark.parametrize("op", ["reduce", "copy"])
+def test_tiles_crossing_chunks(plr, oracle_mod, op):
+    """Few workgroups striding over many tiles, several tiles per chunk and ragged
+    ends on both levels: every chunk's flags are waited for exactly when needed."""
+    W, nbytes = 4, 37 * 1024 + 48
+    if op == "reduce":
+        srcs_np = [synth.normal_np(3, 2, w, nbytes // 2) for w in range(W)]
+        ref = oracle_mod.reduce("bf16", srcs_np)
+        L = plr.plr_layout_create("reduce", "bf16", W, nbytes, "packed", "packed", tile_bytes=1024,
+                                  chunk_bytes=4096, workgroups=3, block=64)
+    else:
+        nbytes = 16 * W * 150
+        srcs_np = [synth.bits_np(3, 4, s, nbytes) for s in range(W)]
+        ref = oracle_mod.copy_layout("scattered", "transposed", srcs_np).view(np.uint16)
+        L = plr.plr_layout_create("copy", "bf16", W, nbytes, "scattered", "transposed", tile_bytes=256,
+                                  chunk_bytes=1024, workgroups=5, block=64)
+    srcs = [to_dev(s) for s in srcs_np]
+    ws = torch.zeros(L.workspace_bytes, dtype=torch.uint8, device="cuda")
+    dst = torch.empty(L.dst_bytes, dtype=torch.uint8, device="cuda")
+    for epoch in range(1, 4):
+        for w in range(W):
+            plr.plr_notify(L, w, ws)
+        (plr.plr_reduce if op == "reduce" else plr.plr_copy)(L, srcs, dst, ws)
+        assert plr.plr_check(L, ws) == plr.PLR_OK
+        assert_same("bf16", dst.cpu().numpy().view(np.uint16), ref, f"epoch {epoch}")

@@ -16,9 +16,9 @@ from conftest import ROOT, golden_lines
 def plr():
     so = os.path.join(ROOT, "reduce_atom_amd", "libplr.so")
     if not os.path.exists(so):
-        from reduce_atom_amd import _build
+        import __graft_entry__
 
-        _build.build()
+        __graft_entry__._load_builder().build()
     import reduce_atom_amd
 
     return reduce_atom_amd
@@ -104,8 +104,22 @@ def test_chunks_and_workspace(plr):
 def test_policy_overrides(plr):
     L = plr.plr_layout_create("reduce", "f16", 4, 1 << 24, "packed", "packed", chunk_bytes=4096,
                               workgroups=33, block=128, unroll=4, datapath=plr.PLR_PATH_DIRECT)
-    assert L.policy() == dict(chunk_bytes=4096, workgroups=33, block=128, unroll=4, stages=2,
-                              datapath=plr.PLR_PATH_DIRECT)
+    assert L.policy() == dict(tile_bytes=4096, chunk_bytes=4096, workgroups=33, block=128, unroll=4,
+                              stages=2, datapath=plr.PLR_PATH_DIRECT)
+
+
+def test_tiles_and_chunks(plr):
+    # a chunk is a whole number of tiles of one segment; ragged ends on both levels
+    L = plr.plr_layout_create("reduce", "bf16", 2, 10 * 1024 + 32, "packed", "packed",
+                              tile_bytes=1024, chunk_bytes=3000 // 16 * 16)
+    p = L.policy()
+    assert p["tile_bytes"] == 1024 and p["chunk_bytes"] == 3072
+    assert L.ntiles == 11 and L.nchunks == 4
+    C = plr.plr_layout_create("copy", "bf16", 4, 4 * 4096, "scattered", "transposed", tile_bytes=1024,
+                              chunk_bytes=2048)
+    assert C.ntiles == 16 * 4 and C.nchunks == 16 * 2
+    T = plr.plr_layout_create("copy", "bf16", 2, 64, "packed", "packed", tile_bytes=1 << 20)
+    assert T.policy()["tile_bytes"] == 64 and T.ntiles == 2 and T.nchunks == 2
 
 
 def _code(fn, *a, **k):
