@@ -117,8 +117,9 @@ typedef struct {
                                  ceil(tiles / workgroups) consecutive tiles */
   int block;                  /* threads per workgroup: 64, 128, 256 or 512 */
   int unroll;                 /* 16-byte vectors per lane per pipeline step: 1, 2 or 4 */
-  int stages;                 /* LDS pipeline depth, 1..4 (PLR_PATH_LDS only) */
-  int datapath;               /* PLR_PATH_POLICY, PLR_PATH_DIRECT or PLR_PATH_LDS */
+  int stages;                 /* reserved (the LDS ring depth is fixed per W: 4, 3 or 2 stages) */
+  int datapath;               /* PLR_PATH_POLICY, PLR_PATH_DIRECT or PLR_PATH_LDS; the LDS path
+                                 needs 256-thread workgroups and tiles of whole 4 KiB slabs */
   uint64_t spin_limit;        /* polls of a chunk flag before PLR_ETIMEOUT; 0 = default (about a second) */
 } plr_layout_desc;
 

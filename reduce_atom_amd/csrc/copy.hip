@@ -55,8 +55,104 @@ __global__ void __launch_bounds__(512) k_copy_direct(const CopyArgs a) {
   }
 }
 
+// Segment addressing of tile t: source index, source and destination byte offsets.
+__device__ __forceinline__ void copy_tile_addr(const CopyArgs& a, uint32_t t, uint32_t& seg,
+                                               uint32_t& part, uint32_t& s, uint64_t& src_off,
+                                               uint64_t& dst_off) {
+  seg = t / a.tiles_per_seg;
+  part = t - seg * a.tiles_per_seg;
+  if (a.mode == kCopyTable) {
+    s = a.seg_src[seg];
+    src_off = a.seg_src_off[seg];
+    dst_off = a.seg_dst_off[seg];
+  } else {
+    s = seg / a.world;
+    const uint32_t d = seg - s * a.world;
+    src_off = (uint64_t)d * a.slice;
+    dst_off = ((uint64_t)d * a.world + s) * a.slice;
+  }
+}
+
+// LDS-staged variant (PLR_PATH_LDS): a workgroup of 256 threads walks its run of
+// tiles as 4 KiB slabs (1 KiB per wave); each wave keeps kCopyStages slabs in flight
+// through a private LDS ring (global->LDS DMA), waits only for the oldest, reads it
+// back and stores it at the layout's destination. Chunk flags are awaited before the
+// first DMA of a chunk.
+constexpr int kCopyStages = 8;
+
+__global__ void __launch_bounds__(256) k_copy_lds(const CopyArgs a) {
+  __shared__ u32x4 ring[4][kCopyStages][64];
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const uint32_t spt = (uint32_t)((a.tile_bytes + 4095) / 4096);  // slabs per tile
+  const uint32_t t0 = blockIdx.x * a.run;
+  const uint32_t t1 = min(a.ntiles, t0 + a.run);
+  const uint32_t j1 = (t1 - t0) * spt;
+  uint32_t ready = 0xFFFFFFFFu;
+
+  // byte offset of this lane's vector inside slab j's segment, and whether it exists
+  auto where = [&](uint32_t j, uint32_t& s, uint64_t& src_b, uint64_t& dst_b, bool& valid) -> uint32_t {
+    const uint32_t t = t0 + j / spt;
+    uint32_t seg, part;
+    uint64_t so, dof;
+    copy_tile_addr(a, t, seg, part, s, so, dof);
+    const uint64_t b = (uint64_t)part * a.tile_bytes + (j % spt) * 4096 + (uint64_t)wave * 1024;
+    const uint64_t tile_end = min((uint64_t)(part + 1) * a.tile_bytes, a.seg_len);
+    const uint64_t bl = b + (uint64_t)lane * 16;
+    valid = bl < tile_end;
+    const uint64_t bc = valid ? bl : a.seg_len - 16;  // ragged lanes re-read a valid vector
+    src_b = so + bc;
+    dst_b = dof + bl;
+    return seg * a.chunks_per_seg + part / a.tiles_per_chunk;
+  };
+
+  auto stage = [&](uint32_t j) -> bool {
+    uint32_t s;
+    uint64_t src_b, dst_b;
+    bool valid;
+    const uint32_t c = where(j, s, src_b, dst_b, valid);
+    if (a.nt.flags) {
+      const uint32_t f = s * a.nchunks + c;
+      if (f != ready) {
+        if (!wg_wait_flags(a.nt, a.nt.flags + f, 0, 1)) return false;
+        ready = f;
+      }
+    }
+    lds_dma16(a.src[s] + src_b, (PLR_LDS void*)&ring[wave][j % kCopyStages][0]);
+    return true;
+  };
+
+  for (uint32_t k = 0; k < kCopyStages - 1; ++k)
+    if (k < j1 && !stage(k)) {
+      wait_vmem<0>();
+      return;
+    }
+  for (uint32_t j = 0; j < j1; ++j) {
+    if (j + kCopyStages - 1 < j1) {
+      if (!stage(j + kCopyStages - 1)) {
+        wait_vmem<0>();
+        return;
+      }
+      wait_vmem<kCopyStages - 1>();
+    } else {
+      wait_vmem<0>();
+    }
+    const u32x4 x = lds_read16((const PLR_LDS u32x4*)&ring[wave][j % kCopyStages][lane]);
+    wait_lds_reads();
+    uint32_t s;
+    uint64_t src_b, dst_b;
+    bool valid;
+    where(j, s, src_b, dst_b, valid);
+    if (valid) st16(reinterpret_cast<u32x4*>(a.dst + dst_b), x);
+  }
+}
+
 hipError_t launch_copy(const CopyArgs& a, const Launch& l, hipStream_t s) {
   dim3 g(l.grid), b(l.block);
+  if (l.datapath == PLR_PATH_LDS) {
+    if (l.block != 256) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(k_copy_lds, g, b, 0, s, a);
+    return hipGetLastError();
+  }
   switch (l.unroll) {
     case 1: hipLaunchKernelGGL((k_copy_direct<1>), g, b, 0, s, a); break;
     case 2: hipLaunchKernelGGL((k_copy_direct<2>), g, b, 0, s, a); break;

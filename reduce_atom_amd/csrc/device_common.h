@@ -171,3 +171,36 @@ __device__ __forceinline__ bool wg_wait_flags(const Notify& nt, const uint64_t* 
 }
 
 }  // namespace plr
+
+namespace plr {
+
+// ---- LDS staging (the Atom pipeline through workgroup-local memory) ----
+// gfx950 global->LDS DMA: each lane's 16 bytes land at lds_base + 16*lane, where
+// lds_base is wave-uniform. The LDS reads that consume a stage are issued as inline
+// ds_read_b128 with explicit waits, so that the compiler does not wait for every
+// DMA in flight (it cannot tell the stages of the ring apart) and the pipeline keeps
+// S-1 stages loading while one is consumed.
+#define PLR_LDS __attribute__((address_space(3)))
+
+__device__ __forceinline__ void lds_dma16(const void* gsrc, PLR_LDS void* lds_base) {
+  __builtin_amdgcn_global_load_lds(gsrc, lds_base, 16, 0, 0);
+}
+
+// Wait until at most N vector-memory operations of this wave are outstanding. Loads
+// complete in issue order, so once at most N operations are outstanding every load
+// issued before the last N memory operations has landed (stores issued in between
+// only make the wait stricter).
+template <int N>
+__device__ __forceinline__ void wait_vmem() {
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+__device__ __forceinline__ u32x4 lds_read16(const PLR_LDS u32x4* p) {
+  u32x4 v;
+  asm volatile("ds_read_b128 %0, %1" : "=v"(v) : "v"((uint32_t)(uintptr_t)p) : "memory");
+  return v;
+}
+
+__device__ __forceinline__ void wait_lds_reads() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
+
+}  // namespace plr

@@ -178,8 +178,13 @@ extern "C" int plr_layout_create(const plr_layout_desc* d, plr_layout** out) {
   }
   if (d->datapath) {
     if (d->datapath != PLR_PATH_DIRECT && d->datapath != PLR_PATH_LDS) return fail(PLR_EINVAL);
-    if (d->datapath == PLR_PATH_LDS) return fail(PLR_EUNSUPPORTED);
     L->datapath = d->datapath;
+  }
+  if (L->datapath == PLR_PATH_LDS) {
+    // the staged pipeline runs 256-thread workgroups over 4 KiB slabs per source
+    if (d->block && d->block != 256) return fail(PLR_EINVAL);
+    L->block = 256;
+    if (!d->tile_bytes && L->tile_bytes % 4096) L->tile_bytes = 4096;
   }
   L->spin_limit = d->spin_limit ? d->spin_limit : kDefaultSpinLimit;
 
@@ -195,6 +200,7 @@ extern "C" int plr_layout_create(const plr_layout_desc* d, plr_layout** out) {
     const uint64_t cps = (tps + tpc - 1) / tpc;
     const uint64_t nseg = L->op == PLR_OP_REDUCE ? 1 : L->segs.size();
     if (tps * nseg > 0x7FFFFFFFull) return fail(PLR_EUNSUPPORTED);
+    if (L->datapath == PLR_PATH_LDS && tps > 1 && tile % 4096) return fail(PLR_EINVAL);
     L->tile_bytes = tile;
     L->chunk_bytes = tile * tpc;
     L->tiles_per_seg = (uint32_t)tps;

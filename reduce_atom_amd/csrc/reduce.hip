@@ -51,9 +51,80 @@ __global__ void __launch_bounds__(512) k_reduce_direct(const ReduceArgs a) {
   }
 }
 
+// LDS-staged variant (PLR_PATH_LDS): the SNAC stage / consume split made explicit.
+// A workgroup of 256 threads walks its run of tiles as slabs of 256 vectors per
+// source; wave k owns vectors [64k, 64k+64) of every slab and a private ring of S
+// stages in LDS (S x W x 1 KiB per wave). The wave issues the DMA of slab j+S-1 into
+// its ring, waits only for slab j, reads slab j's W vectors back from LDS, reduces
+// them in source order and stores. Chunk flags are awaited (by the whole workgroup)
+// before the first DMA into a new chunk.
+template <int W>
+struct LdsRing {
+  static constexpr int S = W <= 4 ? 4 : (W <= 8 ? 3 : 2);  // stages; S*W*4 KiB <= 128 KiB
+};
+
+template <int DT, int W>
+__global__ void __launch_bounds__(256) k_reduce_lds(const ReduceArgs a) {
+  constexpr int S = LdsRing<W>::S;
+  __shared__ u32x4 ring[4][S][W][64];
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  // tiles are whole slabs (or the share is a single tile shorter than one slab)
+  const uint64_t slabs_per_tile = (a.tile_vecs + 255) / 256;
+  const uint64_t nslab_all = (a.nvec + 255) / 256;
+  const uint64_t j0 = (uint64_t)blockIdx.x * a.run * slabs_per_tile;
+  const uint64_t j1 = min(nslab_all, (uint64_t)(blockIdx.x + 1) * a.run * slabs_per_tile);
+  uint32_t ready = 0xFFFFFFFFu;
+
+  // stage slab j: every wave always issues exactly W DMAs (ragged lanes re-read the
+  // last vector instead of skipping), so the wait counts stay exact
+  auto stage = [&](uint64_t j) -> bool {
+    if (a.nt.flags) {
+      const uint32_t c = (uint32_t)(j / slabs_per_tile) / a.tiles_per_chunk;
+      if (c != ready) {
+        if (!wg_wait_flags(a.nt, a.nt.flags + c, a.nchunks, W)) return false;
+        ready = c;
+      }
+    }
+    const uint64_t v = min(j * 256 + (uint64_t)wave * 64 + lane, a.nvec - 1);
+    const int st = (int)(j % S);
+#pragma unroll
+    for (int w = 0; w < W; ++w) lds_dma16(a.src[w] + v, (PLR_LDS void*)&ring[wave][st][w][0]);
+    return true;
+  };
+
+  for (int k = 0; k < S - 1; ++k)
+    if (j0 + k < j1 && !stage(j0 + k)) {
+      wait_vmem<0>();
+      return;
+    }
+  for (uint64_t j = j0; j < j1; ++j) {
+    if (j + S - 1 < j1) {
+      if (!stage(j + S - 1)) {
+        wait_vmem<0>();
+        return;
+      }
+      wait_vmem<(S - 1) * W>();
+    } else {
+      wait_vmem<0>();
+    }
+    const int st = (int)(j % S);
+    u32x4 x[W];
+#pragma unroll
+    for (int w = 0; w < W; ++w) x[w] = lds_read16((const PLR_LDS u32x4*)&ring[wave][st][w][lane]);
+    wait_lds_reads();
+    const uint64_t v = j * 256 + (uint64_t)wave * 64 + lane;
+    if (v < a.nvec) st16(a.dst + v, combine<DT, W>(x));
+  }
+}
+
 template <int DT, int W>
 static hipError_t launch_w(const ReduceArgs& a, const Launch& l, hipStream_t s) {
   dim3 g(l.grid), b(l.block);
+  if (l.datapath == PLR_PATH_LDS) {
+    if (l.block != 256) return hipErrorInvalidValue;
+    hipLaunchKernelGGL((k_reduce_lds<DT, W>), g, b, 0, s, a);
+    return hipGetLastError();
+  }
   switch (l.unroll) {
     case 1: hipLaunchKernelGGL((k_reduce_direct<DT, W, 1>), g, b, 0, s, a); break;
     case 2: hipLaunchKernelGGL((k_reduce_direct<DT, W, 2>), g, b, 0, s, a); break;

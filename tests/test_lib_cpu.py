@@ -186,3 +186,17 @@ def test_strerror(plr):
         assert plr.plr_strerror(code)
     assert "timed out" in plr.plr_strerror(plr.PLR_ETIMEOUT)
     assert plr.plr_version().startswith("plr")
+
+
+def test_lds_datapath_layouts(plr):
+    L = plr.plr_layout_create("reduce", "bf16", 8, 1 << 20, "packed", "packed", datapath=plr.PLR_PATH_LDS)
+    p = L.policy()
+    assert p["datapath"] == plr.PLR_PATH_LDS and p["block"] == 256 and p["tile_bytes"] % 4096 == 0
+    C = plr.plr_layout_create("copy", "bf16", 4, 1 << 16, "packed", "packed", datapath=plr.PLR_PATH_LDS)
+    assert C.policy()["block"] == 256
+    # a single short tile is fine; several tiles must be whole 4 KiB slabs
+    plr.plr_layout_create("reduce", "bf16", 2, 1024, "packed", "packed", datapath=plr.PLR_PATH_LDS)
+    assert _code(plr.plr_layout_create, "reduce", "bf16", 2, 16384, "packed", "packed",
+                 datapath=plr.PLR_PATH_LDS, tile_bytes=2048) == plr.PLR_EINVAL
+    assert _code(plr.plr_layout_create, "reduce", "bf16", 2, 16384, "packed", "packed",
+                 datapath=plr.PLR_PATH_LDS, block=128) == plr.PLR_EINVAL
