@@ -204,7 +204,7 @@ def run_bench(args):
         "alltoall": plr.plr_layout_create("copy", "bf16", W, B4, "scattered", "transposed"),
     }
     ws = {k: torch.zeros(l.workspace_bytes, dtype=torch.uint8, device=dev) for k, l in L.items()}
-    scratch = torch.empty(plr.plr_copy_v_scratch_bytes(W, [R5] * W), dtype=torch.uint8, device=dev)
+    scratch = torch.zeros(plr.plr_copy_v_scratch_bytes(W, [R5] * W), dtype=torch.uint8, device=dev)
 
     def op(name):
         if name == "reduce":

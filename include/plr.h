@@ -83,6 +83,14 @@ typedef enum { PLR_PACKED = 0, PLR_SCATTERED = 1, PLR_TRANSPOSED = 2 } plr_layou
  * workgroup-local memory; on gfx950 it can also go straight through registers) ---- */
 enum { PLR_PATH_POLICY = 0, PLR_PATH_DIRECT = 1, PLR_PATH_LDS = 2 };
 
+/* ---- how a notified call waits (section 3.2 "SNAC": a consumer never reads a chunk
+ * before its flag). PLR_NOTIFY_CHUNKS: every workgroup waits for the flags of each
+ * chunk it enters, then fences (agent-scope acquire). PLR_NOTIFY_CHECK: a one-workgroup
+ * check kernel first reads all flags and records which have arrived; the consuming
+ * kernel reads those chunks without waiting (the kernel boundary orders it after the
+ * producers) and waits, as above, only for the chunks whose flags were still missing. ---- */
+enum { PLR_NOTIFY_POLICY = 0, PLR_NOTIFY_CHUNKS = 1, PLR_NOTIFY_CHECK = 2 };
+
 /* ---- reduction mode (README "Deterministic Reduction"): only the deterministic,
  * source-ordered reduction exists here. ---- */
 enum { PLR_MODE_DETERMINISTIC = 0 };
@@ -121,6 +129,8 @@ typedef struct {
   int datapath;               /* PLR_PATH_POLICY, PLR_PATH_DIRECT or PLR_PATH_LDS; the LDS path
                                  needs 256-thread workgroups and tiles of whole 4 KiB slabs */
   uint64_t spin_limit;        /* polls of a chunk flag before PLR_ETIMEOUT; 0 = default (about a second) */
+  int notify_mode;            /* PLR_NOTIFY_POLICY (check first for shares over 2 MiB, in-kernel
+                                 waits below), PLR_NOTIFY_CHUNKS or PLR_NOTIFY_CHECK */
 } plr_layout_desc;
 
 typedef struct plr_layout plr_layout; /* opaque, host only */
@@ -135,8 +145,9 @@ int plr_layout_create(const plr_layout_desc* desc, plr_layout** out);
 /* Free a layout (NULL is accepted). */
 void plr_layout_destroy(plr_layout* L);
 
-/* Bytes of workspace a notified call needs: a 256-byte header (error word) followed
- * by the chunk flags, uint64_t flags[W][nchunks]. The caller allocates it in device
+/* Bytes of workspace a notified call needs: a 256-byte header (u64 error word at
+ * byte 0, u64 ready word at byte 8), the chunk flags uint64_t flags[W][nchunks], and
+ * their check-time mirror uint64_t mirror[W][nchunks]. The caller allocates it in device
  * memory, ZEROED, once; it is never reset between calls (the epoch only grows,
  * section 4.3 "Epoch Bookkeeping"). One workspace belongs to one layout. */
 size_t plr_layout_workspace_bytes(const plr_layout* L);
@@ -159,7 +170,8 @@ int plr_layout_segment(const plr_layout* L, int k, int* src, size_t* src_off,
 /* The resolved launch policy (after the built-in table and the overrides).
  * workgroups == 0 means one workgroup per tile. Any output pointer may be NULL. */
 int plr_layout_policy(const plr_layout* L, size_t* tile_bytes, size_t* chunk_bytes,
-                      int* workgroups, int* block, int* unroll, int* stages, int* datapath);
+                      int* workgroups, int* block, int* unroll, int* stages, int* datapath,
+                      int* notify_mode);
 
 /* Current epoch E of the layout: the last notified call consumed flags >= E. */
 uint64_t plr_layout_epoch(const plr_layout* L);
@@ -194,7 +206,9 @@ int plr_copy(plr_layout* L, const void* const* srcs, void* dst, void* workspace,
  *                    destinations in order, and sources in order inside one
  *   dst (device, sum(rows) * row_bytes)    row i of source s lands at row
  *                    offsets[d*W + s] + (rows i' < i of source s bound for d)
- *   scratch (device, plr_copy_v_scratch_bytes bytes, contents need no init)
+ *   scratch (device, plr_copy_v_scratch_bytes bytes): zero it once before the first
+ *            call; every call leaves its 256-byte header at zero again (the rank array
+ *            after it needs no initialisation). Concurrent calls need distinct scratch.
  *   srcs, dest_of_row: host arrays of W device pointers; rows_per_src: host array.
  * A destination id outside [0, W) is a caller error: its row is skipped and its
  * counts and offsets are undefined.
@@ -203,7 +217,8 @@ int plr_copy_v(int world, const void* const* srcs, const int64_t* rows_per_src,
                const int32_t* const* dest_of_row, size_t row_bytes, void* dst,
                int64_t* counts, int64_t* offsets, void* scratch, void* stream);
 
-/* Scratch bytes plr_copy_v needs for these row counts (host only). */
+/* Scratch bytes plr_copy_v needs for these row counts (host only): a 256-byte header
+ * plus one int32 per row, rounded up to 256 bytes. */
 size_t plr_copy_v_scratch_bytes(int world, const int64_t* rows_per_src);
 
 /* Producer side of notify (section 3.2 "SNAC"; section 4.3: the epoch supplies the

@@ -29,6 +29,7 @@ PLR_OP_REDUCE, PLR_OP_COPY = 0, 1
 PLR_PACKED, PLR_SCATTERED, PLR_TRANSPOSED = 0, 1, 2
 PLR_PATH_POLICY, PLR_PATH_DIRECT, PLR_PATH_LDS = 0, 1, 2
 PLR_MODE_DETERMINISTIC = 0
+PLR_NOTIFY_POLICY, PLR_NOTIFY_CHUNKS, PLR_NOTIFY_CHECK = 0, 1, 2
 PLR_MAX_WORLD = 16
 
 DTYPE_CODES = {"bf16": PLR_BF16, "f16": PLR_F16, "f32": PLR_F32}
@@ -49,6 +50,7 @@ class plr_layout_desc(_c.Structure):
         ("tile_bytes", _sz), ("chunk_bytes", _sz),
         ("workgroups", _i), ("block", _i), ("unroll", _i), ("stages", _i), ("datapath", _i),
         ("spin_limit", _u64),
+        ("notify_mode", _i),
     ]
 
 
@@ -67,7 +69,7 @@ _lib.plr_layout_epoch.restype = _u64
 _lib.plr_layout_segment.argtypes = [_vp, _i, _c.POINTER(_i), _c.POINTER(_sz), _c.POINTER(_sz),
                                     _c.POINTER(_sz)]
 _lib.plr_layout_segment.restype = _i
-_lib.plr_layout_policy.argtypes = [_vp, _c.POINTER(_sz), _c.POINTER(_sz)] + [_c.POINTER(_i)] * 5
+_lib.plr_layout_policy.argtypes = [_vp, _c.POINTER(_sz), _c.POINTER(_sz)] + [_c.POINTER(_i)] * 6
 _lib.plr_layout_policy.restype = _i
 _lib.plr_reduce.argtypes = [_vp, _c.POINTER(_vp), _vp, _vp, _vp]
 _lib.plr_reduce.restype = _i
@@ -191,17 +193,18 @@ class Layout:
         return _lib.plr_layout_ntiles(self._h)
 
     def policy(self) -> dict:
-        tb, cb, wg, bl, un, st, dp = _sz(), _sz(), _i(), _i(), _i(), _i(), _i()
+        tb, cb, wg, bl, un, st, dp, nm = _sz(), _sz(), _i(), _i(), _i(), _i(), _i(), _i()
         _ok(_lib.plr_layout_policy(self._h, _c.byref(tb), _c.byref(cb), _c.byref(wg), _c.byref(bl),
-                                   _c.byref(un), _c.byref(st), _c.byref(dp)), "plr_layout_policy")
+                                   _c.byref(un), _c.byref(st), _c.byref(dp), _c.byref(nm)),
+            "plr_layout_policy")
         return dict(tile_bytes=tb.value, chunk_bytes=cb.value, workgroups=wg.value, block=bl.value,
-                    unroll=un.value, stages=st.value, datapath=dp.value)
+                    unroll=un.value, stages=st.value, datapath=dp.value, notify_mode=nm.value)
 
 
 def plr_layout_create(op, dtype, world, bytes_per_src, in_kind, out_kind, rank=0,
                       in_offsets=None, out_offsets=None, mode=PLR_MODE_DETERMINISTIC,
                       tile_bytes=0, chunk_bytes=0, workgroups=0, block=0, unroll=0, stages=0, datapath=0,
-                      spin_limit=0) -> Layout:
+                      spin_limit=0, notify_mode=0) -> Layout:
     """Compile a layout. op/dtype/kinds accept the C enum values or their names."""
     d = plr_layout_desc()
     d.op = OP_CODES.get(op, op)
@@ -220,6 +223,7 @@ def plr_layout_create(op, dtype, world, bytes_per_src, in_kind, out_kind, rank=0
         d.out_offsets = _c.cast(a, _c.POINTER(_sz))
     d.mode, d.tile_bytes, d.chunk_bytes, d.workgroups = mode, tile_bytes, chunk_bytes, workgroups
     d.block, d.unroll, d.stages, d.datapath, d.spin_limit = block, unroll, stages, datapath, spin_limit
+    d.notify_mode = notify_mode
     h = _vp()
     _ok(_lib.plr_layout_create(_c.byref(d), _c.byref(h)), "plr_layout_create")
     return Layout(h.value)

@@ -74,12 +74,30 @@ int check_call(const plr_layout* L, plr_op op, const void* const* srcs, const vo
   nt->err = nullptr;
   nt->epoch = L->epoch + 1;
   nt->spin_limit = L->spin_limit;
+  nt->ready = nullptr;
+  nt->mirror = nullptr;
   if (workspace) {
     if (!a16(workspace)) return PLR_EALIGN;
     nt->err = static_cast<uint64_t*>(workspace);
     nt->flags = reinterpret_cast<const uint64_t*>(static_cast<char*>(workspace) + kWorkspaceHeader);
+    if (L->notify_mode == PLR_NOTIFY_CHECK) {
+      nt->ready = static_cast<uint64_t*>(workspace) + 1;
+      nt->mirror = nt->flags + (uint64_t)L->world * L->nchunks;
+    }
   }
   return PLR_OK;
+}
+
+// The check kernel of a notified call in PLR_NOTIFY_CHECK mode.
+hipError_t launch_check_for(const plr_layout* L, const Notify& nt, hipStream_t s) {
+  if (!nt.ready || !L->ntiles) return hipSuccess;
+  CheckArgs c{};
+  c.flags = nt.flags;
+  c.nflags = (uint64_t)L->world * L->nchunks;
+  c.epoch = nt.epoch;
+  c.ready = const_cast<uint64_t*>(nt.ready);
+  c.mirror = const_cast<uint64_t*>(nt.mirror);
+  return launch_check(c, s);
 }
 
 }  // namespace
@@ -103,7 +121,8 @@ extern "C" int plr_reduce(plr_layout* L, const void* const* srcs, void* dst, voi
     a.nt = nt;
     const Launch l = launch_of(L, nt.flags != nullptr);
     a.run = l.run;
-    hipError_t e = launch_reduce(a, L->dtype, l, static_cast<hipStream_t>(stream));
+    hipError_t e = launch_check_for(L, nt, static_cast<hipStream_t>(stream));
+    if (e == hipSuccess) e = launch_reduce(a, L->dtype, l, static_cast<hipStream_t>(stream));
     if (e != hipSuccess) return hip_fail(e);
   }
   if (workspace) L->epoch = nt.epoch;
@@ -142,19 +161,23 @@ extern "C" int plr_copy(plr_layout* L, const void* const* srcs, void* dst, void*
     }
     const Launch l = launch_of(L, nt.flags != nullptr);
     a.run = l.run;
-    hipError_t e = launch_copy(a, l, static_cast<hipStream_t>(stream));
+    hipError_t e = launch_check_for(L, nt, static_cast<hipStream_t>(stream));
+    if (e == hipSuccess) e = launch_copy(a, l, static_cast<hipStream_t>(stream));
     if (e != hipSuccess) return hip_fail(e);
   }
   if (workspace) L->epoch = nt.epoch;
   return PLR_OK;
 }
 
+// Scratch of plr_copy_v: a 256-byte header (u32 ticket at byte 0) then int32 rank[rows].
+constexpr uint64_t kCopyVScratchHeader = 256;
+
 extern "C" size_t plr_copy_v_scratch_bytes(int world, const int64_t* rows_per_src) {
   if (world < 1 || world > PLR_MAX_WORLD || !rows_per_src) return 0;
   uint64_t total = 0;
   for (int s = 0; s < world; ++s) total += rows_per_src[s] > 0 ? (uint64_t)rows_per_src[s] : 0;
   const uint64_t bytes = total * sizeof(int32_t);
-  return (size_t)std::max<uint64_t>(256, (bytes + 255) & ~255ull);
+  return (size_t)(kCopyVScratchHeader + ((bytes + 255) & ~255ull));
 }
 
 extern "C" int plr_copy_v(int world, const void* const* srcs, const int64_t* rows_per_src,
@@ -192,7 +215,8 @@ extern "C" int plr_copy_v(int world, const void* const* srcs, const int64_t* row
   a.dst = static_cast<uint8_t*>(dst);
   a.counts = counts;
   a.offsets = offsets;
-  a.rank = static_cast<int32_t*>(scratch);
+  a.ticket = static_cast<uint32_t*>(scratch);
+  a.rank = reinterpret_cast<int32_t*>(static_cast<char*>(scratch) + kCopyVScratchHeader);
   a.row_bytes = row_bytes;
   a.world = (uint32_t)world;
   // one row per wave: four rows per 256-thread workgroup

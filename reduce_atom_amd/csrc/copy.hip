@@ -15,6 +15,7 @@ template <int U>
 __global__ void __launch_bounds__(512) k_copy_direct(const CopyArgs a) {
   const uint32_t nthr = blockDim.x;
   uint32_t ready = 0xFFFFFFFFu;  // flag (source, chunk) this workgroup has already seen
+  const bool wait = must_wait(a.nt);
   const uint32_t t_end = min(a.ntiles, (blockIdx.x + 1) * a.run);
   for (uint32_t t = blockIdx.x * a.run; t < t_end; ++t) {
     const uint32_t seg = t / a.tiles_per_seg;
@@ -31,11 +32,11 @@ __global__ void __launch_bounds__(512) k_copy_direct(const CopyArgs a) {
       src_off = (uint64_t)d * a.slice;
       dst_off = ((uint64_t)d * a.world + s) * a.slice;
     }
-    if (a.nt.flags) {
+    if (wait) {
       const uint32_t c = seg * a.chunks_per_seg + part / a.tiles_per_chunk;
       const uint32_t f = s * a.nchunks + c;
       if (f != ready) {
-        if (!wg_wait_flags(a.nt, a.nt.flags + f, 0, 1)) return;
+        if (!wg_wait_flags(a.nt, f, 0, 1)) return;
         ready = f;
       }
     }
@@ -88,6 +89,7 @@ __global__ void __launch_bounds__(256) k_copy_lds(const CopyArgs a) {
   const uint32_t t1 = min(a.ntiles, t0 + a.run);
   const uint32_t j1 = (t1 - t0) * spt;
   uint32_t ready = 0xFFFFFFFFu;
+  const bool wait = must_wait(a.nt);
 
   // byte offset of this lane's vector inside slab j's segment, and whether it exists
   auto where = [&](uint32_t j, uint32_t& s, uint64_t& src_b, uint64_t& dst_b, bool& valid) -> uint32_t {
@@ -110,10 +112,10 @@ __global__ void __launch_bounds__(256) k_copy_lds(const CopyArgs a) {
     uint64_t src_b, dst_b;
     bool valid;
     const uint32_t c = where(j, s, src_b, dst_b, valid);
-    if (a.nt.flags) {
+    if (wait) {
       const uint32_t f = s * a.nchunks + c;
       if (f != ready) {
-        if (!wg_wait_flags(a.nt, a.nt.flags + f, 0, 1)) return false;
+        if (!wg_wait_flags(a.nt, f, 0, 1)) return false;
         ready = f;
       }
     }

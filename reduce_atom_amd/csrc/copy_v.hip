@@ -6,10 +6,10 @@
 //   kernel 1 (one workgroup per source): counts[s][d] and, for every row, its rank
 //            among the earlier rows of the same source bound for the same
 //            destination (wave ballots plus a workgroup-wide exclusive scan);
-//   kernel 2 (many workgroups): a prologue in every workgroup turns the W*W counts
-//            into offsets[d][s] (an exclusive scan in destination-major order),
-//            then each wave moves whole rows with 16-byte loads and stores to row
-//            offsets[d][s] + rank.
+//            The last of those workgroups turns the W*W counts into offsets[d][s]
+//            (an exclusive scan in destination-major order);
+//   kernel 2 (one wave per row): moves whole rows with 16-byte loads and stores to
+//            row offsets[d][s] + rank.
 #include "device_common.h"
 
 namespace plr {
@@ -21,9 +21,14 @@ constexpr int kRankWaves = kRankThreads / 64;
 // one per thread; a wave ballot per destination gives each row its rank among the
 // earlier lanes bound for the same destination, per-wave totals in LDS give the
 // ranks of earlier waves, and a carry per destination accumulates earlier passes.
+// The last workgroup to finish (a ticket counter in scratch, released and acquired
+// at agent scope) turns the W*W counts into offsets[d][s]: an exclusive scan in
+// destination-major order. It leaves the ticket at zero for the next call.
 __global__ void __launch_bounds__(kRankThreads) k_copy_v_rank(const CopyVArgs a) {
   __shared__ int32_t wave_cnt[kRankWaves][PLR_MAX_WORLD];
   __shared__ int32_t carry[PLR_MAX_WORLD];
+  __shared__ int64_t cnt[PLR_MAX_WORLD * PLR_MAX_WORLD];
+  __shared__ int last;
 
   const int s = blockIdx.x;
   const int W = (int)a.world;
@@ -64,50 +69,53 @@ __global__ void __launch_bounds__(kRankThreads) k_copy_v_rank(const CopyVArgs a)
     __syncthreads();
   }
   if (t < W) a.counts[s * W + t] = carry[t];
+
+  // ticket: the last workgroup sees every source's counts
+  __syncthreads();
+  if (t == 0) {
+    const uint32_t done = __hip_atomic_fetch_add(a.ticket, 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
+    last = (done == (uint32_t)W - 1);
+  }
+  __syncthreads();
+  if (!last) return;
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+  const int WW = W * W;
+  if (t < WW) cnt[t] = __hip_atomic_load(a.counts + t, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  __syncthreads();
+  if (t < WW) {
+    // block (d, s): every block of a smaller destination, then the blocks of
+    // smaller sources for the same destination
+    const int d = t / W, s2 = t - d * W;
+    int64_t o = 0;
+    for (int d2 = 0; d2 < d; ++d2)
+      for (int s3 = 0; s3 < W; ++s3) o += cnt[s3 * W + d2];
+    for (int s3 = 0; s3 < s2; ++s3) o += cnt[s3 * W + d];
+    a.offsets[t] = o;
+  }
+  if (t == 0) __hip_atomic_store(a.ticket, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 constexpr int kScatterThreads = 256;
 constexpr int kScatterUnroll = 16;
 
-// Kernel 2: a prologue in every workgroup scans the W*W counts (workgroup 0 also
-// writes them out as offsets); then wave k of the grid moves row k: all of a
+// Kernel 2: wave k of the grid moves row k. The row's loads are issued first (a
+// source row exists whatever its destination); its destination, rank and block
+// offset are read meanwhile, and the stores go to row offsets[d][s] + rank. All of a
 // 14,336-byte row (14 vectors per lane) is in flight at once.
 __global__ void __launch_bounds__(kScatterThreads) k_copy_v_scatter(const CopyVArgs a) {
-  __shared__ int64_t cnt[PLR_MAX_WORLD * PLR_MAX_WORLD];
-  __shared__ int64_t off[PLR_MAX_WORLD * PLR_MAX_WORLD];
   const int W = (int)a.world;
-  const int WW = W * W;
-  const int t = threadIdx.x;
-  if (t < WW) cnt[t] = a.counts[t];
-  __syncthreads();
-  if (t < WW) {
-    // block (d, s): every block of a smaller destination, then the blocks of
-    // smaller sources for the same destination
-    const int d = t / W, s = t - d * W;
-    int64_t o = 0;
-    for (int d2 = 0; d2 < d; ++d2)
-      for (int s2 = 0; s2 < W; ++s2) o += cnt[s2 * W + d2];
-    for (int s2 = 0; s2 < s; ++s2) o += cnt[s2 * W + d];
-    off[t] = o;
-    if (blockIdx.x == 0) a.offsets[t] = o;
-  }
-  __syncthreads();
-
-  const int lane = t & 63;
+  const int lane = threadIdx.x & 63;
   const uint64_t nvec = a.row_bytes >> 4;
   const int64_t total = a.row_start[W];
   const int waves_per_block = kScatterThreads / 64;
-  const int64_t wave = (int64_t)blockIdx.x * waves_per_block + __builtin_amdgcn_readfirstlane(t >> 6);
+  const int64_t wave =
+      (int64_t)blockIdx.x * waves_per_block + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int64_t nwaves = (int64_t)gridDim.x * waves_per_block;
   for (int64_t r = wave; r < total; r += nwaves) {
     int s = 0;
     while (r >= a.row_start[s + 1]) ++s;
     const int64_t i = r - a.row_start[s];
-    const int32_t d = a.dest[s][i];
-    if (d < 0 || d >= W) continue;
-    const int64_t out = off[d * W + s] + a.rank[r];
     const u32x4* src = reinterpret_cast<const u32x4*>(a.src[s] + (uint64_t)i * a.row_bytes);
-    u32x4* dst = reinterpret_cast<u32x4*>(a.dst + (uint64_t)out * a.row_bytes);
     for (uint64_t v0 = 0; v0 < nvec; v0 += 64 * kScatterUnroll) {
       u32x4 x[kScatterUnroll];
 #pragma unroll
@@ -115,6 +123,10 @@ __global__ void __launch_bounds__(kScatterThreads) k_copy_v_scatter(const CopyVA
         const uint64_t v = v0 + (uint64_t)u * 64 + lane;
         if (v < nvec) x[u] = ld16(src + v);
       }
+      const int32_t d = a.dest[s][i];
+      if (d < 0 || d >= W) break;  // not a destination: the row is dropped
+      const int64_t out = a.offsets[d * W + s] + a.rank[r];
+      u32x4* dst = reinterpret_cast<u32x4*>(a.dst + (uint64_t)out * a.row_bytes);
 #pragma unroll
       for (int u = 0; u < kScatterUnroll; ++u) {
         const uint64_t v = v0 + (uint64_t)u * 64 + lane;

@@ -119,30 +119,35 @@ __device__ __forceinline__ u32x4 combine(const u32x4* x) {
 }
 
 // ---- consumer side of notify (section 3.2) ----
-// Lanes 0..n-1 of the calling wave each poll one flag (first + lane*stride) until it
-// reaches nt.epoch, with a bounded number of polls. Returns true when every flag
-// arrived; the acquire fence then orders the wave's later loads after the producer's
-// release. On a timeout one lane records PLR_ETIMEOUT in the sticky error word;
-// if another wave already recorded an error the wave gives up too. All lanes of the
-// wave must call this together.
-__device__ __forceinline__ bool wait_flags(const Notify& nt, const uint64_t* first, uint64_t stride,
-                                           int n) {
+// Lanes 0..n-1 of the calling wave each own one flag, index first + lane*stride in the
+// layout's flag array. A lane whose flag the check kernel already saw arrive (mirror,
+// check mode) needs nothing more: that kernel's acquire and the kernel boundary order
+// this kernel after the producer. Otherwise the lane polls the flag until it reaches
+// nt.epoch, within a bounded number of polls, and the wave then executes one
+// agent-scope acquire fence. On a timeout one lane records PLR_ETIMEOUT in the sticky
+// error word; if another wave already recorded an error the wave gives up too.
+// Returns true when every flag has arrived. All lanes of the wave call this together.
+__device__ __forceinline__ bool wait_flags(const Notify& nt, uint64_t first, uint64_t stride, int n) {
   const int lane = __lane_id();
-  int bad = 0;
+  int bad = 0, polled = 0;
   if (lane < n) {
-    const uint64_t* f = first + (uint64_t)lane * stride;
-    uint64_t polls = 0;
-    while (__hip_atomic_load(f, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < nt.epoch) {
-      if (++polls >= nt.spin_limit) {
-        bad = 1;
-        break;
+    const uint64_t i = first + (uint64_t)lane * stride;
+    if (!(nt.mirror && nt.mirror[i] == nt.epoch)) {
+      polled = 1;
+      const uint64_t* f = nt.flags + i;
+      uint64_t polls = 0;
+      while (__hip_atomic_load(f, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < nt.epoch) {
+        if (++polls >= nt.spin_limit) {
+          bad = 1;
+          break;
+        }
+        if ((polls & 63) == 0 &&
+            __hip_atomic_load(nt.err, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0) {
+          bad = 2;
+          break;
+        }
+        __builtin_amdgcn_s_sleep(2);
       }
-      if ((polls & 63) == 0 &&
-          __hip_atomic_load(nt.err, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0) {
-        bad = 2;
-        break;
-      }
-      __builtin_amdgcn_s_sleep(2);
     }
   }
   const uint64_t timed_out = __ballot(bad == 1);
@@ -155,8 +160,14 @@ __device__ __forceinline__ bool wait_flags(const Notify& nt, const uint64_t* fir
     }
     return false;
   }
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+  if (__ballot(polled)) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
   return true;
+}
+
+// True when the call must look at chunk flags itself: it is notified and the check
+// kernel that ran before it (stream order) did not find every flag already arrived.
+__device__ __forceinline__ bool must_wait(const Notify& nt) {
+  return nt.flags && !(nt.ready && *nt.ready == nt.epoch);
 }
 
 // Workgroup form: only wave 0 polls and executes the agent-scope acquire (on a chip
@@ -164,8 +175,7 @@ __device__ __forceinline__ bool wait_flags(const Notify& nt, const uint64_t* fir
 // workgroup and chunk, not once per wave); the workgroup barrier then orders the
 // other waves' loads after it. Returns false on a timeout or an earlier error. Every
 // thread of the workgroup must call this together.
-__device__ __forceinline__ bool wg_wait_flags(const Notify& nt, const uint64_t* first, uint64_t stride,
-                                              int n) {
+__device__ __forceinline__ bool wg_wait_flags(const Notify& nt, uint64_t first, uint64_t stride, int n) {
   const bool ok = (threadIdx.x >> 6) ? true : wait_flags(nt, first, stride, n);
   return !__syncthreads_or(!ok);
 }

@@ -14,6 +14,8 @@ namespace plr {
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));  // one 16-byte vector
 
 constexpr int kMaxTableSegs = 64;   // explicit segment table carried in kernarg
+// Workspace: u64 error word at byte 0, u64 ready word at byte 8, then
+// uint64 flags[W][nchunks], then their check-time mirror uint64 mirror[W][nchunks].
 constexpr size_t kWorkspaceHeader = 256;
 constexpr uint64_t kDefaultSpinLimit = 1ull << 20;
 
@@ -31,8 +33,18 @@ struct Launch {
 struct Notify {
   const uint64_t* flags;  // [W][nchunks], or nullptr when the call is not notified
   uint64_t* err;          // sticky error word (workspace header), or nullptr
+  const uint64_t* ready;  // set to epoch by the check kernel when every flag had arrived, or nullptr
+  const uint64_t* mirror; // per flag: epoch if that flag had arrived at check time (check mode)
   uint64_t epoch;         // a chunk may be consumed once its flags are >= epoch
   uint64_t spin_limit;    // polls before giving up with PLR_ETIMEOUT
+};
+
+struct CheckArgs {
+  const uint64_t* flags;  // the layout's W*nchunks flags
+  uint64_t nflags;
+  uint64_t epoch;
+  uint64_t* ready;        // receives epoch if every flag is >= epoch, else 0
+  uint64_t* mirror;       // per flag: epoch if it is >= epoch, else 0
 };
 
 // Work division shared by reduce and copy: a workgroup consumes a run of whole
@@ -90,6 +102,7 @@ struct CopyVArgs {
   int64_t* counts;   // [s][d]
   int64_t* offsets;  // [d][s]
   int32_t* rank;     // scratch: rank of each row inside its (source, destination) block
+  uint32_t* ticket;  // scratch: count of finished rank workgroups (zero between calls)
   uint64_t row_bytes;
   uint32_t world;
   uint32_t pad;
@@ -106,5 +119,6 @@ hipError_t launch_reduce(const ReduceArgs& a, int dtype, const Launch& l, hipStr
 hipError_t launch_copy(const CopyArgs& a, const Launch& l, hipStream_t s);
 hipError_t launch_copy_v(const CopyVArgs& a, uint32_t scatter_grid, hipStream_t s);
 hipError_t launch_notify(const NotifyArgs& a, hipStream_t s);
+hipError_t launch_check(const CheckArgs& a, hipStream_t s);
 
 }  // namespace plr

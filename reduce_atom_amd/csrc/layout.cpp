@@ -33,6 +33,9 @@ static void default_policy(plr_layout* L) {
   L->workgroups = 0;
   L->wg_per_cu = 0;
   L->run = 1;  // one tile per workgroup: the grid covers every tile
+  // throughput regime: check first, so that stream-ordered producers cost no per-chunk
+  // acquires; latency regime: wait inside the kernel (a check launch costs more)
+  L->notify_mode = L->seg_len <= (2u << 20) ? PLR_NOTIFY_CHUNKS : PLR_NOTIFY_CHECK;
   L->run_notified = L->op == PLR_OP_REDUCE ? 2 : 4;
   if (L->op == PLR_OP_REDUCE) {
     if (L->seg_len <= (2u << 20)) {  // latency regime: every tile in one dispatch wave
@@ -187,6 +190,13 @@ extern "C" int plr_layout_create(const plr_layout_desc* d, plr_layout** out) {
     if (!d->tile_bytes && L->tile_bytes % 4096) L->tile_bytes = 4096;
   }
   L->spin_limit = d->spin_limit ? d->spin_limit : kDefaultSpinLimit;
+  if (d->notify_mode) {
+    if (d->notify_mode != PLR_NOTIFY_CHUNKS && d->notify_mode != PLR_NOTIFY_CHECK) return fail(PLR_EINVAL);
+    L->notify_mode = d->notify_mode;
+  }
+  // in check mode only chunks still missing at check time pay a wait and a fence, so
+  // notified copies can use shorter runs
+  if (L->notify_mode == PLR_NOTIFY_CHECK && L->op == PLR_OP_COPY) L->run_notified = 2;
 
   // tile and chunk tables; a chunk is a whole number of tiles of one segment
   if (L->seg_len == 0) {
@@ -217,7 +227,7 @@ extern "C" void plr_layout_destroy(plr_layout* L) { delete L; }
 
 extern "C" size_t plr_layout_workspace_bytes(const plr_layout* L) {
   if (!L) return 0;
-  return kWorkspaceHeader + (size_t)L->world * L->nchunks * sizeof(uint64_t);
+  return kWorkspaceHeader + 2 * (size_t)L->world * L->nchunks * sizeof(uint64_t);
 }
 
 extern "C" size_t plr_layout_dst_bytes(const plr_layout* L) { return L ? L->dst_bytes : 0; }
@@ -239,7 +249,7 @@ extern "C" int plr_layout_segment(const plr_layout* L, int k, int* src, size_t* 
 
 extern "C" int plr_layout_policy(const plr_layout* L, size_t* tile_bytes, size_t* chunk_bytes,
                                  int* workgroups, int* block, int* unroll, int* stages,
-                                 int* datapath) {
+                                 int* datapath, int* notify_mode) {
   if (!L) return PLR_EINVAL;
   if (tile_bytes) *tile_bytes = L->tile_bytes;
   if (chunk_bytes) *chunk_bytes = L->chunk_bytes;
@@ -248,5 +258,6 @@ extern "C" int plr_layout_policy(const plr_layout* L, size_t* tile_bytes, size_t
   if (unroll) *unroll = L->unroll;
   if (stages) *stages = L->stages;
   if (datapath) *datapath = L->datapath;
+  if (notify_mode) *notify_mode = L->notify_mode;
   return PLR_OK;
 }

@@ -46,6 +46,7 @@ struct plr_layout {
   int wg_per_cu;   // grid = compute units * wg_per_cu when workgroups == 0 and this is > 0
   int run;           // tiles per workgroup when neither of the above is set
   int run_notified;  // the same for notified calls (each workgroup pays one acquire per chunk)
+  int notify_mode;   // PLR_NOTIFY_CHUNKS or PLR_NOTIFY_CHECK
   int block;
   int unroll;
   int stages;

@@ -14,6 +14,30 @@ __global__ void __launch_bounds__(256) k_notify(const NotifyArgs a) {
     __hip_atomic_store(a.flags + i, a.epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
+// Check ahead of a notified consumer: one workgroup reads every chunk flag once
+// (agent-scope atomic loads), mirrors which ones have reached the epoch, and if all
+// have it records the epoch in the workspace's ready word. The acquire fence makes
+// the producers' releases happen before this kernel's end, so the consuming kernel
+// that follows in stream order may read every chunk whose flag was mirrored without
+// waiting or fencing; only the chunks still missing are waited for one by one
+// (section 3.2: a consumer never reads a chunk before its flag).
+__global__ void __launch_bounds__(1024) k_check(const CheckArgs a) {
+  int ok = 1;
+  for (uint64_t i = threadIdx.x; i < a.nflags; i += blockDim.x) {
+    const bool arrived = __hip_atomic_load(a.flags + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) >= a.epoch;
+    a.mirror[i] = arrived ? a.epoch : 0;
+    ok &= arrived;
+  }
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+  const int all = __syncthreads_and(ok);
+  if (threadIdx.x == 0) *a.ready = all ? a.epoch : 0;
+}
+
+hipError_t launch_check(const CheckArgs& a, hipStream_t s) {
+  hipLaunchKernelGGL(k_check, dim3(1), dim3(1024), 0, s, a);
+  return hipGetLastError();
+}
+
 hipError_t launch_notify(const NotifyArgs& a, hipStream_t s) {
   uint64_t blocks = (a.nflags + 255) / 256;
   if (blocks < 1) blocks = 1;

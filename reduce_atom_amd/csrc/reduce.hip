@@ -20,12 +20,13 @@ template <int DT, int W, int U>
 __global__ void __launch_bounds__(512) k_reduce_direct(const ReduceArgs a) {
   const uint32_t nthr = blockDim.x;
   uint32_t ready = 0xFFFFFFFFu;  // chunk whose flags this workgroup has already seen
+  const bool wait = must_wait(a.nt);
   const uint32_t t_end = min(a.ntiles, (blockIdx.x + 1) * a.run);
   for (uint32_t t = blockIdx.x * a.run; t < t_end; ++t) {
-    if (a.nt.flags) {
+    if (wait) {
       const uint32_t c = t / a.tiles_per_chunk;
       if (c != ready) {
-        if (!wg_wait_flags(a.nt, a.nt.flags + c, a.nchunks, W)) return;
+        if (!wg_wait_flags(a.nt, c, a.nchunks, W)) return;
         ready = c;
       }
     }
@@ -74,14 +75,15 @@ __global__ void __launch_bounds__(256) k_reduce_lds(const ReduceArgs a) {
   const uint64_t j0 = (uint64_t)blockIdx.x * a.run * slabs_per_tile;
   const uint64_t j1 = min(nslab_all, (uint64_t)(blockIdx.x + 1) * a.run * slabs_per_tile);
   uint32_t ready = 0xFFFFFFFFu;
+  const bool wait = must_wait(a.nt);
 
   // stage slab j: every wave always issues exactly W DMAs (ragged lanes re-read the
   // last vector instead of skipping), so the wait counts stay exact
   auto stage = [&](uint64_t j) -> bool {
-    if (a.nt.flags) {
+    if (wait) {
       const uint32_t c = (uint32_t)(j / slabs_per_tile) / a.tiles_per_chunk;
       if (c != ready) {
-        if (!wg_wait_flags(a.nt, a.nt.flags + c, a.nchunks, W)) return false;
+        if (!wg_wait_flags(a.nt, c, a.nchunks, W)) return false;
         ready = c;
       }
     }

@@ -29,7 +29,7 @@ def _run(plr, srcs_np, dests_np, row_bytes):
     dst = torch.full((max(total * row_bytes, 16),), 0x77, dtype=torch.uint8, device="cuda")
     counts = torch.full((W * W,), -1, dtype=torch.int64, device="cuda")
     offsets = torch.full((W * W,), -1, dtype=torch.int64, device="cuda")
-    scratch = torch.empty(plr.plr_copy_v_scratch_bytes(W, rows), dtype=torch.uint8, device="cuda")
+    scratch = torch.zeros(plr.plr_copy_v_scratch_bytes(W, rows), dtype=torch.uint8, device="cuda")
     plr.plr_copy_v(srcs, rows, dests, row_bytes, dst, counts, offsets, scratch)
     torch.cuda.synchronize()
     return (dst.cpu().numpy()[:total * row_bytes], counts.cpu().numpy().reshape(W, W),
@@ -93,3 +93,29 @@ def test_config5_moe_dispatch(plr, oracle_mod):
     dests = [synth.categorical_np(0, 5, s, R, p) for s in range(W)]
     srcs = [synth.bits_np(0, 6, s, R * rb) for s in range(W)]
     _check(plr, oracle_mod, srcs, dests, rb)
+
+
+def test_scratch_reused_across_calls(plr, oracle_mod):
+    """The scratch header (the finished-workgroup ticket) returns to zero after every
+    call, so one zeroed scratch serves many calls with different row counts."""
+    W, rb = 4, 32
+    p = synth.zipf_weights(1.1, W)
+    scratch = torch.zeros(plr.plr_copy_v_scratch_bytes(W, [3000] * W), dtype=torch.uint8, device="cuda")
+    for k, rows_each in enumerate([3000, 17, 1000, 0, 2999]):
+        rows = [rows_each] * W
+        dests_np = [synth.categorical_np(k, 5, s, rows_each, p) for s in range(W)]
+        srcs_np = [synth.bits_np(k, 6, s, max(rows_each, 1) * rb) for s in range(W)]
+        srcs = [to_dev(s) for s in srcs_np]
+        dests = [torch.from_numpy(d.copy()).cuda() if d.size else torch.zeros(4, dtype=torch.int32, device="cuda")
+                 for d in dests_np]
+        total = sum(rows)
+        dst = torch.zeros(max(total * rb, 16), dtype=torch.uint8, device="cuda")
+        counts = torch.empty(W * W, dtype=torch.int64, device="cuda")
+        offsets = torch.empty(W * W, dtype=torch.int64, device="cuda")
+        plr.plr_copy_v(srcs, rows, dests, rb, dst, counts, offsets, scratch)
+        torch.cuda.synchronize()
+        ref, rc, ro = oracle_mod.copy_v(srcs_np, dests_np, rb)
+        assert np.array_equal(counts.cpu().numpy().reshape(W, W), rc)
+        assert np.array_equal(offsets.cpu().numpy().reshape(W, W), ro)
+        assert np.array_equal(dst.cpu().numpy()[:total * rb], ref)
+        assert int(scratch[:4].view(torch.int32).item()) == 0

@@ -19,12 +19,17 @@ def plr():
     return reduce_atom_amd
 
 
-def test_many_calls_without_reset(plr, oracle_mod):
+MODES = {"chunks": 1, "check": 2}
+
+
+@pytest.mark.parametrize("mode", list(MODES))
+def test_many_calls_without_reset(plr, oracle_mod, mode):
     W, n = 4, 8192
     srcs_np = [synth.normal_np(1, 2, w, n) for w in range(W)]
     ref = oracle_mod.reduce("bf16", srcs_np)
     srcs = [to_dev(s) for s in srcs_np]
-    L = plr.plr_layout_create("reduce", "bf16", W, 2 * n, "packed", "packed", chunk_bytes=2048)
+    L = plr.plr_layout_create("reduce", "bf16", W, 2 * n, "packed", "packed", chunk_bytes=2048,
+                              notify_mode=MODES[mode])
     ws = torch.zeros(L.workspace_bytes, dtype=torch.uint8, device="cuda")
     dst = torch.empty(2 * n, dtype=torch.uint8, device="cuda")
     for i in range(1000):
@@ -34,16 +39,18 @@ def test_many_calls_without_reset(plr, oracle_mod):
     assert plr.plr_check(L, ws) == plr.PLR_OK
     assert L.epoch == 1000
     assert_same("bf16", dst.cpu().numpy().view(np.uint16), ref)
-    flags = ws[256:].view(torch.int64).cpu().numpy()
+    flags = ws[256:256 + 8 * W * L.nchunks].view(torch.int64).cpu().numpy()
     assert (flags == 1000).all()
 
 
+@pytest.mark.parametrize("mode", list(MODES))
 @pytest.mark.parametrize("op", ["reduce", "copy"])
-def test_withheld_notify_times_out(plr, op):
+def test_withheld_notify_times_out(plr, op, mode):
     W, nbytes = 4, 16384
     srcs = [torch.zeros(nbytes, dtype=torch.uint8, device="cuda") for _ in range(W)]
     kinds = ("packed", "packed")
-    L = plr.plr_layout_create(op, "bf16", W, nbytes, *kinds, chunk_bytes=4096, spin_limit=2000)
+    L = plr.plr_layout_create(op, "bf16", W, nbytes, *kinds, chunk_bytes=4096, spin_limit=2000,
+                              notify_mode=MODES[mode])
     ws = torch.zeros(L.workspace_bytes, dtype=torch.uint8, device="cuda")
     dst = torch.empty(L.dst_bytes, dtype=torch.uint8, device="cuda")
     for w in range(W - 1):  # the last source never notifies
@@ -57,17 +64,22 @@ def test_withheld_notify_times_out(plr, op):
     assert plr.plr_check(L, ws) == plr.PLR_OK
 
 
-def test_delayed_producer_on_another_stream(plr, oracle_mod):
-    """The producer writes poison, waits, writes the real data, then notifies, all on its
-    own stream; the consumer is queued first on another stream and must wait for the
-    flags: its output must be the reduction of the real data, never of the poison."""
+@pytest.mark.parametrize("mode", list(MODES))
+def test_delayed_producer_on_another_stream(plr, oracle_mod, mode):
+    """The producer writes poison, sleeps, writes the real data and notifies, all on its
+    own stream; the consumer is queued right after on another stream. Where the two
+    streams run concurrently the consumer reaches the flags long before they are set and
+    must wait for them; its output must be the reduction of the real data, never of the
+    poison. (HIP may also run the streams one after the other; the result must be the
+    same, so the producer is queued first: a consumer queued first on a hardware queue
+    it shares with the producer could only time out.)"""
     W, n = 8, 1 << 16
     real_np = [synth.normal_np(2, 2, w, n) for w in range(W)]
     ref = oracle_mod.reduce("bf16", real_np)
     real = [to_dev(s) for s in real_np]
     srcs = [torch.empty_like(r) for r in real]
     L = plr.plr_layout_create("reduce", "bf16", W, 2 * n, "packed", "packed", chunk_bytes=4096,
-                              workgroups=4, block=64, spin_limit=1 << 22)
+                              workgroups=4, block=64, spin_limit=1 << 22, notify_mode=MODES[mode])
     ws = torch.zeros(L.workspace_bytes, dtype=torch.uint8, device="cuda")
     dst = torch.empty(2 * n, dtype=torch.uint8, device="cuda")
     torch.cuda.synchronize()
@@ -76,22 +88,21 @@ def test_delayed_producer_on_another_stream(plr, oracle_mod):
     with torch.cuda.stream(producer):
         for s in srcs:
             s.fill_(0xFF)  # NaN poison
-    producer.synchronize()
-    with torch.cuda.stream(consumer):
-        plr.plr_reduce(L, srcs, dst, ws)  # waits on flags of epoch 1
-    with torch.cuda.stream(producer):
         if hasattr(torch.cuda, "_sleep"):
             torch.cuda._sleep(20_000_000)
         for s, r in zip(srcs, real):
             s.copy_(r)
-        plr.plr_notify(L, -1, ws)
+        plr.plr_notify(L, -1, ws)  # epoch 1
+    with torch.cuda.stream(consumer):
+        plr.plr_reduce(L, srcs, dst, ws)  # waits on flags of epoch 1
     torch.cuda.synchronize()
     assert plr.plr_check(L, ws, consumer) == plr.PLR_OK
     assert_same("bf16", dst.cpu().numpy().view(np.uint16), ref)
 
 
+@pytest.mark.parametrize("mode", list(MODES))
 @pytest.mark.parametrize("op", ["reduce", "copy"])
-def test_tiles_crossing_chunks(plr, oracle_mod, op):
+def test_tiles_crossing_chunks(plr, oracle_mod, op, mode):
     """Few workgroups striding over many tiles, several tiles per chunk and ragged
     ends on both levels: every chunk's flags are waited for exactly when needed."""
     W, nbytes = 4, 37 * 1024 + 48
@@ -99,13 +110,13 @@ def test_tiles_crossing_chunks(plr, oracle_mod, op):
         srcs_np = [synth.normal_np(3, 2, w, nbytes // 2) for w in range(W)]
         ref = oracle_mod.reduce("bf16", srcs_np)
         L = plr.plr_layout_create("reduce", "bf16", W, nbytes, "packed", "packed", tile_bytes=1024,
-                                  chunk_bytes=4096, workgroups=3, block=64)
+                                  chunk_bytes=4096, workgroups=3, block=64, notify_mode=MODES[mode])
     else:
         nbytes = 16 * W * 150
         srcs_np = [synth.bits_np(3, 4, s, nbytes) for s in range(W)]
         ref = oracle_mod.copy_layout("scattered", "transposed", srcs_np).view(np.uint16)
         L = plr.plr_layout_create("copy", "bf16", W, nbytes, "scattered", "transposed", tile_bytes=256,
-                                  chunk_bytes=1024, workgroups=5, block=64)
+                                  chunk_bytes=1024, workgroups=5, block=64, notify_mode=MODES[mode])
     srcs = [to_dev(s) for s in srcs_np]
     ws = torch.zeros(L.workspace_bytes, dtype=torch.uint8, device="cuda")
     dst = torch.empty(L.dst_bytes, dtype=torch.uint8, device="cuda")
@@ -115,3 +126,44 @@ def test_tiles_crossing_chunks(plr, oracle_mod, op):
         (plr.plr_reduce if op == "reduce" else plr.plr_copy)(L, srcs, dst, ws)
         assert plr.plr_check(L, ws) == plr.PLR_OK
         assert_same("bf16", dst.cpu().numpy().view(np.uint16), ref, f"epoch {epoch}")
+
+
+@pytest.mark.parametrize("op", ["reduce", "copy"])
+def test_check_mode_partial_arrival(plr, oracle_mod, op):
+    """Check mode where half the sources are notified before the call and half by a
+    delayed producer on a second stream: when the streams overlap the check finds flags
+    missing and the consumer takes the per-chunk path; the late sources are still waited
+    for."""
+    W, nbytes = 4, 64 * 1024
+    real_np = [synth.bits_np(7, 4, s, nbytes) for s in range(W)]
+    if op == "reduce":
+        real_np = [synth.normal_np(7, 2, w, nbytes // 2) for w in range(W)]
+        ref = oracle_mod.reduce("bf16", real_np)
+    else:
+        ref = oracle_mod.copy_layout("packed", "packed", real_np).view(np.uint16)
+    real = [to_dev(s) for s in real_np]
+    srcs = [torch.empty_like(r) for r in real]
+    L = plr.plr_layout_create(op, "bf16", W, nbytes, "packed", "packed", chunk_bytes=8192,
+                              workgroups=4, block=64, spin_limit=1 << 22, notify_mode=MODES["check"])
+    ws = torch.zeros(L.workspace_bytes, dtype=torch.uint8, device="cuda")
+    dst = torch.empty(L.dst_bytes, dtype=torch.uint8, device="cuda")
+    for s, r in zip(srcs[:2], real[:2]):
+        s.copy_(r)
+    for w in range(2):
+        plr.plr_notify(L, w, ws)
+    torch.cuda.synchronize()
+    producer, consumer = torch.cuda.Stream(), torch.cuda.Stream()
+    with torch.cuda.stream(producer):  # queued first: see test_delayed_producer_on_another_stream
+        for s in srcs[2:]:
+            s.fill_(0xFF)
+        if hasattr(torch.cuda, "_sleep"):
+            torch.cuda._sleep(20_000_000)
+        for s, r in zip(srcs[2:], real[2:]):
+            s.copy_(r)
+        for w in range(2, W):
+            plr.plr_notify(L, w, ws)
+    with torch.cuda.stream(consumer):
+        (plr.plr_reduce if op == "reduce" else plr.plr_copy)(L, srcs, dst, ws)
+    torch.cuda.synchronize()
+    assert plr.plr_check(L, ws, consumer) == plr.PLR_OK
+    assert_same("bf16", dst.cpu().numpy().view(np.uint16), ref)

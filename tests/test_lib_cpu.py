@@ -92,9 +92,9 @@ def test_chunks_and_workspace(plr):
     pol = L.policy()
     n = -(-8192 * 7168 * 2 // pol["chunk_bytes"])
     assert L.nchunks == n
-    assert L.workspace_bytes == 256 + 8 * n * 8
+    assert L.workspace_bytes == 256 + 2 * 8 * n * 8
     C = plr.plr_layout_create("copy", "bf16", 8, 64 << 20, "scattered", "transposed", chunk_bytes=1 << 20)
-    assert C.nchunks == 64 * 8 and C.workspace_bytes == 256 + 8 * 512 * 8
+    assert C.nchunks == 64 * 8 and C.workspace_bytes == 256 + 2 * 8 * 512 * 8
     R = plr.plr_layout_create("copy", "bf16", 3, 48 * 3, "packed", "packed", chunk_bytes=32)
     assert R.nchunks == 3 * 5  # 144-byte segments in 32-byte chunks: ragged last chunk
     E = plr.plr_layout_create("reduce", "bf16", 4, 0, "packed", "packed")
@@ -105,7 +105,12 @@ def test_policy_overrides(plr):
     L = plr.plr_layout_create("reduce", "f16", 4, 1 << 24, "packed", "packed", chunk_bytes=4096,
                               workgroups=33, block=128, unroll=4, datapath=plr.PLR_PATH_DIRECT)
     assert L.policy() == dict(tile_bytes=4096, chunk_bytes=4096, workgroups=33, block=128, unroll=4,
-                              stages=2, datapath=plr.PLR_PATH_DIRECT)
+                              stages=2, datapath=plr.PLR_PATH_DIRECT, notify_mode=plr.PLR_NOTIFY_CHECK)
+    S = plr.plr_layout_create("reduce", "bf16", 8, 7168 * 2, "packed", "packed")
+    assert S.policy()["notify_mode"] == plr.PLR_NOTIFY_CHUNKS  # decode-size share
+    M = plr.plr_layout_create("reduce", "bf16", 8, 7168 * 2, "packed", "packed", notify_mode=plr.PLR_NOTIFY_CHECK)
+    assert M.policy()["notify_mode"] == plr.PLR_NOTIFY_CHECK
+    assert _code(plr.plr_layout_create, "reduce", "bf16", 8, 64, "packed", "packed", notify_mode=3) == plr.PLR_EINVAL
 
 
 def test_tiles_and_chunks(plr):
@@ -176,8 +181,8 @@ def test_call_validation_without_device(plr):
 
 
 def test_scratch_bytes(plr):
-    assert plr.plr_copy_v_scratch_bytes(8, [4096] * 8) == 8 * 4096 * 4
-    assert plr.plr_copy_v_scratch_bytes(2, [1, 2]) == 256
+    assert plr.plr_copy_v_scratch_bytes(8, [4096] * 8) == 256 + 8 * 4096 * 4
+    assert plr.plr_copy_v_scratch_bytes(2, [1, 2]) == 512
     assert plr.plr_copy_v_scratch_bytes(0, []) == 0
 
 
