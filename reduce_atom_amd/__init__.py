@@ -51,6 +51,7 @@ class plr_layout_desc(_c.Structure):
         ("workgroups", _i), ("block", _i), ("unroll", _i), ("stages", _i), ("datapath", _i),
         ("spin_limit", _u64),
         ("notify_mode", _i),
+        ("xcd_order", _i),
     ]
 
 
@@ -204,7 +205,7 @@ class Layout:
 def plr_layout_create(op, dtype, world, bytes_per_src, in_kind, out_kind, rank=0,
                       in_offsets=None, out_offsets=None, mode=PLR_MODE_DETERMINISTIC,
                       tile_bytes=0, chunk_bytes=0, workgroups=0, block=0, unroll=0, stages=0, datapath=0,
-                      spin_limit=0, notify_mode=0) -> Layout:
+                      spin_limit=0, notify_mode=0, xcd_order=0) -> Layout:
     """Compile a layout. op/dtype/kinds accept the C enum values or their names."""
     d = plr_layout_desc()
     d.op = OP_CODES.get(op, op)
@@ -224,6 +225,7 @@ def plr_layout_create(op, dtype, world, bytes_per_src, in_kind, out_kind, rank=0
     d.mode, d.tile_bytes, d.chunk_bytes, d.workgroups = mode, tile_bytes, chunk_bytes, workgroups
     d.block, d.unroll, d.stages, d.datapath, d.spin_limit = block, unroll, stages, datapath, spin_limit
     d.notify_mode = notify_mode
+    d.xcd_order = xcd_order
     h = _vp()
     _ok(_lib.plr_layout_create(_c.byref(d), _c.byref(h)), "plr_layout_create")
     return Layout(h.value)

@@ -16,8 +16,9 @@ __global__ void __launch_bounds__(512) k_copy_direct(const CopyArgs a) {
   const uint32_t nthr = blockDim.x;
   uint32_t ready = 0xFFFFFFFFu;  // flag (source, chunk) this workgroup has already seen
   const bool wait = must_wait(a.nt);
-  const uint32_t t_end = min(a.ntiles, (blockIdx.x + 1) * a.run);
-  for (uint32_t t = blockIdx.x * a.run; t < t_end; ++t) {
+  const uint32_t b = logical_block(a.xcd);
+  const uint32_t t_end = min(a.ntiles, (b + 1) * a.run);
+  for (uint32_t t = b * a.run; t < t_end; ++t) {
     const uint32_t seg = t / a.tiles_per_seg;
     const uint32_t part = t - seg * a.tiles_per_seg;
     uint32_t s;
@@ -85,7 +86,7 @@ __global__ void __launch_bounds__(256) k_copy_lds(const CopyArgs a) {
   __shared__ u32x4 ring[4][kCopyStages][64];
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const uint32_t spt = (uint32_t)((a.tile_bytes + 4095) / 4096);  // slabs per tile
-  const uint32_t t0 = blockIdx.x * a.run;
+  const uint32_t t0 = logical_block(a.xcd) * a.run;
   const uint32_t t1 = min(a.ntiles, t0 + a.run);
   const uint32_t j1 = (t1 - t0) * spt;
   uint32_t ready = 0xFFFFFFFFu;

@@ -109,7 +109,7 @@ __global__ void __launch_bounds__(kScatterThreads) k_copy_v_scatter(const CopyVA
   const int64_t total = a.row_start[W];
   const int waves_per_block = kScatterThreads / 64;
   const int64_t wave =
-      (int64_t)blockIdx.x * waves_per_block + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+      (int64_t)logical_block(a.xcd) * waves_per_block + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int64_t nwaves = (int64_t)gridDim.x * waves_per_block;
   for (int64_t r = wave; r < total; r += nwaves) {
     int s = 0;

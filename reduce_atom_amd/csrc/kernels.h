@@ -14,6 +14,7 @@ namespace plr {
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));  // one 16-byte vector
 
 constexpr int kMaxTableSegs = 64;   // explicit segment table carried in kernarg
+enum { kXcdOff = 0, kXcdOn = 1, kXcdUnnotified = 2 };
 // Workspace: u64 error word at byte 0, u64 ready word at byte 8, then
 // uint64 flags[W][nchunks], then their check-time mirror uint64 mirror[W][nchunks].
 constexpr size_t kWorkspaceHeader = 256;
@@ -27,6 +28,7 @@ struct Launch {
   int stages;
   int datapath;  // PLR_PATH_DIRECT or PLR_PATH_LDS
   uint32_t run;  // consecutive tiles per workgroup
+  int xcd;       // XCD-aware workgroup order
 };
 
 // Notification state of one consuming launch (section 3.2, SNAC "notify").
@@ -61,7 +63,7 @@ struct ReduceArgs {
   uint32_t nchunks;     // flags per source
   uint32_t world;
   uint32_t run;         // consecutive tiles per workgroup
-  uint32_t pad;
+  uint32_t xcd;         // XCD-aware workgroup order
   Notify nt;
 };
 
@@ -86,7 +88,7 @@ struct CopyArgs {
   uint32_t world;
   uint32_t mode;
   uint32_t run;    // consecutive tiles per workgroup
-  uint32_t pad;
+  uint32_t xcd;    // XCD-aware workgroup order
   uint64_t slice;  // kCopyTransposed: bytes per slice
   Notify nt;
   uint32_t seg_src[kMaxTableSegs];
@@ -105,7 +107,7 @@ struct CopyVArgs {
   uint32_t* ticket;  // scratch: count of finished rank workgroups (zero between calls)
   uint64_t row_bytes;
   uint32_t world;
-  uint32_t pad;
+  uint32_t xcd;      // XCD-aware workgroup order (scatter)
 };
 
 struct NotifyArgs {

@@ -21,8 +21,9 @@ __global__ void __launch_bounds__(512) k_reduce_direct(const ReduceArgs a) {
   const uint32_t nthr = blockDim.x;
   uint32_t ready = 0xFFFFFFFFu;  // chunk whose flags this workgroup has already seen
   const bool wait = must_wait(a.nt);
-  const uint32_t t_end = min(a.ntiles, (blockIdx.x + 1) * a.run);
-  for (uint32_t t = blockIdx.x * a.run; t < t_end; ++t) {
+  const uint32_t b = logical_block(a.xcd);
+  const uint32_t t_end = min(a.ntiles, (b + 1) * a.run);
+  for (uint32_t t = b * a.run; t < t_end; ++t) {
     if (wait) {
       const uint32_t c = t / a.tiles_per_chunk;
       if (c != ready) {
@@ -72,8 +73,9 @@ __global__ void __launch_bounds__(256) k_reduce_lds(const ReduceArgs a) {
   // tiles are whole slabs (or the share is a single tile shorter than one slab)
   const uint64_t slabs_per_tile = (a.tile_vecs + 255) / 256;
   const uint64_t nslab_all = (a.nvec + 255) / 256;
-  const uint64_t j0 = (uint64_t)blockIdx.x * a.run * slabs_per_tile;
-  const uint64_t j1 = min(nslab_all, (uint64_t)(blockIdx.x + 1) * a.run * slabs_per_tile);
+  const uint32_t b = logical_block(a.xcd);
+  const uint64_t j0 = (uint64_t)b * a.run * slabs_per_tile;
+  const uint64_t j1 = min(nslab_all, (uint64_t)(b + 1) * a.run * slabs_per_tile);
   uint32_t ready = 0xFFFFFFFFu;
   const bool wait = must_wait(a.nt);
 

@@ -104,7 +104,7 @@ def test_chunks_and_workspace(plr):
 def test_policy_overrides(plr):
     L = plr.plr_layout_create("reduce", "f16", 4, 1 << 24, "packed", "packed", chunk_bytes=4096,
                               workgroups=33, block=128, unroll=4, datapath=plr.PLR_PATH_DIRECT)
-    assert L.policy() == dict(tile_bytes=4096, chunk_bytes=4096, workgroups=33, block=128, unroll=4,
+    assert L.policy() == dict(tile_bytes=2048, chunk_bytes=4096, workgroups=33, block=128, unroll=4,
                               stages=2, datapath=plr.PLR_PATH_DIRECT, notify_mode=plr.PLR_NOTIFY_CHECK)
     S = plr.plr_layout_create("reduce", "bf16", 8, 7168 * 2, "packed", "packed")
     assert S.policy()["notify_mode"] == plr.PLR_NOTIFY_CHUNKS  # decode-size share
