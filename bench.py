@@ -9,8 +9,11 @@ plr_notify, then the consumer waits on its per-chunk flags):
   4. alltoallv W=8 x 4096 rows of 7168 bf16, Zipf(1.1) destinations -> 32768 packed rows
 `value` is the step's algorithmic HBM bytes (bytes read + bytes written) divided by
 the wall-clock time of a step, in GB/s. Decode-size latency (W=8 x [T, 7168] bf16,
-T in 1/8/32/64) is reported beside it as p50/p90 microseconds of the reduce kernel,
-notify off and on.
+T in 1/8/32/64) is reported beside it, notify off and on, two ways: the time per call
+of many calls issued back to back on one stream (for notify on, a call is the producer's
+notify plus the reduce), and p50/p90 of HIP-event pairs around single reduce launches
+(which include the events' own cost of several microseconds; kernel-only durations
+come from the rocprofv3 trace kept in profiles/).
 
 Prints one JSON line. Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
 """
@@ -285,6 +288,16 @@ def run_decode(args, torch, plr, synth, dev):
 
             for _ in range(args.decode_warmup):
                 once()
+            # (a) back to back: many calls between one pair of events, per call
+            a0, b0 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            torch.cuda.synchronize()
+            a0.record()
+            for _ in range(args.decode_iters):
+                once()
+            b0.record()
+            torch.cuda.synchronize()
+            per_call = a0.elapsed_time(b0) * 1e3 / args.decode_iters
+            # (b) one pair of events around every reduce launch (includes the events' own cost)
             evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
                    for _ in range(args.decode_iters)]
             torch.cuda.synchronize()
@@ -298,8 +311,9 @@ def run_decode(args, torch, plr, synth, dev):
             us = sorted(a.elapsed_time(b) * 1e3 for a, b in evs)
             if ws is not None and plr.plr_check(L, ws) != plr.PLR_OK:
                 raise RuntimeError("decode: device error")
-            res[mode] = {"p50_us": round(us[len(us) // 2], 2), "p90_us": round(us[int(len(us) * 0.9)], 2)}
-        res["GB/s_at_p50"] = round((W + 1) * n * 2 / (res["notify_off"]["p50_us"] * 1e-6) / 1e9, 1)
+            res[mode] = {"us_per_call_back_to_back": round(per_call, 2),
+                         "event_pair_p50_us": round(us[len(us) // 2], 2),
+                         "event_pair_p90_us": round(us[int(len(us) * 0.9)], 2)}
         out[f"T={T}"] = res
     return out
 

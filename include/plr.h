@@ -148,8 +148,9 @@ int plr_layout_create(const plr_layout_desc* desc, plr_layout** out);
 void plr_layout_destroy(plr_layout* L);
 
 /* Bytes of workspace a notified call needs: a 256-byte header (u64 error word at
- * byte 0, u64 ready word at byte 8), the chunk flags uint64_t flags[W][nchunks], and
- * their check-time mirror uint64_t mirror[W][nchunks]. The caller allocates it in device
+ * byte 0, u64 ready word at byte 8, u32 check ticket at byte 16), the chunk flags
+ * uint64_t flags[W][nchunks], their check-time mirror uint64_t mirror[W][nchunks],
+ * and one u64 per 1024 flags for the check's partial results. The caller allocates it in device
  * memory, ZEROED, once; it is never reset between calls (the epoch only grows,
  * section 4.3 "Epoch Bookkeeping"). One workspace belongs to one layout. */
 size_t plr_layout_workspace_bytes(const plr_layout* L);
@@ -219,8 +220,9 @@ int plr_copy_v(int world, const void* const* srcs, const int64_t* rows_per_src,
                const int32_t* const* dest_of_row, size_t row_bytes, void* dst,
                int64_t* counts, int64_t* offsets, void* scratch, void* stream);
 
-/* Scratch bytes plr_copy_v needs for these row counts (host only): a 256-byte header
- * plus one int32 per row, rounded up to 256 bytes. */
+/* Scratch bytes plr_copy_v needs for these row counts (host only): a 256-byte header,
+ * one int32 per row, and two int32 per destination for every 1024-row segment of a
+ * source, each region rounded up to 256 bytes. 0 for invalid arguments. */
 size_t plr_copy_v_scratch_bytes(int world, const int64_t* rows_per_src);
 
 /* Producer side of notify (section 3.2 "SNAC"; section 4.3: the epoch supplies the

@@ -98,6 +98,8 @@ hipError_t launch_check_for(const plr_layout* L, const Notify& nt, hipStream_t s
   c.epoch = nt.epoch;
   c.ready = const_cast<uint64_t*>(nt.ready);
   c.mirror = const_cast<uint64_t*>(nt.mirror);
+  c.partial = c.mirror + c.nflags;
+  c.ticket = reinterpret_cast<uint32_t*>(const_cast<uint64_t*>(nt.ready) + 1);
   return launch_check(c, s);
 }
 
@@ -172,15 +174,37 @@ extern "C" int plr_copy(plr_layout* L, const void* const* srcs, void* dst, void*
   return PLR_OK;
 }
 
-// Scratch of plr_copy_v: a 256-byte header (u32 ticket at byte 0) then int32 rank[rows].
+// Scratch of plr_copy_v: a 256-byte header (u32 ticket at byte 0), int32 rank[rows],
+// then int32 seg_count[segments][W] and int32 seg_base[segments][W], each region
+// rounded up to 256 bytes; a segment is kRankSeg rows of one source.
 constexpr uint64_t kCopyVScratchHeader = 256;
+
+static uint64_t up256(uint64_t x) { return (x + 255) & ~255ull; }
+
+struct CopyVScratch {
+  uint64_t rank_off, count_off, base_off, bytes;
+};
+
+static CopyVScratch copy_v_scratch(int world, const int64_t* rows_per_src) {
+  uint64_t total = 0, segs = 0;
+  for (int s = 0; s < world; ++s) {
+    const uint64_t r = rows_per_src[s] > 0 ? (uint64_t)rows_per_src[s] : 0;
+    total += r;
+    segs += (r + kRankSeg - 1) / kRankSeg;
+  }
+  CopyVScratch c;
+  c.rank_off = kCopyVScratchHeader;
+  c.count_off = c.rank_off + up256(total * sizeof(int32_t));
+  c.base_off = c.count_off + up256(segs * world * sizeof(int32_t));
+  c.bytes = c.base_off + up256(segs * world * sizeof(int32_t));
+  return c;
+}
 
 extern "C" size_t plr_copy_v_scratch_bytes(int world, const int64_t* rows_per_src) {
   if (world < 1 || world > PLR_MAX_WORLD || !rows_per_src) return 0;
-  uint64_t total = 0;
-  for (int s = 0; s < world; ++s) total += rows_per_src[s] > 0 ? (uint64_t)rows_per_src[s] : 0;
-  const uint64_t bytes = total * sizeof(int32_t);
-  return (size_t)(kCopyVScratchHeader + ((bytes + 255) & ~255ull));
+  for (int s = 0; s < world; ++s)
+    if (rows_per_src[s] < 0) return 0;
+  return (size_t)copy_v_scratch(world, rows_per_src).bytes;
 }
 
 extern "C" int plr_copy_v(int world, const void* const* srcs, const int64_t* rows_per_src,
@@ -218,8 +242,15 @@ extern "C" int plr_copy_v(int world, const void* const* srcs, const int64_t* row
   a.dst = static_cast<uint8_t*>(dst);
   a.counts = counts;
   a.offsets = offsets;
+  const CopyVScratch layout = copy_v_scratch(world, rows_per_src);
   a.ticket = static_cast<uint32_t*>(scratch);
-  a.rank = reinterpret_cast<int32_t*>(static_cast<char*>(scratch) + kCopyVScratchHeader);
+  a.rank = reinterpret_cast<int32_t*>(static_cast<char*>(scratch) + layout.rank_off);
+  a.seg_count = reinterpret_cast<int32_t*>(static_cast<char*>(scratch) + layout.count_off);
+  a.seg_base = reinterpret_cast<int32_t*>(static_cast<char*>(scratch) + layout.base_off);
+  a.seg_start[0] = 0;
+  for (int s = 0; s < world; ++s)
+    a.seg_start[s + 1] = a.seg_start[s] + (uint32_t)((rows_per_src[s] + kRankSeg - 1) / kRankSeg);
+  for (int s = world + 1; s <= PLR_MAX_WORLD; ++s) a.seg_start[s] = a.seg_start[world];
   a.row_bytes = row_bytes;
   a.world = (uint32_t)world;
   a.xcd = 0;  // measured: the XCD-contiguous order slowed the row scatter (185 vs 172 us)

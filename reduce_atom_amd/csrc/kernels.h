@@ -15,8 +15,9 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));  // one 16-byte vect
 
 constexpr int kMaxTableSegs = 64;   // explicit segment table carried in kernarg
 enum { kXcdOff = 0, kXcdOn = 1, kXcdUnnotified = 2 };
-// Workspace: u64 error word at byte 0, u64 ready word at byte 8, then
-// uint64 flags[W][nchunks], then their check-time mirror uint64 mirror[W][nchunks].
+// Workspace: u64 error word at byte 0, u64 ready word at byte 8, u32 check ticket
+// at byte 16, then uint64 flags[W][nchunks], their check-time mirror
+// uint64 mirror[W][nchunks], and one u64 partial result per check workgroup.
 constexpr size_t kWorkspaceHeader = 256;
 constexpr uint64_t kDefaultSpinLimit = 1ull << 20;
 
@@ -47,7 +48,10 @@ struct CheckArgs {
   uint64_t epoch;
   uint64_t* ready;        // receives epoch if every flag is >= epoch, else 0
   uint64_t* mirror;       // per flag: epoch if it is >= epoch, else 0
+  uint64_t* partial;      // per check workgroup: 1 if all of its flags had arrived
+  uint32_t* ticket;       // finished check workgroups (zero between calls)
 };
+constexpr int kCheckThreads = 1024;  // flags per check workgroup
 
 // Work division shared by reduce and copy: a workgroup consumes a run of whole
 // consecutive tiles (a tile is the Atom's step), and tiles_per_chunk consecutive
@@ -96,14 +100,19 @@ struct CopyArgs {
   uint64_t seg_dst_off[kMaxTableSegs];
 };
 
+constexpr int kRankSeg = 1024;  // rows per rank workgroup (one per thread)
+
 struct CopyVArgs {
   const uint8_t* src[PLR_MAX_WORLD];
   const int32_t* dest[PLR_MAX_WORLD];
   int64_t row_start[PLR_MAX_WORLD + 1];  // prefix of rows_per_src
+  uint32_t seg_start[PLR_MAX_WORLD + 1]; // prefix of ceil(rows_per_src / kRankSeg)
+  int32_t* seg_count;  // scratch [segments][W]: rows of a segment bound for each destination
+  int32_t* seg_base;   // scratch [segments][W]: rows of earlier segments of the same source
   uint8_t* dst;
   int64_t* counts;   // [s][d]
   int64_t* offsets;  // [d][s]
-  int32_t* rank;     // scratch: rank of each row inside its (source, destination) block
+  int32_t* rank;     // scratch: rank of each row inside its segment and destination
   uint32_t* ticket;  // scratch: count of finished rank workgroups (zero between calls)
   uint64_t row_bytes;
   uint32_t world;

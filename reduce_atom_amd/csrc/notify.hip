@@ -14,27 +14,46 @@ __global__ void __launch_bounds__(256) k_notify(const NotifyArgs a) {
     __hip_atomic_store(a.flags + i, a.epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// Check ahead of a notified consumer: one workgroup reads every chunk flag once
-// (agent-scope atomic loads), mirrors which ones have reached the epoch, and if all
-// have it records the epoch in the workspace's ready word. The acquire fence makes
+// Check ahead of a notified consumer: it reads every chunk flag once (agent-scope
+// atomic loads), mirrors which ones have reached the epoch, and if all have it records
+// the epoch in the workspace's ready word. The acquire fence makes
 // the producers' releases happen before this kernel's end, so the consuming kernel
 // that follows in stream order may read every chunk whose flag was mirrored without
 // waiting or fencing; only the chunks still missing are waited for one by one
 // (section 3.2: a consumer never reads a chunk before its flag).
-__global__ void __launch_bounds__(1024) k_check(const CheckArgs a) {
+// Many flags: one workgroup per kCheckThreads flags; each records whether all of its
+// flags had arrived, and the last workgroup to finish (a ticket, acquire-release at
+// agent scope, reset by that workgroup) combines them into the ready word.
+__global__ void __launch_bounds__(kCheckThreads) k_check(const CheckArgs a) {
+  __shared__ int last;
+  const uint64_t i = (uint64_t)blockIdx.x * kCheckThreads + threadIdx.x;
   int ok = 1;
-  for (uint64_t i = threadIdx.x; i < a.nflags; i += blockDim.x) {
-    const bool arrived = __hip_atomic_load(a.flags + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) >= a.epoch;
-    a.mirror[i] = arrived ? a.epoch : 0;
-    ok &= arrived;
+  if (i < a.nflags) {
+    ok = __hip_atomic_load(a.flags + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) >= a.epoch;
+    a.mirror[i] = ok ? a.epoch : 0;
   }
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
   const int all = __syncthreads_and(ok);
-  if (threadIdx.x == 0) *a.ready = all ? a.epoch : 0;
+  if (threadIdx.x == 0) {
+    a.partial[blockIdx.x] = all;
+    const uint32_t done = __hip_atomic_fetch_add(a.ticket, 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
+    last = done == gridDim.x - 1;
+  }
+  __syncthreads();
+  if (!last) return;
+  int every = 1;
+  for (uint32_t w = threadIdx.x; w < gridDim.x; w += kCheckThreads)
+    every &= __hip_atomic_load(a.partial + w, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0;
+  every = __syncthreads_and(every);
+  if (threadIdx.x == 0) {
+    *a.ready = every ? a.epoch : 0;
+    __hip_atomic_store(a.ticket, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
 }
 
 hipError_t launch_check(const CheckArgs& a, hipStream_t s) {
-  hipLaunchKernelGGL(k_check, dim3(1), dim3(1024), 0, s, a);
+  const uint64_t blocks = (a.nflags + kCheckThreads - 1) / kCheckThreads;
+  hipLaunchKernelGGL(k_check, dim3((uint32_t)(blocks ? blocks : 1)), dim3(kCheckThreads), 0, s, a);
   return hipGetLastError();
 }
 

@@ -92,9 +92,9 @@ def test_chunks_and_workspace(plr):
     pol = L.policy()
     n = -(-8192 * 7168 * 2 // pol["chunk_bytes"])
     assert L.nchunks == n
-    assert L.workspace_bytes == 256 + 2 * 8 * n * 8
+    assert L.workspace_bytes == 256 + (2 * 8 * n + -(-8 * n // 1024)) * 8
     C = plr.plr_layout_create("copy", "bf16", 8, 64 << 20, "scattered", "transposed", chunk_bytes=1 << 20)
-    assert C.nchunks == 64 * 8 and C.workspace_bytes == 256 + 2 * 8 * 512 * 8
+    assert C.nchunks == 64 * 8 and C.workspace_bytes == 256 + (2 * 8 * 512 + 4) * 8
     R = plr.plr_layout_create("copy", "bf16", 3, 48 * 3, "packed", "packed", chunk_bytes=32)
     assert R.nchunks == 3 * 5  # 144-byte segments in 32-byte chunks: ragged last chunk
     E = plr.plr_layout_create("reduce", "bf16", 4, 0, "packed", "packed")
@@ -181,8 +181,11 @@ def test_call_validation_without_device(plr):
 
 
 def test_scratch_bytes(plr):
-    assert plr.plr_copy_v_scratch_bytes(8, [4096] * 8) == 256 + 8 * 4096 * 4
-    assert plr.plr_copy_v_scratch_bytes(2, [1, 2]) == 512
+    # header + ranks + 2 x (segments x W) int32, each rounded up to 256 bytes
+    assert plr.plr_copy_v_scratch_bytes(8, [4096] * 8) == 256 + 8 * 4096 * 4 + 2 * (32 * 8 * 4)
+    assert plr.plr_copy_v_scratch_bytes(2, [1, 2]) == 256 + 256 + 2 * 256
+    assert plr.plr_copy_v_scratch_bytes(2, [1025, 0]) == 256 + 4352 + 2 * 256
+    assert plr.plr_copy_v_scratch_bytes(2, [-1, 0]) == 0
     assert plr.plr_copy_v_scratch_bytes(0, []) == 0
 
 
