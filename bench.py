@@ -10,8 +10,9 @@ plr_notify, then the consumer waits on its per-chunk flags):
 `value` is the step's algorithmic HBM bytes (bytes read + bytes written) divided by
 the wall-clock time of a step, in GB/s. Decode-size latency (W=8 x [T, 7168] bf16,
 T in 1/8/32/64) is reported beside it, notify off and on, two ways: the time per call
-of many calls issued back to back on one stream (for notify on, a call is the producer's
-notify plus the reduce), and p50/p90 of HIP-event pairs around single reduce launches
+of 50 calls captured in a HIP graph and replayed back to back (for notify on, a call is
+the producer's notify plus the reduce), and p50/p90 of HIP-event pairs around single
+reduce launches
 (which include the events' own cost of several microseconds; kernel-only durations
 come from the rocprofv3 trace kept in profiles/).
 
@@ -288,15 +289,27 @@ def run_decode(args, torch, plr, synth, dev):
 
             for _ in range(args.decode_warmup):
                 once()
-            # (a) back to back: many calls between one pair of events, per call
+            # (a) back to back on the GPU: 50 calls captured in one HIP graph, replayed,
+            # so that host-side call overhead does not starve the GPU (the captured
+            # launches are the library's kernels only; no memory-set nodes)
+            graph = torch.cuda.CUDAGraph()
+            side = torch.cuda.Stream()
+            side.wait_stream(torch.cuda.current_stream())
+            with torch.cuda.stream(side):
+                with torch.cuda.graph(graph, stream=side):
+                    for _ in range(50):
+                        once()
+            torch.cuda.current_stream().wait_stream(side)
+            graph.replay()
             a0, b0 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             torch.cuda.synchronize()
             a0.record()
-            for _ in range(args.decode_iters):
-                once()
+            for _ in range(args.decode_iters // 50):
+                graph.replay()
             b0.record()
             torch.cuda.synchronize()
-            per_call = a0.elapsed_time(b0) * 1e3 / args.decode_iters
+            per_call = a0.elapsed_time(b0) * 1e3 / (50 * (args.decode_iters // 50))
+            del graph
             # (b) one pair of events around every reduce launch (includes the events' own cost)
             evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
                    for _ in range(args.decode_iters)]
@@ -311,10 +324,45 @@ def run_decode(args, torch, plr, synth, dev):
             us = sorted(a.elapsed_time(b) * 1e3 for a, b in evs)
             if ws is not None and plr.plr_check(L, ws) != plr.PLR_OK:
                 raise RuntimeError("decode: device error")
-            res[mode] = {"us_per_call_back_to_back": round(per_call, 2),
+            res[mode] = {"us_per_call_graph": round(per_call, 2),
                          "event_pair_p50_us": round(us[len(us) // 2], 2),
                          "event_pair_p90_us": round(us[int(len(us) * 0.9)], 2)}
         out[f"T={T}"] = res
+    return out
+
+
+def run_next(args):
+    """Rows beyond the step (measured beside it, not part of `value`): the AllReduce of
+    W=8 contributions of [8192, 7168] bf16 into 8 outputs, fused and composed."""
+    import torch
+
+    import reduce_atom_amd as plr
+    import synth
+
+    dev = torch.device("cuda:0")
+    out = {}
+    srcs = [synth.normal_t(args.seed, 3, w, R3 * C3, 0.5, device=dev) for w in range(W)]
+    dsts = [torch.empty(R3 * C3, dtype=torch.bfloat16, device=dev) for _ in range(W)]
+    algo = 2 * W * R3 * C3 * 2  # W contributions read, W outputs written
+    for name, path in (("allreduce_fused", plr.PLR_PATH_DIRECT), ("allreduce_composed", plr.PLR_PATH_COMPOSED)):
+        L = plr.plr_layout_create("allreduce", "bf16", W, R3 * C3 * 2, "scattered", "scattered", datapath=path)
+        ws = torch.zeros(max(L.workspace_bytes, 256), dtype=torch.uint8, device=dev)
+        for _ in range(3):
+            plr.plr_allreduce(L, srcs, dsts, ws)
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(10):
+            plr.plr_allreduce(L, srcs, dsts, ws)
+        b.record()
+        torch.cuda.synchronize()
+        if plr.plr_check(L, ws) != plr.PLR_OK:
+            raise RuntimeError(f"{name}: device error")
+        us = a.elapsed_time(b) * 1e3 / 10
+        out[name] = {"avg_us": round(us, 2), "GB/s": round(algo / (us * 1e-6) / 1e9, 1),
+                     "algorithmic_bytes": algo}
+    del srcs, dsts
+    torch.cuda.empty_cache()
     return out
 
 
@@ -402,6 +450,7 @@ def main():
                           "launches": 5}), flush=True)
         return
     value, ms, roofline, per_op, decode = run_bench(args)
+    nxt = None if args.no_decode else run_next(args)
     cpu = None if args.no_cpu_baseline else run_cpu_baseline(args)
     line = {
         "metric": METRIC, "value": round(value, 1), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
@@ -412,6 +461,7 @@ def main():
                                "7168 bf16, Zipf(1.1) destinations",
                    "world": W, "notify": True, "seed": args.seed, "step_bytes": sum(BYTES.values())},
         "roofline": roofline, "cpu_baseline": cpu, "per_op": per_op, "decode_reduce_us": decode,
+        "beyond_step": nxt,
     }
     print(json.dumps(line), flush=True)
 

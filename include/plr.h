@@ -34,6 +34,10 @@
  *     notification timeout is sticky in the workspace and surfaces through plr_check.
  *   - Calls are not thread-safe on one plr_layout (its epoch advances per call);
  *     distinct layouts may be used from distinct threads.
+ *   - Every call is kernel launches only (no memory-set or copy nodes), so calls can be
+ *     captured in a HIP graph. A notified call (or a composed AllReduce) captured in a
+ *     graph keeps the epoch it was captured with: replays do not wait for fresh
+ *     notifications, so capture un-notified calls when replays must wait.
  */
 #ifndef PLR_H
 #define PLR_H
@@ -61,7 +65,7 @@ enum {
 typedef enum { PLR_BF16 = 0, PLR_F16 = 1, PLR_F32 = 2 } plr_dtype;
 
 /* ---- the operation a collective applies between its layouts (section 3.1) ---- */
-typedef enum { PLR_OP_REDUCE = 0, PLR_OP_COPY = 1 } plr_op;
+typedef enum { PLR_OP_REDUCE = 0, PLR_OP_COPY = 1, PLR_OP_ALLREDUCE = 2 } plr_op;
 
 /* ---- layout kinds (section 3.1 "Layouts") ----
  * PACKED:     a rank's region is one contiguous block of bytes_per_src bytes.
@@ -76,12 +80,14 @@ typedef enum { PLR_OP_REDUCE = 0, PLR_OP_COPY = 1 } plr_op;
  *   copy    SCATTERED -> TRANSPOSED AllToAll: slice d of source s lands at slice d*W + s
  *   copy    SCATTERED -> SCATTERED  gather half of AllReduce: slice s of source s lands
  *                                   at slice s of the output
+ *   allreduce SCATTERED -> SCATTERED  AllReduce = ReduceScatter then AllGather: every one
+ *                                   of W outputs receives the reduction of all W sources
  */
 typedef enum { PLR_PACKED = 0, PLR_SCATTERED = 1, PLR_TRANSPOSED = 2 } plr_layout_kind;
 
 /* ---- datapath choice (section 3.3: the Atom's pipeline stages data through
  * workgroup-local memory; on gfx950 it can also go straight through registers) ---- */
-enum { PLR_PATH_POLICY = 0, PLR_PATH_DIRECT = 1, PLR_PATH_LDS = 2 };
+enum { PLR_PATH_POLICY = 0, PLR_PATH_DIRECT = 1, PLR_PATH_LDS = 2, PLR_PATH_COMPOSED = 3 };
 
 /* ---- how a notified call waits (section 3.2 "SNAC": a consumer never reads a chunk
  * before its flag). PLR_NOTIFY_CHUNKS: every workgroup waits for the flags of each
@@ -200,6 +206,27 @@ int plr_reduce(plr_layout* L, const void* const* srcs, void* dst, void* workspac
  *             source's flag.
  * Errors: as plr_reduce. */
 int plr_copy(plr_layout* L, const void* const* srcs, void* dst, void* workspace, void* stream);
+
+/* AllReduce of W contributions into W outputs (section 3.1 "Layouts": AllReduce is
+ * ReduceScatter followed by AllGather, composed into one kernel; section 2.1: every
+ * rank ends with the reduction of all contributions). The layout is op
+ * PLR_OP_ALLREDUCE, SCATTERED -> SCATTERED, bytes_per_src a multiple of 16*W. For every
+ * element i and every output w:
+ *   dsts[w][i] = round(((x_0[i] + x_1[i]) + ...) + x_{W-1}[i])   (as plr_reduce)
+ *   srcs      host array of W device pointers, bytes_per_src bytes each
+ *   dsts      host array of W device pointers, bytes_per_src bytes each; they must not
+ *             overlap each other or any source
+ *   workspace datapath PLR_PATH_DIRECT (the policy's, "fused": each tile is reduced once
+ *             and stored to all W outputs): NULL or any. PLR_PATH_COMPOSED (section 3.2's
+ *             role split in one kernel: a workgroup reduces tile k into the output of
+ *             the rank that owns k's slice and releases a per-tile flag, then acquires
+ *             the flag of tile k-lag and copies that tile into the other W-1 outputs):
+ *             required, plr_layout_workspace_bytes(L) bytes, zeroed once; the layout's
+ *             epoch advances per call. Producer-side notification does not apply.
+ * Errors: PLR_EINVAL (wrong op, NULL, overlaps, missing workspace), PLR_EALIGN, PLR_EHIP;
+ * a composed call whose flags never arrive reports PLR_ETIMEOUT through plr_check. */
+int plr_allreduce(plr_layout* L, const void* const* srcs, void* const* dsts, void* workspace,
+                  void* stream);
 
 /* Variable-length AllToAll packing (appendix C.4 "Variable-Length Collectives";
  * section 4: partition sizes at run time, prefix sums). Source s has rows_per_src[s]

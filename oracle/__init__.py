@@ -172,6 +172,15 @@ def reduce_layout(dtype: str, in_kind: str, rank: int, srcs) -> np.ndarray:
     return reduce(dtype, srcs, offs, n)
 
 
+def allreduce(dtype: str, srcs):
+    """AllReduce of W contributions (Purlin paper, section 2.1: every rank ends with the
+    reduction of all contributions): W outputs, each the rank-order reduction of the
+    W sources. Written from that definition; the composition ReduceScatter then
+    AllGather (section 3.1) is checked against it in the tests."""
+    out = reduce(dtype, srcs)
+    return [out.copy() for _ in srcs]
+
+
 # ------------------------------------------------------------------ copy
 def copy(srcs, segments, dst_bytes: int, fill: int = 0) -> np.ndarray:
     """Apply byte segments (src, src_off, dst_off, len) to a fresh output buffer."""

@@ -25,16 +25,16 @@ _lib = ctypes.CDLL(LIB_PATH)
 # ---- constants (include/plr.h) ----
 PLR_OK, PLR_EINVAL, PLR_EALIGN, PLR_EUNSUPPORTED, PLR_EHIP, PLR_ETIMEOUT = range(6)
 PLR_BF16, PLR_F16, PLR_F32 = 0, 1, 2
-PLR_OP_REDUCE, PLR_OP_COPY = 0, 1
+PLR_OP_REDUCE, PLR_OP_COPY, PLR_OP_ALLREDUCE = 0, 1, 2
 PLR_PACKED, PLR_SCATTERED, PLR_TRANSPOSED = 0, 1, 2
-PLR_PATH_POLICY, PLR_PATH_DIRECT, PLR_PATH_LDS = 0, 1, 2
+PLR_PATH_POLICY, PLR_PATH_DIRECT, PLR_PATH_LDS, PLR_PATH_COMPOSED = 0, 1, 2, 3
 PLR_MODE_DETERMINISTIC = 0
 PLR_NOTIFY_POLICY, PLR_NOTIFY_CHUNKS, PLR_NOTIFY_CHECK = 0, 1, 2
 PLR_MAX_WORLD = 16
 
 DTYPE_CODES = {"bf16": PLR_BF16, "f16": PLR_F16, "f32": PLR_F32}
 KIND_CODES = {"packed": PLR_PACKED, "scattered": PLR_SCATTERED, "transposed": PLR_TRANSPOSED}
-OP_CODES = {"reduce": PLR_OP_REDUCE, "copy": PLR_OP_COPY}
+OP_CODES = {"reduce": PLR_OP_REDUCE, "copy": PLR_OP_COPY, "allreduce": PLR_OP_ALLREDUCE}
 
 _c = ctypes
 _vp, _sz, _i, _u64, _i64p = _c.c_void_p, _c.c_size_t, _c.c_int, _c.c_uint64, _c.POINTER(_c.c_int64)
@@ -76,6 +76,8 @@ _lib.plr_reduce.argtypes = [_vp, _c.POINTER(_vp), _vp, _vp, _vp]
 _lib.plr_reduce.restype = _i
 _lib.plr_copy.argtypes = [_vp, _c.POINTER(_vp), _vp, _vp, _vp]
 _lib.plr_copy.restype = _i
+_lib.plr_allreduce.argtypes = [_vp, _c.POINTER(_vp), _c.POINTER(_vp), _vp, _vp]
+_lib.plr_allreduce.restype = _i
 _lib.plr_copy_v.argtypes = [_i, _c.POINTER(_vp), _i64p, _c.POINTER(_vp), _sz, _vp, _vp, _vp, _vp, _vp]
 _lib.plr_copy_v.restype = _i
 _lib.plr_copy_v_scratch_bytes.argtypes = [_i, _i64p]
@@ -94,7 +96,7 @@ _lib.plr_version.restype = _c.c_char_p
 EXPORTS = [
     "plr_layout_create", "plr_layout_destroy", "plr_layout_workspace_bytes", "plr_layout_dst_bytes",
     "plr_layout_nchunks", "plr_layout_ntiles", "plr_layout_nsegments", "plr_layout_segment", "plr_layout_policy",
-    "plr_layout_epoch", "plr_reduce", "plr_copy", "plr_copy_v", "plr_copy_v_scratch_bytes",
+    "plr_layout_epoch", "plr_reduce", "plr_copy", "plr_allreduce", "plr_copy_v", "plr_copy_v_scratch_bytes",
     "plr_notify", "plr_check", "plr_strerror", "plr_last_hip_error", "plr_version",
 ]
 
@@ -243,6 +245,11 @@ def plr_reduce(layout: Layout, srcs, dst, workspace=None, stream=None) -> None:
 def plr_copy(layout: Layout, srcs, dst, workspace=None, stream=None) -> None:
     _ok(_lib.plr_copy(layout.handle, _ptrs(srcs), _addr(dst), _addr(workspace), _stream(stream)),
         "plr_copy")
+
+
+def plr_allreduce(layout: Layout, srcs, dsts, workspace=None, stream=None) -> None:
+    _ok(_lib.plr_allreduce(layout.handle, _ptrs(srcs), _ptrs(dsts), _addr(workspace), _stream(stream)),
+        "plr_allreduce")
 
 
 def plr_copy_v_scratch_bytes(world: int, rows_per_src) -> int:

@@ -62,6 +62,7 @@ Launch launch_of(const plr_layout* L, bool notified) {
 int check_call(const plr_layout* L, plr_op op, const void* const* srcs, const void* dst,
                void* workspace, Notify* nt) {
   if (!L || L->op != op || !srcs || !dst) return PLR_EINVAL;
+  if (L->datapath == PLR_PATH_COMPOSED) return PLR_EINVAL;
   if (!a16(dst)) return PLR_EALIGN;
   for (int w = 0; w < L->world; ++w) {
     if (!srcs[w]) return PLR_EINVAL;
@@ -261,8 +262,58 @@ extern "C" int plr_copy_v(int world, const void* const* srcs, const int64_t* row
   return PLR_OK;
 }
 
+extern "C" int plr_allreduce(plr_layout* L, const void* const* srcs, void* const* dsts,
+                             void* workspace, void* stream) {
+  if (!L || L->op != PLR_OP_ALLREDUCE || !srcs || !dsts) return PLR_EINVAL;
+  const int W = L->world;
+  const uint64_t S = L->seg_len;
+  for (int w = 0; w < W; ++w) {
+    if (!srcs[w] || !dsts[w]) return PLR_EINVAL;
+    if (!a16(srcs[w]) || !a16(dsts[w])) return PLR_EALIGN;
+  }
+  for (int w = 0; w < W; ++w)
+    for (int v = 0; v < W; ++v) {
+      if (overlaps((uintptr_t)dsts[w], S, (uintptr_t)srcs[v], S)) return PLR_EINVAL;
+      if (v != w && overlaps((uintptr_t)dsts[w], S, (uintptr_t)dsts[v], S)) return PLR_EINVAL;
+    }
+  const bool composed = L->datapath == PLR_PATH_COMPOSED;
+  if (composed && !workspace) return PLR_EINVAL;
+  if (workspace && !a16(workspace)) return PLR_EALIGN;
+  if (!L->ntiles) return PLR_OK;
+  AllReduceArgs a{};
+  for (int w = 0; w < W; ++w) {
+    a.src[w] = static_cast<const u32x4*>(srcs[w]);
+    a.dst[w] = static_cast<u32x4*>(dsts[w]);
+  }
+  a.slice_vecs = S / W / 16;
+  a.tile_vecs = L->tile_bytes / 16;
+  a.tiles_per_slice = L->tiles_per_seg;
+  a.ntiles = L->ntiles;
+  a.world = (uint32_t)W;
+  a.run = 1;
+  a.lag = (uint32_t)L->lag;
+  Launch l{};
+  l.block = (uint32_t)L->block;
+  l.datapath = L->datapath;
+  if (composed) {
+    a.nt.err = static_cast<uint64_t*>(workspace);
+    a.nt.flags = reinterpret_cast<const uint64_t*>(static_cast<char*>(workspace) + kWorkspaceHeader);
+    a.nt.epoch = L->epoch + 1;
+    a.nt.spin_limit = L->spin_limit;
+    l.grid = L->ntiles + a.lag;
+  } else {
+    a.run = run_for(L, false);
+    l.grid = (uint32_t)std::max<uint64_t>(1, ((uint64_t)L->ntiles + a.run - 1) / a.run);
+  }
+  hipError_t e = launch_allreduce(a, L->dtype, l, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e);
+  if (composed) L->epoch = a.nt.epoch;
+  return PLR_OK;
+}
+
 extern "C" int plr_notify(plr_layout* L, int src, void* workspace, void* stream) {
   if (!L || !workspace) return PLR_EINVAL;
+  if (L->op == PLR_OP_ALLREDUCE) return PLR_EINVAL;
   if (src < -1 || src >= L->world) return PLR_EINVAL;
   if (!a16(workspace)) return PLR_EALIGN;
   if (L->nchunks == 0) return PLR_OK;

@@ -119,6 +119,22 @@ struct CopyVArgs {
   uint32_t xcd;      // XCD-aware workgroup order (scatter)
 };
 
+// AllReduce of W contributions into W outputs. The share of every output is cut into
+// W slices (slice r belongs to rank r) and each slice into tiles.
+struct AllReduceArgs {
+  const u32x4* src[PLR_MAX_WORLD];
+  u32x4* dst[PLR_MAX_WORLD];
+  uint64_t slice_vecs;       // 16-byte vectors per slice
+  uint64_t tile_vecs;
+  uint32_t tiles_per_slice;
+  uint32_t ntiles;           // world * tiles_per_slice
+  uint32_t world;
+  uint32_t run;              // fused: tiles per workgroup
+  uint32_t lag;              // composed: a workgroup gathers the tile `lag` below its own
+  uint32_t pad;
+  Notify nt;                 // composed: per-tile flags (the reducer releases, gatherers acquire)
+};
+
 struct NotifyArgs {
   uint64_t* flags;
   uint64_t nflags;  // flags to store, starting at `flags`
@@ -129,6 +145,7 @@ struct NotifyArgs {
 hipError_t launch_reduce(const ReduceArgs& a, int dtype, const Launch& l, hipStream_t s);
 hipError_t launch_copy(const CopyArgs& a, const Launch& l, hipStream_t s);
 hipError_t launch_copy_v(const CopyVArgs& a, uint32_t scatter_grid, hipStream_t s);
+hipError_t launch_allreduce(const AllReduceArgs& a, int dtype, const Launch& l, hipStream_t s);
 hipError_t launch_notify(const NotifyArgs& a, hipStream_t s);
 hipError_t launch_check(const CheckArgs& a, hipStream_t s);
 

@@ -52,12 +52,18 @@ static void default_policy(plr_layout* L) {
       L->tile_bytes = 2u << 10;
       L->chunk_bytes = 256u << 10;
     }
-  } else {
+  } else if (L->op == PLR_OP_COPY) {
     L->block = 128;
     L->unroll = 1;
     L->tile_bytes = 2u << 10;
     L->chunk_bytes = 256u << 10;
+  } else {  // allreduce: fused by default; the composed path uses 64 KiB tiles
+    L->block = 128;
+    L->unroll = 1;
+    L->tile_bytes = 2u << 10;
+    L->chunk_bytes = L->tile_bytes;
   }
+  L->lag = 16;
 }
 
 }  // namespace plr
@@ -72,7 +78,7 @@ extern "C" int plr_layout_create(const plr_layout_desc* d, plr_layout** out) {
   if (d->world < 1) return PLR_EINVAL;
   if (d->world > PLR_MAX_WORLD) return PLR_EUNSUPPORTED;
   if (d->mode != PLR_MODE_DETERMINISTIC) return PLR_EUNSUPPORTED;
-  if (d->op != PLR_OP_REDUCE && d->op != PLR_OP_COPY) return PLR_EINVAL;
+  if (d->op != PLR_OP_REDUCE && d->op != PLR_OP_COPY && d->op != PLR_OP_ALLREDUCE) return PLR_EINVAL;
   if (d->dtype != PLR_BF16 && d->dtype != PLR_F16 && d->dtype != PLR_F32) return PLR_EINVAL;
   if (d->in_kind < PLR_PACKED || d->in_kind > PLR_TRANSPOSED) return PLR_EINVAL;
   if (d->out_kind < PLR_PACKED || d->out_kind > PLR_TRANSPOSED) return PLR_EINVAL;
@@ -117,6 +123,13 @@ extern "C" int plr_layout_create(const plr_layout_desc* d, plr_layout** out) {
     }
     L->seg_len = share;
     L->dst_bytes = share;
+  } else if (d->op == PLR_OP_ALLREDUCE) {
+    if (d->in_kind != PLR_SCATTERED || d->out_kind != PLR_SCATTERED) return fail(PLR_EINVAL);
+    if (d->in_offsets || d->out_offsets) return fail(PLR_EINVAL);
+    if (B % (16ull * W)) return fail(PLR_EALIGN);
+    for (int w = 0; w < W; ++w) L->segs.push_back({w, 0, 0, B});
+    L->seg_len = B;
+    L->dst_bytes = B;
   } else {
     if (d->in_kind == PLR_PACKED && d->out_kind == PLR_PACKED) {  // AllGather
       for (int s = 0; s < W; ++s) L->segs.push_back({s, 0, (uint64_t)s * B, B});
@@ -182,8 +195,15 @@ extern "C" int plr_layout_create(const plr_layout_desc* d, plr_layout** out) {
     L->stages = d->stages;
   }
   if (d->datapath) {
-    if (d->datapath != PLR_PATH_DIRECT && d->datapath != PLR_PATH_LDS) return fail(PLR_EINVAL);
+    if (d->datapath != PLR_PATH_DIRECT && d->datapath != PLR_PATH_LDS && d->datapath != PLR_PATH_COMPOSED)
+      return fail(PLR_EINVAL);
+    if ((d->datapath == PLR_PATH_COMPOSED) != (d->op == PLR_OP_ALLREDUCE && d->datapath != PLR_PATH_DIRECT))
+      return fail(PLR_EINVAL);  // composed is the AllReduce role split; AllReduce has no LDS path
     L->datapath = d->datapath;
+    if (d->datapath == PLR_PATH_COMPOSED) {
+      if (!d->tile_bytes) L->tile_bytes = 64u << 10;
+      if (!d->block) L->block = 256;
+    }
   }
   if (L->datapath == PLR_PATH_LDS) {
     // the staged pipeline runs 256-thread workgroups over 4 KiB slabs per source
@@ -205,7 +225,21 @@ extern "C" int plr_layout_create(const plr_layout_desc* d, plr_layout** out) {
   if (L->notify_mode == PLR_NOTIFY_CHECK) L->run_notified = L->op == PLR_OP_REDUCE ? 1 : 2;
 
   // tile and chunk tables; a chunk is a whole number of tiles of one segment
-  if (L->seg_len == 0) {
+  if (L->op == PLR_OP_ALLREDUCE) {  // tiles of the W slices; one flag per tile
+    const uint64_t slice = L->seg_len / W;
+    if (slice == 0) {
+      L->tiles_per_seg = L->tiles_per_chunk = L->chunks_per_seg = 0;
+      L->ntiles = L->nchunks = 0;
+    } else {
+      const uint64_t tile = std::min<uint64_t>(L->tile_bytes, slice);
+      const uint64_t tps = (slice + tile - 1) / tile;
+      if (tps * W > 0x7FFFFFFFull) return fail(PLR_EUNSUPPORTED);
+      L->tile_bytes = L->chunk_bytes = tile;
+      L->tiles_per_seg = (uint32_t)tps;  // tiles per slice
+      L->tiles_per_chunk = L->chunks_per_seg = 1;
+      L->ntiles = L->nchunks = (uint32_t)(tps * W);
+    }
+  } else if (L->seg_len == 0) {
     L->tiles_per_seg = L->tiles_per_chunk = L->chunks_per_seg = 0;
     L->ntiles = L->nchunks = 0;
   } else {
@@ -233,6 +267,7 @@ extern "C" void plr_layout_destroy(plr_layout* L) { delete L; }
 
 extern "C" size_t plr_layout_workspace_bytes(const plr_layout* L) {
   if (!L) return 0;
+  if (L->op == PLR_OP_ALLREDUCE) return kWorkspaceHeader + (size_t)L->nchunks * sizeof(uint64_t);
   const size_t nflags = (size_t)L->world * L->nchunks;
   const size_t partials = (nflags + kCheckThreads - 1) / kCheckThreads;
   return kWorkspaceHeader + (2 * nflags + partials) * sizeof(uint64_t);

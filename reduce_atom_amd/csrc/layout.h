@@ -48,6 +48,7 @@ struct plr_layout {
   int run_notified;  // the same for notified calls (each workgroup pays one acquire per chunk)
   int notify_mode;   // PLR_NOTIFY_CHUNKS or PLR_NOTIFY_CHECK
   int xcd_order;     // kXcdOff, kXcdOn, or kXcdUnnotified (on for calls without a workspace)
+  int lag;           // allreduce, composed: tiles between a workgroup's reduction and its gather
   int block;
   int unroll;
   int stages;

@@ -208,3 +208,22 @@ def test_lds_datapath_layouts(plr):
                  datapath=plr.PLR_PATH_LDS, tile_bytes=2048) == plr.PLR_EINVAL
     assert _code(plr.plr_layout_create, "reduce", "bf16", 2, 16384, "packed", "packed",
                  datapath=plr.PLR_PATH_LDS, block=128) == plr.PLR_EINVAL
+
+
+def test_allreduce_layouts(plr):
+    L = plr.plr_layout_create("allreduce", "bf16", 8, 16 * 8 * 100, "scattered", "scattered")
+    assert L.policy()["datapath"] == plr.PLR_PATH_DIRECT and L.dst_bytes == 16 * 8 * 100
+    C = plr.plr_layout_create("allreduce", "bf16", 4, 4 * 64 * 1024 * 3, "scattered", "scattered",
+                              datapath=plr.PLR_PATH_COMPOSED)
+    assert C.policy()["tile_bytes"] == 64 * 1024 and C.ntiles == 4 * 3 and C.nchunks == 12
+    assert C.workspace_bytes == 256 + 12 * 8
+    mk = plr.plr_layout_create
+    assert _code(mk, "allreduce", "bf16", 4, 64, "packed", "packed") == plr.PLR_EINVAL
+    assert _code(mk, "allreduce", "bf16", 3, 16 * 4, "scattered", "scattered") == plr.PLR_EALIGN
+    assert _code(mk, "allreduce", "bf16", 2, 64, "scattered", "scattered", datapath=plr.PLR_PATH_LDS) == plr.PLR_EINVAL
+    assert _code(mk, "reduce", "bf16", 2, 64, "packed", "packed", datapath=plr.PLR_PATH_COMPOSED) == plr.PLR_EINVAL
+    A, B = 1 << 40, (1 << 40) + (1 << 24)
+    assert _code(plr.plr_allreduce, C, [A + 16 * k for k in range(4)], [B] * 4) in (plr.PLR_EINVAL, plr.PLR_EALIGN)
+    assert _code(plr.plr_allreduce, C, [A + (1 << 20) * k for k in range(4)],
+                 [B + (1 << 20) * k for k in range(4)]) == plr.PLR_EINVAL  # composed needs a workspace
+    assert _code(plr.plr_notify, C, 0, B) == plr.PLR_EINVAL
