@@ -273,19 +273,32 @@ def run_bench(args):
 
 def run_decode(args, torch, plr, synth, dev):
     out = {}
-    for T in DECODE_T:
+    for T in (args.decode_t or DECODE_T):
         n = T * 7168
         srcs = [synth.normal_t(args.seed, 2, w, n, 1.0, device=dev) for w in range(W)]
         dst = torch.empty(n, dtype=torch.bfloat16, device=dev)
         res = {}
-        for mode in ("notify_off", "notify_on"):
+        for mode in ("notify_off", "notify_on", "packets"):
             L = plr.plr_layout_create("reduce", "bf16", W, 2 * n, "packed", "packed")
-            ws = torch.zeros(L.workspace_bytes, dtype=torch.uint8, device=dev) if mode == "notify_on" else None
+            ws = torch.zeros(max(L.workspace_bytes, 256), dtype=torch.uint8, device=dev) if mode != "notify_off" else None
+            pk = [torch.zeros(L.packet_bytes, dtype=torch.uint8, device=dev) for _ in range(W)] \
+                if mode == "packets" else None
+
+            def produce():
+                if pk is not None:
+                    plr.plr_pack(L, -1, srcs, pk)
+                elif ws is not None:
+                    plr.plr_notify(L, -1, ws)
+
+            def consume():
+                if pk is not None:
+                    plr.plr_reduce_packets(L, pk, dst, ws)
+                else:
+                    plr.plr_reduce(L, srcs, dst, ws)
 
             def once():
-                if ws is not None:
-                    plr.plr_notify(L, -1, ws)
-                plr.plr_reduce(L, srcs, dst, ws)
+                produce()
+                consume()
 
             for _ in range(args.decode_warmup):
                 once()
@@ -315,10 +328,9 @@ def run_decode(args, torch, plr, synth, dev):
                    for _ in range(args.decode_iters)]
             torch.cuda.synchronize()
             for a, b in evs:
-                if ws is not None:
-                    plr.plr_notify(L, -1, ws)
+                produce()
                 a.record()
-                plr.plr_reduce(L, srcs, dst, ws)
+                consume()
                 b.record()
             torch.cuda.synchronize()
             us = sorted(a.elapsed_time(b) * 1e3 for a, b in evs)
@@ -411,6 +423,10 @@ def main():
     ap.add_argument("--decode-iters", type=int, default=1000)
     ap.add_argument("--decode-warmup", type=int, default=100)
     ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--decode-only", action="store_true",
+                    help="only the decode-size latency runs (for profiling them), printed as JSON")
+    ap.add_argument("--decode-t", type=lambda v: [int(x) for x in v.split(",")], default=None,
+                    help="decode token counts T (comma separated; default 1,8,32,64)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-fraction", type=float, default=0.125)
     ap.add_argument("--cpu-reps", type=int, default=3)
@@ -448,6 +464,15 @@ def main():
         torch.cuda.synchronize()
         print(json.dumps({"calibrate": "torch copy_", "bytes_read": 1 << 30, "bytes_written": 1 << 30,
                           "launches": 5}), flush=True)
+        return
+    if args.decode_only:
+        import torch
+
+        import reduce_atom_amd as plr
+        import synth
+
+        print(json.dumps({"decode_reduce_us": run_decode(args, torch, plr, synth, torch.device("cuda:0"))}),
+              flush=True)
         return
     value, ms, roofline, per_op, decode = run_bench(args)
     nxt = None if args.no_decode else run_next(args)

@@ -228,6 +228,32 @@ int plr_copy(plr_layout* L, const void* const* srcs, void* dst, void* workspace,
 int plr_allreduce(plr_layout* L, const void* const* srcs, void* const* dsts, void* workspace,
                   void* stream);
 
+/* Latency path (section 3.2 and Figure 7: for latency-bound transfers the producer
+ * pushes packets that carry payload and notification together, doubling the data
+ * volume, so the consumer needs no separate flag round trip; section 3.3: the packets
+ * are reduced one output element per thread in source order). On gfx950 a packet is
+ * one 8-byte atomic: a 4-byte payload word in the low half and the low 32 bits of the
+ * epoch in the high half. Only for reduce layouts.
+ * plr_layout_packet_bytes: bytes of one source's packet buffer (2 x the share); the
+ * caller allocates W of them in device memory, zeroed once, never reset. */
+size_t plr_layout_packet_bytes(const plr_layout* L);
+
+/* Producer: stamp source src's share (src = -1: every source's, in one launch) with
+ * epoch E+1 into its packet buffer, after the work queued on `stream`; E does not
+ * change. data, packets: host arrays of W device pointers (source buffers, the layout's
+ * offsets are applied; packet buffers); only the entries of the packed sources are read.
+ * Errors: PLR_EINVAL (wrong op, src out of range, NULL, a packet buffer overlapping a
+ * share or another packet buffer), PLR_EALIGN, PLR_EHIP. */
+int plr_pack(plr_layout* L, int src, const void* const* data, void* const* packets, void* stream);
+
+/* Consumer: for every output element, poll the W sources' packets until they carry
+ * epoch E+1 (bounded; PLR_ETIMEOUT through plr_check), then reduce their payloads as
+ * plr_reduce does; E advances by one. packets: host array of W device pointers.
+ * workspace: device, at least 256 bytes, zeroed (the sticky error word).
+ * Errors: PLR_EINVAL (wrong op, NULL, overlaps), PLR_EALIGN, PLR_EHIP. */
+int plr_reduce_packets(plr_layout* L, const void* const* packets, void* dst, void* workspace,
+                       void* stream);
+
 /* Variable-length AllToAll packing (appendix C.4 "Variable-Length Collectives";
  * section 4: partition sizes at run time, prefix sums). Source s has rows_per_src[s]
  * rows of row_bytes bytes; row i goes to destination dest_of_row[s][i] in [0, W).

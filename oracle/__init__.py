@@ -181,6 +181,23 @@ def allreduce(dtype: str, srcs):
     return [out.copy() for _ in srcs]
 
 
+def pack(data: np.ndarray, epoch: int) -> np.ndarray:
+    """Latency-path packets (Purlin paper, section 3.2 and Figure 7: payload and
+    notification combined in one atomic packet, doubling the data volume). Reading:
+    an 8-byte packet per 4-byte payload word, the word in the low half and the low 32
+    bits of the epoch in the high half (little-endian), so that one 8-byte atomic
+    carries both. Returns uint64 packets."""
+    words = np.ascontiguousarray(data).reshape(-1).view(np.uint32).astype(np.uint64)
+    return words | (np.uint64(epoch & 0xFFFFFFFF) << np.uint64(32))
+
+
+def unpack(packets: np.ndarray, epoch: int):
+    """(payload bytes, mask of packets whose stamp equals the epoch)."""
+    p = np.ascontiguousarray(packets).view(np.uint64)
+    ok = (p >> np.uint64(32)) == np.uint64(epoch & 0xFFFFFFFF)
+    return (p & np.uint64(0xFFFFFFFF)).astype(np.uint32).view(np.uint8), ok
+
+
 # ------------------------------------------------------------------ copy
 def copy(srcs, segments, dst_bytes: int, fill: int = 0) -> np.ndarray:
     """Apply byte segments (src, src_off, dst_off, len) to a fresh output buffer."""

@@ -78,6 +78,12 @@ _lib.plr_copy.argtypes = [_vp, _c.POINTER(_vp), _vp, _vp, _vp]
 _lib.plr_copy.restype = _i
 _lib.plr_allreduce.argtypes = [_vp, _c.POINTER(_vp), _c.POINTER(_vp), _vp, _vp]
 _lib.plr_allreduce.restype = _i
+_lib.plr_layout_packet_bytes.argtypes = [_vp]
+_lib.plr_layout_packet_bytes.restype = _sz
+_lib.plr_pack.argtypes = [_vp, _i, _c.POINTER(_vp), _c.POINTER(_vp), _vp]
+_lib.plr_pack.restype = _i
+_lib.plr_reduce_packets.argtypes = [_vp, _c.POINTER(_vp), _vp, _vp, _vp]
+_lib.plr_reduce_packets.restype = _i
 _lib.plr_copy_v.argtypes = [_i, _c.POINTER(_vp), _i64p, _c.POINTER(_vp), _sz, _vp, _vp, _vp, _vp, _vp]
 _lib.plr_copy_v.restype = _i
 _lib.plr_copy_v_scratch_bytes.argtypes = [_i, _i64p]
@@ -97,6 +103,7 @@ EXPORTS = [
     "plr_layout_create", "plr_layout_destroy", "plr_layout_workspace_bytes", "plr_layout_dst_bytes",
     "plr_layout_nchunks", "plr_layout_ntiles", "plr_layout_nsegments", "plr_layout_segment", "plr_layout_policy",
     "plr_layout_epoch", "plr_reduce", "plr_copy", "plr_allreduce", "plr_copy_v", "plr_copy_v_scratch_bytes",
+    "plr_layout_packet_bytes", "plr_pack", "plr_reduce_packets",
     "plr_notify", "plr_check", "plr_strerror", "plr_last_hip_error", "plr_version",
 ]
 
@@ -192,6 +199,10 @@ class Layout:
         return out
 
     @property
+    def packet_bytes(self) -> int:
+        return _lib.plr_layout_packet_bytes(self._h)
+
+    @property
     def ntiles(self) -> int:
         return _lib.plr_layout_ntiles(self._h)
 
@@ -250,6 +261,15 @@ def plr_copy(layout: Layout, srcs, dst, workspace=None, stream=None) -> None:
 def plr_allreduce(layout: Layout, srcs, dsts, workspace=None, stream=None) -> None:
     _ok(_lib.plr_allreduce(layout.handle, _ptrs(srcs), _ptrs(dsts), _addr(workspace), _stream(stream)),
         "plr_allreduce")
+
+
+def plr_pack(layout: Layout, src: int, data, packets, stream=None) -> None:
+    _ok(_lib.plr_pack(layout.handle, src, _ptrs(data), _ptrs(packets), _stream(stream)), "plr_pack")
+
+
+def plr_reduce_packets(layout: Layout, packets, dst, workspace, stream=None) -> None:
+    _ok(_lib.plr_reduce_packets(layout.handle, _ptrs(packets), _addr(dst), _addr(workspace), _stream(stream)),
+        "plr_reduce_packets")
 
 
 def plr_copy_v_scratch_bytes(world: int, rows_per_src) -> int:

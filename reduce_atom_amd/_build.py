@@ -31,7 +31,8 @@ COMMON = [
 DEVICE = [f"--offload-arch={ARCH}", "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
           "-fno-gpu-rdc"]
 
-SOURCES = ["api.cpp", "layout.cpp", "reduce.hip", "copy.hip", "copy_v.hip", "notify.hip", "allreduce.hip"]
+SOURCES = ["api.cpp", "layout.cpp", "reduce.hip", "copy.hip", "copy_v.hip", "notify.hip", "allreduce.hip",
+           "packets.hip"]
 
 
 def _compile(src: str, build_dir: str = BUILD, defines=(), csrc: str = CSRC) -> str:

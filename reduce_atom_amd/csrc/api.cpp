@@ -311,6 +311,64 @@ extern "C" int plr_allreduce(plr_layout* L, const void* const* srcs, void* const
   return PLR_OK;
 }
 
+extern "C" size_t plr_layout_packet_bytes(const plr_layout* L) {
+  return (L && L->op == PLR_OP_REDUCE) ? 2 * (size_t)L->seg_len : 0;
+}
+
+extern "C" int plr_pack(plr_layout* L, int src, const void* const* data, void* const* packets,
+                        void* stream) {
+  if (!L || L->op != PLR_OP_REDUCE || !data || !packets) return PLR_EINVAL;
+  if (src < -1 || src >= L->world) return PLR_EINVAL;
+  const int s0 = src < 0 ? 0 : src, s1 = src < 0 ? L->world : src + 1;
+  PackArgs a{};
+  for (int s = s0; s < s1; ++s) {
+    if (!data[s] || !packets[s]) return PLR_EINVAL;
+    if (!a16(data[s]) || !a16(packets[s])) return PLR_EALIGN;
+    const char* share = static_cast<const char*>(data[s]) + L->segs[s].src_off;
+    for (int t = s0; t < s1; ++t) {  // a packet buffer overlaps no share and no other buffer
+      const char* other = static_cast<const char*>(data[t]) + L->segs[t].src_off;
+      if (overlaps((uintptr_t)packets[s], 2 * L->seg_len, (uintptr_t)other, L->seg_len)) return PLR_EINVAL;
+      if (t != s && overlaps((uintptr_t)packets[s], 2 * L->seg_len, (uintptr_t)packets[t], 2 * L->seg_len))
+        return PLR_EINVAL;
+    }
+    a.data[s] = reinterpret_cast<const uint32_t*>(share);
+    a.packets[s] = static_cast<uint64_t*>(packets[s]);
+  }
+  if (!L->seg_len) return PLR_OK;
+  a.nwords = L->seg_len / 4;
+  a.first = (uint32_t)s0;
+  a.stamp = (uint32_t)(L->epoch + 1);
+  hipError_t e = launch_pack(a, (uint32_t)(s1 - s0), static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e);
+  return PLR_OK;
+}
+
+extern "C" int plr_reduce_packets(plr_layout* L, const void* const* packets, void* dst, void* workspace,
+                                  void* stream) {
+  if (!L || L->op != PLR_OP_REDUCE || !packets || !dst || !workspace) return PLR_EINVAL;
+  if (!a16(dst) || !a16(workspace)) return PLR_EALIGN;
+  for (int w = 0; w < L->world; ++w) {
+    if (!packets[w]) return PLR_EINVAL;
+    if (!a16(packets[w])) return PLR_EALIGN;
+    if (overlaps((uintptr_t)dst, L->seg_len, (uintptr_t)packets[w], 2 * L->seg_len)) return PLR_EINVAL;
+  }
+  const uint64_t epoch = L->epoch + 1;
+  if (L->seg_len) {
+    PacketReduceArgs a{};
+    for (int w = 0; w < L->world; ++w) a.pk[w] = static_cast<const uint64_t*>(packets[w]);
+    a.dst = static_cast<uint32_t*>(dst);
+    a.nwords = L->seg_len / 4;
+    a.world = (uint32_t)L->world;
+    a.stamp = (uint32_t)epoch;
+    a.err = static_cast<uint64_t*>(workspace);
+    a.spin_limit = L->spin_limit;
+    hipError_t e = launch_reduce_packets(a, L->dtype, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return hip_fail(e);
+  }
+  L->epoch = epoch;
+  return PLR_OK;
+}
+
 extern "C" int plr_notify(plr_layout* L, int src, void* workspace, void* stream) {
   if (!L || !workspace) return PLR_EINVAL;
   if (L->op == PLR_OP_ALLREDUCE) return PLR_EINVAL;

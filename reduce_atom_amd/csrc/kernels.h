@@ -135,6 +135,26 @@ struct AllReduceArgs {
   Notify nt;                 // composed: per-tile flags (the reducer releases, gatherers acquire)
 };
 
+// Latency-path packets: one uint64 per 4-byte payload word, the low 32 bits of the
+// epoch in the high half.
+struct PackArgs {
+  const uint32_t* data[PLR_MAX_WORLD];  // every source's share
+  uint64_t* packets[PLR_MAX_WORLD];
+  uint64_t nwords;  // payload words per source (a multiple of 4)
+  uint32_t first;   // first source of the launch (one source per grid row)
+  uint32_t stamp;
+};
+
+struct PacketReduceArgs {
+  const uint64_t* pk[PLR_MAX_WORLD];  // packets of every source
+  uint32_t* dst;
+  uint64_t nwords;     // payload words (one packet per source each)
+  uint32_t world;
+  uint32_t stamp;
+  uint64_t* err;
+  uint64_t spin_limit;
+};
+
 struct NotifyArgs {
   uint64_t* flags;
   uint64_t nflags;  // flags to store, starting at `flags`
@@ -146,6 +166,8 @@ hipError_t launch_reduce(const ReduceArgs& a, int dtype, const Launch& l, hipStr
 hipError_t launch_copy(const CopyArgs& a, const Launch& l, hipStream_t s);
 hipError_t launch_copy_v(const CopyVArgs& a, uint32_t scatter_grid, hipStream_t s);
 hipError_t launch_allreduce(const AllReduceArgs& a, int dtype, const Launch& l, hipStream_t s);
+hipError_t launch_pack(const PackArgs& a, uint32_t nsrc, hipStream_t s);
+hipError_t launch_reduce_packets(const PacketReduceArgs& a, int dtype, hipStream_t s);
 hipError_t launch_notify(const NotifyArgs& a, hipStream_t s);
 hipError_t launch_check(const CheckArgs& a, hipStream_t s);
 

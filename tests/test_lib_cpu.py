@@ -227,3 +227,26 @@ def test_allreduce_layouts(plr):
     assert _code(plr.plr_allreduce, C, [A + (1 << 20) * k for k in range(4)],
                  [B + (1 << 20) * k for k in range(4)]) == plr.PLR_EINVAL  # composed needs a workspace
     assert _code(plr.plr_notify, C, 0, B) == plr.PLR_EINVAL
+
+
+def test_packet_layouts_and_validation(plr):
+    L = plr.plr_layout_create("reduce", "bf16", 4, 4 * 4096, "scattered", "packed", rank=1)
+    assert L.packet_bytes == 2 * 4096
+    C = plr.plr_layout_create("copy", "bf16", 2, 4096, "packed", "packed")
+    assert C.packet_bytes == 0
+    A, P, D, WS = 1 << 40, (1 << 40) + (1 << 24), (1 << 40) + (2 << 24), (1 << 40) + (3 << 24)
+    pk = [P + k * 8192 for k in range(4)]
+    src = [A + k * (1 << 20) for k in range(4)]
+    assert _code(plr.plr_pack, C, 0, src[:2], pk[:2]) == plr.PLR_EINVAL  # copy layouts have no packets
+    assert _code(plr.plr_pack, L, 4, src, pk) == plr.PLR_EINVAL  # no source 4
+    assert _code(plr.plr_pack, L, -2, src, pk) == plr.PLR_EINVAL
+    assert _code(plr.plr_pack, L, 0, [A + 8] + src[1:], pk) == plr.PLR_EALIGN
+    assert _code(plr.plr_pack, L, -1, src[:3] + [A + 8], pk) == plr.PLR_EALIGN
+    # source 1's share of a scattered layout at rank 1 starts 4096 bytes into its buffer
+    assert _code(plr.plr_pack, L, 1, src, pk[:1] + [src[1] + 4096 + 16] + pk[2:]) == plr.PLR_EINVAL
+    assert _code(plr.plr_pack, L, -1, src, pk[:3] + [pk[2] + 4096]) == plr.PLR_EINVAL  # packets overlap
+    assert _code(plr.plr_reduce_packets, L, pk, D, 0) == plr.PLR_EINVAL  # workspace required
+    assert _code(plr.plr_reduce_packets, L, pk, D, WS + 8) == plr.PLR_EALIGN
+    assert _code(plr.plr_reduce_packets, L, pk, pk[2] + 16, WS) == plr.PLR_EINVAL  # dst inside packets
+    assert _code(plr.plr_reduce_packets, L, pk[:3] + [pk[3] + 4], D, WS) == plr.PLR_EALIGN
+    assert L.epoch == 0  # rejected calls do not advance the epoch
