@@ -228,16 +228,22 @@ def run_bench(args):
             if name in L:
                 plr.plr_notify(L[name], -1, ws[name])
             if events is not None:
-                events[name][0].record()
+                # the library records this pair right around the op's datapath kernels
+                # (after a notified call's check kernel), on the stream they run on
+                plr.plr_set_timing_events(*events[name])
             op(name)
-            if events is not None:
-                events[name][1].record()
+        if events is not None:
+            plr.plr_set_timing_events()
 
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
     ev = [{n: (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for n in ops}
           for _ in range(args.steps)]
+    for e in ev:  # create the HIP events before the timed region
+        for a, b in e.values():
+            a.record()
+            b.record()
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for k in range(args.steps):
@@ -323,15 +329,18 @@ def run_decode(args, torch, plr, synth, dev):
             torch.cuda.synchronize()
             per_call = a0.elapsed_time(b0) * 1e3 / (50 * (args.decode_iters // 50))
             del graph
-            # (b) one pair of events around every reduce launch (includes the events' own cost)
+            # (b) one pair of events around every reduce kernel (includes the events' own cost)
             evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
                    for _ in range(args.decode_iters)]
+            for a, b in evs:
+                a.record()
+                b.record()
             torch.cuda.synchronize()
             for a, b in evs:
                 produce()
-                a.record()
+                plr.plr_set_timing_events(a, b)
                 consume()
-                b.record()
+            plr.plr_set_timing_events()
             torch.cuda.synchronize()
             us = sorted(a.elapsed_time(b) * 1e3 for a, b in evs)
             if ws is not None and plr.plr_check(L, ws) != plr.PLR_OK:
@@ -428,7 +437,7 @@ def main():
     ap.add_argument("--decode-t", type=lambda v: [int(x) for x in v.split(",")], default=None,
                     help="decode token counts T (comma separated; default 1,8,32,64)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-fraction", type=float, default=0.125)
+    ap.add_argument("--cpu-fraction", type=float, default=0.5)
     ap.add_argument("--cpu-reps", type=int, default=3)
     ap.add_argument("--summarize-trace", metavar="CSV",
                     help="print per-kernel durations of a rocprofv3 kernel-trace CSV and exit")

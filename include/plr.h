@@ -263,8 +263,8 @@ int plr_reduce_packets(plr_layout* L, const void* const* packets, void* dst, voi
  *   dst (device, sum(rows) * row_bytes)    row i of source s lands at row
  *                    offsets[d*W + s] + (rows i' < i of source s bound for d)
  *   scratch (device, plr_copy_v_scratch_bytes bytes): zero it once before the first
- *            call; every call leaves its 256-byte header at zero again (the rank array
- *            after it needs no initialisation). Concurrent calls need distinct scratch.
+ *            call; every call leaves its 256-byte header at zero again (the rest of
+ *            it needs no initialisation). Concurrent calls need distinct scratch.
  *   srcs, dest_of_row: host arrays of W device pointers; rows_per_src: host array.
  * A destination id outside [0, W) is a caller error: its row is skipped and its
  * counts and offsets are undefined.
@@ -274,8 +274,9 @@ int plr_copy_v(int world, const void* const* srcs, const int64_t* rows_per_src,
                int64_t* counts, int64_t* offsets, void* scratch, void* stream);
 
 /* Scratch bytes plr_copy_v needs for these row counts (host only): a 256-byte header,
- * one int32 per row, and two int32 per destination for every 1024-row segment of a
- * source, each region rounded up to 256 bytes. 0 for invalid arguments. */
+ * one 32-bit key per row, and for every 1024-row segment of a source W int32 counts
+ * and 16 int32 first output rows, each region rounded up to 256 bytes. 0 for invalid
+ * arguments. */
 size_t plr_copy_v_scratch_bytes(int world, const int64_t* rows_per_src);
 
 /* Producer side of notify (section 3.2 "SNAC"; section 4.3: the epoch supplies the
@@ -289,6 +290,16 @@ int plr_notify(plr_layout* L, int src, void* workspace, void* stream);
  * Returns PLR_OK, PLR_ETIMEOUT (some chunk's flag never reached its epoch; that
  * call's output is undefined), or PLR_EHIP / PLR_EINVAL for the check itself. */
 int plr_check(plr_layout* L, void* workspace, void* stream);
+
+/* Measurement aid (not part of the method): while `before` and `after` are set, every
+ * datapath call made by the calling host thread (plr_reduce, plr_copy, plr_copy_v,
+ * plr_allreduce, plr_reduce_packets) records `before` on its stream right before its
+ * datapath kernels are launched (after a notified call's check kernel) and `after`
+ * right after them, so that the pair times the datapath kernels alone. Both are
+ * hipEvent_t handles owned by the caller; NULL, NULL turns this off. The setting is
+ * per host thread. Errors: PLR_EINVAL if exactly one of the two is NULL. A failed
+ * event record makes the call return PLR_EHIP. */
+int plr_set_timing_events(void* before, void* after);
 
 /* Static text for an error code. */
 const char* plr_strerror(int code);

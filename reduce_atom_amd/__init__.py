@@ -92,6 +92,8 @@ _lib.plr_notify.argtypes = [_vp, _i, _vp, _vp]
 _lib.plr_notify.restype = _i
 _lib.plr_check.argtypes = [_vp, _vp, _vp]
 _lib.plr_check.restype = _i
+_lib.plr_set_timing_events.argtypes = [_vp, _vp]
+_lib.plr_set_timing_events.restype = _i
 _lib.plr_strerror.argtypes = [_i]
 _lib.plr_strerror.restype = _c.c_char_p
 _lib.plr_last_hip_error.argtypes = []
@@ -104,7 +106,8 @@ EXPORTS = [
     "plr_layout_nchunks", "plr_layout_ntiles", "plr_layout_nsegments", "plr_layout_segment", "plr_layout_policy",
     "plr_layout_epoch", "plr_reduce", "plr_copy", "plr_allreduce", "plr_copy_v", "plr_copy_v_scratch_bytes",
     "plr_layout_packet_bytes", "plr_pack", "plr_reduce_packets",
-    "plr_notify", "plr_check", "plr_strerror", "plr_last_hip_error", "plr_version",
+    "plr_notify", "plr_check", "plr_set_timing_events", "plr_strerror", "plr_last_hip_error",
+    "plr_version",
 ]
 
 
@@ -287,6 +290,19 @@ def plr_copy_v(srcs, rows_per_src, dest_of_row, row_bytes, dst, counts, offsets,
 
 def plr_notify(layout: Layout, src: int, workspace, stream=None) -> None:
     _ok(_lib.plr_notify(layout.handle, src, _addr(workspace), _stream(stream)), "plr_notify")
+
+
+def plr_set_timing_events(before=None, after=None) -> None:
+    """Bracket the datapath kernels of this thread's next calls with two torch.cuda.Event
+    objects (created with enable_timing=True); no arguments turns it off. The events
+    are recorded once here so that they exist as HIP events before the library records them."""
+    if before is None and after is None:
+        _ok(_lib.plr_set_timing_events(None, None), "plr_set_timing_events")
+        return
+    for e in (before, after):
+        if not e.cuda_event:  # torch creates its HIP event at the first record
+            e.record()
+    _ok(_lib.plr_set_timing_events(before.cuda_event, after.cuda_event), "plr_set_timing_events")
 
 
 def plr_check(layout: Layout, workspace, stream=None) -> int:

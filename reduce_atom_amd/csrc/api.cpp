@@ -15,6 +15,13 @@ namespace {
 
 thread_local int g_last_hip = 0;
 
+// Measurement events of the calling thread (plr_set_timing_events), or null.
+thread_local hipEvent_t g_ev_before = nullptr, g_ev_after = nullptr;
+
+// Brackets the datapath kernels of one call with the thread's measurement events.
+hipError_t mark_before(hipStream_t s) { return g_ev_before ? hipEventRecord(g_ev_before, s) : hipSuccess; }
+hipError_t mark_after(hipStream_t s) { return g_ev_after ? hipEventRecord(g_ev_after, s) : hipSuccess; }
+
 int hip_fail(hipError_t e) {
   g_last_hip = (int)e;
   return PLR_EHIP;
@@ -126,8 +133,11 @@ extern "C" int plr_reduce(plr_layout* L, const void* const* srcs, void* dst, voi
     const Launch l = launch_of(L, nt.flags != nullptr);
     a.run = l.run;
     a.xcd = (uint32_t)l.xcd;
-    hipError_t e = launch_check_for(L, nt, static_cast<hipStream_t>(stream));
-    if (e == hipSuccess) e = launch_reduce(a, L->dtype, l, static_cast<hipStream_t>(stream));
+    const hipStream_t s = static_cast<hipStream_t>(stream);
+    hipError_t e = launch_check_for(L, nt, s);
+    if (e == hipSuccess) e = mark_before(s);
+    if (e == hipSuccess) e = launch_reduce(a, L->dtype, l, s);
+    if (e == hipSuccess) e = mark_after(s);
     if (e != hipSuccess) return hip_fail(e);
   }
   if (workspace) L->epoch = nt.epoch;
@@ -167,23 +177,26 @@ extern "C" int plr_copy(plr_layout* L, const void* const* srcs, void* dst, void*
     const Launch l = launch_of(L, nt.flags != nullptr);
     a.run = l.run;
     a.xcd = (uint32_t)l.xcd;
-    hipError_t e = launch_check_for(L, nt, static_cast<hipStream_t>(stream));
-    if (e == hipSuccess) e = launch_copy(a, l, static_cast<hipStream_t>(stream));
+    const hipStream_t s = static_cast<hipStream_t>(stream);
+    hipError_t e = launch_check_for(L, nt, s);
+    if (e == hipSuccess) e = mark_before(s);
+    if (e == hipSuccess) e = launch_copy(a, l, s);
+    if (e == hipSuccess) e = mark_after(s);
     if (e != hipSuccess) return hip_fail(e);
   }
   if (workspace) L->epoch = nt.epoch;
   return PLR_OK;
 }
 
-// Scratch of plr_copy_v: a 256-byte header (u32 ticket at byte 0), int32 rank[rows],
-// then int32 seg_count[segments][W] and int32 seg_base[segments][W], each region
-// rounded up to 256 bytes; a segment is kRankSeg rows of one source.
+// Scratch of plr_copy_v: a 256-byte header (u32 ticket at byte 0), uint32 key[rows],
+// then int32 seg_count[segments][W] and int32 seg_out[segments][PLR_MAX_WORLD], each
+// region rounded up to 256 bytes; a segment is kRankSeg rows of one source.
 constexpr uint64_t kCopyVScratchHeader = 256;
 
 static uint64_t up256(uint64_t x) { return (x + 255) & ~255ull; }
 
 struct CopyVScratch {
-  uint64_t rank_off, count_off, base_off, bytes;
+  uint64_t key_off, count_off, out_off, bytes;
 };
 
 static CopyVScratch copy_v_scratch(int world, const int64_t* rows_per_src) {
@@ -194,10 +207,10 @@ static CopyVScratch copy_v_scratch(int world, const int64_t* rows_per_src) {
     segs += (r + kRankSeg - 1) / kRankSeg;
   }
   CopyVScratch c;
-  c.rank_off = kCopyVScratchHeader;
-  c.count_off = c.rank_off + up256(total * sizeof(int32_t));
-  c.base_off = c.count_off + up256(segs * world * sizeof(int32_t));
-  c.bytes = c.base_off + up256(segs * world * sizeof(int32_t));
+  c.key_off = kCopyVScratchHeader;
+  c.count_off = c.key_off + up256(total * sizeof(uint32_t));
+  c.out_off = c.count_off + up256(segs * world * sizeof(int32_t));
+  c.bytes = c.out_off + up256(segs * PLR_MAX_WORLD * sizeof(int32_t));
   return c;
 }
 
@@ -232,7 +245,7 @@ extern "C" int plr_copy_v(int world, const void* const* srcs, const int64_t* row
   }
   const int64_t total = a.row_start[world];
   for (int s = world + 1; s <= PLR_MAX_WORLD; ++s) a.row_start[s] = total;
-  if (total > 0x7FFFFFFF) return PLR_EUNSUPPORTED;  // ranks are int32
+  if (total > 0x7FFFFFFF) return PLR_EUNSUPPORTED;  // output rows are int32
   if (total > 0) {
     if (!a16(dst)) return PLR_EALIGN;
     const uint64_t out_bytes = (uint64_t)total * row_bytes;
@@ -245,19 +258,23 @@ extern "C" int plr_copy_v(int world, const void* const* srcs, const int64_t* row
   a.offsets = offsets;
   const CopyVScratch layout = copy_v_scratch(world, rows_per_src);
   a.ticket = static_cast<uint32_t*>(scratch);
-  a.rank = reinterpret_cast<int32_t*>(static_cast<char*>(scratch) + layout.rank_off);
+  a.key = reinterpret_cast<uint32_t*>(static_cast<char*>(scratch) + layout.key_off);
   a.seg_count = reinterpret_cast<int32_t*>(static_cast<char*>(scratch) + layout.count_off);
-  a.seg_base = reinterpret_cast<int32_t*>(static_cast<char*>(scratch) + layout.base_off);
+  a.seg_out = reinterpret_cast<int32_t*>(static_cast<char*>(scratch) + layout.out_off);
   a.seg_start[0] = 0;
   for (int s = 0; s < world; ++s)
     a.seg_start[s + 1] = a.seg_start[s] + (uint32_t)((rows_per_src[s] + kRankSeg - 1) / kRankSeg);
   for (int s = world + 1; s <= PLR_MAX_WORLD; ++s) a.seg_start[s] = a.seg_start[world];
   a.row_bytes = row_bytes;
   a.world = (uint32_t)world;
-  a.xcd = 0;  // measured: the XCD-contiguous order slowed the row scatter (185 vs 172 us)
-  // one row per wave: four rows per 256-thread workgroup
-  const uint32_t grid = (uint32_t)std::max<uint64_t>(1, ((uint64_t)total + 3) / 4);
-  hipError_t e = launch_copy_v(a, grid, static_cast<hipStream_t>(stream));
+#ifndef PLR_CV_XCD
+#define PLR_CV_XCD 0
+#endif
+  a.xcd = PLR_CV_XCD;  // XCD-contiguous order of the row scatter
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e = mark_before(s);
+  if (e == hipSuccess) e = launch_copy_v(a, s);
+  if (e == hipSuccess) e = mark_after(s);
   if (e != hipSuccess) return hip_fail(e);
   return PLR_OK;
 }
@@ -305,7 +322,10 @@ extern "C" int plr_allreduce(plr_layout* L, const void* const* srcs, void* const
     a.run = run_for(L, false);
     l.grid = (uint32_t)std::max<uint64_t>(1, ((uint64_t)L->ntiles + a.run - 1) / a.run);
   }
-  hipError_t e = launch_allreduce(a, L->dtype, l, static_cast<hipStream_t>(stream));
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e = mark_before(s);
+  if (e == hipSuccess) e = launch_allreduce(a, L->dtype, l, s);
+  if (e == hipSuccess) e = mark_after(s);
   if (e != hipSuccess) return hip_fail(e);
   if (composed) L->epoch = a.nt.epoch;
   return PLR_OK;
@@ -362,7 +382,10 @@ extern "C" int plr_reduce_packets(plr_layout* L, const void* const* packets, voi
     a.stamp = (uint32_t)epoch;
     a.err = static_cast<uint64_t*>(workspace);
     a.spin_limit = L->spin_limit;
-    hipError_t e = launch_reduce_packets(a, L->dtype, static_cast<hipStream_t>(stream));
+    const hipStream_t s = static_cast<hipStream_t>(stream);
+    hipError_t e = mark_before(s);
+    if (e == hipSuccess) e = launch_reduce_packets(a, L->dtype, s);
+    if (e == hipSuccess) e = mark_after(s);
     if (e != hipSuccess) return hip_fail(e);
   }
   L->epoch = epoch;
@@ -400,6 +423,13 @@ extern "C" int plr_check(plr_layout* L, void* workspace, void* stream) {
     if (e != hipSuccess) return hip_fail(e);
     return v == PLR_ETIMEOUT ? PLR_ETIMEOUT : PLR_EINVAL;
   }
+  return PLR_OK;
+}
+
+extern "C" int plr_set_timing_events(void* before, void* after) {
+  if ((before == nullptr) != (after == nullptr)) return PLR_EINVAL;
+  g_ev_before = static_cast<hipEvent_t>(before);
+  g_ev_after = static_cast<hipEvent_t>(after);
   return PLR_OK;
 }
 

@@ -4,31 +4,36 @@
 // passed at run time) and section 4 (partition offsets come from prefix sums).
 // Output rows are packed per destination, in source then row order:
 //   kernel 1 (one workgroup per 1024-row segment of a source): for every row, its
-//            rank among the earlier rows of its segment bound for the same
-//            destination (wave ballots plus a workgroup-wide exclusive scan), and the
-//            segment's counts; the last of those workgroups scans the segments into
-//            per-segment bases, counts[s][d] and offsets[d][s] (an exclusive scan in
-//            destination-major order);
-//   kernel 2 (one wave per row): moves whole rows with 16-byte loads and stores to
-//            row offsets[d][s] + rank.
+//            destination and its rank among the earlier rows of its segment bound for
+//            the same destination (wave ballots plus a workgroup-wide exclusive scan),
+//            packed into one key, and the segment's counts; the last of those
+//            workgroups scans the segments: counts[s][d], offsets[d][s] (an exclusive
+//            scan in destination-major order) and, per segment and destination, the
+//            output row of the segment's first row bound there;
+//   kernel 2 (row tiles, one per workgroup step): moves every row with 16-byte loads
+//            and stores to that segment row plus the row's rank.
 #include "device_common.h"
 
 namespace plr {
 
 constexpr int kRankThreads = kRankSeg;
 constexpr int kRankWaves = kRankThreads / 64;
+constexpr uint32_t kCountLds = 8192;  // segment counts the last rank workgroup stages in LDS
 
 // Kernel 1: one workgroup per segment of kRankSeg consecutive rows of one source, one
 // row per thread. A wave ballot per destination gives each row its rank among the
 // lower lanes bound for the same destination, and per-wave totals in LDS the rank
 // across waves: the row's rank inside its segment. The segment's per-destination
 // counts go to scratch. The last workgroup to finish (a ticket counter in scratch,
-// acquire-release at agent scope, left at zero again) scans them: per source and
-// destination the rows of earlier segments (seg_base), the totals counts[s][d], and
-// offsets[d][s] (an exclusive scan in destination-major order).
+// acquire-release at agent scope, left at zero again) loads all segment counts at once
+// (into LDS when they fit) and scans them into counts[s][d], offsets[d][s] and
+// seg_out[segment][d] = offsets[d][s] + the rows of the same source's earlier
+// segments bound for d.
 __global__ void __launch_bounds__(kRankThreads) k_copy_v_rank(const CopyVArgs a) {
   __shared__ int32_t wave_cnt[kRankWaves][PLR_MAX_WORLD];
   __shared__ int64_t tot[PLR_MAX_WORLD * PLR_MAX_WORLD];
+  __shared__ int64_t off[PLR_MAX_WORLD * PLR_MAX_WORLD];
+  __shared__ int32_t cnt_lds[kCountLds];
   __shared__ int last;
 
   const int W = (int)a.world;
@@ -52,10 +57,14 @@ __global__ void __launch_bounds__(kRankThreads) k_copy_v_rank(const CopyVArgs a)
     }
   }
   __syncthreads();
-  if (d >= 0 && d < W) {
-    int r = in_wave;
-    for (int w2 = 0; w2 < wave; ++w2) r += wave_cnt[w2][d];
-    a.rank[a.row_start[s] + i] = r;
+  if (i < rows) {
+    uint32_t key = kNoDest << 16;  // no destination: the row is dropped
+    if (d >= 0 && d < W) {
+      int r = in_wave;
+      for (int w2 = 0; w2 < wave; ++w2) r += wave_cnt[w2][d];
+      key = ((uint32_t)d << 16) | (uint32_t)r;
+    }
+    a.key[a.row_start[s] + i] = key;
   }
   if (t < W) {
     int c = 0;
@@ -72,16 +81,23 @@ __global__ void __launch_bounds__(kRankThreads) k_copy_v_rank(const CopyVArgs a)
   __syncthreads();
   if (!last) return;
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+  // every segment count in one round of loads, staged in LDS when they fit
+  const uint64_t nsc = (uint64_t)a.seg_start[W] * W;
+  const bool staged = nsc <= kCountLds;
+  if (staged)
+    for (uint64_t k = t; k < nsc; k += kRankThreads)
+      cnt_lds[k] = __hip_atomic_load(a.seg_count + k, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  __syncthreads();
+  auto seg_cnt = [&](uint64_t k) -> int32_t {
+    return staged ? cnt_lds[k] : __hip_atomic_load(a.seg_count + k, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  };
   const int WW = W * W;
-  if (t < WW) {  // thread (s2, d2): scan source s2's segments for destination d2
+  if (t < WW) {  // thread (s2, d2): source s2's rows bound for d2
     const int s2 = t / W, d2 = t - s2 * W;
     int64_t run = 0;
-    for (uint32_t g = a.seg_start[s2]; g < a.seg_start[s2 + 1]; ++g) {
-      a.seg_base[(uint64_t)g * W + d2] = (int32_t)run;
-      run += __hip_atomic_load(a.seg_count + (uint64_t)g * W + d2, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    }
-    tot[t] = run;  // counts[s2][d2]
-    a.counts[t] = run;
+    for (uint32_t g = a.seg_start[s2]; g < a.seg_start[s2 + 1]; ++g) run += seg_cnt((uint64_t)g * W + d2);
+    tot[t] = run;
+    a.counts[t] = run;  // counts[s2][d2]
   }
   __syncthreads();
   if (t < WW) {
@@ -92,59 +108,105 @@ __global__ void __launch_bounds__(kRankThreads) k_copy_v_rank(const CopyVArgs a)
     for (int dd = 0; dd < d3; ++dd)
       for (int ss = 0; ss < W; ++ss) o += tot[ss * W + dd];
     for (int ss = 0; ss < s3; ++ss) o += tot[ss * W + d3];
-    a.offsets[t] = o;
+    off[t] = o;
+    a.offsets[t] = o;  // offsets[d3][s3]
+  }
+  __syncthreads();
+  if (t < WW) {  // thread (s2, d2) again: first output row of each segment's d2 rows
+    const int s2 = t / W, d2 = t - s2 * W;
+    int64_t run = off[d2 * W + s2];
+    for (uint32_t g = a.seg_start[s2]; g < a.seg_start[s2 + 1]; ++g) {
+      a.seg_out[(uint64_t)g * PLR_MAX_WORLD + d2] = (int32_t)run;
+      run += seg_cnt((uint64_t)g * W + d2);
+    }
   }
   if (t == 0) __hip_atomic_store(a.ticket, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-constexpr int kScatterThreads = 256;
-constexpr int kScatterUnroll = 16;
+// Kernel 2 cuts every row into tiles of kCvTileBytes (the last tile of a row may be
+// shorter); a workgroup of kCvThreads lanes moves kCvRun consecutive tiles, one
+// 16-byte vector per lane per step, so that the chip holds many short workgroups with
+// their loads in flight, as the copy kernel does. A tile's source address and the
+// locations of its row's key and segment table depend only on the row, so all of its
+// loads are issued together; the output row is then the segment table's entry for the
+// key's destination plus the key's rank, with no second dependent load.
+#ifndef PLR_CV_TILE_BYTES
+#define PLR_CV_TILE_BYTES 2048
+#endif
+#ifndef PLR_CV_THREADS
+#define PLR_CV_THREADS 128
+#endif
+#ifndef PLR_CV_RUN
+#define PLR_CV_RUN 2
+#endif
+constexpr uint64_t kCvTileBytes = PLR_CV_TILE_BYTES;
+constexpr int kCvThreads = PLR_CV_THREADS;
+constexpr uint32_t kCvRun = PLR_CV_RUN;
+constexpr int kCvVecs = (int)(kCvTileBytes / 16 / kCvThreads);  // vectors per lane per tile
+static_assert(kCvTileBytes % (16 * kCvThreads) == 0, "a tile is whole vectors of every lane");
 
-// Kernel 2: wave k of the grid moves row k. The row's loads are issued first (a
-// source row exists whatever its destination); its destination, rank and block
-// offset are read meanwhile, and the stores go to row offsets[d][s] + rank. All of a
-// 14,336-byte row (14 vectors per lane) is in flight at once.
-__global__ void __launch_bounds__(kScatterThreads) k_copy_v_scatter(const CopyVArgs a) {
-  const int W = (int)a.world;
-  const int lane = threadIdx.x & 63;
-  const uint64_t nvec = a.row_bytes >> 4;
-  const int64_t total = a.row_start[W];
-  const int waves_per_block = kScatterThreads / 64;
-  const int64_t wave =
-      (int64_t)logical_block(a.xcd) * waves_per_block + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int64_t nwaves = (int64_t)gridDim.x * waves_per_block;
-  for (int64_t r = wave; r < total; r += nwaves) {
-    int s = 0;
-    while (r >= a.row_start[s + 1]) ++s;
-    const int64_t i = r - a.row_start[s];
-    const u32x4* src = reinterpret_cast<const u32x4*>(a.src[s] + (uint64_t)i * a.row_bytes);
-    for (uint64_t v0 = 0; v0 < nvec; v0 += 64 * kScatterUnroll) {
-      u32x4 x[kScatterUnroll];
-#pragma unroll
-      for (int u = 0; u < kScatterUnroll; ++u) {
-        const uint64_t v = v0 + (uint64_t)u * 64 + lane;
-        if (v < nvec) x[u] = ld16(src + v);
-      }
-      const int32_t d = a.dest[s][i];
-      if (d < 0 || d >= W) break;  // not a destination: the row is dropped
+__global__ void __launch_bounds__(kCvThreads) k_copy_v_scatter(const CopyVArgs a) {
+  const uint32_t W = a.world;
+  // Written by kernel 1 and only read here, and the same for every lane of a tile:
+  // read through the constant address space so that they are scalar loads, which
+  // leave the vector memory path to the row's data.
+  const PLR_CONST uint32_t* key_of = (const PLR_CONST uint32_t*)a.key;
+  const PLR_CONST int32_t* seg_out = (const PLR_CONST int32_t*)a.seg_out;
+  const uint64_t tiles_per_row = (a.row_bytes + kCvTileBytes - 1) / kCvTileBytes;
+  const uint64_t ntiles = (uint64_t)a.row_start[W] * tiles_per_row;
+  const uint64_t stride = (uint64_t)gridDim.x * kCvRun;
+  for (uint64_t t0 = (uint64_t)logical_block(a.xcd) * kCvRun; t0 < ntiles; t0 += stride) {
+    const uint64_t t1 = min(t0 + kCvRun, ntiles);
+    for (uint64_t t = t0; t < t1; ++t) {
+      const int64_t r = (int64_t)(t / tiles_per_row);
+      const uint64_t b0 = (t - (uint64_t)r * tiles_per_row) * kCvTileBytes;
+      const uint64_t nv = (min(b0 + kCvTileBytes, a.row_bytes) - b0) >> 4;
+      int s = 0;
+      while (r >= a.row_start[s + 1]) ++s;
+      const int64_t i = r - a.row_start[s];
       const uint64_t g = a.seg_start[s] + (uint64_t)(i / kRankSeg);
-      const int64_t out = a.offsets[d * W + s] + a.seg_base[g * W + d] + a.rank[r];
-      u32x4* dst = reinterpret_cast<u32x4*>(a.dst + (uint64_t)out * a.row_bytes);
+      const u32x4* src = reinterpret_cast<const u32x4*>(a.src[s] + (uint64_t)i * a.row_bytes + b0);
+      u32x4 x[kCvVecs];
 #pragma unroll
-      for (int u = 0; u < kScatterUnroll; ++u) {
-        const uint64_t v = v0 + (uint64_t)u * 64 + lane;
-        if (v < nvec) st16(dst + v, x[u]);
+      for (int u = 0; u < kCvVecs; ++u) {
+        const uint64_t v = (uint64_t)u * kCvThreads + threadIdx.x;
+        if (v < nv) x[u] = ld16(src + v);
+      }
+      // The row's data loads are issued first, then its key and its segment's table
+      // (64 bytes), all before any of them is waited for.
+      asm volatile("" ::: "memory");
+      const uint32_t key = key_of[r];
+      const PLR_CONST int32_t* tp = seg_out + g * PLR_MAX_WORLD;
+      int32_t tab[PLR_MAX_WORLD];
+#pragma unroll
+      for (int k = 0; k < PLR_MAX_WORLD; ++k) tab[k] = tp[k];
+      asm volatile("" ::: "memory");
+      const uint32_t d = key >> 16;
+      if (d >= W) continue;  // not a destination: the row is dropped
+      int32_t base = tab[0];
+#pragma unroll
+      for (int k = 1; k < PLR_MAX_WORLD; ++k) base = (d == (uint32_t)k) ? tab[k] : base;
+      const int64_t out = (int64_t)base + (key & 0xFFFFu);
+      u32x4* dst = reinterpret_cast<u32x4*>(a.dst + (uint64_t)out * a.row_bytes + b0);
+#pragma unroll
+      for (int u = 0; u < kCvVecs; ++u) {
+        const uint64_t v = (uint64_t)u * kCvThreads + threadIdx.x;
+        if (v < nv) st16(dst + v, x[u]);
       }
     }
   }
 }
 
-hipError_t launch_copy_v(const CopyVArgs& a, uint32_t scatter_grid, hipStream_t s) {
+hipError_t launch_copy_v(const CopyVArgs& a, hipStream_t s) {
   const uint32_t segs = a.seg_start[a.world];
   hipLaunchKernelGGL(k_copy_v_rank, dim3(segs ? segs : 1), dim3(kRankThreads), 0, s, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(k_copy_v_scatter, dim3(scatter_grid), dim3(kScatterThreads), 0, s, a);
+  // one workgroup per kCvRun tiles; huge inputs make the grid stride over the tiles
+  const uint64_t tiles = (uint64_t)a.row_start[a.world] * ((a.row_bytes + kCvTileBytes - 1) / kCvTileBytes);
+  const uint64_t groups = (tiles + kCvRun - 1) / kCvRun;
+  const uint32_t grid = (uint32_t)(groups < 1 ? 1 : (groups > (1u << 22) ? (1u << 22) : groups));
+  hipLaunchKernelGGL(k_copy_v_scatter, dim3(grid), dim3(kCvThreads), 0, s, a);
   return hipGetLastError();
 }
 

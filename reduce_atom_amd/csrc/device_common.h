@@ -32,6 +32,11 @@ __device__ __forceinline__ void st16(u32x4* p, u32x4 v) {
 #endif
 }
 
+// Constant address space: loads through such a pointer that are the same for every
+// lane become scalar loads. Only for data that no kernel writes while the reading
+// kernel runs (the scalar cache is refilled at every kernel start).
+#define PLR_CONST __attribute__((address_space(4)))
+
 // ---- XCD-aware workgroup order ----
 // The dispatcher hands workgroup b to XCD b % 8 (MI355X has 8 XCDs, each with its
 // own L2). When `xcd` is set, logical workgroup ids are renumbered so that each XCD

@@ -101,6 +101,7 @@ struct CopyArgs {
 };
 
 constexpr int kRankSeg = 1024;  // rows per rank workgroup (one per thread)
+constexpr uint32_t kNoDest = 0xFFFFu;
 
 struct CopyVArgs {
   const uint8_t* src[PLR_MAX_WORLD];
@@ -108,11 +109,13 @@ struct CopyVArgs {
   int64_t row_start[PLR_MAX_WORLD + 1];  // prefix of rows_per_src
   uint32_t seg_start[PLR_MAX_WORLD + 1]; // prefix of ceil(rows_per_src / kRankSeg)
   int32_t* seg_count;  // scratch [segments][W]: rows of a segment bound for each destination
-  int32_t* seg_base;   // scratch [segments][W]: rows of earlier segments of the same source
+  int32_t* seg_out;    // scratch [segments][PLR_MAX_WORLD]: output row of the segment's first row
+                       // bound for each destination
   uint8_t* dst;
   int64_t* counts;   // [s][d]
   int64_t* offsets;  // [d][s]
-  int32_t* rank;     // scratch: rank of each row inside its segment and destination
+  uint32_t* key;     // scratch, per row: destination << 16 | rank inside its segment and
+                     // destination (kNoDest << 16 for a row that has no destination)
   uint32_t* ticket;  // scratch: count of finished rank workgroups (zero between calls)
   uint64_t row_bytes;
   uint32_t world;
@@ -164,7 +167,7 @@ struct NotifyArgs {
 // Launchers (defined next to their kernels). Return a hipError_t.
 hipError_t launch_reduce(const ReduceArgs& a, int dtype, const Launch& l, hipStream_t s);
 hipError_t launch_copy(const CopyArgs& a, const Launch& l, hipStream_t s);
-hipError_t launch_copy_v(const CopyVArgs& a, uint32_t scatter_grid, hipStream_t s);
+hipError_t launch_copy_v(const CopyVArgs& a, hipStream_t s);
 hipError_t launch_allreduce(const AllReduceArgs& a, int dtype, const Launch& l, hipStream_t s);
 hipError_t launch_pack(const PackArgs& a, uint32_t nsrc, hipStream_t s);
 hipError_t launch_reduce_packets(const PacketReduceArgs& a, int dtype, hipStream_t s);

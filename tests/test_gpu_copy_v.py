@@ -77,6 +77,28 @@ def test_many_tiles_per_source(plr, oracle_mod):
     _check(plr, oracle_mod, srcs, dests, rb)
 
 
+@pytest.mark.parametrize("rb", [2064, 6160, 4096])
+def test_row_tiles_ragged(plr, oracle_mod, rb):
+    """Rows that are not a whole number of the scatter's 2 KiB tiles (a last tile of one
+    vector, or of 2 KiB + 16 bytes), and rows of exactly two tiles."""
+    W = 3
+    rows = [37, 0, 21]
+    p = synth.zipf_weights(1.1, W)
+    dests = [synth.categorical_np(13, 5, s, rows[s], p) for s in range(W)]
+    srcs = [synth.bits_np(13, 6, s, max(rows[s], 1) * rb) for s in range(W)]
+    _check(plr, oracle_mod, srcs, dests, rb)
+
+
+def test_many_segments(plr, oracle_mod):
+    """More segment counts (1024-row segments x W) than the last rank workgroup stages in
+    LDS (8192): W=16 with 36,000 rows per source gives 576 segments, 9216 counts."""
+    W, R, rb = 16, 36000, 16
+    p = synth.zipf_weights(1.1, W)
+    dests = [synth.categorical_np(14, 5, s, R + s, p) for s in range(W)]
+    srcs = [synth.bits_np(14, 6, s, (R + s) * rb) for s in range(W)]
+    _check(plr, oracle_mod, srcs, dests, rb)
+
+
 def test_special_destinations(plr, oracle_mod):
     W, R, rb = 8, 1000, 32
     srcs = [synth.bits_np(11, 6, s, R * rb) for s in range(W)]

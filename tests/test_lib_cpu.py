@@ -181,10 +181,11 @@ def test_call_validation_without_device(plr):
 
 
 def test_scratch_bytes(plr):
-    # header + ranks + 2 x (segments x W) int32, each rounded up to 256 bytes
-    assert plr.plr_copy_v_scratch_bytes(8, [4096] * 8) == 256 + 8 * 4096 * 4 + 2 * (32 * 8 * 4)
-    assert plr.plr_copy_v_scratch_bytes(2, [1, 2]) == 256 + 256 + 2 * 256
-    assert plr.plr_copy_v_scratch_bytes(2, [1025, 0]) == 256 + 4352 + 2 * 256
+    # header + one key per row + (segments x W) counts + (segments x 16) segment rows,
+    # int32 each, every region rounded up to 256 bytes
+    assert plr.plr_copy_v_scratch_bytes(8, [4096] * 8) == 256 + 8 * 4096 * 4 + 32 * 8 * 4 + 32 * 16 * 4
+    assert plr.plr_copy_v_scratch_bytes(2, [1, 2]) == 256 + 256 + 256 + 256
+    assert plr.plr_copy_v_scratch_bytes(2, [1025, 0]) == 256 + 4352 + 256 + 256
     assert plr.plr_copy_v_scratch_bytes(2, [-1, 0]) == 0
     assert plr.plr_copy_v_scratch_bytes(0, []) == 0
 
