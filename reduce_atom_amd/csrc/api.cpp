@@ -91,7 +91,7 @@ int check_call(const plr_layout* L, plr_op op, const void* const* srcs, const vo
     nt->flags = reinterpret_cast<const uint64_t*>(static_cast<char*>(workspace) + kWorkspaceHeader);
     if (L->notify_mode == PLR_NOTIFY_CHECK) {
       nt->ready = static_cast<uint64_t*>(workspace) + 1;
-      nt->mirror = nt->flags + (uint64_t)L->world * L->nchunks;
+      nt->mirror = nt->flags + nflags(L);
     }
   }
   return PLR_OK;
@@ -102,12 +102,10 @@ hipError_t launch_check_for(const plr_layout* L, const Notify& nt, hipStream_t s
   if (!nt.ready || !L->ntiles) return hipSuccess;
   CheckArgs c{};
   c.flags = nt.flags;
-  c.nflags = (uint64_t)L->world * L->nchunks;
+  c.nflags = nflags(L);
   c.epoch = nt.epoch;
   c.ready = const_cast<uint64_t*>(nt.ready);
   c.mirror = const_cast<uint64_t*>(nt.mirror);
-  c.partial = c.mirror + c.nflags;
-  c.ticket = reinterpret_cast<uint32_t*>(const_cast<uint64_t*>(nt.ready) + 1);
   return launch_check(c, s);
 }
 
@@ -400,8 +398,8 @@ extern "C" int plr_notify(plr_layout* L, int src, void* workspace, void* stream)
   if (L->nchunks == 0) return PLR_OK;
   NotifyArgs a{};
   uint64_t* flags = reinterpret_cast<uint64_t*>(static_cast<char*>(workspace) + kWorkspaceHeader);
-  a.flags = src < 0 ? flags : flags + (uint64_t)src * L->nchunks;
-  a.nflags = src < 0 ? (uint64_t)L->world * L->nchunks : L->nchunks;
+  a.flags = src < 0 ? flags : flags + (uint64_t)src * flags_per_src(L);
+  a.nflags = src < 0 ? nflags(L) : flags_per_src(L);
   a.epoch = L->epoch + 1;
   hipError_t e = launch_notify(a, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e);

@@ -35,7 +35,7 @@ __global__ void __launch_bounds__(512) k_copy_direct(const CopyArgs a) {
     }
     if (wait) {
       const uint32_t c = seg * a.chunks_per_seg + part / a.tiles_per_chunk;
-      const uint32_t f = s * a.nchunks + c;
+      const uint32_t f = c;  // flags follow the segments, source by source
       if (f != ready) {
         if (!wg_wait_flags(a.nt, f, 0, 1)) return;
         ready = f;
@@ -114,7 +114,7 @@ __global__ void __launch_bounds__(256) k_copy_lds(const CopyArgs a) {
     bool valid;
     const uint32_t c = where(j, s, src_b, dst_b, valid);
     if (wait) {
-      const uint32_t f = s * a.nchunks + c;
+      const uint32_t f = c;  // flags follow the segments, source by source
       if (f != ready) {
         if (!wg_wait_flags(a.nt, f, 0, 1)) return false;
         ready = f;

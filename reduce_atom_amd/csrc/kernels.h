@@ -15,9 +15,8 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));  // one 16-byte vect
 
 constexpr int kMaxTableSegs = 64;   // explicit segment table carried in kernarg
 enum { kXcdOff = 0, kXcdOn = 1, kXcdUnnotified = 2 };
-// Workspace: u64 error word at byte 0, u64 ready word at byte 8, u32 check ticket
-// at byte 16, then uint64 flags[W][nchunks], their check-time mirror
-// uint64 mirror[W][nchunks], and one u64 partial result per check workgroup.
+// Workspace: u64 error word at byte 0, u64 ready word at byte 8, then
+// uint64 flags[W][nchunks] and their check-time mirror uint64 mirror[W][nchunks].
 constexpr size_t kWorkspaceHeader = 256;
 constexpr uint64_t kDefaultSpinLimit = 1ull << 20;
 
@@ -48,10 +47,8 @@ struct CheckArgs {
   uint64_t epoch;
   uint64_t* ready;        // receives epoch if every flag is >= epoch, else 0
   uint64_t* mirror;       // per flag: epoch if it is >= epoch, else 0
-  uint64_t* partial;      // per check workgroup: 1 if all of its flags had arrived
-  uint32_t* ticket;       // finished check workgroups (zero between calls)
 };
-constexpr int kCheckThreads = 1024;  // flags per check workgroup
+constexpr int kCheckThreads = 1024;  // the check is one workgroup
 
 // Work division shared by reduce and copy: a workgroup consumes a run of whole
 // consecutive tiles (a tile is the Atom's step), and tiles_per_chunk consecutive
@@ -87,7 +84,7 @@ struct CopyArgs {
   uint32_t ntiles;
   uint32_t tiles_per_chunk;
   uint32_t chunks_per_seg;
-  uint32_t nchunks;     // flags per source: segment k's chunk j is flag k*chunks_per_seg + j
+  uint32_t nchunks;     // chunks of all segments: segment k's chunk j is flag k*chunks_per_seg + j
   uint32_t nseg;
   uint32_t world;
   uint32_t mode;

@@ -268,9 +268,7 @@ extern "C" void plr_layout_destroy(plr_layout* L) { delete L; }
 extern "C" size_t plr_layout_workspace_bytes(const plr_layout* L) {
   if (!L) return 0;
   if (L->op == PLR_OP_ALLREDUCE) return kWorkspaceHeader + (size_t)L->nchunks * sizeof(uint64_t);
-  const size_t nflags = (size_t)L->world * L->nchunks;
-  const size_t partials = (nflags + kCheckThreads - 1) / kCheckThreads;
-  return kWorkspaceHeader + (2 * nflags + partials) * sizeof(uint64_t);
+  return kWorkspaceHeader + 2 * (size_t)nflags(L) * sizeof(uint64_t);
 }
 
 extern "C" size_t plr_layout_dst_bytes(const plr_layout* L) { return L ? L->dst_bytes : 0; }

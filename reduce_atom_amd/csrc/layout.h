@@ -60,4 +60,13 @@ struct plr_layout {
 
 namespace plr {
 size_t elem_bytes(plr_dtype t);
+
+// Chunk flags of a notified layout. Reduce: flags[W][nchunks], one per source and chunk
+// of the share. Copy: one per chunk of every segment, in segment order (segment k's
+// chunk j is flag k * chunks_per_seg + j); segments are listed source by source, each
+// source with the same number, so source s's flags are the s-th of W equal ranges.
+inline uint64_t nflags(const plr_layout* L) {
+  return L->op == PLR_OP_COPY ? (uint64_t)L->nchunks : (uint64_t)L->world * L->nchunks;
+}
+inline uint64_t flags_per_src(const plr_layout* L) { return nflags(L) / (uint64_t)L->world; }
 }

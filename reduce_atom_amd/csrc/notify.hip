@@ -16,44 +16,39 @@ __global__ void __launch_bounds__(256) k_notify(const NotifyArgs a) {
 
 // Check ahead of a notified consumer: it reads every chunk flag once (agent-scope
 // atomic loads), mirrors which ones have reached the epoch, and if all have it records
-// the epoch in the workspace's ready word. The acquire fence makes
-// the producers' releases happen before this kernel's end, so the consuming kernel
-// that follows in stream order may read every chunk whose flag was mirrored without
-// waiting or fencing; only the chunks still missing are waited for one by one
-// (section 3.2: a consumer never reads a chunk before its flag).
-// Many flags: one workgroup per kCheckThreads flags; each records whether all of its
-// flags had arrived, and the last workgroup to finish (a ticket, acquire-release at
-// agent scope, reset by that workgroup) combines them into the ready word.
+// the epoch in the workspace's ready word. The acquire fence makes the producers'
+// releases happen before this kernel's end, so the consuming kernel that follows in
+// stream order may read every chunk whose flag was mirrored without waiting or
+// fencing; only the chunks still missing are waited for one by one (section 3.2: a
+// consumer never reads a chunk before its flag). One workgroup does it all, with
+// kCheckUnroll flag loads per lane in flight, so that the verdict needs one round of
+// loads and a workgroup barrier, not a second kernel-wide combining step.
+constexpr int kCheckUnroll = 8;
+
 __global__ void __launch_bounds__(kCheckThreads) k_check(const CheckArgs a) {
-  __shared__ int last;
-  const uint64_t i = (uint64_t)blockIdx.x * kCheckThreads + threadIdx.x;
   int ok = 1;
-  if (i < a.nflags) {
-    ok = __hip_atomic_load(a.flags + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) >= a.epoch;
-    a.mirror[i] = ok ? a.epoch : 0;
+  for (uint64_t base = 0; base < a.nflags; base += (uint64_t)kCheckThreads * kCheckUnroll) {
+    uint64_t f[kCheckUnroll];
+#pragma unroll
+    for (int u = 0; u < kCheckUnroll; ++u) {
+      const uint64_t i = base + (uint64_t)u * kCheckThreads + threadIdx.x;
+      f[u] = i < a.nflags ? __hip_atomic_load(a.flags + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : a.epoch;
+    }
+#pragma unroll
+    for (int u = 0; u < kCheckUnroll; ++u) {
+      const uint64_t i = base + (uint64_t)u * kCheckThreads + threadIdx.x;
+      const bool arrived = f[u] >= a.epoch;
+      if (i < a.nflags) a.mirror[i] = arrived ? a.epoch : 0;
+      ok &= arrived;
+    }
   }
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
   const int all = __syncthreads_and(ok);
-  if (threadIdx.x == 0) {
-    a.partial[blockIdx.x] = all;
-    const uint32_t done = __hip_atomic_fetch_add(a.ticket, 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
-    last = done == gridDim.x - 1;
-  }
-  __syncthreads();
-  if (!last) return;
-  int every = 1;
-  for (uint32_t w = threadIdx.x; w < gridDim.x; w += kCheckThreads)
-    every &= __hip_atomic_load(a.partial + w, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0;
-  every = __syncthreads_and(every);
-  if (threadIdx.x == 0) {
-    *a.ready = every ? a.epoch : 0;
-    __hip_atomic_store(a.ticket, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  }
+  if (threadIdx.x == 0) *a.ready = all ? a.epoch : 0;
 }
 
 hipError_t launch_check(const CheckArgs& a, hipStream_t s) {
-  const uint64_t blocks = (a.nflags + kCheckThreads - 1) / kCheckThreads;
-  hipLaunchKernelGGL(k_check, dim3((uint32_t)(blocks ? blocks : 1)), dim3(kCheckThreads), 0, s, a);
+  hipLaunchKernelGGL(k_check, dim3(1), dim3(kCheckThreads), 0, s, a);
   return hipGetLastError();
 }
 

@@ -125,7 +125,10 @@ def test_tiles_crossing_chunks(plr, oracle_mod, op, mode):
             plr.plr_notify(L, w, ws)
         (plr.plr_reduce if op == "reduce" else plr.plr_copy)(L, srcs, dst, ws)
         assert plr.plr_check(L, ws) == plr.PLR_OK
-        assert_same("bf16", dst.cpu().numpy().view(np.uint16), ref, f"epoch {epoch}")
+        if op == "copy":  # copies are bitwise, NaN payloads included
+            assert np.array_equal(dst.cpu().numpy().view(np.uint16), ref), f"epoch {epoch}"
+        else:
+            assert_same("bf16", dst.cpu().numpy().view(np.uint16), ref, f"epoch {epoch}")
 
 
 @pytest.mark.parametrize("op", ["reduce", "copy"])
@@ -166,4 +169,41 @@ def test_check_mode_partial_arrival(plr, oracle_mod, op):
         (plr.plr_reduce if op == "reduce" else plr.plr_copy)(L, srcs, dst, ws)
     torch.cuda.synchronize()
     assert plr.plr_check(L, ws, consumer) == plr.PLR_OK
-    assert_same("bf16", dst.cpu().numpy().view(np.uint16), ref)
+    if op == "copy":
+        assert np.array_equal(dst.cpu().numpy().view(np.uint16), ref)
+    else:
+        assert_same("bf16", dst.cpu().numpy().view(np.uint16), ref)
+
+
+def test_check_mode_many_flags(plr, oracle_mod):
+    """More flags (16,384) than the check's lanes hold in one round of loads (8,192): the
+    verdict, the ready word and the mirror cover every flag; a flag still missing in the
+    second round sends the consumer to wait and, withheld, to PLR_ETIMEOUT."""
+    W, nbytes = 8, 1 << 20
+    srcs_np = [synth.bits_np(8, 4, s, nbytes) for s in range(W)]
+    ref = oracle_mod.copy_layout("packed", "packed", srcs_np).view(np.uint16)
+    srcs = [to_dev(s) for s in srcs_np]
+    L = plr.plr_layout_create("copy", "bf16", W, nbytes, "packed", "packed", tile_bytes=512, chunk_bytes=512,
+                              spin_limit=2000, notify_mode=MODES["check"])
+    nflags = L.nchunks  # copy: one flag per chunk of every segment
+    assert nflags == 16384
+    ws = torch.zeros(L.workspace_bytes, dtype=torch.uint8, device="cuda")
+    dst = torch.empty(L.dst_bytes, dtype=torch.uint8, device="cuda")
+    plr.plr_notify(L, -1, ws)
+    plr.plr_copy(L, srcs, dst, ws)
+    assert plr.plr_check(L, ws) == plr.PLR_OK
+    assert np.array_equal(dst.cpu().numpy(), ref.view(np.uint8))
+    words = ws.view(torch.int64).cpu().numpy()
+    assert words[1] == 1  # ready: every flag had arrived at epoch 1
+    mirror = words[32 + nflags: 32 + 2 * nflags]
+    assert (mirror == 1).all()
+    # epoch 2: the last source (flags 14,336.. in the check's second round) withholds
+    for w in range(W - 1):
+        plr.plr_notify(L, w, ws)
+    plr.plr_copy(L, srcs, dst, ws)
+    assert plr.plr_check(L, ws) == plr.PLR_ETIMEOUT
+    words = ws.view(torch.int64).cpu().numpy()
+    assert words[1] == 0
+    mirror = words[32 + nflags: 32 + 2 * nflags]
+    own = nflags // W  # the last source's flags: the last of W equal ranges
+    assert (mirror[:nflags - own] == 2).all() and (mirror[nflags - own:] == 0).all()

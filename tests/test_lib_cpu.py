@@ -92,9 +92,10 @@ def test_chunks_and_workspace(plr):
     pol = L.policy()
     n = -(-8192 * 7168 * 2 // pol["chunk_bytes"])
     assert L.nchunks == n
-    assert L.workspace_bytes == 256 + (2 * 8 * n + -(-8 * n // 1024)) * 8
+    assert L.workspace_bytes == 256 + 2 * 8 * n * 8
     C = plr.plr_layout_create("copy", "bf16", 8, 64 << 20, "scattered", "transposed", chunk_bytes=1 << 20)
-    assert C.nchunks == 64 * 8 and C.workspace_bytes == 256 + (2 * 8 * 512 + 4) * 8
+    # copy flags: one per chunk of every segment (not per source and chunk)
+    assert C.nchunks == 64 * 8 and C.workspace_bytes == 256 + 2 * 512 * 8
     R = plr.plr_layout_create("copy", "bf16", 3, 48 * 3, "packed", "packed", chunk_bytes=32)
     assert R.nchunks == 3 * 5  # 144-byte segments in 32-byte chunks: ragged last chunk
     E = plr.plr_layout_create("reduce", "bf16", 4, 0, "packed", "packed")
