@@ -2,25 +2,28 @@
 
 One step = one pass of the whole datapath over one batch of synthetic inputs, all
 resident in HBM before timing starts, every consumer call notified (producer-side
-plr_notify, then the consumer waits on its per-chunk flags):
+plr_notify, then the consumer checks its per-chunk flags):
   1. reduce    W=8 contributions of [8192, 7168] bf16, N(0, 0.5)  -> one [8192, 7168] share
   2. allgather W=8 sources of 64 MiB random bits                  -> 512 MiB, packed by rank
   3. alltoall  W=8 sources of 8 x 8 MiB tiles                     -> 512 MiB, out[d][s] = in[s][d]
   4. alltoallv W=8 x 4096 rows of 7168 bf16, Zipf(1.1) destinations -> 32768 packed rows
 `value` is the step's algorithmic HBM bytes (bytes read + bytes written) divided by
-the wall-clock time of a step, in GB/s. Decode-size latency (W=8 x [T, 7168] bf16,
-T in 1/8/32/64) is reported beside it, notify off and on, two ways: the time per call
-of 50 calls captured in a HIP graph and replayed back to back (for notify on, a call is
-the producer's notify plus the reduce), and p50/p90 of HIP-event pairs around single
-reduce launches
-(which include the events' own cost of several microseconds; kernel-only durations
-come from the rocprofv3 trace kept in profiles/).
+the wall-clock time of a step, K steps timed back to back with nothing in the stream
+but the library's kernels. The same K steps are then run again with every op's
+datapath kernels carrying a pair of timing-only HIP events (plr_set_timing_events);
+their mean durations give `per_op` and the `roofline` of the dominant kernel, the
+figure a kernel trace of the same command reports for that kernel.
+Decode-size latency (W=8 x [T, 7168] bf16, T in 1/8/32/64) is reported beside it,
+notify off and on and through packets: the time per call of 50 calls captured in a
+HIP graph and replayed back to back (for notify on, a call is the producer's notify
+plus the reduce), and p50/p90 of per-call timing-event pairs on the reduce kernel.
 
 Prints one JSON line. Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
 """
 from __future__ import annotations
 
 import argparse
+import ctypes
 import hashlib
 import json
 import os
@@ -51,9 +54,15 @@ KERNEL_NAMES = {"reduce": "k_reduce_direct", "allgather": "k_copy_direct",
 CSRC = os.path.join(ROOT, "reduce_atom_amd", "csrc")
 
 
-def source_hash() -> str:
+# the sources a kernel is compiled from: a counter summary taken on other text of
+# these files no longer describes the kernel
+OP_SOURCES = {"reduce": ("reduce.hip", "device_common.h"), "allgather": ("copy.hip", "device_common.h"),
+              "alltoall": ("copy.hip", "device_common.h"), "alltoallv": ("copy_v.hip", "device_common.h")}
+
+
+def source_hash(op: str) -> str:
     h = hashlib.sha256()
-    for name in sorted(os.listdir(CSRC)):
+    for name in OP_SOURCES[op]:
         with open(os.path.join(CSRC, name), "rb") as f:
             h.update(name.encode() + f.read())
     return h.hexdigest()[:16]
@@ -71,7 +80,7 @@ def counters_traffic(op: str):
             if ":" in line and not line.startswith("#"):
                 k, v = line.split(":", 1)
                 kv[k.strip()] = v.strip()
-    if kv.get("source_hash") != source_hash():
+    if kv.get("source_hash") != source_hash(op):
         return None
     try:
         return float(kv["traffic_bytes_per_launch"])
@@ -152,8 +161,8 @@ def write_counter_profiles(fetch_csv, write_csv, cal_fetch_csv, cal_write_csv, o
     cal_w, _ = _mean_counter(cal_write_csv, "__amd_rocclr_copyBuffer")
     known_kib = (1 << 30) / 1024
     sf, sw = known_kib / cal_f, known_kib / cal_w
-    h = source_hash()
     for op, (kname, _) in OP_KERNELS.items():
+        h = source_hash(op)
         f_kib, nf = _mean_counter(fetch_csv, kname)
         w_kib, nw = _mean_counter(write_csv, kname)
         traffic = (f_kib * sf + w_kib * sw) * 1024
@@ -175,6 +184,45 @@ def write_counter_profiles(fetch_csv, write_csv, cal_fetch_csv, cal_write_csv, o
             out.write(f"traffic_over_algorithmic: {traffic / BYTES[op]:.4f}\n")
             out.write(f"source_hash: {h}\n")
         print(path, f"{traffic / BYTES[op]:.4f}")
+
+
+class TimingEvents:
+    """HIP events for timing only, made with hipEventDisableSystemFence: recording one
+    performs no system-scope cache writeback or invalidate, so it neither stalls the
+    stream for several microseconds nor charges that stall to the kernels it brackets
+    (torch's events do). Created and read through the HIP runtime that torch loaded."""
+
+    FLAGS = 0x20000000  # hipEventDisableSystemFence
+
+    def __init__(self, torch):
+        path = os.path.join(os.path.dirname(torch.__file__), "lib", "libamdhip64.so")
+        self.hip = ctypes.CDLL(path if os.path.exists(path) else "libamdhip64.so")
+        self.made = []
+
+    def create(self) -> int:
+        h = ctypes.c_void_p()
+        rc = self.hip.hipEventCreateWithFlags(ctypes.byref(h), ctypes.c_uint(self.FLAGS))
+        if rc != 0:
+            raise RuntimeError(f"hipEventCreateWithFlags: {rc}")
+        self.made.append(h.value)
+        return h.value
+
+    def elapsed_ms(self, a: int, b: int) -> float:
+        f = ctypes.c_float()
+        rc = self.hip.hipEventElapsedTime(ctypes.byref(f), ctypes.c_void_p(a), ctypes.c_void_p(b))
+        if rc != 0:
+            raise RuntimeError(f"hipEventElapsedTime: {rc}")
+        return f.value
+
+    def record(self, e: int, stream: int) -> None:
+        rc = self.hip.hipEventRecord(ctypes.c_void_p(e), ctypes.c_void_p(stream))
+        if rc != 0:
+            raise RuntimeError(f"hipEventRecord: {rc}")
+
+    def destroy_all(self) -> None:
+        for h in self.made:
+            self.hip.hipEventDestroy(ctypes.c_void_p(h))
+        self.made = []
 
 
 def make_inputs(torch, synth, seed, dev):
@@ -238,24 +286,30 @@ def run_bench(args):
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
-    ev = [{n: (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for n in ops}
-          for _ in range(args.steps)]
-    for e in ev:  # create the HIP events before the timed region
-        for a, b in e.values():
-            a.record()
-            b.record()
-    torch.cuda.synchronize()
+    # (1) the step as a whole: K steps back to back, nothing but the library's kernels
     t0 = time.perf_counter()
+    for k in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms_per_step = (t1 - t0) * 1e3 / args.steps
+    # (2) the same K steps again, every op's datapath kernels carrying a pair of
+    # timing-only events (the kernel-only duration that a kernel trace also reports)
+    E = TimingEvents(torch)
+    ev = [{n: (E.create(), E.create()) for n in ops} for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t2 = time.perf_counter()
     for k in range(args.steps):
         step(ev[k])
     torch.cuda.synchronize()
-    t1 = time.perf_counter()
+    t3 = time.perf_counter()
     for name, l in L.items():
         rc = plr.plr_check(l, ws[name])
         if rc != plr.PLR_OK:
             raise RuntimeError(f"{name}: device error {plr.plr_strerror(rc)}")
-    ms_per_step = (t1 - t0) * 1e3 / args.steps
-    per_op_us = {n: statistics.mean(e[n][0].elapsed_time(e[n][1]) for e in ev) * 1e3 for n in ops}
+    ms_per_step_events = (t3 - t2) * 1e3 / args.steps
+    per_op_us = {n: statistics.mean(E.elapsed_ms(*e[n]) for e in ev) * 1e3 for n in ops}
+    E.destroy_all()
     step_bytes = sum(BYTES.values())
     value = step_bytes / (ms_per_step * 1e-3) / 1e9
 
@@ -274,7 +328,7 @@ def run_bench(args):
     del x, ws, scratch
     torch.cuda.empty_cache()
     decode = run_decode(args, torch, plr, synth, dev) if not args.no_decode else None
-    return value, ms_per_step, roofline, per_op, decode
+    return value, ms_per_step, ms_per_step_events, roofline, per_op, decode
 
 
 def run_decode(args, torch, plr, synth, dev):
@@ -329,12 +383,9 @@ def run_decode(args, torch, plr, synth, dev):
             torch.cuda.synchronize()
             per_call = a0.elapsed_time(b0) * 1e3 / (50 * (args.decode_iters // 50))
             del graph
-            # (b) one pair of events around every reduce kernel (includes the events' own cost)
-            evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-                   for _ in range(args.decode_iters)]
-            for a, b in evs:
-                a.record()
-                b.record()
+            # (b) a pair of timing-only events on every reduce kernel
+            E = TimingEvents(torch)
+            evs = [(E.create(), E.create()) for _ in range(args.decode_iters)]
             torch.cuda.synchronize()
             for a, b in evs:
                 produce()
@@ -342,7 +393,8 @@ def run_decode(args, torch, plr, synth, dev):
                 consume()
             plr.plr_set_timing_events()
             torch.cuda.synchronize()
-            us = sorted(a.elapsed_time(b) * 1e3 for a, b in evs)
+            us = sorted(E.elapsed_ms(a, b) * 1e3 for a, b in evs)
+            E.destroy_all()
             if ws is not None and plr.plr_check(L, ws) != plr.PLR_OK:
                 raise RuntimeError("decode: device error")
             res[mode] = {"us_per_call_graph": round(per_call, 2),
@@ -483,7 +535,7 @@ def main():
         print(json.dumps({"decode_reduce_us": run_decode(args, torch, plr, synth, torch.device("cuda:0"))}),
               flush=True)
         return
-    value, ms, roofline, per_op, decode = run_bench(args)
+    value, ms, ms_events, roofline, per_op, decode = run_bench(args)
     nxt = None if args.no_decode else run_next(args)
     cpu = None if args.no_cpu_baseline else run_cpu_baseline(args)
     line = {
@@ -494,7 +546,8 @@ def main():
                                "allgather 8x64MiB; alltoall 8x(8x8MiB); alltoallv 8x4096 rows x "
                                "7168 bf16, Zipf(1.1) destinations",
                    "world": W, "notify": True, "seed": args.seed, "step_bytes": sum(BYTES.values())},
-        "roofline": roofline, "cpu_baseline": cpu, "per_op": per_op, "decode_reduce_us": decode,
+        "roofline": roofline, "cpu_baseline": cpu, "per_op": per_op,
+        "ms_per_step_with_op_events": round(ms_events, 4), "decode_reduce_us": decode,
         "beyond_step": nxt,
     }
     print(json.dumps(line), flush=True)

@@ -295,12 +295,14 @@ int plr_check(plr_layout* L, void* workspace, void* stream);
 
 /* Measurement aid (not part of the method): while `before` and `after` are set, every
  * datapath call made by the calling host thread (plr_reduce, plr_copy, plr_copy_v,
- * plr_allreduce, plr_reduce_packets) records `before` on its stream right before its
- * datapath kernels are launched (after a notified call's check kernel) and `after`
- * right after them, so that the pair times the datapath kernels alone. Both are
- * hipEvent_t handles owned by the caller; NULL, NULL turns this off. The setting is
- * per host thread. Errors: PLR_EINVAL if exactly one of the two is NULL. A failed
- * event record makes the call return PLR_EHIP. */
+ * plr_allreduce, plr_reduce_packets) launches its first datapath kernel with `before`
+ * and its last with `after` as that dispatch's start and end events
+ * (hipExtLaunchKernel), so the pair times the datapath kernels alone, as a kernel
+ * trace does: a notified call's check kernel is outside it. A call that launches no
+ * datapath kernel (an empty layout) records neither. Both are hipEvent_t handles the
+ * caller owns and has created; NULL, NULL turns this off. The setting is per host
+ * thread and is not for calls captured into a graph. Errors: PLR_EINVAL if exactly one
+ * of the two is NULL. */
 int plr_set_timing_events(void* before, void* after);
 
 /* Static text for an error code. */

@@ -293,16 +293,22 @@ def plr_notify(layout: Layout, src: int, workspace, stream=None) -> None:
 
 
 def plr_set_timing_events(before=None, after=None) -> None:
-    """Bracket the datapath kernels of this thread's next calls with two torch.cuda.Event
-    objects (created with enable_timing=True); no arguments turns it off. The events
-    are recorded once here so that they exist as HIP events before the library records them."""
+    """Bracket the datapath kernels of this thread's next calls with two events: raw
+    hipEvent_t handles (int) or torch.cuda.Event objects made with enable_timing=True
+    (recorded once here if torch has not created their HIP event yet). No arguments
+    turns it off."""
     if before is None and after is None:
         _ok(_lib.plr_set_timing_events(None, None), "plr_set_timing_events")
         return
-    for e in (before, after):
+
+    def handle(e):
+        if isinstance(e, int):
+            return e
         if not e.cuda_event:  # torch creates its HIP event at the first record
             e.record()
-    _ok(_lib.plr_set_timing_events(before.cuda_event, after.cuda_event), "plr_set_timing_events")
+        return e.cuda_event
+
+    _ok(_lib.plr_set_timing_events(handle(before), handle(after)), "plr_set_timing_events")
 
 
 def plr_check(layout: Layout, workspace, stream=None) -> int:

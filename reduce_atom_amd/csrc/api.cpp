@@ -15,12 +15,7 @@ namespace {
 
 thread_local int g_last_hip = 0;
 
-// Measurement events of the calling thread (plr_set_timing_events), or null.
-thread_local hipEvent_t g_ev_before = nullptr, g_ev_after = nullptr;
-
-// Brackets the datapath kernels of one call with the thread's measurement events.
-hipError_t mark_before(hipStream_t s) { return g_ev_before ? hipEventRecord(g_ev_before, s) : hipSuccess; }
-hipError_t mark_after(hipStream_t s) { return g_ev_after ? hipEventRecord(g_ev_after, s) : hipSuccess; }
+thread_local Timing g_timing = {nullptr, nullptr};
 
 int hip_fail(hipError_t e) {
   g_last_hip = (int)e;
@@ -111,6 +106,8 @@ hipError_t launch_check_for(const plr_layout* L, const Notify& nt, hipStream_t s
 
 }  // namespace
 
+const Timing& plr::timing() { return g_timing; }
+
 extern "C" int plr_reduce(plr_layout* L, const void* const* srcs, void* dst, void* workspace,
                           void* stream) {
   Notify nt;
@@ -133,9 +130,7 @@ extern "C" int plr_reduce(plr_layout* L, const void* const* srcs, void* dst, voi
     a.xcd = (uint32_t)l.xcd;
     const hipStream_t s = static_cast<hipStream_t>(stream);
     hipError_t e = launch_check_for(L, nt, s);
-    if (e == hipSuccess) e = mark_before(s);
     if (e == hipSuccess) e = launch_reduce(a, L->dtype, l, s);
-    if (e == hipSuccess) e = mark_after(s);
     if (e != hipSuccess) return hip_fail(e);
   }
   if (workspace) L->epoch = nt.epoch;
@@ -177,9 +172,7 @@ extern "C" int plr_copy(plr_layout* L, const void* const* srcs, void* dst, void*
     a.xcd = (uint32_t)l.xcd;
     const hipStream_t s = static_cast<hipStream_t>(stream);
     hipError_t e = launch_check_for(L, nt, s);
-    if (e == hipSuccess) e = mark_before(s);
     if (e == hipSuccess) e = launch_copy(a, l, s);
-    if (e == hipSuccess) e = mark_after(s);
     if (e != hipSuccess) return hip_fail(e);
   }
   if (workspace) L->epoch = nt.epoch;
@@ -270,9 +263,7 @@ extern "C" int plr_copy_v(int world, const void* const* srcs, const int64_t* row
 #endif
   a.xcd = PLR_CV_XCD;  // XCD-contiguous order of the row scatter
   const hipStream_t s = static_cast<hipStream_t>(stream);
-  hipError_t e = mark_before(s);
-  if (e == hipSuccess) e = launch_copy_v(a, s);
-  if (e == hipSuccess) e = mark_after(s);
+  hipError_t e = launch_copy_v(a, s);
   if (e != hipSuccess) return hip_fail(e);
   return PLR_OK;
 }
@@ -321,9 +312,7 @@ extern "C" int plr_allreduce(plr_layout* L, const void* const* srcs, void* const
     l.grid = (uint32_t)std::max<uint64_t>(1, ((uint64_t)L->ntiles + a.run - 1) / a.run);
   }
   const hipStream_t s = static_cast<hipStream_t>(stream);
-  hipError_t e = mark_before(s);
-  if (e == hipSuccess) e = launch_allreduce(a, L->dtype, l, s);
-  if (e == hipSuccess) e = mark_after(s);
+  hipError_t e = launch_allreduce(a, L->dtype, l, s);
   if (e != hipSuccess) return hip_fail(e);
   if (composed) L->epoch = a.nt.epoch;
   return PLR_OK;
@@ -381,9 +370,7 @@ extern "C" int plr_reduce_packets(plr_layout* L, const void* const* packets, voi
     a.err = static_cast<uint64_t*>(workspace);
     a.spin_limit = L->spin_limit;
     const hipStream_t s = static_cast<hipStream_t>(stream);
-    hipError_t e = mark_before(s);
-    if (e == hipSuccess) e = launch_reduce_packets(a, L->dtype, s);
-    if (e == hipSuccess) e = mark_after(s);
+    hipError_t e = launch_reduce_packets(a, L->dtype, s);
     if (e != hipSuccess) return hip_fail(e);
   }
   L->epoch = epoch;
@@ -426,8 +413,8 @@ extern "C" int plr_check(plr_layout* L, void* workspace, void* stream) {
 
 extern "C" int plr_set_timing_events(void* before, void* after) {
   if ((before == nullptr) != (after == nullptr)) return PLR_EINVAL;
-  g_ev_before = static_cast<hipEvent_t>(before);
-  g_ev_after = static_cast<hipEvent_t>(after);
+  g_timing.start = static_cast<hipEvent_t>(before);
+  g_timing.stop = static_cast<hipEvent_t>(after);
   return PLR_OK;
 }
 

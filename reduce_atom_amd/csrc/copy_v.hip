@@ -199,14 +199,14 @@ __global__ void __launch_bounds__(kCvThreads) k_copy_v_scatter(const CopyVArgs a
 
 hipError_t launch_copy_v(const CopyVArgs& a, hipStream_t s) {
   const uint32_t segs = a.seg_start[a.world];
-  hipLaunchKernelGGL(k_copy_v_rank, dim3(segs ? segs : 1), dim3(kRankThreads), 0, s, a);
+  launch_dp(k_copy_v_rank, dim3(segs ? segs : 1), dim3(kRankThreads), s, true, false, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   // one workgroup per kCvRun tiles; huge inputs make the grid stride over the tiles
   const uint64_t tiles = (uint64_t)a.row_start[a.world] * ((a.row_bytes + kCvTileBytes - 1) / kCvTileBytes);
   const uint64_t groups = (tiles + kCvRun - 1) / kCvRun;
   const uint32_t grid = (uint32_t)(groups < 1 ? 1 : (groups > (1u << 22) ? (1u << 22) : groups));
-  hipLaunchKernelGGL(k_copy_v_scatter, dim3(grid), dim3(kCvThreads), 0, s, a);
+  launch_dp(k_copy_v_scatter, dim3(grid), dim3(kCvThreads), s, false, true, a);
   return hipGetLastError();
 }
 

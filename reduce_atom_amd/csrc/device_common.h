@@ -2,6 +2,7 @@
 // and the consumer side of chunk notification.
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -30,6 +31,15 @@ __device__ __forceinline__ void st16(u32x4* p, u32x4 v) {
 #else
   *p = v;
 #endif
+}
+
+// Launch of a datapath kernel: `first` / `last` say whether it opens / closes the
+// call's datapath, which decides whether it carries the thread's timing events.
+template <typename K, typename... A>
+inline void launch_dp(K kernel, dim3 grid, dim3 block, hipStream_t s, bool first, bool last, A... args) {
+  const Timing& t = timing();
+  hipExtLaunchKernelGGL(kernel, grid, block, 0, s, first ? t.start : nullptr, last ? t.stop : nullptr, 0,
+                        args...);
 }
 
 // Constant address space: loads through such a pointer that are the same for every

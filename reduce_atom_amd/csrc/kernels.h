@@ -161,6 +161,16 @@ struct NotifyArgs {
   uint64_t epoch;
 };
 
+// Measurement events of the calling host thread (plr_set_timing_events), or nulls. The
+// first datapath kernel a call launches carries `start` and its last carries `stop`, as
+// the dispatch's own start and end timestamps (hipExtLaunchKernel), so that the pair
+// times the datapath kernels alone, like a kernel trace.
+struct Timing {
+  hipEvent_t start;
+  hipEvent_t stop;
+};
+const Timing& timing();
+
 // Launchers (defined next to their kernels). Return a hipError_t.
 hipError_t launch_reduce(const ReduceArgs& a, int dtype, const Launch& l, hipStream_t s);
 hipError_t launch_copy(const CopyArgs& a, const Launch& l, hipStream_t s);

@@ -252,3 +252,11 @@ def test_packet_layouts_and_validation(plr):
     assert _code(plr.plr_reduce_packets, L, pk, pk[2] + 16, WS) == plr.PLR_EINVAL  # dst inside packets
     assert _code(plr.plr_reduce_packets, L, pk[:3] + [pk[3] + 4], D, WS) == plr.PLR_EALIGN
     assert L.epoch == 0  # rejected calls do not advance the epoch
+
+
+def test_timing_events_arguments(plr):
+    """Only a full pair (or none) of measurement events is accepted; nothing is launched."""
+    lib = plr._lib
+    assert lib.plr_set_timing_events(ctypes.c_void_p(0x1000), None) == plr.PLR_EINVAL
+    assert lib.plr_set_timing_events(None, ctypes.c_void_p(0x1000)) == plr.PLR_EINVAL
+    assert lib.plr_set_timing_events(None, None) == plr.PLR_OK
