@@ -221,6 +221,38 @@ def copy_layout(in_kind: str, out_kind: str, srcs) -> np.ndarray:
     return copy(srcs, segs, total)
 
 
+# ------------------------------------------------------------------ variable length
+def part_offsets(parts):
+    """Byte offset of every partition: the exclusive prefix sum of the sizes (appendix
+    C.4 and section 4: partition sizes are given at run time, offsets are prefix sums)."""
+    offs, run = [], 0
+    for p in parts:
+        offs.append(run)
+        run += int(p)
+    return offs
+
+
+def allgather_v(srcs, parts) -> np.ndarray:
+    """AllGatherV (section 2.1 and appendix C.4: a contribution of its own size per
+    rank; every rank receives all of them in rank order): source w contributes its
+    first parts[w] bytes, placed at the sum of the sizes before it."""
+    offs = part_offsets(parts)
+    segs = [(w, 0, offs[w], int(parts[w])) for w in range(len(srcs))]
+    return copy(srcs, segs, sum(int(p) for p in parts))
+
+
+def reduce_scatter_v(dtype: str, srcs, parts, rank: int) -> np.ndarray:
+    """ReduceScatterV share of `rank` (appendix C.4: the rank's assigned partition is
+    its output): every source holds all partitions back to back; the share is the
+    rank-order reduction of partition `rank` of every source."""
+    eb = ELEM_BYTES[dtype]
+    off = part_offsets(parts)[rank]
+    if off % eb or int(parts[rank]) % eb:
+        raise ValueError("partition not a whole number of elements")
+    W = len(srcs)
+    return reduce(dtype, srcs, [off // eb] * W, int(parts[rank]) // eb)
+
+
 # ------------------------------------------------------------------ copy_v
 def copy_v(srcs, dests, row_bytes: int):
     """Variable-length AllToAll packing. srcs[s]: rows of source s (any dtype, C order);

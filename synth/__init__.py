@@ -44,6 +44,27 @@ def zipf_weights(s: float, n: int) -> np.ndarray:
     return w / w.sum()
 
 
+def zipf_split(total: int, n: int = 8, s: float = 0.125, granule: int = 16) -> list:
+    """Partition sizes (bytes) of a variable-length collective of total message size
+    `total` over n ranks (Purlin paper, appendix C.4: rank r gets a Zipf-split share
+    with exponent s = 0.125; splits preserve the total; 1 and 2 KiB totals are split
+    uniformly). Reading: below 4 KiB every rank gets total / n; otherwise rank r's
+    weight is (r+1)^-s normalised, every share is rounded down to a multiple of
+    `granule` bytes (the datapath's 16-byte alignment), and the granules left over go
+    one each to ranks 0, 1, 2, ... so that shares never increase with r. `total` must
+    be a multiple of n * granule."""
+    if total % (n * granule):
+        raise ValueError("total must be a multiple of n * granule")
+    if total < 4096:
+        return [total // n] * n
+    w = zipf_weights(s, n)
+    parts = [int(total * float(w[r])) // granule * granule for r in range(n)]
+    left = (total - sum(parts)) // granule
+    for r in range(left):
+        parts[r % n] += granule
+    return parts
+
+
 # --------------------------------------------------------------------------
 # Scalar reference of the generator (pure Python ints), used to pin both
 # vectorised backends.
