@@ -404,9 +404,30 @@ def run_decode(args, torch, plr, synth, dev):
     return out
 
 
+def _time_calls(torch, plr, fn, n=10, warm=3):
+    """Mean datapath-kernel time of n calls, each carrying timing-only events."""
+    for _ in range(warm):
+        fn()
+    torch.cuda.synchronize()
+    E = TimingEvents(torch)
+    evs = [(E.create(), E.create()) for _ in range(n)]
+    for a, b in evs:
+        plr.plr_set_timing_events(a, b)
+        fn()
+    plr.plr_set_timing_events()
+    torch.cuda.synchronize()
+    us = statistics.mean(E.elapsed_ms(a, b) for a, b in evs) * 1e3
+    E.destroy_all()
+    return us
+
+
 def run_next(args):
     """Rows beyond the step (measured beside it, not part of `value`): the AllReduce of
-    W=8 contributions of [8192, 7168] bf16 into 8 outputs, fused and composed."""
+    W=8 contributions of [8192, 7168] bf16 into 8 outputs, fused and composed; and the
+    variable-length collectives of appendix C.4 over 8 ranks with Zipf(s = 0.125)
+    partitions of a total T: AllGatherV (8 contributions -> T bytes) and the largest
+    ReduceScatterV share (rank 0: 8 contributions of T bytes, bf16, N(0, 1)), at
+    T = 1 GiB (bandwidth) and T = 2 MiB (the size of the pages' largest gain)."""
     import torch
 
     import reduce_atom_amd as plr
@@ -414,24 +435,35 @@ def run_next(args):
 
     dev = torch.device("cuda:0")
     out = {}
+    for T in (1 << 30, 2 << 20):
+        parts = synth.zipf_split(T, W)
+        tag = "1GiB" if T == 1 << 30 else "2MiB"
+        srcs = [synth.bits_t(args.seed, 7, w, parts[w], device=dev) for w in range(W)]
+        dst = torch.empty(T, dtype=torch.uint8, device=dev)
+        L = plr.plr_layout_create("copy", "bf16", W, T, "packed", "packed", part_bytes=parts)
+        us = _time_calls(torch, plr, lambda: plr.plr_copy(L, srcs, dst))
+        algo = 2 * T
+        out[f"allgatherv_{tag}"] = {"avg_us": round(us, 2), "GB/s": round(algo / (us * 1e-6) / 1e9, 1),
+                                    "algorithmic_bytes": algo, "parts": parts}
+        del srcs, dst
+        srcs = [synth.normal_t(args.seed, 8, w, T // 2, 1.0, device=dev) for w in range(W)]
+        dst = torch.empty(parts[0], dtype=torch.uint8, device=dev)
+        L = plr.plr_layout_create("reduce", "bf16", W, T, "scattered", "packed", rank=0, part_bytes=parts)
+        us = _time_calls(torch, plr, lambda: plr.plr_reduce(L, srcs, dst))
+        algo = (W + 1) * parts[0]
+        out[f"reducescatterv_rank0_{tag}"] = {"avg_us": round(us, 2), "GB/s": round(algo / (us * 1e-6) / 1e9, 1),
+                                              "algorithmic_bytes": algo}
+        del srcs, dst
+        torch.cuda.empty_cache()
     srcs = [synth.normal_t(args.seed, 3, w, R3 * C3, 0.5, device=dev) for w in range(W)]
     dsts = [torch.empty(R3 * C3, dtype=torch.bfloat16, device=dev) for _ in range(W)]
     algo = 2 * W * R3 * C3 * 2  # W contributions read, W outputs written
     for name, path in (("allreduce_fused", plr.PLR_PATH_DIRECT), ("allreduce_composed", plr.PLR_PATH_COMPOSED)):
         L = plr.plr_layout_create("allreduce", "bf16", W, R3 * C3 * 2, "scattered", "scattered", datapath=path)
         ws = torch.zeros(max(L.workspace_bytes, 256), dtype=torch.uint8, device=dev)
-        for _ in range(3):
-            plr.plr_allreduce(L, srcs, dsts, ws)
-        torch.cuda.synchronize()
-        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        a.record()
-        for _ in range(10):
-            plr.plr_allreduce(L, srcs, dsts, ws)
-        b.record()
-        torch.cuda.synchronize()
+        us = _time_calls(torch, plr, lambda: plr.plr_allreduce(L, srcs, dsts, ws))
         if plr.plr_check(L, ws) != plr.PLR_OK:
             raise RuntimeError(f"{name}: device error")
-        us = a.elapsed_time(b) * 1e3 / 10
         out[name] = {"avg_us": round(us, 2), "GB/s": round(algo / (us * 1e-6) / 1e9, 1),
                      "algorithmic_bytes": algo}
     del srcs, dsts

@@ -82,6 +82,13 @@ typedef enum { PLR_OP_REDUCE = 0, PLR_OP_COPY = 1, PLR_OP_ALLREDUCE = 2 } plr_op
  *                                   at slice s of the output
  *   allreduce SCATTERED -> SCATTERED  AllReduce = ReduceScatter then AllGather: every one
  *                                   of W outputs receives the reduction of all W sources
+ * Variable-length variants (section 2.1, appendix C.4: contributions or partitions of
+ * different sizes, given at run time), selected by part_bytes:
+ *   reduce  SCATTERED -> PACKED     ReduceScatterV: every source holds W partitions of
+ *                                   part_bytes[0..W-1] bytes back to back; rank `rank`
+ *                                   reduces partition `rank` of every source
+ *   copy    PACKED    -> PACKED     AllGatherV: source s contributes part_bytes[s] bytes,
+ *                                   landing at the sum of the sizes before it
  */
 typedef enum { PLR_PACKED = 0, PLR_SCATTERED = 1, PLR_TRANSPOSED = 2 } plr_layout_kind;
 
@@ -139,6 +146,12 @@ typedef struct {
                                  waits below), PLR_NOTIFY_CHUNKS or PLR_NOTIFY_CHECK */
   int xcd_order;              /* 0 = policy (on), 1 = on, 2 = off: renumber workgroups so that each
                                  of the 8 XCDs walks one contiguous range of tiles */
+  /* Variable-length layouts: W partition sizes in bytes (multiples of 16, zero allowed)
+   * whose sum is the message size T, which bytes_per_src must equal; NULL = fixed
+   * length. Copied at creation. A layout holds one set of sizes: for other sizes create
+   * another (host work only). Only the two variable pairs above accept it, on the
+   * direct datapath; a copy's offsets may still be overridden. */
+  const size_t* part_bytes;
 } plr_layout_desc;
 
 typedef struct plr_layout plr_layout; /* opaque, host only */

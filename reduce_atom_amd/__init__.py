@@ -52,6 +52,7 @@ class plr_layout_desc(_c.Structure):
         ("spin_limit", _u64),
         ("notify_mode", _i),
         ("xcd_order", _i),
+        ("part_bytes", _c.POINTER(_sz)),
     ]
 
 
@@ -221,8 +222,9 @@ class Layout:
 def plr_layout_create(op, dtype, world, bytes_per_src, in_kind, out_kind, rank=0,
                       in_offsets=None, out_offsets=None, mode=PLR_MODE_DETERMINISTIC,
                       tile_bytes=0, chunk_bytes=0, workgroups=0, block=0, unroll=0, stages=0, datapath=0,
-                      spin_limit=0, notify_mode=0, xcd_order=0) -> Layout:
-    """Compile a layout. op/dtype/kinds accept the C enum values or their names."""
+                      spin_limit=0, notify_mode=0, xcd_order=0, part_bytes=None) -> Layout:
+    """Compile a layout. op/dtype/kinds accept the C enum values or their names.
+    part_bytes: W partition sizes of a variable-length layout (AllGatherV, ReduceScatterV)."""
     d = plr_layout_desc()
     d.op = OP_CODES.get(op, op)
     d.dtype = DTYPE_CODES.get(dtype, dtype)
@@ -242,6 +244,10 @@ def plr_layout_create(op, dtype, world, bytes_per_src, in_kind, out_kind, rank=0
     d.block, d.unroll, d.stages, d.datapath, d.spin_limit = block, unroll, stages, datapath, spin_limit
     d.notify_mode = notify_mode
     d.xcd_order = xcd_order
+    if part_bytes is not None:
+        a = (_sz * len(part_bytes))(*part_bytes)
+        keep.append(a)
+        d.part_bytes = _c.cast(a, _c.POINTER(_sz))
     h = _vp()
     _ok(_lib.plr_layout_create(_c.byref(d), _c.byref(h)), "plr_layout_create")
     return Layout(h.value)

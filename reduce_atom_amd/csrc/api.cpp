@@ -167,6 +167,17 @@ extern "C" int plr_copy(plr_layout* L, const void* const* srcs, void* dst, void*
       a.mode = kCopyTransposed;
       a.slice = L->seg_len;
     }
+    if (L->var_segs) {  // AllGatherV: segments of their own lengths (at most W of them)
+      a.mode = kCopyVar;
+      for (int k = 0; k <= PLR_MAX_WORLD; ++k) a.var_tile0[k] = ~0u;
+      for (size_t k = 0; k < L->segs.size(); ++k) {
+        a.var_tile0[k] = L->seg_tile0[k];
+        a.var_chunk0[k] = L->seg_chunk0[k];
+        a.var_len[k] = L->segs[k].len;
+      }
+      a.var_tile0[L->segs.size()] = L->seg_tile0[L->segs.size()];
+      a.var_chunk0[L->segs.size()] = L->seg_chunk0[L->segs.size()];
+    }
     const Launch l = launch_of(L, nt.flags != nullptr);
     a.run = l.run;
     a.xcd = (uint32_t)l.xcd;
@@ -385,8 +396,16 @@ extern "C" int plr_notify(plr_layout* L, int src, void* workspace, void* stream)
   if (L->nchunks == 0) return PLR_OK;
   NotifyArgs a{};
   uint64_t* flags = reinterpret_cast<uint64_t*>(static_cast<char*>(workspace) + kWorkspaceHeader);
-  a.flags = src < 0 ? flags : flags + (uint64_t)src * flags_per_src(L);
-  a.nflags = src < 0 ? nflags(L) : flags_per_src(L);
+  if (src < 0) {
+    a.flags = flags;
+    a.nflags = nflags(L);
+  } else {
+    uint64_t first, count;
+    src_flags(L, src, &first, &count);
+    if (count == 0) return PLR_OK;
+    a.flags = flags + first;
+    a.nflags = count;
+  }
   a.epoch = L->epoch + 1;
   hipError_t e = launch_notify(a, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e);

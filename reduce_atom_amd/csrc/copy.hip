@@ -19,11 +19,26 @@ __global__ void __launch_bounds__(512) k_copy_direct(const CopyArgs a) {
   const uint32_t b = logical_block(a.xcd);
   const uint32_t t_end = min(a.ntiles, (b + 1) * a.run);
   for (uint32_t t = b * a.run; t < t_end; ++t) {
-    const uint32_t seg = t / a.tiles_per_seg;
-    const uint32_t part = t - seg * a.tiles_per_seg;
+    uint32_t seg, part, c;
+    uint64_t len;
+    if (a.mode == kCopyVar) {
+      // the last segment starting at or before t owns it (empty segments share the
+      // first tile of the next one; entries past the last segment hold ~0u)
+      seg = 0;
+#pragma unroll
+      for (uint32_t k = 1; k < PLR_MAX_WORLD; ++k) seg = t >= a.var_tile0[k] ? k : seg;
+      part = t - a.var_tile0[seg];
+      len = a.var_len[seg];
+      c = a.var_chunk0[seg] + part / a.tiles_per_chunk;
+    } else {
+      seg = t / a.tiles_per_seg;
+      part = t - seg * a.tiles_per_seg;
+      len = a.seg_len;
+      c = seg * a.chunks_per_seg + part / a.tiles_per_chunk;
+    }
     uint32_t s;
     uint64_t src_off, dst_off;
-    if (a.mode == kCopyTable) {
+    if (a.mode != kCopyTransposed) {
       s = a.seg_src[seg];
       src_off = a.seg_src_off[seg];
       dst_off = a.seg_dst_off[seg];
@@ -34,7 +49,6 @@ __global__ void __launch_bounds__(512) k_copy_direct(const CopyArgs a) {
       dst_off = ((uint64_t)d * a.world + s) * a.slice;
     }
     if (wait) {
-      const uint32_t c = seg * a.chunks_per_seg + part / a.tiles_per_chunk;
       const uint32_t f = c;  // flags follow the segments, source by source
       if (f != ready) {
         if (!wg_wait_flags(a.nt, f, 0, 1)) return;
@@ -42,7 +56,7 @@ __global__ void __launch_bounds__(512) k_copy_direct(const CopyArgs a) {
       }
     }
     const uint64_t b0 = (uint64_t)part * a.tile_bytes;
-    const uint64_t nv = (min(b0 + a.tile_bytes, a.seg_len) - b0) >> 4;
+    const uint64_t nv = (min(b0 + a.tile_bytes, len) - b0) >> 4;
     const u32x4* src = reinterpret_cast<const u32x4*>(a.src[s] + src_off + b0);
     u32x4* dst = reinterpret_cast<u32x4*>(a.dst + dst_off + b0);
     uint64_t v = threadIdx.x;

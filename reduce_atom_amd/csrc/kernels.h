@@ -73,7 +73,9 @@ struct ReduceArgs {
 // Layouts with more than kMaxTableSegs segments (AllToAll with W > 8) use the
 // transposed formula instead of the table: k = s*W + d, src_off = d*slice,
 // dst_off = (d*W + s)*slice.
-enum CopyMode : uint32_t { kCopyTable = 0, kCopyTransposed = 1 };
+// Variable-length layouts (AllGatherV, at most PLR_MAX_WORLD segments) use the table
+// with per-segment lengths and first tiles and chunks instead of one common length.
+enum CopyMode : uint32_t { kCopyTable = 0, kCopyTransposed = 1, kCopyVar = 2 };
 
 struct CopyArgs {
   const uint8_t* src[PLR_MAX_WORLD];
@@ -95,7 +97,15 @@ struct CopyArgs {
   uint32_t seg_src[kMaxTableSegs];
   uint64_t seg_src_off[kMaxTableSegs];
   uint64_t seg_dst_off[kMaxTableSegs];
+  // kCopyVar: first tile and first chunk of every segment (nseg + 1 entries, then
+  // ~0u in var_tile0), lengths
+  uint32_t var_tile0[PLR_MAX_WORLD + 1];
+  uint32_t var_chunk0[PLR_MAX_WORLD + 1];
+  uint64_t var_len[PLR_MAX_WORLD];
 };
+
+// kernel arguments are limited to 4 KiB
+static_assert(sizeof(CopyArgs) <= 4096, "copy kernel arguments exceed 4 KiB");
 
 constexpr int kRankSeg = 1024;  // rows per rank workgroup (one per thread)
 constexpr uint32_t kNoDest = 0xFFFFu;

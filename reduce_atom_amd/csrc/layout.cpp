@@ -102,17 +102,37 @@ extern "C" int plr_layout_create(const plr_layout_desc* d, plr_layout** out) {
     return code;
   };
 
+  // variable-length partitions: sizes and their exclusive prefix sums
+  const bool var = d->part_bytes != nullptr;
+  std::vector<uint64_t> part(W, 0), part0(W + 1, 0);
+  if (var) {
+    if (d->op == PLR_OP_ALLREDUCE) return fail(PLR_EINVAL);
+    for (int w = 0; w < W; ++w) {
+      part[w] = d->part_bytes[w];
+      if (!aligned16(part[w])) return fail(PLR_EALIGN);
+      part0[w + 1] = part0[w] + part[w];
+    }
+    if (part0[W] != B) return fail(PLR_EINVAL);  // the sizes add up to the message size T
+  }
+  L->var_segs = false;
+
   if (d->op == PLR_OP_REDUCE) {
     if (d->out_kind != PLR_PACKED || d->out_offsets) return fail(PLR_EINVAL);
     uint64_t share, off;
     if (d->in_kind == PLR_PACKED) {
+      if (var) return fail(PLR_EINVAL);  // partitions only make sense for a scattered input
       share = B;
       off = 0;
     } else if (d->in_kind == PLR_SCATTERED) {
       if (d->rank < 0 || d->rank >= W) return fail(PLR_EINVAL);
-      if (B % (16ull * W)) return fail(PLR_EALIGN);
-      share = B / W;
-      off = (uint64_t)d->rank * share;
+      if (var) {  // ReduceScatterV: partition `rank` of every source
+        share = part[d->rank];
+        off = part0[d->rank];
+      } else {
+        if (B % (16ull * W)) return fail(PLR_EALIGN);
+        share = B / W;
+        off = (uint64_t)d->rank * share;
+      }
     } else {
       return fail(PLR_EINVAL);
     }
@@ -131,7 +151,17 @@ extern "C" int plr_layout_create(const plr_layout_desc* d, plr_layout** out) {
     L->seg_len = B;
     L->dst_bytes = B;
   } else {
-    if (d->in_kind == PLR_PACKED && d->out_kind == PLR_PACKED) {  // AllGather
+    if (d->in_kind == PLR_PACKED && d->out_kind == PLR_PACKED && var) {  // AllGatherV
+      uint64_t longest = 0;
+      for (int s = 0; s < W; ++s) {
+        L->segs.push_back({s, 0, part0[s], part[s]});
+        longest = std::max(longest, part[s]);
+      }
+      L->seg_len = longest;
+      L->var_segs = true;
+    } else if (var) {
+      return fail(PLR_EINVAL);  // the other copies have no variable-length form here
+    } else if (d->in_kind == PLR_PACKED && d->out_kind == PLR_PACKED) {  // AllGather
       for (int s = 0; s < W; ++s) L->segs.push_back({s, 0, (uint64_t)s * B, B});
       L->seg_len = B;
     } else if (d->in_kind == PLR_SCATTERED &&
@@ -159,7 +189,8 @@ extern "C" int plr_layout_create(const plr_layout_desc* d, plr_layout** out) {
     }
     // output segments must not overlap (two writers of one byte would race)
     std::vector<std::pair<uint64_t, uint64_t>> iv;
-    for (auto& s : L->segs) iv.push_back({s.dst_off, s.dst_off + s.len});
+    for (auto& s : L->segs)
+      if (s.len) iv.push_back({s.dst_off, s.dst_off + s.len});
     std::sort(iv.begin(), iv.end());
     L->dst_bytes = 0;
     for (size_t k = 0; k < iv.size(); ++k) {
@@ -205,6 +236,7 @@ extern "C" int plr_layout_create(const plr_layout_desc* d, plr_layout** out) {
       if (!d->block) L->block = 256;
     }
   }
+  if (L->var_segs && L->datapath == PLR_PATH_LDS) return fail(PLR_EUNSUPPORTED);
   if (L->datapath == PLR_PATH_LDS) {
     // the staged pipeline runs 256-thread workgroups over 4 KiB slabs per source
     if (d->block && d->block != 256) return fail(PLR_EINVAL);
@@ -244,7 +276,7 @@ extern "C" int plr_layout_create(const plr_layout_desc* d, plr_layout** out) {
     L->ntiles = L->nchunks = 0;
   } else {
     const uint64_t tile = std::min<uint64_t>(L->tile_bytes, L->seg_len);
-    const uint64_t tps = (L->seg_len + tile - 1) / tile;
+    const uint64_t tps = (L->seg_len + tile - 1) / tile;  // of the longest segment
     uint64_t tpc = std::max<uint64_t>(1, (L->chunk_bytes + tile - 1) / tile);
     tpc = std::min<uint64_t>(tpc, tps);
     const uint64_t cps = (tps + tpc - 1) / tpc;
@@ -258,6 +290,31 @@ extern "C" int plr_layout_create(const plr_layout_desc* d, plr_layout** out) {
     L->chunks_per_seg = (uint32_t)cps;
     L->ntiles = (uint32_t)(tps * nseg);
     L->nchunks = (uint32_t)(cps * nseg);
+    if (L->var_segs) {  // every segment its own tile and chunk count
+      uint64_t tiles = 0, chunks = 0;
+      for (uint64_t k = 0; k < nseg; ++k) {
+        L->seg_tile0.push_back((uint32_t)tiles);
+        L->seg_chunk0.push_back((uint32_t)chunks);
+        const uint64_t t_k = (L->segs[k].len + tile - 1) / tile;
+        tiles += t_k;
+        chunks += (t_k + tpc - 1) / tpc;
+      }
+      L->seg_tile0.push_back((uint32_t)tiles);
+      L->seg_chunk0.push_back((uint32_t)chunks);
+      L->ntiles = (uint32_t)tiles;
+      L->nchunks = (uint32_t)chunks;
+    }
+  }
+  if (L->op == PLR_OP_COPY) {  // first flag of every source (segments go source by source)
+    const size_t nseg = L->segs.size();
+    L->src_flag0.assign(W + 1, 0);
+    for (size_t k = 0; k < nseg; ++k) {
+      const uint32_t c1 = L->nchunks == 0 ? 0
+                          : L->var_segs ? L->seg_chunk0[k + 1]
+                                        : (uint32_t)((k + 1) * L->chunks_per_seg);
+      L->src_flag0[L->segs[k].src + 1] = c1;
+    }
+    for (int s = 1; s <= W; ++s) L->src_flag0[s] = std::max(L->src_flag0[s], L->src_flag0[s - 1]);
   }
   *out = L;
   return PLR_OK;

@@ -29,6 +29,7 @@ struct plr_layout {
   uint64_t seg_len;
   uint64_t dst_bytes;
   bool table_fits;  // copy: the table is carried in the kernel arguments
+  bool var_segs;    // copy: segments of different lengths (AllGatherV)
 
   // work and notification granules: a tile is what one workgroup consumes per
   // step; a chunk (a whole number of tiles of one segment) is what one flag per
@@ -38,8 +39,12 @@ struct plr_layout {
   uint32_t tiles_per_seg;
   uint32_t tiles_per_chunk;
   uint32_t chunks_per_seg;
-  uint32_t ntiles;           // reduce: tiles of the share; copy: nseg * tiles_per_seg
-  uint32_t nchunks;          // reduce: chunks of the share; copy: nseg * chunks_per_seg
+  uint32_t ntiles;           // reduce: tiles of the share; copy: tiles of all segments
+  uint32_t nchunks;          // reduce: chunks of the share; copy: chunks of all segments
+  // copy: first tile and first chunk of every segment (nseg + 1 entries; with equal
+  // segments k * tiles_per_seg and k * chunks_per_seg), and first flag of every
+  // source (W + 1 entries): segments go source by source
+  std::vector<uint32_t> seg_tile0, seg_chunk0, src_flag0;
 
   // resolved policy (section 4.2 "Codesign Policies and Tuning")
   int workgroups;  // explicit grid size, or 0
@@ -63,10 +68,19 @@ size_t elem_bytes(plr_dtype t);
 
 // Chunk flags of a notified layout. Reduce: flags[W][nchunks], one per source and chunk
 // of the share. Copy: one per chunk of every segment, in segment order (segment k's
-// chunk j is flag k * chunks_per_seg + j); segments are listed source by source, each
-// source with the same number, so source s's flags are the s-th of W equal ranges.
+// chunk j is flag seg_chunk0[k] + j); segments are listed source by source, so source
+// s's flags are one contiguous range.
 inline uint64_t nflags(const plr_layout* L) {
   return L->op == PLR_OP_COPY ? (uint64_t)L->nchunks : (uint64_t)L->world * L->nchunks;
 }
-inline uint64_t flags_per_src(const plr_layout* L) { return nflags(L) / (uint64_t)L->world; }
+// First flag and flag count of source s (reduce: its row of the flag matrix).
+inline void src_flags(const plr_layout* L, int s, uint64_t* first, uint64_t* count) {
+  if (L->op == PLR_OP_COPY) {
+    *first = L->src_flag0[s];
+    *count = (uint64_t)L->src_flag0[s + 1] - L->src_flag0[s];
+  } else {
+    *first = (uint64_t)s * L->nchunks;
+    *count = L->nchunks;
+  }
+}
 }

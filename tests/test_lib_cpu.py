@@ -260,3 +260,40 @@ def test_timing_events_arguments(plr):
     assert lib.plr_set_timing_events(ctypes.c_void_p(0x1000), None) == plr.PLR_EINVAL
     assert lib.plr_set_timing_events(None, ctypes.c_void_p(0x1000)) == plr.PLR_EINVAL
     assert lib.plr_set_timing_events(None, None) == plr.PLR_OK
+
+
+def test_variable_length_layouts(plr, oracle_mod):
+    """AllGatherV and ReduceScatterV layouts (part_bytes): segments follow the oracle's
+    prefix-sum offsets, every segment has its own tile and chunk count, and the flags
+    of a source are its own chunks."""
+    import synth
+
+    W, T = 8, 1 << 20
+    parts = synth.zipf_split(T, W)
+    offs = oracle_mod.part_offsets(parts)
+    G = plr.plr_layout_create("copy", "bf16", W, T, "packed", "packed", part_bytes=parts,
+                              tile_bytes=2048, chunk_bytes=8192)
+    assert G.segments() == [(w, 0, offs[w], parts[w]) for w in range(W)]
+    assert G.dst_bytes == T
+    tiles = [-(-p // 2048) for p in parts]
+    assert G.ntiles == sum(tiles)
+    assert G.nchunks == sum(-(-t // 4) for t in tiles)
+    assert G.workspace_bytes == 256 + 2 * G.nchunks * 8
+    for r in (0, 3, 7):
+        R = plr.plr_layout_create("reduce", "f16", W, T, "scattered", "packed", rank=r, part_bytes=parts)
+        assert R.segments() == [(w, offs[r], 0, parts[r]) for w in range(W)]
+        assert R.dst_bytes == parts[r]
+    # empty partitions: an empty share, and an AllGatherV segment with no tiles
+    Z = plr.plr_layout_create("copy", "bf16", 3, 64, "packed", "packed", part_bytes=[32, 0, 32], tile_bytes=16)
+    assert Z.segments() == [(0, 0, 0, 32), (1, 0, 32, 0), (2, 0, 32, 32)] and Z.ntiles == 4
+    E = plr.plr_layout_create("reduce", "bf16", 3, 64, "scattered", "packed", rank=1, part_bytes=[32, 0, 32])
+    assert E.dst_bytes == 0 and E.ntiles == 0
+    # errors
+    bad = plr.plr_layout_create
+    assert _code(bad, "copy", "bf16", 2, 64, "packed", "packed", part_bytes=[32, 16]) == plr.PLR_EINVAL  # sum
+    assert _code(bad, "copy", "bf16", 2, 64, "packed", "packed", part_bytes=[40, 24]) == plr.PLR_EALIGN
+    assert _code(bad, "copy", "bf16", 2, 64, "scattered", "transposed", part_bytes=[32, 32]) == plr.PLR_EINVAL
+    assert _code(bad, "reduce", "bf16", 2, 64, "packed", "packed", part_bytes=[32, 32]) == plr.PLR_EINVAL
+    assert _code(bad, "allreduce", "bf16", 2, 64, "scattered", "scattered", part_bytes=[32, 32]) == plr.PLR_EINVAL
+    assert _code(bad, "copy", "bf16", 2, 8192, "packed", "packed", part_bytes=[4096, 4096],
+                 datapath=plr.PLR_PATH_LDS) == plr.PLR_EUNSUPPORTED
