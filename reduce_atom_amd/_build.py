@@ -70,6 +70,26 @@ def build(jobs: int | None = None, verbose: bool = False, out: str = OUT, define
     return out
 
 
+def build_user_kernels(src: str, out: str) -> str:
+    """Compile one HIP file of user kernels written on the device-callable Atom
+    (include/plr_atom.h) into its own shared library for gfx950 (always rebuilds)."""
+    build_dir = out + ".objs"
+    os.makedirs(build_dir, exist_ok=True)
+    obj = os.path.join(build_dir, os.path.basename(src) + ".o")
+    cmd = [HIPCC, *COMMON, "-x", "hip", *DEVICE, "-c", src, "-o", obj]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"hipcc failed for {src}:\n{r.stderr}")
+    tmp = out + ".tmp"
+    r = subprocess.run([HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", obj, "-o", tmp],
+                       capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"link failed:\n{r.stderr}")
+    os.replace(tmp, out)
+    shutil.rmtree(build_dir, ignore_errors=True)
+    return out
+
+
 def clean() -> None:
     shutil.rmtree(BUILD, ignore_errors=True)
 

@@ -7,31 +7,17 @@
 #include <stdint.h>
 
 #include "kernels.h"
+#include "plr_atom.h"
 
 namespace plr {
 
-// Streaming access: every byte is touched once, so loads and stores carry the
-// non-temporal hint unless a build selects otherwise.
-#ifndef PLR_LD_NT
-#define PLR_LD_NT 1
-#endif
-#ifndef PLR_ST_NT
-#define PLR_ST_NT 1
-#endif
-__device__ __forceinline__ u32x4 ld16(const u32x4* p) {
-#if PLR_LD_NT
-  return __builtin_nontemporal_load(p);
-#else
-  return *p;
-#endif
-}
-__device__ __forceinline__ void st16(u32x4* p, u32x4 v) {
-#if PLR_ST_NT
-  __builtin_nontemporal_store(v, p);
-#else
-  *p = v;
-#endif
-}
+// Streaming 16-byte access, element conversions and the ordered combine come from the
+// device-callable Atom (include/plr_atom.h), so the library's kernels and user kernels
+// that call the Atom run the same code.
+__device__ __forceinline__ u32x4 ld16(const u32x4* p) { return atom::load16(p); }
+__device__ __forceinline__ void st16(u32x4* p, u32x4 v) { atom::store16(p, v); }
+using atom::combine;
+using atom::Elems;
 
 // Launch of a datapath kernel: `first` / `last` say whether it opens / closes the
 // call's datapath, which decides whether it carries the thread's timing events.
@@ -62,92 +48,6 @@ __device__ __forceinline__ uint32_t logical_block(int xcd) {
   const uint32_t G = gridDim.x, q = G / kXcds, r = G % kXcds;
   const uint32_t x = b % kXcds, k = b / kXcds;
   return x * q + min(x, r) + k;
-}
-
-// ---- element types inside one 16-byte vector ----
-// Element j of a vector is at bits [16j, 16j+16) of the little-endian 128-bit word
-// (32j for fp32). Widening is exact; narrowing is one round-to-nearest-even.
-typedef float f32x2 __attribute__((ext_vector_type(2)));
-typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-
-template <int DT>
-struct Elems;
-
-template <>
-struct Elems<PLR_BF16> {
-  static constexpr int N = 8;
-  __device__ static __forceinline__ void widen(u32x4 v, float* f) {
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      f[2 * k] = __uint_as_float(v[k] << 16);
-      f[2 * k + 1] = __uint_as_float(v[k] & 0xFFFF0000u);
-    }
-  }
-  __device__ static __forceinline__ u32x4 narrow(const float* f) {
-    u32x4 r;
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      bf16x2 b = __builtin_convertvector((f32x2){f[2 * k], f[2 * k + 1]}, bf16x2);
-      r[k] = __builtin_bit_cast(uint32_t, b);
-    }
-    return r;
-  }
-};
-
-template <>
-struct Elems<PLR_F16> {
-  static constexpr int N = 8;
-  // Scalar conversions with explicit bit packing: v_cvt_f32_f16 widens exactly and
-  // v_cvt_f16_f32 rounds to nearest even (denormals kept, the kernels' float mode).
-  __device__ static __forceinline__ void widen(u32x4 v, float* f) {
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      f[2 * k] = (float)__builtin_bit_cast(_Float16, (uint16_t)(v[k] & 0xFFFFu));
-      f[2 * k + 1] = (float)__builtin_bit_cast(_Float16, (uint16_t)(v[k] >> 16));
-    }
-  }
-  __device__ static __forceinline__ u32x4 narrow(const float* f) {
-    u32x4 r;
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      const uint32_t lo = __builtin_bit_cast(uint16_t, (_Float16)f[2 * k]);
-      const uint32_t hi = __builtin_bit_cast(uint16_t, (_Float16)f[2 * k + 1]);
-      r[k] = lo | (hi << 16);
-    }
-    return r;
-  }
-};
-
-template <>
-struct Elems<PLR_F32> {
-  static constexpr int N = 4;
-  __device__ static __forceinline__ void widen(u32x4 v, float* f) {
-#pragma unroll
-    for (int k = 0; k < 4; ++k) f[k] = __uint_as_float(v[k]);
-  }
-  __device__ static __forceinline__ u32x4 narrow(const float* f) {
-    u32x4 r;
-#pragma unroll
-    for (int k = 0; k < 4; ++k) r[k] = __float_as_uint(f[k]);
-    return r;
-  }
-};
-
-// SCORE combine (section 3.3): one lane owns the vector's elements and adds the W
-// sources into a binary32 accumulator in source order, starting from source 0.
-template <int DT, int W>
-__device__ __forceinline__ u32x4 combine(const u32x4* x) {
-  constexpr int N = Elems<DT>::N;
-  float acc[N];
-  Elems<DT>::widen(x[0], acc);
-#pragma unroll
-  for (int w = 1; w < W; ++w) {
-    float t[N];
-    Elems<DT>::widen(x[w], t);
-#pragma unroll
-    for (int j = 0; j < N; ++j) acc[j] = acc[j] + t[j];
-  }
-  return Elems<DT>::narrow(acc);
 }
 
 // ---- consumer side of notify (section 3.2) ----

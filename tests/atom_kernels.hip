@@ -1,0 +1,164 @@
+// User kernels built on the device-callable Atom (include/plr_atom.h), the way the
+// project README's "Device-side" samples use it: a kernel of the Atom's THREADS threads
+// per workgroup calls copy or reduce on its own slice, fused with its own work. The
+// tests load this file's library (tests/libatom_kernels.so) and check every kernel
+// against the oracle.
+//
+//  - atom_block_copy: workgroup b copies bytes [b*per_block, (b+1)*per_block) (the
+//    README's copy sample).
+//  - atom_block_reduce: workgroup b reduces its slice of W sources; with a residual the
+//    epilogue adds it to the binary32 accumulators before the single rounding (an
+//    AllReduce fused with a residual add), which is the ordered reduction of the W
+//    sources followed by the residual as source W.
+//  - atom_pipeline: stage / notify / consume inside one kernel (section 3.2): workgroup
+//    b copies chunk b from src to mid and signals its flag, then waits for the flag of
+//    chunk b - lag and copies that chunk from mid to dst. Workgroups only wait for
+//    lower-numbered ones, which never wait before signalling, and workgroups are
+//    dispatched in increasing order, so every wait ends (the tests keep the grid small
+//    enough to be resident at once in any case); a bounded wait that gives up records 1
+//    in *err and copies nothing.
+#include <hip/hip_runtime.h>
+
+#include "plr_atom.h"
+
+using plr::atom::Atom;
+using plr::atom::Elems;
+using plr::atom::vec16;
+
+namespace {
+
+template <int THREADS>
+__global__ void __launch_bounds__(THREADS) k_block_copy(uint8_t* dst, const uint8_t* src, size_t per_block) {
+  const size_t off = (size_t)blockIdx.x * per_block;
+  Atom<THREADS>::copy(dst + off, src + off, per_block);
+}
+
+struct Srcs {
+  const uint8_t* p[PLR_MAX_WORLD];
+};
+
+// Epilogue: acc += widen(residual vector of the same elements).
+template <int DT>
+struct AddResidual {
+  const vec16* r;
+  __device__ void operator()(float* acc, int n, uint64_t first_element) const {
+    float t[Elems<DT>::N];
+    Elems<DT>::widen(plr::atom::load16(r + first_element / (uint64_t)n), t);
+#pragma unroll
+    for (int j = 0; j < Elems<DT>::N; ++j) acc[j] = acc[j] + t[j];
+  }
+};
+
+template <int DT, int W, int UNROLL>
+__global__ void __launch_bounds__(128) k_block_reduce(uint8_t* dst, Srcs s, const uint8_t* residual,
+                                                      size_t per_block) {
+  constexpr int N = Elems<DT>::N;
+  const size_t off = (size_t)blockIdx.x * per_block;
+  const void* src[W];
+#pragma unroll
+  for (int w = 0; w < W; ++w) src[w] = s.p[w] + off;
+  const uint64_t first = off / 16 * N;  // element index of the slice's first element
+  if (residual)
+    Atom<128, UNROLL>::template reduce<DT, W>(dst + off, src, per_block, first,
+                                              AddResidual<DT>{reinterpret_cast<const vec16*>(residual)});
+  else
+    Atom<128, UNROLL>::template reduce<DT, W>(dst + off, src, per_block, first);
+}
+
+__global__ void __launch_bounds__(256) k_pipeline(const uint8_t* src, uint8_t* mid, uint8_t* dst, size_t chunk,
+                                                  uint32_t nchunks, uint32_t lag, uint64_t* flags,
+                                                  uint64_t signal_epoch, uint64_t wait_epoch, uint64_t spin_limit,
+                                                  uint32_t* err) {
+  const uint32_t b = blockIdx.x;
+  if (b < nchunks) {  // stage: produce chunk b, then notify
+    Atom<256>::copy(mid + (size_t)b * chunk, src + (size_t)b * chunk, chunk);
+    plr::atom::signal_flag(flags + b, signal_epoch);
+  }
+  if (b >= lag) {  // consume chunk b - lag once its flag has arrived
+    const uint32_t c = b - lag;
+    if (!plr::atom::wait_flag(flags + c, wait_epoch, spin_limit)) {
+      if (threadIdx.x == 0) __hip_atomic_store(err, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      return;
+    }
+    Atom<256>::copy(dst + (size_t)c * chunk, mid + (size_t)c * chunk, chunk);
+  }
+}
+
+template <int DT, int W>
+hipError_t launch_reduce_u(int unroll, uint8_t* dst, const Srcs& s, const uint8_t* residual, size_t per_block,
+                           uint32_t nblocks, hipStream_t st) {
+  if (unroll == 2)
+    hipLaunchKernelGGL((k_block_reduce<DT, W, 2>), dim3(nblocks), dim3(128), 0, st, dst, s, residual, per_block);
+  else
+    hipLaunchKernelGGL((k_block_reduce<DT, W, 1>), dim3(nblocks), dim3(128), 0, st, dst, s, residual, per_block);
+  return hipGetLastError();
+}
+
+template <int DT>
+hipError_t launch_reduce_w(int world, int unroll, uint8_t* dst, const Srcs& s, const uint8_t* residual,
+                           size_t per_block, uint32_t nblocks, hipStream_t st) {
+  switch (world) {
+    case 1: return launch_reduce_u<DT, 1>(unroll, dst, s, residual, per_block, nblocks, st);
+    case 2: return launch_reduce_u<DT, 2>(unroll, dst, s, residual, per_block, nblocks, st);
+    case 3: return launch_reduce_u<DT, 3>(unroll, dst, s, residual, per_block, nblocks, st);
+    case 8: return launch_reduce_u<DT, 8>(unroll, dst, s, residual, per_block, nblocks, st);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+bool a16(const void* p) { return ((uintptr_t)p & 15) == 0; }
+
+}  // namespace
+
+// Host launchers: argument checks on the host, then one launch. Return a hipError_t.
+extern "C" int atom_block_copy(void* dst, const void* src, size_t per_block, unsigned nblocks, int threads,
+                               void* stream) {
+  if (!dst || !src || !nblocks || (per_block & 15) || !a16(dst) || !a16(src)) return (int)hipErrorInvalidValue;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  uint8_t* d = static_cast<uint8_t*>(dst);
+  const uint8_t* s = static_cast<const uint8_t*>(src);
+  switch (threads) {
+    case 64: hipLaunchKernelGGL(k_block_copy<64>, dim3(nblocks), dim3(64), 0, st, d, s, per_block); break;
+    case 128: hipLaunchKernelGGL(k_block_copy<128>, dim3(nblocks), dim3(128), 0, st, d, s, per_block); break;
+    case 256: hipLaunchKernelGGL(k_block_copy<256>, dim3(nblocks), dim3(256), 0, st, d, s, per_block); break;
+    case 512: hipLaunchKernelGGL(k_block_copy<512>, dim3(nblocks), dim3(512), 0, st, d, s, per_block); break;
+    default: return (int)hipErrorInvalidValue;
+  }
+  return (int)hipGetLastError();
+}
+
+extern "C" int atom_block_reduce(int dtype, int world, const void* const* srcs, const void* residual, void* dst,
+                                 size_t per_block, unsigned nblocks, int unroll, void* stream) {
+  if (!srcs || !dst || !nblocks || (per_block & 15) || !a16(dst) || world < 1 || world > PLR_MAX_WORLD)
+    return (int)hipErrorInvalidValue;
+  if (residual && !a16(residual)) return (int)hipErrorInvalidValue;
+  Srcs s{};
+  for (int w = 0; w < world; ++w) {
+    if (!srcs[w] || !a16(srcs[w])) return (int)hipErrorInvalidValue;
+    s.p[w] = static_cast<const uint8_t*>(srcs[w]);
+  }
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  uint8_t* d = static_cast<uint8_t*>(dst);
+  const uint8_t* r = static_cast<const uint8_t*>(residual);
+  switch (dtype) {
+    case PLR_BF16: return (int)launch_reduce_w<PLR_BF16>(world, unroll, d, s, r, per_block, nblocks, st);
+    case PLR_F16: return (int)launch_reduce_w<PLR_F16>(world, unroll, d, s, r, per_block, nblocks, st);
+    case PLR_F32: return (int)launch_reduce_w<PLR_F32>(world, unroll, d, s, r, per_block, nblocks, st);
+    default: return (int)hipErrorInvalidValue;
+  }
+}
+
+// signal_epoch is what producers store, wait_epoch what consumers wait for (equal in
+// normal use; a smaller signal_epoch makes every bounded wait give up).
+extern "C" int atom_pipeline(const void* src, void* mid, void* dst, size_t chunk, unsigned nchunks, unsigned lag,
+                             void* flags, unsigned long long signal_epoch, unsigned long long wait_epoch,
+                             unsigned long long spin_limit, void* err, void* stream) {
+  if (!src || !mid || !dst || !flags || !err || !nchunks || !lag || (chunk & 15) || !a16(src) || !a16(mid) ||
+      !a16(dst) || ((uintptr_t)flags & 7) || ((uintptr_t)err & 3))
+    return (int)hipErrorInvalidValue;
+  hipLaunchKernelGGL(k_pipeline, dim3(nchunks + lag), dim3(256), 0, static_cast<hipStream_t>(stream),
+                     static_cast<const uint8_t*>(src), static_cast<uint8_t*>(mid), static_cast<uint8_t*>(dst), chunk,
+                     (uint32_t)nchunks, (uint32_t)lag, static_cast<uint64_t*>(flags), (uint64_t)signal_epoch,
+                     (uint64_t)wait_epoch, (uint64_t)spin_limit, static_cast<uint32_t*>(err));
+  return (int)hipGetLastError();
+}

@@ -297,3 +297,23 @@ def test_variable_length_layouts(plr, oracle_mod):
     assert _code(bad, "allreduce", "bf16", 2, 64, "scattered", "scattered", part_bytes=[32, 32]) == plr.PLR_EINVAL
     assert _code(bad, "copy", "bf16", 2, 8192, "packed", "packed", part_bytes=[4096, 4096],
                  datapath=plr.PLR_PATH_LDS) == plr.PLR_EUNSUPPORTED
+
+
+def test_atom_header_standalone(tmp_path):
+    """include/plr_atom.h compiles on its own for gfx950 (only plr.h beside it) and the
+    user-kernel library the GPU tests load exports its launchers."""
+    src = tmp_path / "user.hip"
+    src.write_text('#include "plr_atom.h"\n'
+                   "__global__ void k(void* d, const void* s, size_t n) {\n"
+                   "  plr::atom::Atom<256, 2>::copy(d, s, n);\n"
+                   "  const void* srcs[2] = {s, s};\n"
+                   "  plr::atom::Atom<256>::reduce<PLR_BF16, 2>(d, srcs, n);\n}\n")
+    r = subprocess.run(["/opt/rocm/bin/hipcc", "-x", "hip", "--offload-arch=gfx950", "--cuda-device-only",
+                        "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops", "-std=c++17", "-O3",
+                        "-I", os.path.join(ROOT, "include"), "-c", str(src), "-o", str(tmp_path / "user.o")],
+                       capture_output=True, text=True)
+    assert r.returncode == 0, r.stderr
+    lib = os.path.join(ROOT, "tests", "libatom_kernels.so")
+    if os.path.exists(lib):
+        out = subprocess.run(["nm", "-D", "--defined-only", lib], capture_output=True, text=True).stdout
+        assert {"atom_block_copy", "atom_block_reduce", "atom_pipeline"} <= set(re.findall(r" T (atom_\w+)", out))
