@@ -74,16 +74,24 @@ def test_nan_payloads_preserved(plr):
     assert _run(plr, L, srcs).tobytes() == srcs[0].tobytes() + srcs[1].tobytes()
 
 
+@pytest.mark.parametrize("notified", [False, True])
 @pytest.mark.parametrize("kind", ["allgather", "alltoall"])
-def test_config4_full(plr, oracle_mod, kind):
+def test_config4_full(plr, oracle_mod, kind, notified):
     """8 sources of 64 MiB of random bits; AllGather into 512 MiB, AllToAll of 8 MiB
-    tiles; the whole output compared with the oracle, default policy."""
+    tiles; the whole output compared with the oracle, default policy, un-notified and in
+    the bench's launch configuration (notified, check mode: runs of 2 tiles)."""
     W, B = 8, 64 << 20
     srcs = [synth.bits_t(0, 4, s, B, device="cuda") for s in range(W)]
     L = plr.plr_layout_create("copy", "bf16", W, B, *PAIRS[kind])
-    dst = torch.empty(L.dst_bytes, dtype=torch.uint8, device="cuda")
-    plr.plr_copy(L, srcs, dst)
+    dst = torch.full((L.dst_bytes,), 0x5A, dtype=torch.uint8, device="cuda")
+    ws = None
+    if notified:
+        ws = torch.zeros(L.workspace_bytes, dtype=torch.uint8, device="cuda")
+        plr.plr_notify(L, -1, ws)
+    plr.plr_copy(L, srcs, dst, ws)
     torch.cuda.synchronize()
+    if notified:
+        assert plr.plr_check(L, ws) == plr.PLR_OK
     ref = oracle_mod.copy_layout(*PAIRS[kind], [s.cpu().numpy() for s in srcs])
     assert np.array_equal(dst.cpu().numpy(), ref)
 

@@ -162,15 +162,24 @@ def test_config2_decode_share(plr, oracle_mod, T):
                     f"T={T} ws={ws}")
 
 
-def test_config3_prefill_share_sampled(plr, oracle_mod):
+@pytest.mark.parametrize("notified", [False, True])
+def test_config3_prefill_share_sampled(plr, oracle_mod, notified):
     """8 contributions of [8192, 7168] bf16, N(0, 0.5), at full size with the default
-    policy; 96 sampled rows (first, last and random) are checked against the oracle."""
+    policy, un-notified and in the bench's launch configuration (notified, check mode);
+    96 sampled rows (first, last and random) are checked against the oracle."""
     W, R, C = 8, 8192, 7168
     srcs = [synth.normal_t(0, 3, w, R * C, 0.5, device="cuda") for w in range(W)]
-    dst = torch.empty(R * C, dtype=torch.bfloat16, device="cuda")
+    dst = torch.full((R * C,), float("nan"), dtype=torch.bfloat16, device="cuda")
     L = plr.plr_layout_create("reduce", "bf16", W, R * C * 2, "packed", "packed")
-    plr.plr_reduce(L, srcs, dst)
+    ws = None
+    if notified:
+        assert L.policy()["notify_mode"] == plr.PLR_NOTIFY_CHECK
+        ws = torch.zeros(L.workspace_bytes, dtype=torch.uint8, device="cuda")
+        plr.plr_notify(L, -1, ws)
+    plr.plr_reduce(L, srcs, dst, ws)
     torch.cuda.synchronize()
+    if notified:
+        assert plr.plr_check(L, ws) == plr.PLR_OK
     rows = np.unique(np.concatenate([[0, 1, R - 1], np.random.default_rng(0).integers(0, R, 93)]))
     idx = torch.from_numpy(rows).cuda()
     got = dst.view(R, C)[idx].view(torch.int16).cpu().numpy().view(np.uint16)
