@@ -12,6 +12,8 @@
 //            output row of the segment's first row bound there;
 //   kernel 2 (row tiles, one per workgroup step): moves every row with 16-byte loads
 //            and stores to that segment row plus the row's rank.
+#include <algorithm>
+
 #include "device_common.h"
 
 namespace plr {
@@ -124,12 +126,13 @@ __global__ void __launch_bounds__(kRankThreads) k_copy_v_rank(const CopyVArgs a)
 }
 
 // Kernel 2 cuts every row into tiles of kCvTileBytes (the last tile of a row may be
-// shorter); a workgroup of kCvThreads lanes moves kCvRun consecutive tiles, one
-// 16-byte vector per lane per step, so that the chip holds many short workgroups with
-// their loads in flight, as the copy kernel does. A tile's source address and the
-// locations of its row's key and segment table depend only on the row, so all of its
-// loads are issued together; the output row is then the segment table's entry for the
-// key's destination plus the key's rank, with no second dependent load.
+// shorter); a workgroup of kCvThreads lanes moves kCvRun consecutive tiles of one
+// source (grid row y = source y), one 16-byte vector per lane per step, so that the
+// chip holds many short workgroups with their loads in flight, as the copy kernel
+// does. A tile's source address and the locations of its row's key and segment table
+// depend only on the row, so all of its loads are issued together; the output row is
+// then the segment table's entry for the key's destination plus the key's rank, with
+// no second dependent load.
 #ifndef PLR_CV_TILE_BYTES
 #define PLR_CV_TILE_BYTES 2048
 #endif
@@ -152,20 +155,20 @@ __global__ void __launch_bounds__(kCvThreads) k_copy_v_scatter(const CopyVArgs a
   // leave the vector memory path to the row's data.
   const PLR_CONST uint32_t* key_of = (const PLR_CONST uint32_t*)a.key;
   const PLR_CONST int32_t* seg_out = (const PLR_CONST int32_t*)a.seg_out;
-  const uint64_t tiles_per_row = (a.row_bytes + kCvTileBytes - 1) / kCvTileBytes;
-  const uint64_t ntiles = (uint64_t)a.row_start[W] * tiles_per_row;
+  // grid row s moves source s's rows: no search for the source of a tile
+  const uint32_t s = blockIdx.y;
+  const int64_t r0 = a.row_start[s];
+  const uint64_t ntiles = (uint64_t)(a.row_start[s + 1] - r0) * a.tiles_per_row;
+  const uint8_t* src_s = a.src[s];
+  const uint32_t seg0 = a.seg_start[s];
   const uint64_t stride = (uint64_t)gridDim.x * kCvRun;
   for (uint64_t t0 = (uint64_t)logical_block(a.xcd) * kCvRun; t0 < ntiles; t0 += stride) {
     const uint64_t t1 = min(t0 + kCvRun, ntiles);
     for (uint64_t t = t0; t < t1; ++t) {
-      const int64_t r = (int64_t)(t / tiles_per_row);
-      const uint64_t b0 = (t - (uint64_t)r * tiles_per_row) * kCvTileBytes;
+      const uint64_t i = (ntiles >> 32) ? t / a.tiles_per_row : (uint32_t)t / (uint32_t)a.tiles_per_row;
+      const uint64_t b0 = (t - i * a.tiles_per_row) * kCvTileBytes;
       const uint64_t nv = (min(b0 + kCvTileBytes, a.row_bytes) - b0) >> 4;
-      int s = 0;
-      while (r >= a.row_start[s + 1]) ++s;
-      const int64_t i = r - a.row_start[s];
-      const uint64_t g = a.seg_start[s] + (uint64_t)(i / kRankSeg);
-      const u32x4* src = reinterpret_cast<const u32x4*>(a.src[s] + (uint64_t)i * a.row_bytes + b0);
+      const u32x4* src = reinterpret_cast<const u32x4*>(src_s + i * a.row_bytes + b0);
       u32x4 x[kCvVecs];
 #pragma unroll
       for (int u = 0; u < kCvVecs; ++u) {
@@ -175,8 +178,8 @@ __global__ void __launch_bounds__(kCvThreads) k_copy_v_scatter(const CopyVArgs a
       // The row's data loads are issued first, then its key and its segment's table
       // (64 bytes), all before any of them is waited for.
       asm volatile("" ::: "memory");
-      const uint32_t key = key_of[r];
-      const PLR_CONST int32_t* tp = seg_out + g * PLR_MAX_WORLD;
+      const uint32_t key = key_of[r0 + (int64_t)i];
+      const PLR_CONST int32_t* tp = seg_out + (seg0 + i / kRankSeg) * PLR_MAX_WORLD;
       int32_t tab[PLR_MAX_WORLD];
 #pragma unroll
       for (int k = 0; k < PLR_MAX_WORLD; ++k) tab[k] = tp[k];
@@ -197,16 +200,20 @@ __global__ void __launch_bounds__(kCvThreads) k_copy_v_scatter(const CopyVArgs a
   }
 }
 
-hipError_t launch_copy_v(const CopyVArgs& a, hipStream_t s) {
+hipError_t launch_copy_v(const CopyVArgs& args, hipStream_t s) {
+  CopyVArgs a = args;
+  a.tiles_per_row = (a.row_bytes + kCvTileBytes - 1) / kCvTileBytes;
   const uint32_t segs = a.seg_start[a.world];
   launch_dp(k_copy_v_rank, dim3(segs ? segs : 1), dim3(kRankThreads), s, true, false, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  // one workgroup per kCvRun tiles; huge inputs make the grid stride over the tiles
-  const uint64_t tiles = (uint64_t)a.row_start[a.world] * ((a.row_bytes + kCvTileBytes - 1) / kCvTileBytes);
-  const uint64_t groups = (tiles + kCvRun - 1) / kCvRun;
-  const uint32_t grid = (uint32_t)(groups < 1 ? 1 : (groups > (1u << 22) ? (1u << 22) : groups));
-  launch_dp(k_copy_v_scatter, dim3(grid), dim3(kCvThreads), s, false, true, a);
+  // grid row s covers source s: one workgroup per kCvRun tiles of the longest source;
+  // huge inputs make every row stride over its tiles
+  int64_t most = 0;
+  for (uint32_t w = 0; w < a.world; ++w) most = std::max<int64_t>(most, a.row_start[w + 1] - a.row_start[w]);
+  const uint64_t groups = ((uint64_t)most * a.tiles_per_row + kCvRun - 1) / kCvRun;
+  const uint32_t gx = (uint32_t)(groups < 1 ? 1 : (groups > (1u << 22) ? (1u << 22) : groups));
+  launch_dp(k_copy_v_scatter, dim3(gx, a.world), dim3(kCvThreads), s, false, true, a);
   return hipGetLastError();
 }
 

@@ -125,6 +125,7 @@ struct CopyVArgs {
                      // destination (kNoDest << 16 for a row that has no destination)
   uint32_t* ticket;  // scratch: count of finished rank workgroups (zero between calls)
   uint64_t row_bytes;
+  uint64_t tiles_per_row;  // scatter tiles per row (the kernel's tile size)
   uint32_t world;
   uint32_t xcd;      // XCD-aware workgroup order (scatter)
 };
