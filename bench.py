@@ -466,8 +466,71 @@ def run_next(args):
             raise RuntimeError(f"{name}: device error")
         out[name] = {"avg_us": round(us, 2), "GB/s": round(algo / (us * 1e-6) / 1e9, 1),
                      "algorithmic_bytes": algo}
-    del srcs, dsts
+    del dsts
+    out.update(run_atom_user_kernels(torch, srcs))
+    del srcs
     torch.cuda.empty_cache()
+    return out
+
+
+def run_atom_user_kernels(torch, srcs):
+    """User kernels written on the device-callable Atom (include/plr_atom.h; built by
+    build() into tests/libatom_kernels.so), timed with events around single launches:
+    the reduce of the 8 prefill contributions fused with a residual add (one more
+    contribution read, so 10 x 117 MB of traffic), 2 KiB per 128-thread workgroup,
+    and a 512 MiB copy in 2 KiB workgroup slices (the README's device-side sample)."""
+    path = os.path.join(ROOT, "tests", "libatom_kernels.so")
+    if not os.path.exists(path):
+        return {"atom_user_kernels": "not built"}
+    lib = ctypes.CDLL(path)
+    vp, sz, i, u = ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int, ctypes.c_uint
+    lib.atom_block_reduce.argtypes = [i, i, ctypes.POINTER(vp), vp, vp, sz, u, i, vp]
+    lib.atom_block_copy.argtypes = [vp, vp, sz, u, i, vp]
+    E = TimingEvents(torch)
+    stream = torch.cuda.current_stream().cuda_stream
+
+    def timed(fn, n=10):
+        for _ in range(3):
+            fn()
+        evs = [(E.create(), E.create()) for _ in range(n)]
+        torch.cuda.synchronize()
+        for a, b in evs:
+            E.record(a, stream)
+            fn()
+            E.record(b, stream)
+        torch.cuda.synchronize()
+        return statistics.mean(E.elapsed_ms(a, b) for a, b in evs) * 1e3
+
+    out = {}
+    share = R3 * C3 * 2
+    res = torch.empty(R3 * C3, dtype=torch.bfloat16, device=srcs[0].device).normal_()
+    dst = torch.empty_like(res)
+    ptrs = (vp * W)(*[s.data_ptr() for s in srcs])
+    per, nblk = 2048, share // 2048
+
+    def red():
+        rc = lib.atom_block_reduce(0, W, ptrs, res.data_ptr(), dst.data_ptr(), per, nblk, 1, stream)
+        if rc:
+            raise RuntimeError(f"atom_block_reduce: {rc}")
+
+    us = timed(red)
+    algo = (W + 2) * share
+    out["atom_reduce_residual"] = {"avg_us": round(us, 2), "GB/s": round(algo / (us * 1e-6) / 1e9, 1),
+                                   "algorithmic_bytes": algo}
+    del res, dst
+    n = W * B4
+    a = torch.empty(n, dtype=torch.uint8, device=srcs[0].device).fill_(1)
+    b = torch.empty_like(a)
+
+    def cp():
+        rc = lib.atom_block_copy(b.data_ptr(), a.data_ptr(), 2048, n // 2048, 128, stream)
+        if rc:
+            raise RuntimeError(f"atom_block_copy: {rc}")
+
+    us = timed(cp)
+    out["atom_block_copy"] = {"avg_us": round(us, 2), "GB/s": round(2 * n / (us * 1e-6) / 1e9, 1),
+                              "algorithmic_bytes": 2 * n}
+    E.destroy_all()
     return out
 
 

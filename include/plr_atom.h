@@ -121,17 +121,24 @@ struct Elems<PLR_F32> {
   }
 };
 
+// Epilogues run on the binary32 accumulators of one 16-byte output vector, before the
+// single rounding. An epilogue type provides
+//   Pre  load(uint64_t vec) const   issued together with the sources' loads of output
+//                                   vector `vec` (so that its own loads overlap them);
+//   void operator()(float* acc, int n, uint64_t first_element, const Pre&) const
+//                                   transforms the n accumulators in place.
 // No epilogue: the accumulators are rounded as they are.
 struct NoEpilogue {
-  __device__ __forceinline__ void operator()(float*, int, uint64_t) const {}
+  struct Pre {};
+  __device__ __forceinline__ Pre load(uint64_t) const { return {}; }
+  __device__ __forceinline__ void operator()(float*, int, uint64_t, const Pre&) const {}
 };
 
 // SCORE combine of one vector per source (x[0..W-1], in source order): binary32
-// accumulation from source 0, then `epi(acc, N, first_element)` may transform the N
-// accumulators in place (a fused epilogue, still before the single rounding), then one
-// round-to-nearest-even.
+// accumulation from source 0, then the epilogue, then one round-to-nearest-even.
 template <int DT, int W, class Epi = NoEpilogue>
-__device__ __forceinline__ vec16 combine(const vec16* x, uint64_t first_element = 0, const Epi& epi = Epi()) {
+__device__ __forceinline__ vec16 combine(const vec16* x, uint64_t first_element = 0, const Epi& epi = Epi(),
+                                         const typename Epi::Pre& pre = typename Epi::Pre()) {
   constexpr int N = Elems<DT>::N;
   float acc[N];
   Elems<DT>::widen(x[0], acc);
@@ -142,7 +149,7 @@ __device__ __forceinline__ vec16 combine(const vec16* x, uint64_t first_element 
 #pragma unroll
     for (int j = 0; j < N; ++j) acc[j] = acc[j] + t[j];
   }
-  epi(acc, N, first_element);
+  epi(acc, N, first_element, pre);
   return Elems<DT>::narrow(acc);
 }
 
@@ -173,9 +180,11 @@ struct Atom {
   }
 
   // dst = the ordered reduction of srcs[0..W-1] over `bytes` bytes of element type DT
-  // (PLR_BF16, PLR_F16 or PLR_F32). `first_element` is the index of the slice's first
-  // element in the caller's numbering, handed to the epilogue with every vector's own
-  // first element. All W*UNROLL loads of a lane are issued before its first add.
+  // (PLR_BF16, PLR_F16 or PLR_F32), with an optional epilogue. `first_element` is the
+  // index of the slice's first element in the caller's numbering (a multiple of the
+  // elements per vector); the epilogue sees every vector's own first element and loads
+  // by vector index in the same numbering. All W*UNROLL loads of a lane (and the
+  // epilogue's) are issued before its first add.
   template <int DT, int W, class Epi = NoEpilogue>
   __device__ static __forceinline__ void reduce(void* dst, const void* const* srcs, size_t bytes,
                                                 uint64_t first_element = 0, const Epi& epi = Epi()) {
@@ -187,23 +196,28 @@ struct Atom {
     vec16* d = static_cast<vec16*>(dst);
     const uint64_t nv = bytes >> 4;
     uint64_t v = threadIdx.x;
+    const uint64_t first_vec = first_element / N;
     for (; v + (uint64_t)(UNROLL - 1) * THREADS < nv; v += (uint64_t)UNROLL * THREADS) {
       vec16 x[UNROLL][W];
+      typename Epi::Pre pre[UNROLL];
 #pragma unroll
-      for (int u = 0; u < UNROLL; ++u)
+      for (int u = 0; u < UNROLL; ++u) {
 #pragma unroll
         for (int w = 0; w < W; ++w) x[u][w] = load16(s[w] + v + (uint64_t)u * THREADS);
+        pre[u] = epi.load(first_vec + v + (uint64_t)u * THREADS);
+      }
 #pragma unroll
       for (int u = 0; u < UNROLL; ++u) {
         const uint64_t vv = v + (uint64_t)u * THREADS;
-        store16(d + vv, combine<DT, W, Epi>(x[u], first_element + vv * N, epi));
+        store16(d + vv, combine<DT, W, Epi>(x[u], first_element + vv * N, epi, pre[u]));
       }
     }
     for (; v < nv; v += THREADS) {
       vec16 x[W];
 #pragma unroll
       for (int w = 0; w < W; ++w) x[w] = load16(s[w] + v);
-      store16(d + v, combine<DT, W, Epi>(x, first_element + v * N, epi));
+      const typename Epi::Pre pre = epi.load(first_vec + v);
+      store16(d + v, combine<DT, W, Epi>(x, first_element + v * N, epi, pre));
     }
   }
 };

@@ -16,9 +16,11 @@
 //    rank that owns the tile's slice, then releases the tile's flag (agent scope).
 //    It then acts as a gatherer for tile b - lag: it waits for that tile's flag,
 //    acquires, and copies the reduced tile into the other W-1 outputs. A workgroup
-//    only ever waits for a lower-numbered workgroup, whose reduction never waits, and
-//    workgroups are dispatched in increasing order, so the waits always end; a bounded
-//    spin turns any surprise into PLR_ETIMEOUT.
+//    only ever waits for a lower-numbered workgroup, whose reduction never waits;
+//    workgroups go round-robin to the 8 XCDs and each XCD dispatches its own in
+//    increasing order, and lag is a multiple of 8, so the producer is on the same XCD
+//    and was dispatched first: the waits always end. A bounded spin turns any
+//    surprise into PLR_ETIMEOUT.
 #include "device_common.h"
 
 namespace plr {

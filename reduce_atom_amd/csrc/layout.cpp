@@ -63,6 +63,10 @@ static void default_policy(plr_layout* L) {
     L->tile_bytes = 2u << 10;
     L->chunk_bytes = L->tile_bytes;
   }
+  // composed AllReduce: workgroup b gathers the tile of workgroup b - lag. The
+  // dispatcher hands workgroup b to XCD b % 8 and dispatches each XCD's workgroups in
+  // increasing order, so with a multiple of 8 the producer sits on the same XCD and
+  // was dispatched first: every wait is for a resident or finished workgroup.
   L->lag = 16;
 }
 

@@ -37,13 +37,16 @@ struct Srcs {
   const uint8_t* p[PLR_MAX_WORLD];
 };
 
-// Epilogue: acc += widen(residual vector of the same elements).
+// Epilogue: acc += widen(residual vector of the same elements); the residual vector is
+// loaded together with the sources' vectors.
 template <int DT>
 struct AddResidual {
   const vec16* r;
-  __device__ void operator()(float* acc, int n, uint64_t first_element) const {
+  typedef vec16 Pre;
+  __device__ Pre load(uint64_t vec) const { return plr::atom::load16(r + vec); }
+  __device__ void operator()(float* acc, int, uint64_t, const Pre& x) const {
     float t[Elems<DT>::N];
-    Elems<DT>::widen(plr::atom::load16(r + first_element / (uint64_t)n), t);
+    Elems<DT>::widen(x, t);
 #pragma unroll
     for (int j = 0; j < Elems<DT>::N; ++j) acc[j] = acc[j] + t[j];
   }
