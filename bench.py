@@ -473,6 +473,57 @@ def run_next(args):
     return out
 
 
+def run_v_sweep(args):
+    """AllGatherV and the rank-0 ReduceScatterV share over 8 ranks with the Zipf
+    (s = 0.125) split of a total T, for T = 1 KiB .. 1 GiB (appendix C.4's sweep):
+    kernel-only time per call (timing-only events, median of 20 after 5 warmup calls)
+    and the algorithmic GB/s at that time. Sources are allocated once at the largest T."""
+    import torch
+
+    import reduce_atom_amd as plr
+    import synth
+
+    dev = torch.device("cuda:0")
+    Tmax = 1 << 30
+    E = TimingEvents(torch)
+    stream = torch.cuda.current_stream().cuda_stream
+
+    def median_us(fn, n=20):
+        for _ in range(5):
+            fn()
+        evs = [(E.create(), E.create()) for _ in range(n)]
+        torch.cuda.synchronize()
+        for a, b in evs:
+            plr.plr_set_timing_events(a, b)
+            fn()
+        plr.plr_set_timing_events()
+        torch.cuda.synchronize()
+        t = sorted(E.elapsed_ms(a, b) * 1e3 for a, b in evs)
+        return t[len(t) // 2]
+
+    rows = []
+    big = synth.zipf_split(Tmax, W)
+    g_src = [synth.bits_t(args.seed, 7, w, big[w], device=dev) for w in range(W)]
+    g_dst = torch.empty(Tmax, dtype=torch.uint8, device=dev)
+    r_src = [synth.normal_t(args.seed, 8, w, Tmax // 2, 1.0, device=dev) for w in range(W)]
+    r_dst = torch.empty(big[0], dtype=torch.uint8, device=dev)
+    T = 1024
+    while T <= Tmax:
+        parts = synth.zipf_split(T, W)
+        L = plr.plr_layout_create("copy", "bf16", W, T, "packed", "packed", part_bytes=parts)
+        ag = median_us(lambda: plr.plr_copy(L, g_src, g_dst))
+        R = plr.plr_layout_create("reduce", "bf16", W, T, "scattered", "packed", rank=0, part_bytes=parts)
+        rs = median_us(lambda: plr.plr_reduce(R, r_src, r_dst))
+        rows.append({"T": T, "largest_part": parts[0],
+                     "allgatherv_us": round(ag, 2), "allgatherv_GB/s": round(2 * T / ag / 1e3, 1),
+                     "reducescatterv_rank0_us": round(rs, 2),
+                     "reducescatterv_rank0_GB/s": round((W + 1) * parts[0] / rs / 1e3, 1)})
+        T *= 2
+    E.destroy_all()
+    del stream
+    return rows
+
+
 def run_atom_user_kernels(torch, srcs):
     """User kernels written on the device-callable Atom (include/plr_atom.h; built by
     build() into tests/libatom_kernels.so), timed with events around single launches:
@@ -584,6 +635,8 @@ def main():
     ap.add_argument("--decode-t", type=lambda v: [int(x) for x in v.split(",")], default=None,
                     help="decode token counts T (comma separated; default 1,8,32,64)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--v-sweep", action="store_true",
+                    help="only the AllGatherV / ReduceScatterV sweep over T = 1 KiB .. 1 GiB, as JSON")
     ap.add_argument("--cpu-fraction", type=float, default=0.5)
     ap.add_argument("--cpu-reps", type=int, default=3)
     ap.add_argument("--summarize-trace", metavar="CSV",
@@ -620,6 +673,9 @@ def main():
         torch.cuda.synchronize()
         print(json.dumps({"calibrate": "torch copy_", "bytes_read": 1 << 30, "bytes_written": 1 << 30,
                           "launches": 5}), flush=True)
+        return
+    if args.v_sweep:
+        print(json.dumps({"v_sweep": run_v_sweep(args)}), flush=True)
         return
     if args.decode_only:
         import torch
