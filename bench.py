@@ -328,6 +328,8 @@ def run_bench(args):
     del x, ws, scratch
     torch.cuda.empty_cache()
     decode = run_decode(args, torch, plr, synth, dev) if not args.no_decode else None
+    if decode is not None:
+        decode = {"decode": decode, "local": run_local_reduce(args, torch, plr, synth, dev)}
     return value, ms_per_step, ms_per_step_events, roofline, per_op, decode
 
 
@@ -470,6 +472,38 @@ def run_next(args):
     out.update(run_atom_user_kernels(torch, srcs))
     del srcs
     torch.cuda.empty_cache()
+    return out
+
+
+def run_local_reduce(args, torch, plr, synth, dev):
+    """The local reduce of 8 contributions of 1,048,576 bf16 (uniform[-1, 1]) into one
+    share, 18 MiB of traffic per call: warm (the same buffers back to back, L2 and the
+    256 MB Infinity Cache hold them) and cold (rotating among 40 buffer sets, 720 MiB,
+    so that every call's inputs have left the caches). Kernel-only time per call from
+    timing-only events, median of 50 after 10 warmup calls."""
+    n = 1 << 20
+    sets = 40
+    bufs = [[synth.uniform_pm1_t(args.seed, 1, w, n, device=dev) if k == 0 else None for w in range(W)]
+            for k in range(sets)]
+    for k in range(1, sets):  # the same values in every set, different memory
+        bufs[k] = [b.clone() for b in bufs[0]]
+    dst = torch.empty(n, dtype=torch.bfloat16, device=dev)
+    L = plr.plr_layout_create("reduce", "bf16", W, 2 * n, "packed", "packed")
+    E = TimingEvents(torch)
+    out = {}
+    for mode in ("warm", "cold"):
+        calls = [0] * 60 if mode == "warm" else [k % sets for k in range(60)]
+        evs = [(E.create(), E.create()) for _ in calls]
+        torch.cuda.synchronize()
+        for (a, b), k in zip(evs, calls):
+            plr.plr_set_timing_events(a, b)
+            plr.plr_reduce(L, bufs[k], dst)
+        plr.plr_set_timing_events()
+        torch.cuda.synchronize()
+        us = sorted(E.elapsed_ms(a, b) * 1e3 for a, b in evs[10:])
+        p50 = us[len(us) // 2]
+        out[mode] = {"p50_us": round(p50, 2), "GB/s_at_p50": round(9 * 2 * n / (p50 * 1e-6) / 1e9, 1)}
+    E.destroy_all()
     return out
 
 
@@ -686,7 +720,9 @@ def main():
         print(json.dumps({"decode_reduce_us": run_decode(args, torch, plr, synth, torch.device("cuda:0"))}),
               flush=True)
         return
-    value, ms, ms_events, roofline, per_op, decode = run_bench(args)
+    value, ms, ms_events, roofline, per_op, small = run_bench(args)
+    decode = small["decode"] if small else None
+    local = small["local"] if small else None
     nxt = None if args.no_decode else run_next(args)
     cpu = None if args.no_cpu_baseline else run_cpu_baseline(args)
     line = {
@@ -699,6 +735,7 @@ def main():
                    "world": W, "notify": True, "seed": args.seed, "step_bytes": sum(BYTES.values())},
         "roofline": roofline, "cpu_baseline": cpu, "per_op": per_op,
         "ms_per_step_with_op_events": round(ms_events, 4), "decode_reduce_us": decode,
+        "local_reduce_8x1M_bf16": local,
         "beyond_step": nxt,
     }
     print(json.dumps(line), flush=True)
