@@ -283,7 +283,8 @@ int plr_reduce_packets(plr_layout* L, const void* const* packets, void* dst, voi
  *   srcs, dest_of_row: host arrays of W device pointers; rows_per_src: host array.
  * A destination id outside [0, W) is a caller error: its row is skipped and its
  * counts and offsets are undefined.
- * Errors: PLR_EINVAL, PLR_EALIGN (row_bytes, srcs, dst), PLR_EUNSUPPORTED (W > 16), PLR_EHIP. */
+ * Errors: PLR_EINVAL, PLR_EALIGN (row_bytes, srcs, dst), PLR_EUNSUPPORTED (W > 16, or more
+ * than 2^31 - 1 rows in all), PLR_EHIP. */
 int plr_copy_v(int world, const void* const* srcs, const int64_t* rows_per_src,
                const int32_t* const* dest_of_row, size_t row_bytes, void* dst,
                int64_t* counts, int64_t* offsets, void* scratch, void* stream);
