@@ -20,6 +20,14 @@ LIB_PATH = os.path.join(_HERE, "libplr.so")
 if not os.path.exists(LIB_PATH):
     raise ImportError(f"{LIB_PATH} is missing: build it with `python reduce_atom_amd/_build.py`")
 
+# libplr.so must run on the HIP runtime that owns torch's memory and streams. torch
+# loads its bundled libamdhip64 by file name, so if libplr.so came first, its own
+# dependency (the system ROCm runtime, same soname) would be loaded and torch would
+# then load a second runtime beside it: the library's launches would go to a runtime
+# that owns neither torch's memory nor its streams.
+# Importing torch first makes libplr.so bind to torch's runtime.
+import torch  # noqa: E402,F401
+
 _lib = ctypes.CDLL(LIB_PATH)
 
 # ---- constants (include/plr.h) ----

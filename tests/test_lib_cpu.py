@@ -317,3 +317,17 @@ def test_atom_header_standalone(tmp_path):
     if os.path.exists(lib):
         out = subprocess.run(["nm", "-D", "--defined-only", lib], capture_output=True, text=True).stdout
         assert {"atom_block_copy", "atom_block_reduce", "atom_pipeline"} <= set(re.findall(r" T (atom_\w+)", out))
+
+
+def test_one_hip_runtime_whatever_the_import_order(plr):
+    """Importing the binding before torch must still leave a single HIP runtime in the
+    process (torch's), so that the library launches on the runtime that owns torch's
+    memory and streams."""
+    code = ("import reduce_atom_amd, torch\n"
+            "maps = open('/proc/self/maps').read().split('\\n')\n"
+            "print(sorted({l.split()[-1] for l in maps if 'libamdhip64' in l}))\n")
+    out = subprocess.run([os.sys.executable, "-c", code], capture_output=True, text=True, cwd=ROOT,
+                         timeout=300)
+    assert out.returncode == 0, out.stderr
+    paths = eval(out.stdout.strip().splitlines()[-1])
+    assert len(paths) == 1, paths
