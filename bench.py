@@ -11,8 +11,9 @@ plr_notify, then the consumer checks its per-chunk flags):
 the wall-clock time of a step, K steps timed back to back with nothing in the stream
 but the library's kernels. The same K steps are then run again with every op's
 datapath kernels carrying a pair of timing-only HIP events (plr_set_timing_events);
-their mean durations give `per_op` and the `roofline` of the dominant kernel, the
-figure a kernel trace of the same command reports for that kernel.
+their mean durations give `per_op` (with medians beside them) and the `roofline` of the
+dominant kernel, the figure a kernel trace of the same command reports for that kernel.
+Defaults: 10 warmup steps, then 50 timed.
 Decode-size latency (W=8 x [T, 7168] bf16, T in 1/8/32/64) is reported beside it,
 notify off and on and through packets: the time per call of 50 calls captured in a
 HIP graph and replayed back to back (for notify on, a call is the producer's notify
@@ -309,6 +310,7 @@ def run_bench(args):
             raise RuntimeError(f"{name}: device error {plr.plr_strerror(rc)}")
     ms_per_step_events = (t3 - t2) * 1e3 / args.steps
     per_op_us = {n: statistics.mean(E.elapsed_ms(*e[n]) for e in ev) * 1e3 for n in ops}
+    per_op_p50 = {n: statistics.median(E.elapsed_ms(*e[n]) for e in ev) * 1e3 for n in ops}
     E.destroy_all()
     step_bytes = sum(BYTES.values())
     value = step_bytes / (ms_per_step * 1e-3) / 1e9
@@ -321,7 +323,7 @@ def run_bench(args):
                 "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": counters_traffic(dom),
                 "kernel": KERNEL_NAMES[dom], "op": dom, "algorithmic_bytes": BYTES[dom],
                 "avg_us": round(per_op_us[dom], 2)}
-    per_op = {n: {"avg_us": round(per_op_us[n], 2),
+    per_op = {n: {"avg_us": round(per_op_us[n], 2), "p50_us": round(per_op_p50[n], 2),
                   "GB/s": round(BYTES[n] / (per_op_us[n] * 1e-6) / 1e9, 1),
                   "frac": round(BYTES[n] / (per_op_us[n] * 1e-6) / 1e9 / PEAK_HBM_GBS, 4)}
               for n in ops}
@@ -658,8 +660,8 @@ def run_cpu_baseline(args):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--decode-iters", type=int, default=1000)
     ap.add_argument("--decode-warmup", type=int, default=100)
