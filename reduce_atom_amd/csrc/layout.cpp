@@ -27,6 +27,8 @@ size_t elem_bytes(plr_dtype t) { return t == PLR_F32 ? 4 : 2; }
 // acquire per chunk it enters, and those acquires invalidate L2 lines, so large
 // notified calls give each workgroup a run of 2 (reduce) or 4 (copy) tiles; decode-size
 // shares (at most 2 MiB) keep one tile per workgroup, where latency rules.
+constexpr uint64_t kCus = 256;  // compute units of an MI355X (the composed AllReduce's tiles)
+
 static void default_policy(plr_layout* L) {
   L->stages = 2;
   L->datapath = PLR_PATH_DIRECT;
@@ -57,7 +59,7 @@ static void default_policy(plr_layout* L) {
     L->unroll = 1;
     L->tile_bytes = 2u << 10;
     L->chunk_bytes = 256u << 10;
-  } else {  // allreduce: fused by default; the composed path uses 64 KiB tiles
+  } else {  // allreduce: fused by default; the composed path's tiles follow the slice
     L->block = 128;
     L->unroll = 1;
     L->tile_bytes = 2u << 10;
@@ -236,7 +238,7 @@ extern "C" int plr_layout_create(const plr_layout_desc* d, plr_layout** out) {
       return fail(PLR_EINVAL);  // composed is the AllReduce role split; AllReduce has no LDS path
     L->datapath = d->datapath;
     if (d->datapath == PLR_PATH_COMPOSED) {
-      if (!d->tile_bytes) L->tile_bytes = 64u << 10;
+      if (!d->tile_bytes) L->tile_bytes = 0;  // chosen from the slice below
       if (!d->block) L->block = 256;
     }
   }
@@ -267,7 +269,19 @@ extern "C" int plr_layout_create(const plr_layout_desc* d, plr_layout** out) {
       L->tiles_per_seg = L->tiles_per_chunk = L->chunks_per_seg = 0;
       L->ntiles = L->nchunks = 0;
     } else {
-      const uint64_t tile = std::min<uint64_t>(L->tile_bytes, slice);
+      uint64_t tile = L->tile_bytes;
+      if (tile == 0) {
+        // composed policy: every tile pays one agent-scope release, an L2 writeback
+        // that the XCD's workgroups go through one at a time, so take as few tiles as
+        // keep every CU busy with all ntiles + lag workgroups resident in one round;
+        // whole steps of the workgroup (block x 16 bytes) when a tile holds one
+        const uint64_t per_slice = std::max<uint64_t>(1, (kCus - L->lag) / (uint64_t)W);
+        const uint64_t raw = (slice + per_slice - 1) / per_slice;
+        const uint64_t step = (uint64_t)L->block * 16;
+        const uint64_t g = raw >= step ? step : 16;
+        tile = (raw + g - 1) / g * g;
+      }
+      tile = std::min<uint64_t>(tile, slice);
       const uint64_t tps = (slice + tile - 1) / tile;
       if (tps * W > 0x7FFFFFFFull) return fail(PLR_EUNSUPPORTED);
       L->tile_bytes = L->chunk_bytes = tile;

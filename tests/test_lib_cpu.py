@@ -216,9 +216,25 @@ def test_allreduce_layouts(plr):
     L = plr.plr_layout_create("allreduce", "bf16", 8, 16 * 8 * 100, "scattered", "scattered")
     assert L.policy()["datapath"] == plr.PLR_PATH_DIRECT and L.dst_bytes == 16 * 8 * 100
     C = plr.plr_layout_create("allreduce", "bf16", 4, 4 * 64 * 1024 * 3, "scattered", "scattered",
-                              datapath=plr.PLR_PATH_COMPOSED)
+                              datapath=plr.PLR_PATH_COMPOSED, tile_bytes=64 * 1024)
     assert C.policy()["tile_bytes"] == 64 * 1024 and C.ntiles == 4 * 3 and C.nchunks == 12
     assert C.workspace_bytes == 256 + 12 * 8
+    # the composed policy: as few tiles as keep all ntiles + 16 (the gather lag)
+    # workgroups of a call resident at once on 256 CUs, i.e. at most (256 - 16) / W
+    # tiles per slice: the smallest such tile in whole workgroup steps (256 threads x
+    # 16 bytes), or in 16-byte vectors when a tile is shorter than one step
+    for W, S in [(4, 4 * 64 * 1024 * 3), (8, 8192 * 7168 * 2), (2, 1 << 24), (16, 16 * 16 * 1000), (3, 48 * 1000)]:
+        P = plr.plr_layout_create("allreduce", "bf16", W, S, "scattered", "scattered",
+                                  datapath=plr.PLR_PATH_COMPOSED)
+        tile, slice_ = P.policy()["tile_bytes"], S // W
+        tps = -(-slice_ // tile)
+        g = 4096 if tile >= 4096 else 16
+        assert tile % g == 0 and P.ntiles == W * tps and P.ntiles + 16 <= 256, (W, S, tile)
+        per_slice = (256 - 16) // W
+        assert tps <= per_slice and (tile == g or -(-slice_ // (tile - g)) > per_slice), (W, S, tile)
+        assert P.workspace_bytes == 256 + P.ntiles * 8
+    assert plr.plr_layout_create("allreduce", "bf16", 8, 8192 * 7168 * 2, "scattered", "scattered",
+                                 datapath=plr.PLR_PATH_COMPOSED).ntiles == 240
     mk = plr.plr_layout_create
     assert _code(mk, "allreduce", "bf16", 4, 64, "packed", "packed") == plr.PLR_EINVAL
     assert _code(mk, "allreduce", "bf16", 3, 16 * 4, "scattered", "scattered") == plr.PLR_EALIGN
