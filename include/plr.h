@@ -144,7 +144,7 @@ typedef struct {
   uint64_t spin_limit;        /* polls of a chunk flag before PLR_ETIMEOUT; 0 = default (about a second) */
   int notify_mode;            /* PLR_NOTIFY_POLICY (check first for shares over 2 MiB, in-kernel
                                  waits below), PLR_NOTIFY_CHUNKS or PLR_NOTIFY_CHECK */
-  int xcd_order;              /* 0 = policy (on), 1 = on, 2 = off: renumber workgroups so that each
+  int xcd_order;              /* 0 = policy (off), 1 = on, 2 = off: renumber workgroups so that each
                                  of the 8 XCDs walks one contiguous range of tiles */
   /* Variable-length layouts: W partition sizes in bytes (multiples of 16, zero allowed)
    * whose sum is the message size T, which bytes_per_src must equal; NULL = fixed

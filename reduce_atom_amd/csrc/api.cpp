@@ -56,7 +56,7 @@ uint32_t run_for(const plr_layout* L, bool notified) {
 Launch launch_of(const plr_layout* L, bool notified) {
   const uint32_t run = run_for(L, notified);
   const uint32_t grid = (uint32_t)std::max<uint64_t>(1, ((uint64_t)L->ntiles + run - 1) / run);
-  const int xcd = L->xcd_order == kXcdOn || (L->xcd_order == kXcdUnnotified && !notified);
+  const int xcd = L->xcd_order == kXcdOn;
   return Launch{grid, (uint32_t)L->block, L->unroll, L->stages, L->datapath, run, xcd};
 }
 

@@ -14,7 +14,7 @@ namespace plr {
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));  // one 16-byte vector
 
 constexpr int kMaxTableSegs = 64;   // explicit segment table carried in kernarg
-enum { kXcdOff = 0, kXcdOn = 1, kXcdUnnotified = 2 };
+enum { kXcdOff = 0, kXcdOn = 1 };
 // Workspace: u64 error word at byte 0, u64 ready word at byte 8, then
 // uint64 flags[W][nchunks] and their check-time mirror uint64 mirror[W][nchunks].
 constexpr size_t kWorkspaceHeader = 256;

@@ -19,14 +19,16 @@ namespace plr {
 size_t elem_bytes(plr_dtype t) { return t == PLR_F32 ? 4 : 2; }
 
 // gfx950 policy table (measured on MI355X with 8 x 117 MB bf16 reduces and 512 MiB
-// copies): the best streaming rate comes from one short step per workgroup and a
-// grid that covers every tile, so the dispatcher walks the whole chip through memory
-// front to back; 16-byte non-temporal loads and stores. Tiles: 2 KiB per source for
-// the reduce and the copies (128 threads, one vector per lane per source). Flags cover 256 KiB
-// chunks (16 KiB for decode-size shares). A notified workgroup pays one agent-scope
-// acquire per chunk it enters, and those acquires invalidate L2 lines, so large
-// notified calls give each workgroup a run of 2 (reduce) or 4 (copy) tiles; decode-size
-// shares (at most 2 MiB) keep one tile per workgroup, where latency rules.
+// copies): the best streaming rate comes from short steps per workgroup and a grid
+// that covers every tile, so the dispatcher walks the whole chip through memory front
+// to back, in plain workgroup order; 16-byte non-temporal loads and stores. Tiles:
+// 2 KiB per source for the reduce and the copies (128 threads, one vector per lane per
+// source); a reduce workgroup takes one tile, a copy workgroup two once a call has
+// 4096 tiles (8 MiB) or more. Flags cover 256 KiB chunks (16 KiB for decode-size
+// shares). With in-kernel waits a notified workgroup pays one agent-scope acquire per
+// chunk it enters, and those acquires invalidate L2 lines, so such calls give each
+// workgroup a run of 2 (reduce) or 4 (copy) tiles; decode-size shares (at most 2 MiB)
+// keep one tile per workgroup, where latency rules.
 constexpr uint64_t kCus = 256;  // compute units of an MI355X (the composed AllReduce's tiles)
 
 static void default_policy(plr_layout* L) {
@@ -34,9 +36,9 @@ static void default_policy(plr_layout* L) {
   L->datapath = PLR_PATH_DIRECT;
   L->workgroups = 0;
   L->wg_per_cu = 0;
-  L->run = 1;  // one tile per workgroup: the grid covers every tile
-  // XCD-contiguous order helped un-notified copies (+7%) and cost the reduce 1-8%
-  L->xcd_order = L->op == PLR_OP_COPY ? kXcdUnnotified : kXcdOff;
+  L->run = 1;  // one tile per workgroup (copies: set from the tile count below)
+  // XCD-contiguous order cost the reduce 1-8% and the copies at their policy run 0-7%
+  L->xcd_order = kXcdOff;
   // throughput regime: check first, so that stream-ordered producers cost no per-chunk
   // acquires; latency regime: wait inside the kernel (a check launch costs more)
   L->notify_mode = L->seg_len <= (2u << 20) ? PLR_NOTIFY_CHUNKS : PLR_NOTIFY_CHECK;
@@ -323,6 +325,11 @@ extern "C" int plr_layout_create(const plr_layout_desc* d, plr_layout** out) {
       L->nchunks = (uint32_t)chunks;
     }
   }
+  // copies: runs of 2 tiles once a call has 4096 tiles, as in check mode (measured
+  // without notification on 8 sources: AllGather and AllToAll of 8 x 64 MiB 166 us
+  // with runs of 2 against 184-189 us with 1, AllGatherV of 1 GiB 350 against 382 us;
+  // at 256 KiB per source one tile per workgroup is as fast or faster)
+  if (L->op == PLR_OP_COPY) L->run = L->ntiles >= 4096 ? 2 : 1;
   if (L->op == PLR_OP_COPY) {  // first flag of every source (segments go source by source)
     const size_t nseg = L->segs.size();
     L->src_flag0.assign(W + 1, 0);

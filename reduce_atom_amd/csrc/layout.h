@@ -52,7 +52,7 @@ struct plr_layout {
   int run;           // tiles per workgroup when neither of the above is set
   int run_notified;  // the same for notified calls (each workgroup pays one acquire per chunk)
   int notify_mode;   // PLR_NOTIFY_CHUNKS or PLR_NOTIFY_CHECK
-  int xcd_order;     // kXcdOff, kXcdOn, or kXcdUnnotified (on for calls without a workspace)
+  int xcd_order;     // kXcdOff or kXcdOn
   int lag;           // allreduce, composed: tiles between a workgroup's reduction and its gather
   int block;
   int unroll;
