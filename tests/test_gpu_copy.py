@@ -54,6 +54,32 @@ def test_notified(plr, oracle_mod, kind):
     assert np.array_equal(_run(plr, L, srcs, workspace=True), ref)
 
 
+def _sizes_around_run_switch(plr, kind, W=8):
+    """Per-source sizes whose layouts have just under 4096 tiles, exactly 4096 and just
+    over (all but the exact one with a ragged last tile)."""
+    q = 16 * W
+    lay = lambda B: plr.plr_layout_create("copy", "bf16", W, B, *PAIRS[kind])
+    exact = (1 << 20) * 4096 // lay(1 << 20).ntiles
+    assert lay(exact).ntiles == 4096, (kind, exact, lay(exact).ntiles)
+    below = exact - q
+    while lay(below).ntiles >= 4096:
+        below -= q
+    return [below - q, exact, exact + q]
+
+
+@pytest.mark.parametrize("kind", list(PAIRS))
+def test_policy_run_boundary(plr, oracle_mod, kind):
+    """Copies of 4096 tiles or more run two 2 KiB tiles per workgroup: both sides of the
+    switch, un-notified and notified."""
+    W = 8
+    for B in _sizes_around_run_switch(plr, kind, W):
+        srcs = [synth.bits_np(7, 4, s, B) for s in range(W)]
+        ref = oracle_mod.copy_layout(*PAIRS[kind], srcs)
+        L = plr.plr_layout_create("copy", "bf16", W, B, *PAIRS[kind])
+        assert np.array_equal(_run(plr, L, srcs), ref), (kind, B, L.ntiles)
+        assert np.array_equal(_run(plr, L, srcs, workspace=True), ref), (kind, B, L.ntiles)
+
+
 def test_explicit_offsets(plr, oracle_mod):
     W, B = 4, 4096
     srcs = [synth.bits_np(3, 4, s, 2 * B) for s in range(W)]
