@@ -37,9 +37,10 @@ inline void launch_dp(K kernel, dim3 grid, dim3 block, hipStream_t s, bool first
 // The dispatcher hands workgroup b to XCD b % 8 (MI355X has 8 XCDs, each with its
 // own L2). When `xcd` is set, logical workgroup ids are renumbered so that each XCD
 // runs one contiguous range of them: XCD x gets ids [x*q + min(x, r), ...) where
-// q, r = grid / 8, grid % 8. This is a bijection on [0, grid). Measured on MI355X:
-// reading 8 streams at once runs 10% faster when each XCD walks its own contiguous
-// part of every stream.
+// q, r = grid / 8, grid % 8. This is a bijection on [0, grid). Measured on MI355X: a
+// kernel that only reads 8 streams ran 10% faster this way, but the reduce and the
+// copies, which also write, ran 1-8% slower, so the layouts' policy leaves it off and
+// it stays an option (xcd_order).
 constexpr uint32_t kXcds = 8;
 
 __device__ __forceinline__ uint32_t logical_block(int xcd) {
