@@ -126,6 +126,9 @@ typedef struct {
    * copy:   one entry per segment in the derived segment order (source-major:
    *         W segments for AllGather / AllReduce gather, W*W for AllToAll with
    *         segment s*W + d); at most 64 segments; output segments must not overlap.
+   * With explicit in_offsets a source must hold every byte its segments read (offset
+   * plus length), which may reach past bytes_per_src; the library cannot see buffer
+   * sizes. A segment whose end would pass 2^64 - 1 is PLR_EINVAL.
    * The arrays are copied at creation; the caller keeps ownership. */
   const size_t* in_offsets;
   const size_t* out_offsets;
@@ -206,6 +209,7 @@ uint64_t plr_layout_epoch(const plr_layout* L);
  * one round-to-nearest-even into the element type at the end. Each output element
  * is produced by one lane, sources in order, so the result is bitwise repeatable.
  *   srcs      host array of W device pointers (source w = rank w), each bytes_per_src bytes
+ *             (with explicit in_offsets: up to the end of the bytes it reads)
  *   dst       device, plr_layout_dst_bytes(L) bytes; must not overlap any source share
  *   workspace device workspace of plr_layout_workspace_bytes(L), or NULL. When given,
  *             every chunk waits for flags[w][c] >= E+1 for all w (notify, section 3.2),
@@ -215,7 +219,8 @@ int plr_reduce(plr_layout* L, const void* const* srcs, void* dst, void* workspac
 
 /* Copy (section 3.1 "Layouts", section 3.3 "The Atom"): moves every segment of the
  * layout's table, bytes only (NaN payloads and any bit pattern are preserved).
- *   srcs      host array of W device pointers, each bytes_per_src bytes
+ *   srcs      host array of W device pointers, each bytes_per_src bytes (with explicit
+ *             in_offsets: up to the end of the bytes its segments read)
  *   dst       device, plr_layout_dst_bytes(L) bytes; must not overlap any source
  *   workspace as for plr_reduce; a chunk of a segment waits only for its own
  *             source's flag.

@@ -9,6 +9,8 @@
 // per-GPU table that callers may override.
 #include "layout.h"
 
+#include <string.h>
+
 #include <algorithm>
 #include <new>
 
@@ -83,24 +85,36 @@ static bool aligned16(uint64_t x) { return (x & 15) == 0; }
 extern "C" int plr_layout_create(const plr_layout_desc* d, plr_layout** out) {
   if (!d || !out) return PLR_EINVAL;
   *out = nullptr;
+  // A C caller may store any int in the enum-typed fields, and loading a value outside
+  // an enumeration's range through its type is undefined in C++: read them as ints.
+  static_assert(sizeof(plr_op) == sizeof(int) && sizeof(plr_dtype) == sizeof(int) &&
+                    sizeof(plr_layout_kind) == sizeof(int),
+                "the descriptor's enum fields are ints");
+  auto field = [](const void* p) {
+    int v;
+    memcpy(&v, p, sizeof v);
+    return v;
+  };
+  const int op = field(&d->op), dtype = field(&d->dtype);
+  const int in_kind = field(&d->in_kind), out_kind = field(&d->out_kind);
   if (d->world < 1) return PLR_EINVAL;
   if (d->world > PLR_MAX_WORLD) return PLR_EUNSUPPORTED;
   if (d->mode != PLR_MODE_DETERMINISTIC) return PLR_EUNSUPPORTED;
-  if (d->op != PLR_OP_REDUCE && d->op != PLR_OP_COPY && d->op != PLR_OP_ALLREDUCE) return PLR_EINVAL;
-  if (d->dtype != PLR_BF16 && d->dtype != PLR_F16 && d->dtype != PLR_F32) return PLR_EINVAL;
-  if (d->in_kind < PLR_PACKED || d->in_kind > PLR_TRANSPOSED) return PLR_EINVAL;
-  if (d->out_kind < PLR_PACKED || d->out_kind > PLR_TRANSPOSED) return PLR_EINVAL;
+  if (op != PLR_OP_REDUCE && op != PLR_OP_COPY && op != PLR_OP_ALLREDUCE) return PLR_EINVAL;
+  if (dtype != PLR_BF16 && dtype != PLR_F16 && dtype != PLR_F32) return PLR_EINVAL;
+  if (in_kind < PLR_PACKED || in_kind > PLR_TRANSPOSED) return PLR_EINVAL;
+  if (out_kind < PLR_PACKED || out_kind > PLR_TRANSPOSED) return PLR_EINVAL;
   if (!aligned16(d->bytes_per_src)) return PLR_EALIGN;
 
   plr_layout* L = new (std::nothrow) plr_layout();
   if (!L) return PLR_EINVAL;
-  L->op = d->op;
-  L->dtype = d->dtype;
+  L->op = (plr_op)op;
+  L->dtype = (plr_dtype)dtype;
   L->world = d->world;
   L->rank = d->rank;
   L->bytes_per_src = d->bytes_per_src;
-  L->in_kind = d->in_kind;
-  L->out_kind = d->out_kind;
+  L->in_kind = (plr_layout_kind)in_kind;
+  L->out_kind = (plr_layout_kind)out_kind;
   L->epoch = 0;
 
   const int W = d->world;
@@ -114,7 +128,7 @@ extern "C" int plr_layout_create(const plr_layout_desc* d, plr_layout** out) {
   const bool var = d->part_bytes != nullptr;
   std::vector<uint64_t> part(W, 0), part0(W + 1, 0);
   if (var) {
-    if (d->op == PLR_OP_ALLREDUCE) return fail(PLR_EINVAL);
+    if (op == PLR_OP_ALLREDUCE) return fail(PLR_EINVAL);
     for (int w = 0; w < W; ++w) {
       part[w] = d->part_bytes[w];
       if (!aligned16(part[w])) return fail(PLR_EALIGN);
@@ -124,14 +138,14 @@ extern "C" int plr_layout_create(const plr_layout_desc* d, plr_layout** out) {
   }
   L->var_segs = false;
 
-  if (d->op == PLR_OP_REDUCE) {
-    if (d->out_kind != PLR_PACKED || d->out_offsets) return fail(PLR_EINVAL);
+  if (op == PLR_OP_REDUCE) {
+    if (out_kind != PLR_PACKED || d->out_offsets) return fail(PLR_EINVAL);
     uint64_t share, off;
-    if (d->in_kind == PLR_PACKED) {
+    if (in_kind == PLR_PACKED) {
       if (var) return fail(PLR_EINVAL);  // partitions only make sense for a scattered input
       share = B;
       off = 0;
-    } else if (d->in_kind == PLR_SCATTERED) {
+    } else if (in_kind == PLR_SCATTERED) {
       if (d->rank < 0 || d->rank >= W) return fail(PLR_EINVAL);
       if (var) {  // ReduceScatterV: partition `rank` of every source
         share = part[d->rank];
@@ -147,19 +161,20 @@ extern "C" int plr_layout_create(const plr_layout_desc* d, plr_layout** out) {
     for (int w = 0; w < W; ++w) {
       const uint64_t o = d->in_offsets ? d->in_offsets[w] : off;
       if (!aligned16(o)) return fail(PLR_EALIGN);
+      if (o > ~0ull - share) return fail(PLR_EINVAL);  // the share's end would wrap around
       L->segs.push_back({w, o, 0, share});
     }
     L->seg_len = share;
     L->dst_bytes = share;
-  } else if (d->op == PLR_OP_ALLREDUCE) {
-    if (d->in_kind != PLR_SCATTERED || d->out_kind != PLR_SCATTERED) return fail(PLR_EINVAL);
+  } else if (op == PLR_OP_ALLREDUCE) {
+    if (in_kind != PLR_SCATTERED || out_kind != PLR_SCATTERED) return fail(PLR_EINVAL);
     if (d->in_offsets || d->out_offsets) return fail(PLR_EINVAL);
     if (B % (16ull * W)) return fail(PLR_EALIGN);
     for (int w = 0; w < W; ++w) L->segs.push_back({w, 0, 0, B});
     L->seg_len = B;
     L->dst_bytes = B;
   } else {
-    if (d->in_kind == PLR_PACKED && d->out_kind == PLR_PACKED && var) {  // AllGatherV
+    if (in_kind == PLR_PACKED && out_kind == PLR_PACKED && var) {  // AllGatherV
       uint64_t longest = 0;
       for (int s = 0; s < W; ++s) {
         L->segs.push_back({s, 0, part0[s], part[s]});
@@ -169,14 +184,14 @@ extern "C" int plr_layout_create(const plr_layout_desc* d, plr_layout** out) {
       L->var_segs = true;
     } else if (var) {
       return fail(PLR_EINVAL);  // the other copies have no variable-length form here
-    } else if (d->in_kind == PLR_PACKED && d->out_kind == PLR_PACKED) {  // AllGather
+    } else if (in_kind == PLR_PACKED && out_kind == PLR_PACKED) {  // AllGather
       for (int s = 0; s < W; ++s) L->segs.push_back({s, 0, (uint64_t)s * B, B});
       L->seg_len = B;
-    } else if (d->in_kind == PLR_SCATTERED &&
-               (d->out_kind == PLR_TRANSPOSED || d->out_kind == PLR_SCATTERED)) {
+    } else if (in_kind == PLR_SCATTERED &&
+               (out_kind == PLR_TRANSPOSED || out_kind == PLR_SCATTERED)) {
       if (B % (16ull * W)) return fail(PLR_EALIGN);
       const uint64_t t = B / W;
-      if (d->out_kind == PLR_TRANSPOSED) {  // AllToAll: out slice (d, s) = in slice (s, d)
+      if (out_kind == PLR_TRANSPOSED) {  // AllToAll: out slice (d, s) = in slice (s, d)
         for (int s = 0; s < W; ++s)
           for (int dd = 0; dd < W; ++dd)
             L->segs.push_back({s, (uint64_t)dd * t, ((uint64_t)dd * W + s) * t, t});
@@ -194,6 +209,8 @@ extern "C" int plr_layout_create(const plr_layout_desc* d, plr_layout** out) {
       if (d->in_offsets) L->segs[k].src_off = d->in_offsets[k];
       if (d->out_offsets) L->segs[k].dst_off = d->out_offsets[k];
       if (!aligned16(L->segs[k].src_off) || !aligned16(L->segs[k].dst_off)) return fail(PLR_EALIGN);
+      const uint64_t len = L->segs[k].len;  // no segment end may wrap around
+      if (L->segs[k].src_off > ~0ull - len || L->segs[k].dst_off > ~0ull - len) return fail(PLR_EINVAL);
     }
     // output segments must not overlap (two writers of one byte would race)
     std::vector<std::pair<uint64_t, uint64_t>> iv;
@@ -236,7 +253,7 @@ extern "C" int plr_layout_create(const plr_layout_desc* d, plr_layout** out) {
   if (d->datapath) {
     if (d->datapath != PLR_PATH_DIRECT && d->datapath != PLR_PATH_LDS && d->datapath != PLR_PATH_COMPOSED)
       return fail(PLR_EINVAL);
-    if ((d->datapath == PLR_PATH_COMPOSED) != (d->op == PLR_OP_ALLREDUCE && d->datapath != PLR_PATH_DIRECT))
+    if ((d->datapath == PLR_PATH_COMPOSED) != (op == PLR_OP_ALLREDUCE && d->datapath != PLR_PATH_DIRECT))
       return fail(PLR_EINVAL);  // composed is the AllReduce role split; AllReduce has no LDS path
     L->datapath = d->datapath;
     if (d->datapath == PLR_PATH_COMPOSED) {

@@ -157,7 +157,25 @@ def test_layout_errors(plr):
     assert _code(mk, "copy", "bf16", 2, 64, "packed", "packed", chunk_bytes=24) == plr.PLR_EALIGN
     assert _code(mk, "copy", "bf16", 2, 64, "packed", "packed", block=100) == plr.PLR_EINVAL
     assert _code(mk, "copy", "bf16", 2, 64, "packed", "packed", unroll=3) == plr.PLR_EINVAL
+    top = (1 << 64) - 16  # a segment that would end past 2^64 - 1
+    assert _code(mk, "reduce", "bf16", 2, 64, "packed", "packed", in_offsets=[0, top]) == plr.PLR_EINVAL
+    assert _code(mk, "copy", "bf16", 2, 64, "packed", "packed", in_offsets=[top, 0]) == plr.PLR_EINVAL
+    assert _code(mk, "copy", "bf16", 2, 64, "packed", "packed", out_offsets=[0, top]) == plr.PLR_EINVAL
     assert issubclass(E, RuntimeError)
+
+
+def test_layout_enum_fields_out_of_range(plr):
+    """A C caller may store any int in the descriptor's enum fields: out-of-range values
+    are PLR_EINVAL."""
+    import ctypes
+
+    for field, bad in [("op", -1), ("op", 3), ("dtype", 7), ("in_kind", -2), ("out_kind", 3)]:
+        d = plr.plr_layout_desc()
+        d.op, d.dtype, d.world, d.bytes_per_src = plr.PLR_OP_COPY, plr.PLR_BF16, 2, 64
+        setattr(d, field, bad)
+        h = ctypes.c_void_p()
+        assert plr._lib.plr_layout_create(ctypes.byref(d), ctypes.byref(h)) == plr.PLR_EINVAL, field
+        assert not h.value
 
 
 def test_call_validation_without_device(plr):
