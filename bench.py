@@ -55,10 +55,12 @@ KERNEL_NAMES = {"reduce": "k_reduce_direct", "allgather": "k_copy_direct",
 CSRC = os.path.join(ROOT, "reduce_atom_amd", "csrc")
 
 
-# the sources a kernel is compiled from: a counter summary taken on other text of
-# these files no longer describes the kernel
-OP_SOURCES = {"reduce": ("reduce.hip", "device_common.h"), "allgather": ("copy.hip", "device_common.h"),
-              "alltoall": ("copy.hip", "device_common.h"), "alltoallv": ("copy_v.hip", "device_common.h")}
+# the sources a kernel and its launch are built from (the kernel's own file, the shared
+# device code and argument blocks, and the host code that resolves its launch policy):
+# a counter summary taken on other text of these files no longer describes the kernel
+_HOST = ("device_common.h", "kernels.h", "layout.cpp", "api.cpp")
+OP_SOURCES = {"reduce": ("reduce.hip",) + _HOST, "allgather": ("copy.hip",) + _HOST,
+              "alltoall": ("copy.hip",) + _HOST, "alltoallv": ("copy_v.hip",) + _HOST}
 
 
 def source_hash(op: str) -> str:
