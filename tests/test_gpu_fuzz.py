@@ -1,8 +1,10 @@
 """Seeded random configurations of the whole boundary against the oracle: op and layout
 kind (reduce share, AllGather, AllToAll, AllReduce gather, AllGatherV, ReduceScatterV),
 W, element type, ragged sizes, policy overrides (tile, chunk, block, unroll, grid,
-XCD order, datapath) and notification (none, per-chunk waits, check first). Each case
-is small; a failure prints its configuration."""
+XCD order, datapath) and notification (none, per-chunk waits, check first). Most cases
+are small, one in ten has thousands of tiles; a failure prints its configuration."""
+import os
+
 import numpy as np
 import pytest
 import torch
@@ -12,6 +14,8 @@ from plrtest import assert_same, empty_dev, from_dev, to_dev
 
 pytestmark = pytest.mark.gpu
 
+# PLR_FUZZ_SCALE multiplies every seed count (a longer campaign; the default is 1)
+SCALE = int(os.environ.get("PLR_FUZZ_SCALE", "1"))
 KINDS = ["reduce_packed", "reduce_scattered", "allgather", "alltoall", "ar_gather", "agv", "rsv"]
 EB = {"bf16": 2, "f16": 2, "f32": 4}
 
@@ -58,13 +62,14 @@ def _sizes(rng, kind, W):
         if sum(parts) == 0:
             parts[0] = 16
         return sum(parts), parts
-    per = 16 * int(rng.integers(1, 3000))
+    large = rng.random() < 0.1  # now and then thousands of tiles (copies: runs of 2)
+    per = 16 * int(rng.integers(1, 131072 if large else 3000))
     if kind in ("reduce_scattered", "alltoall", "ar_gather"):
-        per = 16 * W * int(rng.integers(1, 300))
+        per = 16 * W * int(rng.integers(1, 16384 // W if large else 300))
     return per, None
 
 
-@pytest.mark.parametrize("seed", range(200))
+@pytest.mark.parametrize("seed", range(200 * SCALE))
 def test_fuzz(plr, oracle_mod, seed):
     rng = np.random.default_rng(1000 + seed)
     kind, W, dtype, pol, notify = _draw(rng)
@@ -118,7 +123,7 @@ def test_fuzz(plr, oracle_mod, seed):
             assert_same(dtype, got, ref.view(np.uint8), what)
 
 
-@pytest.mark.parametrize("seed", range(40))
+@pytest.mark.parametrize("seed", range(40 * SCALE))
 def test_fuzz_copy_v(plr, oracle_mod, seed):
     """Variable-length AllToAll: random W, rows per source (empty ones included), row
     sizes (16 B to 20 KiB, ragged against the 2 KiB scatter tile) and destination skews."""
@@ -148,7 +153,7 @@ def test_fuzz_copy_v(plr, oracle_mod, seed):
     assert np.array_equal(from_dev(dst)[:total * rb], ref), what
 
 
-@pytest.mark.parametrize("seed", range(30))
+@pytest.mark.parametrize("seed", range(30 * SCALE))
 def test_fuzz_allreduce(plr, oracle_mod, seed):
     """AllReduce into W outputs, fused and composed, random W, element type, size and tile."""
     rng = np.random.default_rng(7000 + seed)
