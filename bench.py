@@ -562,6 +562,136 @@ def run_v_sweep(args):
     return rows
 
 
+COLLECTIVES = ("ar", "a2a", "a2av", "ag", "agv", "rs", "rsv")
+
+
+def run_collective_sweep(args):
+    """The pages' per-collective microbenchmarks (testAR, testA2A, testA2AV, testAG,
+    testAGV, testRS, testRSV: minimum and maximum bytes, graph launches, runs, warmup,
+    seed) on one GPU's share of W = 8 ranks, sizes doubling from min to max. Size
+    convention of the pages' benchmarks: the output size for AllGather(V), the per-rank
+    input size for the others. Per size: `graph_launches` un-notified calls captured in
+    one HIP graph, `warmup` untimed replays, then `runs` replays each bracketed by
+    timing-only events; the time per call is the median replay over graph_launches.
+    algbw = page-convention bytes / time (the pages' figure); hbm = the share's
+    algorithmic HBM bytes (read + written) / time.
+      ar   AllReduce, fused: W sources of S bytes -> W outputs       hbm 2*W*S
+      a2a  AllToAll: W sources of S bytes (W tiles) -> W*S           hbm 2*W*S
+      a2av AllToAllV: W sources of S // row_bytes rows (row_bytes 14,336, or 256 when
+           S < 14,336), Zipf(1.1) destinations                    hbm 2*W*rows*row_bytes + 4*W*rows
+      ag   AllGather: W sources of S / W bytes -> S                  hbm 2*S
+      agv  AllGatherV: Zipf(s = 0.125) split of S -> S               hbm 2*S
+      rs   ReduceScatter share of rank 0: W x S / W bf16 -> S / W    hbm (W+1)*S/W
+      rsv  ReduceScatterV share of rank 0 (Zipf split of S)          hbm (W+1)*part_0"""
+    import torch
+
+    import reduce_atom_amd as plr
+    import synth
+
+    dev = torch.device("cuda:0")
+    names = COLLECTIVES if args.collective == "all" else (args.collective,)
+    E = TimingEvents(torch)
+    out = {}
+    for name in names:
+        smax = args.max_bytes
+        S_list = []
+        S = args.min_bytes
+        while S <= smax:
+            S_list.append(S)
+            S *= 2
+        # buffers at the largest size; smaller sizes use their leading bytes
+        if name in ("ar", "a2a", "rs", "a2av"):
+            srcs = [synth.bits_t(args.seed, 11, w, smax, device=dev) if name != "rs"
+                    else synth.normal_t(args.seed, 12, w, smax // 2, 1.0, device=dev).view(torch.uint8)
+                    for w in range(W)]
+        elif name == "ag":
+            srcs = [synth.bits_t(args.seed, 13, w, smax // W, device=dev) for w in range(W)]
+        elif name == "agv":
+            srcs = [synth.bits_t(args.seed, 14, w, p, device=dev) for w, p in enumerate(synth.zipf_split(smax, W))]
+        else:  # rsv
+            srcs = [synth.normal_t(args.seed, 15, w, smax // 2, 1.0, device=dev).view(torch.uint8) for w in range(W)]
+        if name == "ar":
+            dsts = [torch.empty(smax, dtype=torch.uint8, device=dev) for _ in range(W)]
+        elif name in ("a2a", "a2av"):
+            dst = torch.empty(W * smax, dtype=torch.uint8, device=dev)
+        elif name in ("ag", "agv"):
+            dst = torch.empty(smax, dtype=torch.uint8, device=dev)
+        else:
+            dst = torch.empty(smax, dtype=torch.uint8, device=dev)
+        if name == "a2av":
+            zp = synth.zipf_weights(1.1, W)
+            rmax = max(smax // 14336, smax // 256)
+            dests = [synth.categorical_t(args.seed, 16, w, rmax, zp, device=dev) for w in range(W)]
+            counts = torch.empty(W * W, dtype=torch.int64, device=dev)
+            offsets = torch.empty(W * W, dtype=torch.int64, device=dev)
+            scratch = torch.zeros(plr.plr_copy_v_scratch_bytes(W, [rmax] * W), dtype=torch.uint8, device=dev)
+        rows_out = []
+        for S in S_list:
+            if name == "ar":
+                L = plr.plr_layout_create("allreduce", "bf16", W, S, "scattered", "scattered")
+                call = lambda: plr.plr_allreduce(L, srcs, dsts)  # noqa: E731
+                page, hbm = S, 2 * W * S
+            elif name == "a2a":
+                L = plr.plr_layout_create("copy", "bf16", W, S, "scattered", "transposed")
+                call = lambda: plr.plr_copy(L, srcs, dst)  # noqa: E731
+                page, hbm = S, 2 * W * S
+            elif name == "a2av":
+                rb = 14336 if S >= 14336 else 256
+                rows = S // rb
+                call = lambda: plr.plr_copy_v(srcs, [rows] * W, dests, rb, dst, counts, offsets, scratch)  # noqa: E731
+                page, hbm = rows * rb, 2 * W * rows * rb + 4 * W * rows
+            elif name == "ag":
+                L = plr.plr_layout_create("copy", "bf16", W, S // W, "packed", "packed")
+                call = lambda: plr.plr_copy(L, srcs, dst)  # noqa: E731
+                page, hbm = S, 2 * S
+            elif name == "agv":
+                parts = synth.zipf_split(S, W)
+                L = plr.plr_layout_create("copy", "bf16", W, S, "packed", "packed", part_bytes=parts)
+                call = lambda: plr.plr_copy(L, srcs, dst)  # noqa: E731
+                page, hbm = S, 2 * S
+            elif name == "rs":
+                L = plr.plr_layout_create("reduce", "bf16", W, S, "scattered", "packed", rank=0)
+                call = lambda: plr.plr_reduce(L, srcs, dst)  # noqa: E731
+                page, hbm = S, (W + 1) * S // W
+            else:
+                parts = synth.zipf_split(S, W)
+                L = plr.plr_layout_create("reduce", "bf16", W, S, "scattered", "packed", rank=0, part_bytes=parts)
+                call = lambda: plr.plr_reduce(L, srcs, dst)  # noqa: E731
+                page, hbm = S, (W + 1) * parts[0]
+            call()
+            torch.cuda.synchronize()
+            graph = torch.cuda.CUDAGraph()
+            side = torch.cuda.Stream()
+            side.wait_stream(torch.cuda.current_stream())
+            with torch.cuda.stream(side):
+                with torch.cuda.graph(graph, stream=side):
+                    for _ in range(args.graph_launches):
+                        call()
+            torch.cuda.current_stream().wait_stream(side)
+            for _ in range(args.warmup):
+                graph.replay()
+            stream = torch.cuda.current_stream().cuda_stream
+            evs = [(E.create(), E.create()) for _ in range(args.runs)]
+            torch.cuda.synchronize()
+            for a, b in evs:
+                E.record(a, stream)
+                graph.replay()
+                E.record(b, stream)
+            torch.cuda.synchronize()
+            t = sorted(E.elapsed_ms(a, b) * 1e3 / args.graph_launches for a, b in evs)
+            us = t[len(t) // 2]
+            del graph
+            rows_out.append({"bytes": S, "page_bytes": page, "us": round(us, 2),
+                             "algbw_GB/s": round(page / us / 1e3, 1), "hbm_GB/s": round(hbm / us / 1e3, 1)})
+        out[name] = rows_out
+        print(f"collective sweep: {name} done ({len(rows_out)} sizes)", file=sys.stderr, flush=True)
+        del srcs
+        dst = dsts = None
+        torch.cuda.empty_cache()
+    E.destroy_all()
+    return out
+
+
 def run_atom_user_kernels(torch, srcs):
     """User kernels written on the device-callable Atom (include/plr_atom.h; built by
     build() into tests/libatom_kernels.so), timed with events around single launches:
@@ -675,6 +805,12 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--v-sweep", action="store_true",
                     help="only the AllGatherV / ReduceScatterV sweep over T = 1 KiB .. 1 GiB, as JSON")
+    ap.add_argument("--collective", choices=COLLECTIVES + ("all",),
+                    help="only the per-collective size sweep (the pages' testAR ... testRSV), as JSON")
+    ap.add_argument("--min-bytes", type=int, default=1 << 10)
+    ap.add_argument("--max-bytes", type=int, default=1 << 30)
+    ap.add_argument("--graph-launches", type=int, default=10)
+    ap.add_argument("--runs", type=int, default=20)
     ap.add_argument("--cpu-fraction", type=float, default=0.5)
     ap.add_argument("--cpu-reps", type=int, default=3)
     ap.add_argument("--summarize-trace", metavar="CSV",
@@ -714,6 +850,13 @@ def main():
         return
     if args.v_sweep:
         print(json.dumps({"v_sweep": run_v_sweep(args)}), flush=True)
+        return
+    if args.collective:
+        lo, hi = args.min_bytes, args.max_bytes
+        if lo < 16 * W * 8 or lo & (lo - 1) or hi < lo or hi & (hi - 1):
+            sys.exit("--min-bytes and --max-bytes must be powers of two, at least 1024")
+        print(json.dumps({"collective_sweep": run_collective_sweep(args), "graph_launches": args.graph_launches,
+                          "runs": args.runs, "warmup": args.warmup, "seed": args.seed}), flush=True)
         return
     if args.decode_only:
         import torch

@@ -12,6 +12,10 @@
 //            output row of the segment's first row bound there;
 //   kernel 2 (row tiles, one per workgroup step): moves every row with 16-byte loads
 //            and stores to that segment row plus the row's rank.
+// Small inputs (at most 64 segment counts) skip the last workgroup's scan: kernel 1
+// stops at the counts, and kernel 2 derives each tile's segment row from them with
+// one wave sum, and writes counts and offsets from one workgroup; that removes a
+// chain of dependent global round trips from the latency of small calls.
 #include <algorithm>
 
 #include "device_common.h"
@@ -42,10 +46,14 @@ __global__ void __launch_bounds__(kRankThreads) k_copy_v_rank(const CopyVArgs a)
   const int t = threadIdx.x;
   const int lane = t & 63, wave = t >> 6;
   const uint32_t seg = blockIdx.x;
+  // With no rows at all the launch still has one workgroup, which owns no segment and
+  // only writes the (zero) counts and offsets.
+  const bool has_seg = seg < a.seg_start[W];
   int s = 0;
-  while (seg >= a.seg_start[s + 1]) ++s;
-  const int64_t i = (int64_t)(seg - a.seg_start[s]) * kRankSeg + t;  // row within source s
-  const int64_t rows = a.row_start[s + 1] - a.row_start[s];
+  if (has_seg)
+    while (seg >= a.seg_start[s + 1]) ++s;
+  const int64_t i = has_seg ? (int64_t)(seg - a.seg_start[s]) * kRankSeg + t : 0;  // row within source s
+  const int64_t rows = has_seg ? a.row_start[s + 1] - a.row_start[s] : 0;
   const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));  // lanes < this one
 
   const int d = (i < rows) ? a.dest[s][i] : -1;
@@ -68,12 +76,14 @@ __global__ void __launch_bounds__(kRankThreads) k_copy_v_rank(const CopyVArgs a)
     }
     a.key[a.row_start[s] + i] = key;
   }
-  if (t < W) {
+  if (has_seg && t < W) {
     int c = 0;
     for (int w2 = 0; w2 < kRankWaves; ++w2) c += wave_cnt[w2][t];
     a.seg_count[(uint64_t)seg * W + t] = c;
   }
 
+  // small form: the scatter kernel reads the segment counts itself
+  if (a.small) return;
   // ticket: the last workgroup sees every segment's counts
   __syncthreads();
   if (t == 0) {
@@ -148,8 +158,63 @@ constexpr uint32_t kCvRun = PLR_CV_RUN;
 constexpr int kCvVecs = (int)(kCvTileBytes / 16 / kCvThreads);  // vectors per lane per tile
 static_assert(kCvTileBytes % (16 * kCvThreads) == 0, "a tile is whole vectors of every lane");
 
+// Small form (segments x W <= kSmallCounts): kernel 1 stopped after the segment counts.
+// Lane k of every wave keeps count k (segment k / W, destination k % W); the output row
+// of a tile's first row of segment g bound for d is then the sum of the counts of every
+// smaller destination plus those of d in earlier segments (segments go source by
+// source, so that is every row placed before it): one wave sum per tile. One extra
+// workgroup, with no tiles, writes counts and offsets from the same counts, so that
+// no tile waits for it.
+__device__ __forceinline__ int32_t wave_sum(int32_t x) {
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) x += __shfl_xor(x, off, 64);
+  return x;
+}
+
+__device__ void small_counts_and_offsets(const CopyVArgs& a, int32_t my_cnt) {
+  __shared__ int32_t cnt[kSmallCounts];
+  __shared__ int32_t tot[PLR_MAX_WORLD * PLR_MAX_WORLD];
+  const uint32_t W = a.world, n = a.seg_start[W] * W, WW = W * W;
+  if (threadIdx.x < kSmallCounts) cnt[threadIdx.x] = threadIdx.x < n ? my_cnt : 0;
+  __syncthreads();
+  for (uint32_t q = threadIdx.x; q < WW; q += blockDim.x) {  // q = (s, d): rows of s bound for d
+    const uint32_t s = q / W, d = q - s * W;
+    int32_t c = 0;
+    for (uint32_t g = a.seg_start[s]; g < a.seg_start[s + 1]; ++g) c += cnt[g * W + d];
+    tot[q] = c;
+    a.counts[q] = c;
+  }
+  __syncthreads();
+  for (uint32_t q = threadIdx.x; q < WW; q += blockDim.x) {
+    // q = (d, s): every row bound for a smaller destination, then the rows bound for d
+    // from smaller sources
+    const uint32_t d = q / W, s = q - d * W;
+    int64_t o = 0;
+    for (uint32_t dd = 0; dd < d; ++dd)
+      for (uint32_t ss = 0; ss < W; ++ss) o += tot[ss * W + dd];
+    for (uint32_t ss = 0; ss < s; ++ss) o += tot[ss * W + d];
+    a.offsets[q] = o;
+  }
+}
+
+template <bool kSmall>
 __global__ void __launch_bounds__(kCvThreads) k_copy_v_scatter(const CopyVArgs a) {
   const uint32_t W = a.world;
+  const uint32_t nsegs = a.seg_start[W];
+  int32_t my_cnt = 0;
+  uint32_t my_seg = 0, my_dest = 0;
+  if (kSmall) {
+    const uint32_t k = __lane_id();
+    if (k < nsegs * W) {
+      my_cnt = a.seg_count[k];
+      my_seg = k / W;
+      my_dest = k - my_seg * W;
+    }
+    if (blockIdx.x == gridDim.x - 1) {  // the extra column: no tiles
+      if (blockIdx.y == 0) small_counts_and_offsets(a, my_cnt);
+      return;
+    }
+  }
   // Written by kernel 1 and only read here, and the same for every lane of a tile:
   // read through the constant address space so that they are scalar loads, which
   // leave the vector memory path to the row's data.
@@ -179,16 +244,25 @@ __global__ void __launch_bounds__(kCvThreads) k_copy_v_scatter(const CopyVArgs a
       // (64 bytes), all before any of them is waited for.
       asm volatile("" ::: "memory");
       const uint32_t key = key_of[r0 + (int64_t)i];
-      const PLR_CONST int32_t* tp = seg_out + (seg0 + i / kRankSeg) * PLR_MAX_WORLD;
-      int32_t tab[PLR_MAX_WORLD];
+      const uint32_t g = seg0 + (uint32_t)(i / kRankSeg);
+      int32_t base = 0;
+      if (kSmall) {
+        asm volatile("" ::: "memory");
+        const uint32_t d = key >> 16;
+        if (d >= W) continue;  // not a destination: the row is dropped
+        base = wave_sum((my_dest < d || (my_dest == d && my_seg < g)) ? my_cnt : 0);
+      } else {
+        const PLR_CONST int32_t* tp = seg_out + g * PLR_MAX_WORLD;
+        int32_t tab[PLR_MAX_WORLD];
 #pragma unroll
-      for (int k = 0; k < PLR_MAX_WORLD; ++k) tab[k] = tp[k];
-      asm volatile("" ::: "memory");
-      const uint32_t d = key >> 16;
-      if (d >= W) continue;  // not a destination: the row is dropped
-      int32_t base = tab[0];
+        for (int k = 0; k < PLR_MAX_WORLD; ++k) tab[k] = tp[k];
+        asm volatile("" ::: "memory");
+        const uint32_t d = key >> 16;
+        if (d >= W) continue;  // not a destination: the row is dropped
+        base = tab[0];
 #pragma unroll
-      for (int k = 1; k < PLR_MAX_WORLD; ++k) base = (d == (uint32_t)k) ? tab[k] : base;
+        for (int k = 1; k < PLR_MAX_WORLD; ++k) base = (d == (uint32_t)k) ? tab[k] : base;
+      }
       const int64_t out = (int64_t)base + (key & 0xFFFFu);
       u32x4* dst = reinterpret_cast<u32x4*>(a.dst + (uint64_t)out * a.row_bytes + b0);
 #pragma unroll
@@ -204,6 +278,8 @@ hipError_t launch_copy_v(const CopyVArgs& args, hipStream_t s) {
   CopyVArgs a = args;
   a.tiles_per_row = (a.row_bytes + kCvTileBytes - 1) / kCvTileBytes;
   const uint32_t segs = a.seg_start[a.world];
+  a.small = (uint64_t)segs * a.world <= kSmallCounts;
+  if (a.small) a.xcd = 0;  // the extra column must stay the last workgroup of each row
   launch_dp(k_copy_v_rank, dim3(segs ? segs : 1), dim3(kRankThreads), s, true, false, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
@@ -213,7 +289,10 @@ hipError_t launch_copy_v(const CopyVArgs& args, hipStream_t s) {
   for (uint32_t w = 0; w < a.world; ++w) most = std::max<int64_t>(most, a.row_start[w + 1] - a.row_start[w]);
   const uint64_t groups = ((uint64_t)most * a.tiles_per_row + kCvRun - 1) / kCvRun;
   const uint32_t gx = (uint32_t)(groups < 1 ? 1 : (groups > (1u << 22) ? (1u << 22) : groups));
-  launch_dp(k_copy_v_scatter, dim3(gx, a.world), dim3(kCvThreads), s, false, true, a);
+  if (a.small)  // one more column: the workgroup that writes counts and offsets
+    launch_dp(k_copy_v_scatter<true>, dim3(gx + 1, a.world), dim3(kCvThreads), s, false, true, a);
+  else
+    launch_dp(k_copy_v_scatter<false>, dim3(gx, a.world), dim3(kCvThreads), s, false, true, a);
   return hipGetLastError();
 }
 

@@ -128,7 +128,10 @@ struct CopyVArgs {
   uint64_t tiles_per_row;  // scatter tiles per row (the kernel's tile size)
   uint32_t world;
   uint32_t xcd;      // XCD-aware workgroup order (scatter)
+  uint32_t small;    // at most kSmallCounts segment counts: no ticket; the scatter derives
+                     // the segments' output rows, counts and offsets from the counts itself
 };
+constexpr uint32_t kSmallCounts = 64;  // segments x W of the small form (one per lane of a wave)
 
 // AllReduce of W contributions into W outputs. The share of every output is cut into
 // W slices (slice r belongs to rank r) and each slice into tiles.

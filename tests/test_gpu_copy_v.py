@@ -141,3 +141,24 @@ def test_scratch_reused_across_calls(plr, oracle_mod):
         assert np.array_equal(offsets.cpu().numpy().reshape(W, W), ro)
         assert np.array_equal(dst.cpu().numpy()[:total * rb], ref)
         assert int(scratch[:4].view(torch.int32).item()) == 0
+
+
+@pytest.mark.parametrize("W", [1, 8, 16])
+def test_all_sources_empty(plr, oracle_mod, W):
+    """No rows anywhere: counts and offsets come back zero and nothing is moved."""
+    srcs = [np.zeros(16, np.uint8) for _ in range(W)]
+    dests = [np.zeros(0, np.int32) for _ in range(W)]
+    out, c, o = _run(plr, srcs, dests, 16)
+    assert out.size == 0 and not c.any() and not o.any()
+
+
+@pytest.mark.parametrize("W,rows", [(8, [1024] * 8), (8, [1025] + [1024] * 7), (4, [4096] * 4),
+                                    (4, [4096] * 3 + [4097]), (2, [1, 0]), (16, [3] * 4 + [0] * 12)])
+def test_small_and_ticket_forms(plr, oracle_mod, W, rows):
+    """Both sides of the switch between the small form (at most 64 segment counts, the
+    scatter derives the output rows from the counts) and the ticket form (the last rank
+    workgroup scans them)."""
+    p = synth.zipf_weights(1.1, W)
+    dests = [synth.categorical_np(W, 9, s, rows[s], p) for s in range(W)]
+    srcs = [synth.bits_np(W, 10, s, max(rows[s], 1) * 64) for s in range(W)]
+    _check(plr, oracle_mod, srcs, dests, 64)
