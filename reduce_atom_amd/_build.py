@@ -90,6 +90,23 @@ def build_user_kernels(src: str, out: str) -> str:
     return out
 
 
+def build_host_program(src: str, out: str) -> str:
+    """Compile a host-only C program that calls the C ABI of include/plr.h and links
+    libplr.so (found next to the program through its run path) and the HIP runtime.
+    Always rebuilds."""
+    cc = os.environ.get("PLR_CC", "/opt/rocm/llvm/bin/clang")
+    rel = os.path.relpath(PKG, os.path.dirname(os.path.abspath(out)))
+    tmp = out + ".tmp"
+    cmd = [cc, "-std=c11", "-O2", "-Wall", "-Wextra", "-D__HIP_PLATFORM_AMD__", "-I/opt/rocm/include",
+           "-I", os.path.join(ROOT, "include"), src, "-L", PKG, "-lplr", "-L/opt/rocm/lib", "-lamdhip64",
+           f"-Wl,-rpath,$ORIGIN/{rel}", "-Wl,-rpath,/opt/rocm/lib", "-o", tmp]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"compiling {src} failed:\n{r.stderr}")
+    os.replace(tmp, out)
+    return out
+
+
 def clean() -> None:
     shutil.rmtree(BUILD, ignore_errors=True)
 
