@@ -824,6 +824,8 @@ def main():
                     help="only run torch's plain device copy of 1 GiB five times (the reference "
                          "for scaling HBM byte counters)")
     args = ap.parse_args()
+    if args.steps < 1 or args.warmup < 0 or args.runs < 1 or args.graph_launches < 1:
+        sys.exit("--steps, --runs and --graph-launches must be at least 1, --warmup at least 0")
     if args.gpus != 1:
         sys.exit(f"bench.py runs on one GPU only (got --gpus {args.gpus}): this datapath holds the W "
                  "contributions of one GPU's share in that GPU's memory and uses no second GPU.")
