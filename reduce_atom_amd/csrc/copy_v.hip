@@ -12,7 +12,7 @@
 //            output row of the segment's first row bound there;
 //   kernel 2 (row tiles, one per workgroup step): moves every row with 16-byte loads
 //            and stores to that segment row plus the row's rank.
-// Small inputs (at most 64 segment counts) skip the last workgroup's scan: kernel 1
+// Calls with at most 256 segment counts skip the last workgroup's scan: kernel 1
 // stops at the counts, and kernel 2 derives each tile's segment row from them with
 // one wave sum, and writes counts and offsets from one workgroup; that removes a
 // chain of dependent global round trips from the latency of small calls.
@@ -159,23 +159,26 @@ constexpr int kCvVecs = (int)(kCvTileBytes / 16 / kCvThreads);  // vectors per l
 static_assert(kCvTileBytes % (16 * kCvThreads) == 0, "a tile is whole vectors of every lane");
 
 // Small form (segments x W <= kSmallCounts): kernel 1 stopped after the segment counts.
-// Lane k of every wave keeps count k (segment k / W, destination k % W); the output row
-// of a tile's first row of segment g bound for d is then the sum of the counts of every
-// smaller destination plus those of d in earlier segments (segments go source by
-// source, so that is every row placed before it): one wave sum per tile. One extra
-// workgroup, with no tiles, writes counts and offsets from the same counts, so that
-// no tile waits for it.
+// Lane k of every wave keeps CPL of them (counts k*CPL .. k*CPL+CPL-1; count c is
+// segment c / W, destination c % W); the output row of a tile's first row of segment g
+// bound for d is the sum of the counts of every smaller destination plus those of d in
+// earlier segments (segments go source by source, so that is every row placed before
+// it): one wave sum per tile. One extra workgroup, with no tiles, writes counts and
+// offsets from the same counts, so that no tile waits for it.
 __device__ __forceinline__ int32_t wave_sum(int32_t x) {
 #pragma unroll
   for (int off = 32; off > 0; off >>= 1) x += __shfl_xor(x, off, 64);
   return x;
 }
 
-__device__ void small_counts_and_offsets(const CopyVArgs& a, int32_t my_cnt) {
-  __shared__ int32_t cnt[kSmallCounts];
+template <int CPL>
+__device__ void small_counts_and_offsets(const CopyVArgs& a, const int32_t (&my_cnt)[CPL]) {
+  __shared__ int32_t cnt[64 * CPL];
   __shared__ int32_t tot[PLR_MAX_WORLD * PLR_MAX_WORLD];
-  const uint32_t W = a.world, n = a.seg_start[W] * W, WW = W * W;
-  if (threadIdx.x < kSmallCounts) cnt[threadIdx.x] = threadIdx.x < n ? my_cnt : 0;
+  const uint32_t W = a.world, WW = W * W;
+  if (threadIdx.x < 64)
+#pragma unroll
+    for (int j = 0; j < CPL; ++j) cnt[threadIdx.x * CPL + j] = my_cnt[j];  // zero past the counts
   __syncthreads();
   for (uint32_t q = threadIdx.x; q < WW; q += blockDim.x) {  // q = (s, d): rows of s bound for d
     const uint32_t s = q / W, d = q - s * W;
@@ -197,21 +200,29 @@ __device__ void small_counts_and_offsets(const CopyVArgs& a, int32_t my_cnt) {
   }
 }
 
-template <bool kSmall>
+// CPL = counts per lane of the small form; 0 = the ticket form (segment table).
+template <int CPL>
 __global__ void __launch_bounds__(kCvThreads) k_copy_v_scatter(const CopyVArgs a) {
+  constexpr int C = CPL > 0 ? CPL : 1;
   const uint32_t W = a.world;
-  const uint32_t nsegs = a.seg_start[W];
-  int32_t my_cnt = 0;
-  uint32_t my_seg = 0, my_dest = 0;
-  if (kSmall) {
-    const uint32_t k = __lane_id();
-    if (k < nsegs * W) {
-      my_cnt = a.seg_count[k];
-      my_seg = k / W;
-      my_dest = k - my_seg * W;
+  int32_t my_cnt[C];
+  uint32_t my_seg[C], my_dest[C];
+  if (CPL > 0) {
+    const uint32_t n = a.seg_start[W] * W, k0 = __lane_id() * CPL;
+    if (CPL == 4 && k0 + 3 < n) {  // one 16-byte load (the count region is 256-byte aligned)
+      const int4 v = *reinterpret_cast<const int4*>(a.seg_count + k0);
+      my_cnt[0] = v.x, my_cnt[1 % C] = v.y, my_cnt[2 % C] = v.z, my_cnt[3 % C] = v.w;
+    } else {
+#pragma unroll
+      for (int j = 0; j < C; ++j) my_cnt[j] = k0 + j < n ? a.seg_count[k0 + j] : 0;
+    }
+#pragma unroll
+    for (int j = 0; j < C; ++j) {
+      my_seg[j] = (k0 + j) / W;
+      my_dest[j] = k0 + j - my_seg[j] * W;
     }
     if (blockIdx.x == gridDim.x - 1) {  // the extra column: no tiles
-      if (blockIdx.y == 0) small_counts_and_offsets(a, my_cnt);
+      if (blockIdx.y == 0) small_counts_and_offsets<C>(a, my_cnt);
       return;
     }
   }
@@ -246,11 +257,14 @@ __global__ void __launch_bounds__(kCvThreads) k_copy_v_scatter(const CopyVArgs a
       const uint32_t key = key_of[r0 + (int64_t)i];
       const uint32_t g = seg0 + (uint32_t)(i / kRankSeg);
       int32_t base = 0;
-      if (kSmall) {
+      if (CPL > 0) {
         asm volatile("" ::: "memory");
         const uint32_t d = key >> 16;
         if (d >= W) continue;  // not a destination: the row is dropped
-        base = wave_sum((my_dest < d || (my_dest == d && my_seg < g)) ? my_cnt : 0);
+        int32_t part = 0;
+#pragma unroll
+        for (int j = 0; j < C; ++j) part += (my_dest[j] < d || (my_dest[j] == d && my_seg[j] < g)) ? my_cnt[j] : 0;
+        base = wave_sum(part);
       } else {
         const PLR_CONST int32_t* tp = seg_out + g * PLR_MAX_WORLD;
         int32_t tab[PLR_MAX_WORLD];
@@ -278,7 +292,9 @@ hipError_t launch_copy_v(const CopyVArgs& args, hipStream_t s) {
   CopyVArgs a = args;
   a.tiles_per_row = (a.row_bytes + kCvTileBytes - 1) / kCvTileBytes;
   const uint32_t segs = a.seg_start[a.world];
-  a.small = (uint64_t)segs * a.world <= kSmallCounts;
+  const uint64_t n = (uint64_t)segs * a.world;
+  const int cpl = n <= 64 ? 1 : (n <= kSmallCounts ? 4 : 0);
+  a.small = cpl > 0;
   if (a.small) a.xcd = 0;  // the extra column must stay the last workgroup of each row
   launch_dp(k_copy_v_rank, dim3(segs ? segs : 1), dim3(kRankThreads), s, true, false, a);
   hipError_t e = hipGetLastError();
@@ -289,10 +305,13 @@ hipError_t launch_copy_v(const CopyVArgs& args, hipStream_t s) {
   for (uint32_t w = 0; w < a.world; ++w) most = std::max<int64_t>(most, a.row_start[w + 1] - a.row_start[w]);
   const uint64_t groups = ((uint64_t)most * a.tiles_per_row + kCvRun - 1) / kCvRun;
   const uint32_t gx = (uint32_t)(groups < 1 ? 1 : (groups > (1u << 22) ? (1u << 22) : groups));
-  if (a.small)  // one more column: the workgroup that writes counts and offsets
-    launch_dp(k_copy_v_scatter<true>, dim3(gx + 1, a.world), dim3(kCvThreads), s, false, true, a);
+  // the small forms have one more column: the workgroup that writes counts and offsets
+  if (cpl == 1)
+    launch_dp(k_copy_v_scatter<1>, dim3(gx + 1, a.world), dim3(kCvThreads), s, false, true, a);
+  else if (cpl == 4)
+    launch_dp(k_copy_v_scatter<4>, dim3(gx + 1, a.world), dim3(kCvThreads), s, false, true, a);
   else
-    launch_dp(k_copy_v_scatter<false>, dim3(gx, a.world), dim3(kCvThreads), s, false, true, a);
+    launch_dp(k_copy_v_scatter<0>, dim3(gx, a.world), dim3(kCvThreads), s, false, true, a);
   return hipGetLastError();
 }
 

@@ -131,7 +131,7 @@ struct CopyVArgs {
   uint32_t small;    // at most kSmallCounts segment counts: no ticket; the scatter derives
                      // the segments' output rows, counts and offsets from the counts itself
 };
-constexpr uint32_t kSmallCounts = 64;  // segments x W of the small form (one per lane of a wave)
+constexpr uint32_t kSmallCounts = 256;  // segments x W of the small form (4 per lane of a wave)
 
 // AllReduce of W contributions into W outputs. The share of every output is cut into
 // W slices (slice r belongs to rank r) and each slice into tiles.
