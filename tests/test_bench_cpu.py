@@ -1,0 +1,88 @@
+"""Host-side checks of the measurement code in bench.py (no GPU): the kernel-trace and
+counter summaries it writes into profiles/, the HBM-traffic scaling against the
+calibration copy, the source hash that voids a stale counter summary, and the
+command-line contract."""
+import csv
+import os
+import subprocess
+import sys
+
+import pytest
+
+from conftest import ROOT
+
+sys.path.insert(0, ROOT)
+import bench  # noqa: E402
+
+
+def _write_csv(path, fields, rows):
+    with open(path, "w", newline="") as f:
+        w = csv.DictWriter(f, fieldnames=fields)
+        w.writeheader()
+        for r in rows:
+            w.writerow(r)
+
+
+def test_summarize_trace_groups_by_kernel_and_shape(tmp_path):
+    fields = ["Kernel_Name", "Grid_Size_X", "Workgroup_Size_X", "Start_Timestamp", "End_Timestamp"]
+    rows = [{"Kernel_Name": "void plr::k_copy_direct<1>(plr::CopyArgs)", "Grid_Size_X": 1024,
+             "Workgroup_Size_X": 128, "Start_Timestamp": 1000 * k, "End_Timestamp": 1000 * k + d}
+            for k, d in enumerate([3000, 1000, 2000])]
+    rows.append({"Kernel_Name": "void plr::k_copy_direct<1>(plr::CopyArgs)", "Grid_Size_X": 2048,
+                 "Workgroup_Size_X": 128, "Start_Timestamp": 0, "End_Timestamp": 5000})
+    rows.append({"Kernel_Name": "some_other_kernel", "Grid_Size_X": 1, "Workgroup_Size_X": 1,
+                 "Start_Timestamp": 0, "End_Timestamp": 1})
+    p = tmp_path / "t.csv"
+    _write_csv(p, fields, rows)
+    lines = bench.summarize_trace(str(p)).splitlines()
+    assert len(lines) == 3 and "some_other" not in "".join(lines)
+    f = lines[1].split()
+    assert f[-7] == "1024" and f[-5] == "3"  # grid, calls
+    assert [float(v) for v in f[-4:]] == [2.0, 2.0, 3.0, 1.0]  # avg, p50, p90, min (us)
+    assert lines[2].split()[-4] == "5.00"
+
+
+def test_counter_profiles_scale_by_the_calibration_copy(tmp_path, monkeypatch):
+    fields = ["Kernel_Name", "Grid_Size", "Counter_Name", "Counter_Value"]
+    names = {op: k for op, (k, _) in bench.OP_KERNELS.items()}
+    fetch, write = tmp_path / "f.csv", tmp_path / "w.csv"
+    _write_csv(fetch, fields, [{"Kernel_Name": names[op] + "(x)", "Grid_Size": 1, "Counter_Name": "FETCH_SIZE",
+                                "Counter_Value": 1000.0 * (i + 1)} for i, op in enumerate(names)])
+    _write_csv(write, fields, [{"Kernel_Name": names[op] + "(x)", "Grid_Size": 1, "Counter_Name": "WRITE_SIZE",
+                                "Counter_Value": 100.0 * (i + 1)} for i, op in enumerate(names)])
+    cal_f, cal_w = tmp_path / "cf.csv", tmp_path / "cw.csv"
+    kib = (1 << 30) // 1024
+    _write_csv(cal_f, fields, [{"Kernel_Name": "__amd_rocclr_copyBuffer", "Grid_Size": 1, "Counter_Name": "FETCH_SIZE",
+                                "Counter_Value": kib / 2}])
+    _write_csv(cal_w, fields, [{"Kernel_Name": "__amd_rocclr_copyBuffer", "Grid_Size": 1, "Counter_Name": "WRITE_SIZE",
+                                "Counter_Value": kib}])
+    out = tmp_path / "profiles"
+    out.mkdir()
+    bench.write_counter_profiles(str(fetch), str(write), str(cal_f), str(cal_w), str(out))
+    monkeypatch.setattr(bench, "ROOT", str(tmp_path))
+    for op in names:
+        # fetch counts half of a copy's reads (scale 2), write counts all of its writes (scale
+        # 1); ops that launch the same kernel (allgather, alltoall) share its mean
+        same = [i for i, o in enumerate(names) if names[o] == names[op]]
+        f = sum(1000.0 * (i + 1) for i in same) / len(same)
+        w = sum(100.0 * (i + 1) for i in same) / len(same)
+        assert bench.counters_traffic(op) == pytest.approx((2 * f + w) * 1024), op
+    # a summary taken on other sources is void
+    p = out / "reduce_counters.txt"
+    p.write_text(p.read_text().replace(bench.source_hash("reduce"), "0" * 16))
+    assert bench.counters_traffic("reduce") is None
+
+
+def test_source_hash_covers_kernel_and_launch_code():
+    for op, files in bench.OP_SOURCES.items():
+        assert {"device_common.h", "kernels.h", "layout.cpp", "api.cpp"} <= set(files)
+        assert any(f.endswith(".hip") for f in files)
+        assert len(bench.source_hash(op)) == 16
+
+
+@pytest.mark.parametrize("args,msg", [(["--gpus", "2"], "one GPU only"), (["--steps", "0"], "at least 1"),
+                                      (["--collective", "ag", "--min-bytes", "100"], "powers of two")])
+def test_command_line_contract(args, msg):
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), *args], capture_output=True, text=True,
+                       timeout=120)
+    assert r.returncode != 0 and msg in r.stderr, (r.returncode, r.stderr)
