@@ -12,10 +12,11 @@
 //            output row of the segment's first row bound there;
 //   kernel 2 (row tiles, one per workgroup step): moves every row with 16-byte loads
 //            and stores to that segment row plus the row's rank.
-// Calls with at most 256 segment counts skip the last workgroup's scan: kernel 1
-// stops at the counts, and kernel 2 derives each tile's segment row from them with
-// one wave sum, and writes counts and offsets from one workgroup; that removes a
-// chain of dependent global round trips from the latency of small calls.
+// Calls with at most 256 segment counts (segments x W) skip the last workgroup's
+// scan: kernel 1 stops at the counts, and kernel 2 derives each tile's segment row from
+// them with one wave sum and writes counts and offsets from one extra workgroup; that
+// removes a chain of dependent global round trips (release, ticket, acquire, loads)
+// from every such call.
 #include <algorithm>
 
 #include "device_common.h"
