@@ -433,7 +433,9 @@ def run_next(args):
     variable-length collectives of appendix C.4 over 8 ranks with Zipf(s = 0.125)
     partitions of a total T: AllGatherV (8 contributions -> T bytes) and the largest
     ReduceScatterV share (rank 0: 8 contributions of T bytes, bf16, N(0, 1)), at
-    T = 1 GiB (bandwidth) and T = 2 MiB (the size of the pages' largest gain)."""
+    T = 1 GiB (bandwidth) and T = 2 MiB (the size of the pages' largest gain); the
+    LDS-staged pipeline beside the direct path at the step's reduce and AllGather; and
+    the Atom user kernels."""
     import torch
 
     import reduce_atom_amd as plr
@@ -473,6 +475,29 @@ def run_next(args):
         out[name] = {"avg_us": round(us, 2), "GB/s": round(algo / (us * 1e-6) / 1e9, 1),
                      "algorithmic_bytes": algo}
     del dsts
+    # the LDS-staged pipeline (PLR_PATH_LDS) at the step's reduce and AllGather shapes,
+    # notified as in the step, beside the direct path the policy uses
+    rdst = torch.empty(R3 * C3, dtype=torch.bfloat16, device=dev)
+    csrc = [synth.bits_t(args.seed, 4, s, B4, device=dev) for s in range(W)]
+    cdst = torch.empty(W * B4, dtype=torch.uint8, device=dev)
+    for name, make, call, algo in (
+            ("reduce", lambda p: plr.plr_layout_create("reduce", "bf16", W, R3 * C3 * 2, "packed", "packed", datapath=p),
+             lambda L, ws: plr.plr_reduce(L, srcs, rdst, ws), BYTES["reduce"]),
+            ("allgather", lambda p: plr.plr_layout_create("copy", "bf16", W, B4, "packed", "packed", datapath=p),
+             lambda L, ws: plr.plr_copy(L, csrc, cdst, ws), BYTES["allgather"])):
+        for tag, path in (("lds", plr.PLR_PATH_LDS), ("direct", plr.PLR_PATH_DIRECT)):
+            L = make(path)
+            ws = torch.zeros(L.workspace_bytes, dtype=torch.uint8, device=dev)
+
+            def notified(L=L, ws=ws):
+                plr.plr_notify(L, -1, ws)
+                call(L, ws)
+            us = _time_calls(torch, plr, notified)
+            if plr.plr_check(L, ws) != plr.PLR_OK:
+                raise RuntimeError(f"{name} {tag}: device error")
+            out[f"{name}_{tag}_path"] = {"avg_us": round(us, 2), "GB/s": round(algo / (us * 1e-6) / 1e9, 1),
+                                          "algorithmic_bytes": algo}
+    del rdst, csrc, cdst
     out.update(run_atom_user_kernels(torch, srcs))
     del srcs
     torch.cuda.empty_cache()

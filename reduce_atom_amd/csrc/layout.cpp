@@ -263,10 +263,14 @@ extern "C" int plr_layout_create(const plr_layout_desc* d, plr_layout** out) {
   }
   if (L->var_segs && L->datapath == PLR_PATH_LDS) return fail(PLR_EUNSUPPORTED);
   if (L->datapath == PLR_PATH_LDS) {
-    // the staged pipeline runs 256-thread workgroups over 4 KiB slabs per source
+    // the staged pipeline runs 256-thread workgroups over 4 KiB slabs per source; a
+    // ring only pipelines across the slabs of one workgroup, so each streams a run of
+    // them: 8 workgroups per CU was the best grid measured (reduce and AllGather of the
+    // 8 x 117 MB / 8 x 64 MiB shapes; one slab per workgroup was 15-20% slower)
     if (d->block && d->block != 256) return fail(PLR_EINVAL);
     L->block = 256;
     if (!d->tile_bytes && L->tile_bytes % 4096) L->tile_bytes = 4096;
+    if (!d->workgroups) L->wg_per_cu = 8;
   }
   L->spin_limit = d->spin_limit ? d->spin_limit : kDefaultSpinLimit;
   if (d->xcd_order) {
