@@ -140,7 +140,9 @@ typedef struct {
   int workgroups;             /* grid size; each workgroup then consumes a run of
                                  ceil(tiles / workgroups) consecutive tiles */
   int block;                  /* threads per workgroup: 64, 128, 256 or 512 */
-  int unroll;                 /* 16-byte vectors per lane per pipeline step: 1, 2 or 4 */
+  int unroll;                 /* 16-byte vectors per lane per pipeline step: 1, 2 or 4 (a reduce
+                                 with W >= 15 takes at most 2: 4 x W vectors would not fit the
+                                 registers; plr_layout_policy reports the value used) */
   int stages;                 /* reserved (the LDS ring depth is fixed per W: 4, 3 or 2 stages) */
   int datapath;               /* PLR_PATH_POLICY, PLR_PATH_DIRECT or PLR_PATH_LDS; the LDS path
                                  needs 256-thread workgroups and tiles of whole 4 KiB slabs */

@@ -32,7 +32,8 @@
  *
  * Policy (section 4.2 "Codesign Policies and Tuning": applications may define their
  * own): THREADS (64, 128, 256 or 512) and UNROLL (16-byte vectors per lane in flight
- * per source, 1, 2 or 4). The library's measured gfx950 choice for streaming shares is
+ * per source, 1, 2 or 4; a reduce holds UNROLL x W vectors per lane, and beyond about 56
+ * of them, e.g. UNROLL 4 with W >= 15, the compiler spills registers). The library's measured gfx950 choice for streaming shares is
  * 128 threads, 1 vector, one 2 KiB slice per workgroup and a grid that covers the data.
  */
 #pragma once

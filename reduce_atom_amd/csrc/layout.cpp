@@ -246,6 +246,9 @@ extern "C" int plr_layout_create(const plr_layout_desc* d, plr_layout** out) {
     if (d->unroll != 1 && d->unroll != 2 && d->unroll != 4) return fail(PLR_EINVAL);
     L->unroll = d->unroll;
   }
+  // a reduce lane holds unroll x W vectors at once: 4 x 15 or 4 x 16 no longer fit the
+  // registers (the compiler spills them), so those take 2 vectors per lane
+  if (L->op == PLR_OP_REDUCE && L->unroll * W > 56) L->unroll = 2;
   if (d->stages) {
     if (d->stages < 1 || d->stages > 4) return fail(PLR_EINVAL);
     L->stages = d->stages;

@@ -365,3 +365,13 @@ def test_one_hip_runtime_whatever_the_import_order(plr):
     assert out.returncode == 0, out.stderr
     paths = eval(out.stdout.strip().splitlines()[-1])
     assert len(paths) == 1, paths
+
+
+def test_reduce_unroll_fits_the_registers(plr):
+    """A reduce lane holds unroll x W vectors: four per source is kept up to W = 14 and
+    becomes two from W = 15 (4 x 15 vectors would spill)."""
+    for W, want in [(1, 4), (8, 4), (14, 4), (15, 2), (16, 2)]:
+        L = plr.plr_layout_create("reduce", "bf16", W, 16 * W * 64, "packed", "packed", unroll=4)
+        assert L.policy()["unroll"] == want, W
+    C = plr.plr_layout_create("copy", "bf16", 16, 16 * 64, "packed", "packed", unroll=4)
+    assert C.policy()["unroll"] == 4
