@@ -437,8 +437,9 @@ def run_next(args):
     partitions of a total T: AllGatherV (8 contributions -> T bytes) and the largest
     ReduceScatterV share (rank 0: 8 contributions of T bytes, bf16, N(0, 1)), at
     T = 1 GiB (bandwidth) and T = 2 MiB (the size of the pages' largest gain); the
-    LDS-staged pipeline beside the direct path at the step's reduce and AllGather; and
-    the Atom user kernels."""
+    LDS-staged pipeline beside the direct path at the step's reduce and AllGather; the
+    HIP runtime's own device-to-device copy of the same 512 MiB; and the Atom user
+    kernels."""
     import torch
 
     import reduce_atom_amd as plr
@@ -500,7 +501,28 @@ def run_next(args):
                 raise RuntimeError(f"{name} {tag}: device error")
             out[f"{name}_{tag}_path"] = {"avg_us": round(us, 2), "GB/s": round(algo / (us * 1e-6) / 1e9, 1),
                                           "algorithmic_bytes": algo}
-    del rdst, csrc, cdst
+    # the HIP runtime's own device-to-device copy (torch's copy_ of one contiguous
+    # buffer: hipMemcpyAsync) of the step AllGather's 512 MiB, as an anchor for what a
+    # plain copy reaches on this machine; events on the stream the copy runs on
+    E = TimingEvents(torch)
+    flat = torch.cat([c.view(-1) for c in csrc])
+    st = torch.cuda.current_stream().cuda_stream
+    for _ in range(3):
+        cdst.copy_(flat)
+    torch.cuda.synchronize()
+    evs = [(E.create(), E.create()) for _ in range(10)]
+    for a, b in evs:
+        E.record(a, st)
+        cdst.copy_(flat)
+        E.record(b, st)
+    torch.cuda.synchronize()
+    us = statistics.mean(E.elapsed_ms(a, b) for a, b in evs) * 1e3
+    E.destroy_all()
+    if not torch.equal(cdst, flat):
+        raise RuntimeError("runtime copy: wrong result")
+    out["runtime_copy_512MiB"] = {"avg_us": round(us, 2), "GB/s": round(BYTES["allgather"] / (us * 1e-6) / 1e9, 1),
+                                  "algorithmic_bytes": BYTES["allgather"]}
+    del rdst, csrc, cdst, flat
     out.update(run_atom_user_kernels(torch, srcs))
     del srcs
     torch.cuda.empty_cache()
