@@ -4,7 +4,6 @@
 #include <hip/hip_runtime_api.h>
 
 #include <algorithm>
-#include <atomic>
 
 #include "kernels.h"
 #include "layout.h"
@@ -28,27 +27,11 @@ bool overlaps(uintptr_t a0, uint64_t alen, uintptr_t b0, uint64_t blen) {
   return alen && blen && a0 < b0 + blen && b0 < a0 + alen;
 }
 
-// Compute units of the current device, cached per device id.
-std::atomic<int> g_cu_cache[64];
-
-int cu_count() {
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-  int v = g_cu_cache[dev].load(std::memory_order_relaxed);
-  if (v > 0) return v;
-  int n = 0;
-  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
-    n = 256;
-  g_cu_cache[dev].store(n, std::memory_order_relaxed);
-  return n;
-}
-
-// Tiles per workgroup: the policy's run, or what an explicit (or per-compute-unit)
-// workgroup count implies; the grid then covers every tile once.
+// Tiles per workgroup: the policy's run, or what an explicit workgroup count implies;
+// the grid then covers every tile once.
 uint32_t run_for(const plr_layout* L, bool notified) {
   uint64_t g = 0;
   if (L->workgroups > 0) g = (uint64_t)L->workgroups;
-  else if (L->wg_per_cu > 0) g = (uint64_t)cu_count() * L->wg_per_cu;
   if (g == 0) return (uint32_t)std::max(1, notified ? L->run_notified : L->run);
   return (uint32_t)std::max<uint64_t>(1, (L->ntiles + g - 1) / g);
 }

@@ -94,7 +94,6 @@ __device__ __forceinline__ void copy_tile_addr(const CopyArgs& a, uint32_t t, ui
 // through a private LDS ring (global->LDS DMA), waits only for the oldest, reads it
 // back and stores it at the layout's destination. Chunk flags are awaited before the
 // first DMA of a chunk.
-constexpr int kCopyStages = 8;
 
 __global__ void __launch_bounds__(256) k_copy_lds(const CopyArgs a) {
   __shared__ u32x4 ring[4][kCopyStages][64];

@@ -34,10 +34,9 @@ size_t elem_bytes(plr_dtype t) { return t == PLR_F32 ? 4 : 2; }
 constexpr uint64_t kCus = 256;  // compute units of an MI355X (the composed AllReduce's tiles)
 
 static void default_policy(plr_layout* L) {
-  L->stages = 2;
+  L->stages = 0;  // no ring on the direct path
   L->datapath = PLR_PATH_DIRECT;
   L->workgroups = 0;
-  L->wg_per_cu = 0;
   L->run = 1;  // one tile per workgroup (copies: set from the tile count below)
   // XCD-contiguous order cost the reduce 1-8% and the copies at their policy run 0-7%
   L->xcd_order = kXcdOff;
@@ -266,14 +265,19 @@ extern "C" int plr_layout_create(const plr_layout_desc* d, plr_layout** out) {
   }
   if (L->var_segs && L->datapath == PLR_PATH_LDS) return fail(PLR_EUNSUPPORTED);
   if (L->datapath == PLR_PATH_LDS) {
-    // the staged pipeline runs 256-thread workgroups over 4 KiB slabs per source; a
-    // ring only pipelines across the slabs of one workgroup, so each streams a run of
-    // them: 8 workgroups per CU was the best grid measured (reduce and AllGather of the
-    // 8 x 117 MB / 8 x 64 MiB shapes; one slab per workgroup was 15-20% slower)
+    // the staged pipeline runs 256-thread workgroups over 4 KiB slabs per source, and a
+    // ring only pipelines across the slabs of one workgroup. Measured on the 8 x 117 MB
+    // reduce and the 8 x 64 MiB AllGather, runs of about one ring are fastest: the
+    // reduce (3 stages) at 4 slabs per workgroup, 184 us against 196 us at 8 workgroups
+    // per CU (14 slabs) and 190 us at 3 slabs; the copy (8 stages) at 8 slabs, 178 us
+    // against 209 us at 8 workgroups per CU (64 slabs), 194 us at 4 and 200 us at 16
     if (d->block && d->block != 256) return fail(PLR_EINVAL);
     L->block = 256;
     if (!d->tile_bytes && L->tile_bytes % 4096) L->tile_bytes = 4096;
-    if (!d->workgroups) L->wg_per_cu = 8;
+    L->stages = op == PLR_OP_REDUCE ? lds_reduce_stages(W) : kCopyStages;
+    const int slabs = op == PLR_OP_REDUCE ? L->stages + 1 : L->stages;
+    const uint64_t per_tile = L->tile_bytes / 4096 ? L->tile_bytes / 4096 : 1;
+    L->run = L->run_notified = (int)std::max<uint64_t>(1, (uint64_t)slabs / per_tile);
   }
   L->spin_limit = d->spin_limit ? d->spin_limit : kDefaultSpinLimit;
   if (d->xcd_order) {
@@ -286,7 +290,8 @@ extern "C" int plr_layout_create(const plr_layout_desc* d, plr_layout** out) {
   }
   // in check mode only chunks still missing at check time pay a wait and a fence, so
   // notified calls can use shorter runs (measured: reduce 1, copy 2)
-  if (L->notify_mode == PLR_NOTIFY_CHECK) L->run_notified = L->op == PLR_OP_REDUCE ? 1 : 2;
+  if (L->notify_mode == PLR_NOTIFY_CHECK && L->datapath != PLR_PATH_LDS)
+    L->run_notified = L->op == PLR_OP_REDUCE ? 1 : 2;
 
   // tile and chunk tables; a chunk is a whole number of tiles of one segment
   if (L->op == PLR_OP_ALLREDUCE) {  // tiles of the W slices; one flag per tile
@@ -353,7 +358,7 @@ extern "C" int plr_layout_create(const plr_layout_desc* d, plr_layout** out) {
   // without notification on 8 sources: AllGather and AllToAll of 8 x 64 MiB 166 us
   // with runs of 2 against 184-189 us with 1, AllGatherV of 1 GiB 350 against 382 us;
   // at 256 KiB per source one tile per workgroup is as fast or faster)
-  if (L->op == PLR_OP_COPY) L->run = L->ntiles >= 4096 ? 2 : 1;
+  if (L->op == PLR_OP_COPY && L->datapath != PLR_PATH_LDS) L->run = L->ntiles >= 4096 ? 2 : 1;
   if (L->op == PLR_OP_COPY) {  // first flag of every source (segments go source by source)
     const size_t nseg = L->segs.size();
     L->src_flag0.assign(W + 1, 0);

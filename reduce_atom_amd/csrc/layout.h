@@ -48,8 +48,7 @@ struct plr_layout {
 
   // resolved policy (section 4.2 "Codesign Policies and Tuning")
   int workgroups;  // explicit grid size, or 0
-  int wg_per_cu;   // grid = compute units * wg_per_cu when workgroups == 0 and this is > 0
-  int run;           // tiles per workgroup when neither of the above is set
+  int run;           // tiles per workgroup when workgroups is 0
   int run_notified;  // the same for notified calls (each workgroup pays one acquire per chunk)
   int notify_mode;   // PLR_NOTIFY_CHUNKS or PLR_NOTIFY_CHECK
   int xcd_order;     // kXcdOff or kXcdOn

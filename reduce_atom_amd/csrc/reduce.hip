@@ -62,7 +62,7 @@ __global__ void __launch_bounds__(512) k_reduce_direct(const ReduceArgs a) {
 // before the first DMA into a new chunk.
 template <int W>
 struct LdsRing {
-  static constexpr int S = W <= 4 ? 4 : (W <= 8 ? 3 : 2);  // stages; S*W*4 KiB <= 128 KiB
+  static constexpr int S = lds_reduce_stages(W);  // S*W*4 KiB <= 128 KiB
 };
 
 template <int DT, int W>
