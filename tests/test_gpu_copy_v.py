@@ -155,11 +155,13 @@ def test_all_sources_empty(plr, oracle_mod, W):
 @pytest.mark.parametrize("W,rows", [(8, [1024] * 8), (8, [1025] + [1024] * 7), (4, [4096] * 4),
                                     (4, [4096] * 3 + [4097]), (2, [1, 0]), (16, [3] * 4 + [0] * 12),
                                     (8, [4096] * 8), (8, [4097] + [4096] * 7), (16, [1024] * 16),
-                                    (16, [1025] + [1024] * 15), (3, [40000, 0, 3])])
+                                    (16, [1025] + [1024] * 15), (3, [40000, 0, 3]), (8, [8192] * 8),
+                                    (8, [8193] + [8192] * 7), (16, [2048] * 16), (16, [2049] + [2048] * 15)])
 def test_small_and_ticket_forms(plr, oracle_mod, W, rows):
     """Both sides of each switch between the small forms (at most 64 segment counts, one
     per lane; at most 256, four per lane: the scatter derives the output rows from the
-    counts) and the ticket form (the last rank workgroup scans them)."""
+    counts) and the ticket form (the last rank workgroup scans them), and the ticket form
+    at 512 segment counts and beyond."""
     p = synth.zipf_weights(1.1, W)
     dests = [synth.categorical_np(W, 9, s, rows[s], p) for s in range(W)]
     srcs = [synth.bits_np(W, 10, s, max(rows[s], 1) * 64) for s in range(W)]
