@@ -141,9 +141,10 @@ __global__ void __launch_bounds__(kRankThreads) k_copy_v_rank(const CopyVArgs a)
 // source (grid row y = source y), one 16-byte vector per lane per step, so that the
 // chip holds many short workgroups with their loads in flight, as the copy kernel
 // does. A tile's source address and the locations of its row's key and segment table
-// depend only on the row, so all of its loads are issued together; the output row is
-// then the segment table's entry for the key's destination plus the key's rank, with
-// no second dependent load.
+// depend only on the row, so a workgroup issues the data loads of its whole run, then
+// the keys and tables, computes each output row (the segment table's entry for the
+// key's destination plus the key's rank, with no second dependent load) and stores
+// last.
 #ifndef PLR_CV_TILE_BYTES
 #define PLR_CV_TILE_BYTES 2048
 #endif
@@ -252,52 +253,75 @@ __global__ void __launch_bounds__(kCvThreads) k_copy_v_scatter(const CopyVArgs a
   const uint32_t seg0 = a.seg_start[s];
   const uint64_t stride = (uint64_t)gridDim.x * kCvRun;
   for (uint64_t t0 = (uint64_t)logical_block(a.xcd) * kCvRun; t0 < ntiles; t0 += stride) {
-    const uint64_t t1 = min(t0 + kCvRun, ntiles);
-    for (uint64_t t = t0; t < t1; ++t) {
-      const uint64_t i = (ntiles >> 32) ? t / a.tiles_per_row : (uint32_t)t / (uint32_t)a.tiles_per_row;
-      const uint64_t b0 = (t - i * a.tiles_per_row) * kCvTileBytes;
-      const uint64_t nv = (min(b0 + kCvTileBytes, a.row_bytes) - b0) >> 4;
-      const u32x4* src = reinterpret_cast<const u32x4*>(src_s + i * a.row_bytes + b0);
-      u32x4 x[kCvVecs];
+    const uint32_t m = (uint32_t)min<uint64_t>(kCvRun, ntiles - t0);  // tiles of this run
+    // Every data load of the run is issued first, then every key and segment table, and
+    // the stores come last: no store of one tile sits between the next tile's loads or
+    // its output-row arithmetic and the registers they reuse (which would make them wait
+    // for the store), and all of the run's bytes are in flight at once.
+    // Straight-line code for every run: a tile past the run's end repeats its last tile's
+    // row with no vectors, so it loads and stores nothing.
+    uint64_t row[kCvRun], b0[kCvRun], nv[kCvRun];
+    u32x4 x[kCvRun][kCvVecs];
+#pragma unroll
+    for (uint32_t k = 0; k < kCvRun; ++k) {
+      const uint64_t t = t0 + min(k, m - 1);
+      row[k] = (ntiles >> 32) ? t / a.tiles_per_row : (uint32_t)t / (uint32_t)a.tiles_per_row;
+      b0[k] = (t - row[k] * a.tiles_per_row) * kCvTileBytes;
+      nv[k] = k < m ? (min(b0[k] + kCvTileBytes, a.row_bytes) - b0[k]) >> 4 : 0;
+      const u32x4* src = reinterpret_cast<const u32x4*>(src_s + row[k] * a.row_bytes + b0[k]);
 #pragma unroll
       for (int u = 0; u < kCvVecs; ++u) {
         const uint64_t v = (uint64_t)u * kCvThreads + threadIdx.x;
-        if (v < nv) x[u] = ld16(src + v);
-      }
-      // The row's data loads are issued first, then its key and its segment's table
-      // (64 bytes), all before any of them is waited for.
-      asm volatile("" ::: "memory");
-      const uint32_t key = key_of[r0 + (int64_t)i];
-      const uint32_t g = seg0 + (uint32_t)(i / kRankSeg);
-      int32_t base = 0;
-      if (CPL > 0) {
-        asm volatile("" ::: "memory");
-        const uint32_t d = key >> 16;
-        if (d >= W) continue;  // not a destination: the row is dropped
-        int32_t part = 0;
-#pragma unroll
-        for (int j = 0; j < C; ++j) part += (my_dest[j] < d || (my_dest[j] == d && my_seg[j] < g)) ? my_cnt[j] : 0;
-        base = wave_sum(part);
-      } else {
-        const PLR_CONST int32_t* tp = seg_out + g * PLR_MAX_WORLD;
-        int32_t tab[PLR_MAX_WORLD];
-#pragma unroll
-        for (int k = 0; k < PLR_MAX_WORLD; ++k) tab[k] = tp[k];
-        asm volatile("" ::: "memory");
-        const uint32_t d = key >> 16;
-        if (d >= W) continue;  // not a destination: the row is dropped
-        base = tab[0];
-#pragma unroll
-        for (int k = 1; k < PLR_MAX_WORLD; ++k) base = (d == (uint32_t)k) ? tab[k] : base;
-      }
-      const int64_t out = (int64_t)base + (key & 0xFFFFu);
-      u32x4* dst = reinterpret_cast<u32x4*>(a.dst + (uint64_t)out * a.row_bytes + b0);
-#pragma unroll
-      for (int u = 0; u < kCvVecs; ++u) {
-        const uint64_t v = (uint64_t)u * kCvThreads + threadIdx.x;
-        if (v < nv) st16(dst + v, x[u]);
+        if (v < nv[k]) x[k][u] = ld16(src + v);
       }
     }
+    asm volatile("" ::: "memory");
+    uint32_t key[kCvRun], g[kCvRun];
+    int32_t tab[kCvRun][PLR_MAX_WORLD];
+#pragma unroll
+    for (uint32_t k = 0; k < kCvRun; ++k) {
+      key[k] = key_of[r0 + (int64_t)row[k]];
+      g[k] = seg0 + (uint32_t)(row[k] / kRankSeg);
+      if (CPL == 0) {
+        const PLR_CONST int32_t* tp = seg_out + g[k] * PLR_MAX_WORLD;
+#pragma unroll
+        for (int e = 0; e < PLR_MAX_WORLD; ++e) tab[k][e] = tp[e];
+      }
+    }
+    asm volatile("" ::: "memory");
+    int64_t out[kCvRun];  // output row of each tile's row; -1: the row is dropped
+#pragma unroll
+    for (uint32_t k = 0; k < kCvRun; ++k) {
+      // branch-free, so that nothing here waits on the loads in flight
+      const uint32_t d = key[k] >> 16;  // >= W: not a destination, the row is dropped
+      int32_t base;
+      if (CPL > 0) {
+        int32_t part = 0;
+#pragma unroll
+        for (int j = 0; j < C; ++j)
+          part += ((my_dest[j] < d) | ((my_dest[j] == d) & (my_seg[j] < g[k]))) ? my_cnt[j] : 0;
+        base = wave_sum(part);
+      } else {
+        base = tab[k][0];
+#pragma unroll
+        for (int e = 1; e < PLR_MAX_WORLD; ++e) base = (d == (uint32_t)e) ? tab[k][e] : base;
+      }
+      out[k] = d < W ? (int64_t)base + (key[k] & 0xFFFFu) : -1;
+    }
+#pragma unroll
+    for (uint32_t k = 0; k < kCvRun; ++k) {
+      if (out[k] < 0) continue;
+      u32x4* dst = reinterpret_cast<u32x4*>(a.dst + (uint64_t)out[k] * a.row_bytes + b0[k]);
+#pragma unroll
+      for (int u = 0; u < kCvVecs; ++u) {
+        const uint64_t v = (uint64_t)u * kCvThreads + threadIdx.x;
+        if (v < nv[k]) st16(dst + v, x[k][u]);
+      }
+    }
+    // Only calls of more than 2^22 runs per source take another turn of this loop; the
+    // wait keeps its stores from holding registers the next turn's loads and arithmetic
+    // reuse (which would put waits for the whole memory queue between them).
+    wait_vmem<0>();
   }
 }
 
