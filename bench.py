@@ -278,12 +278,13 @@ def run_bench(args):
             if name in L:
                 plr.plr_notify(L[name], -1, ws[name])
             if events is not None:
-                # the library records this pair right around the op's datapath kernels
-                # (after a notified call's check kernel), on the stream they run on
-                plr.plr_set_timing_events(*events[name])
+                # the library records these around the op's datapath kernels (after a
+                # notified call's check kernel), on the stream they run on: start and end
+                # of the first dispatch and of the last (the same one for one kernel)
+                plr.plr_set_timing_events_split(*events[name])
             op(name)
         if events is not None:
-            plr.plr_set_timing_events()
+            plr.plr_set_timing_events_split()
 
     for _ in range(args.warmup):
         step()
@@ -295,10 +296,17 @@ def run_bench(args):
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     ms_per_step = (t1 - t0) * 1e3 / args.steps
-    # (2) the same K steps again, every op's datapath kernels carrying a pair of
-    # timing-only events (the kernel-only duration that a kernel trace also reports)
+    # (2) the same K steps again, every op's datapath kernels carrying timing-only events:
+    # the kernel-only duration that a kernel trace also reports. AllToAllV runs two
+    # kernels, timed each on its own and summed (an event on the first dispatch delays
+    # the second by about 4 us, which is not the op's time)
     E = TimingEvents(torch)
-    ev = [{n: (E.create(), E.create()) for n in ops} for _ in range(args.steps)]
+    ev = [{n: (E.create(), E.create(), E.create(), E.create()) for n in ops} for _ in range(args.steps)]
+
+    def op_ms(n, e):
+        if n == "alltoallv":
+            return E.elapsed_ms(e[0], e[1]) + E.elapsed_ms(e[2], e[3])
+        return E.elapsed_ms(e[0], e[3])
     torch.cuda.synchronize()
     t2 = time.perf_counter()
     for k in range(args.steps):
@@ -310,8 +318,8 @@ def run_bench(args):
         if rc != plr.PLR_OK:
             raise RuntimeError(f"{name}: device error {plr.plr_strerror(rc)}")
     ms_per_step_events = (t3 - t2) * 1e3 / args.steps
-    per_op_us = {n: statistics.mean(E.elapsed_ms(*e[n]) for e in ev) * 1e3 for n in ops}
-    per_op_p50 = {n: statistics.median(E.elapsed_ms(*e[n]) for e in ev) * 1e3 for n in ops}
+    per_op_us = {n: statistics.mean(op_ms(n, e[n]) for e in ev) * 1e3 for n in ops}
+    per_op_p50 = {n: statistics.median(op_ms(n, e[n]) for e in ev) * 1e3 for n in ops}
     E.destroy_all()
     step_bytes = sum(BYTES.values())
     value = step_bytes / (ms_per_step * 1e-3) / 1e9

@@ -149,8 +149,9 @@ typedef struct {
   int datapath;               /* PLR_PATH_POLICY, PLR_PATH_DIRECT or PLR_PATH_LDS; the LDS path
                                  needs 256-thread workgroups and tiles of whole 4 KiB slabs */
   uint64_t spin_limit;        /* polls of a chunk flag before PLR_ETIMEOUT; 0 = default (about a second) */
-  int notify_mode;            /* PLR_NOTIFY_POLICY (check first for shares over 2 MiB, in-kernel
-                                 waits below), PLR_NOTIFY_CHUNKS or PLR_NOTIFY_CHECK */
+  int notify_mode;            /* PLR_NOTIFY_POLICY (check first when some source contributes over
+                                 2 MiB, in-kernel waits otherwise), PLR_NOTIFY_CHUNKS or
+                                 PLR_NOTIFY_CHECK */
   int xcd_order;              /* 0 = policy (off), 1 = on, 2 = off: renumber workgroups so that each
                                  of the 8 XCDs walks one contiguous range of tiles */
   /* Variable-length layouts: W partition sizes in bytes (multiples of 16, zero allowed)
@@ -327,6 +328,15 @@ int plr_check(plr_layout* L, void* workspace, void* stream);
  * thread and is not for calls captured into a graph. Errors: PLR_EINVAL if exactly one
  * of the two is NULL. */
 int plr_set_timing_events(void* before, void* after);
+
+/* Measurement aid, as plr_set_timing_events, for calls of two datapath kernels (the
+ * variable-length AllToAll's rank and scatter kernels): the first dispatch carries
+ * `before` and `first_after` as its start and end events, the last carries
+ * `last_before` and `after`, so the two durations can be summed without the time
+ * between the dispatches (timing the first dispatch delays the next one). A call of one
+ * datapath kernel records only `before` and `after` on it. Errors: PLR_EINVAL unless
+ * all four are NULL (off) or none is. */
+int plr_set_timing_events_split(void* before, void* first_after, void* last_before, void* after);
 
 /* Static text for an error code. */
 const char* plr_strerror(int code);

@@ -103,6 +103,8 @@ _lib.plr_check.argtypes = [_vp, _vp, _vp]
 _lib.plr_check.restype = _i
 _lib.plr_set_timing_events.argtypes = [_vp, _vp]
 _lib.plr_set_timing_events.restype = _i
+_lib.plr_set_timing_events_split.argtypes = [_vp, _vp, _vp, _vp]
+_lib.plr_set_timing_events_split.restype = _i
 _lib.plr_strerror.argtypes = [_i]
 _lib.plr_strerror.restype = _c.c_char_p
 _lib.plr_last_hip_error.argtypes = []
@@ -115,7 +117,8 @@ EXPORTS = [
     "plr_layout_nchunks", "plr_layout_ntiles", "plr_layout_nsegments", "plr_layout_segment", "plr_layout_policy",
     "plr_layout_epoch", "plr_reduce", "plr_copy", "plr_allreduce", "plr_copy_v", "plr_copy_v_scratch_bytes",
     "plr_layout_packet_bytes", "plr_pack", "plr_reduce_packets",
-    "plr_notify", "plr_check", "plr_set_timing_events", "plr_strerror", "plr_last_hip_error",
+    "plr_notify", "plr_check", "plr_set_timing_events", "plr_set_timing_events_split", "plr_strerror",
+    "plr_last_hip_error",
     "plr_version",
 ]
 
@@ -323,6 +326,13 @@ def plr_set_timing_events(before=None, after=None) -> None:
         return e.cuda_event
 
     _ok(_lib.plr_set_timing_events(handle(before), handle(after)), "plr_set_timing_events")
+
+
+def plr_set_timing_events_split(before=None, first_after=None, last_before=None, after=None) -> None:
+    """Four raw hipEvent_t handles (int): the first datapath dispatch of this thread's
+    next calls carries before / first_after, the last carries last_before / after. No
+    arguments turns it off."""
+    _ok(_lib.plr_set_timing_events_split(before, first_after, last_before, after), "plr_set_timing_events_split")
 
 
 def plr_check(layout: Layout, workspace, stream=None) -> int:

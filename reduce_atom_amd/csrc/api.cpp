@@ -14,7 +14,7 @@ namespace {
 
 thread_local int g_last_hip = 0;
 
-thread_local Timing g_timing = {nullptr, nullptr};
+thread_local Timing g_timing = {nullptr, nullptr, nullptr, nullptr};
 
 int hip_fail(hipError_t e) {
   g_last_hip = (int)e;
@@ -415,8 +415,15 @@ extern "C" int plr_check(plr_layout* L, void* workspace, void* stream) {
 
 extern "C" int plr_set_timing_events(void* before, void* after) {
   if ((before == nullptr) != (after == nullptr)) return PLR_EINVAL;
-  g_timing.start = static_cast<hipEvent_t>(before);
-  g_timing.stop = static_cast<hipEvent_t>(after);
+  g_timing = Timing{static_cast<hipEvent_t>(before), static_cast<hipEvent_t>(after), nullptr, nullptr};
+  return PLR_OK;
+}
+
+extern "C" int plr_set_timing_events_split(void* before, void* first_after, void* last_before, void* after) {
+  const int set = (before != nullptr) + (first_after != nullptr) + (last_before != nullptr) + (after != nullptr);
+  if (set != 0 && set != 4) return PLR_EINVAL;
+  g_timing = Timing{static_cast<hipEvent_t>(before), static_cast<hipEvent_t>(after),
+                    static_cast<hipEvent_t>(first_after), static_cast<hipEvent_t>(last_before)};
   return PLR_OK;
 }
 

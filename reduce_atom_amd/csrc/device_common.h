@@ -20,12 +20,13 @@ using atom::combine;
 using atom::Elems;
 
 // Launch of a datapath kernel: `first` / `last` say whether it opens / closes the
-// call's datapath, which decides whether it carries the thread's timing events.
+// call's datapath, which decides which of the thread's timing events it carries.
 template <typename K, typename... A>
 inline void launch_dp(K kernel, dim3 grid, dim3 block, hipStream_t s, bool first, bool last, A... args) {
   const Timing& t = timing();
-  hipExtLaunchKernelGGL(kernel, grid, block, 0, s, first ? t.start : nullptr, last ? t.stop : nullptr, 0,
-                        args...);
+  hipEvent_t a = first ? t.start : (last ? t.last_start : nullptr);
+  hipEvent_t b = last ? t.stop : (first ? t.first_stop : nullptr);
+  hipExtLaunchKernelGGL(kernel, grid, block, 0, s, a, b, 0, args...);
 }
 
 // Constant address space: loads through such a pointer that are the same for every

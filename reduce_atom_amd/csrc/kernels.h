@@ -186,8 +186,10 @@ struct NotifyArgs {
 // the dispatch's own start and end timestamps (hipExtLaunchKernel), so that the pair
 // times the datapath kernels alone, like a kernel trace.
 struct Timing {
-  hipEvent_t start;
-  hipEvent_t stop;
+  hipEvent_t start;        // start of the first datapath dispatch
+  hipEvent_t stop;         // end of the last
+  hipEvent_t first_stop;   // end of the first, when it is not also the last (or null)
+  hipEvent_t last_start;   // start of the last, when it is not also the first (or null)
 };
 const Timing& timing();
 

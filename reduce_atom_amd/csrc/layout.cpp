@@ -23,10 +23,10 @@ size_t elem_bytes(plr_dtype t) { return t == PLR_F32 ? 4 : 2; }
 // gfx950 policy table (measured on MI355X with 8 x 117 MB bf16 reduces and 512 MiB
 // copies): the best streaming rate comes from short steps per workgroup and a grid
 // that covers every tile, so the dispatcher walks the whole chip through memory front
-// to back, in plain workgroup order; 16-byte non-temporal loads and stores. Tiles:
-// 2 KiB per source for the reduce and the copies (128 threads, one vector per lane per
-// source); a reduce workgroup takes one tile, a copy workgroup two once a call has
-// 4096 tiles (8 MiB) or more. Flags cover 256 KiB chunks (16 KiB for decode-size
+// to back, in plain workgroup order; 16-byte non-temporal loads and stores. Tiles of
+// 128 threads: 2 KiB per source for the reduce (one vector per lane per source), one
+// per workgroup; 4 KiB for copies of segments over 2 MiB, one per workgroup, else
+// 2 KiB, two per workgroup once a call has 4096 tiles (8 MiB) or more. Flags cover 256 KiB chunks (16 KiB for decode-size
 // shares). With in-kernel waits a notified workgroup pays one agent-scope acquire per
 // chunk it enters, and those acquires invalidate L2 lines, so such calls give each
 // workgroup a run of 2 (reduce) or 4 (copy) tiles; decode-size shares (at most 2 MiB)
@@ -41,11 +41,13 @@ static void default_policy(plr_layout* L) {
   // XCD-contiguous order cost the reduce 1-8% and the copies at their policy run 0-7%
   L->xcd_order = kXcdOff;
   // throughput regime: check first, so that stream-ordered producers cost no per-chunk
-  // acquires; latency regime: wait inside the kernel (a check launch costs more)
-  L->notify_mode = L->seg_len <= (2u << 20) ? PLR_NOTIFY_CHUNKS : PLR_NOTIFY_CHECK;
+  // acquires; latency regime (at most 2 MiB from any source): wait inside the kernel (a
+  // check launch costs more). Judged by the bytes per source, not per segment: a
+  // notified AllToAll of 8 x 4 MiB (512 KiB slices) took 42.5 us with in-kernel waits.
+  L->notify_mode = L->src_bytes <= (2u << 20) ? PLR_NOTIFY_CHUNKS : PLR_NOTIFY_CHECK;
   L->run_notified = L->op == PLR_OP_REDUCE ? 2 : 4;
   if (L->op == PLR_OP_REDUCE) {
-    if (L->seg_len <= (2u << 20)) {  // latency regime: every tile in one dispatch wave
+    if (L->src_bytes <= (2u << 20)) {  // latency regime: every tile in one dispatch wave
       L->block = 256;
       L->unroll = 1;
       L->tile_bytes = 4u << 10;
@@ -58,9 +60,13 @@ static void default_policy(plr_layout* L) {
       L->chunk_bytes = 256u << 10;
     }
   } else if (L->op == PLR_OP_COPY) {
+    // throughput regime (over 2 MiB from a source): 4 KiB tiles, one per workgroup (each
+    // lane moves two vectors in turn); measured on 8 x 64 MiB, AllGather 158-159 us and AllToAll 159 us against
+    // 165 us for 2 KiB tiles in runs of 2, notified or not, while 4 KiB at 256 threads
+    // took 187 us, 8 KiB 166-170 us and 16 KiB 173-176 us
     L->block = 128;
     L->unroll = 1;
-    L->tile_bytes = 2u << 10;
+    L->tile_bytes = L->src_bytes > (2u << 20) ? 4u << 10 : 2u << 10;
     L->chunk_bytes = 256u << 10;
   } else {  // allreduce: fused by default; the composed path's tiles follow the slice
     L->block = 128;
@@ -225,6 +231,12 @@ extern "C" int plr_layout_create(const plr_layout_desc* d, plr_layout** out) {
   }
 
   // policy: built-in table, then the caller's overrides
+  {
+    std::vector<uint64_t> per(W, 0);
+    for (auto& s : L->segs) per[s.src] += s.len;
+    L->src_bytes = 0;
+    for (uint64_t v : per) L->src_bytes = std::max(L->src_bytes, v);
+  }
   default_policy(L);
   if (d->tile_bytes) {
     if (!aligned16(d->tile_bytes)) return fail(PLR_EALIGN);
@@ -289,9 +301,10 @@ extern "C" int plr_layout_create(const plr_layout_desc* d, plr_layout** out) {
     L->notify_mode = d->notify_mode;
   }
   // in check mode only chunks still missing at check time pay a wait and a fence, so
-  // notified calls can use shorter runs (measured: reduce 1, copy 2)
+  // notified calls can use shorter runs (measured: reduce 1, copy 2 tiles of 2 KiB or 1
+  // of 4 KiB)
   if (L->notify_mode == PLR_NOTIFY_CHECK && L->datapath != PLR_PATH_LDS)
-    L->run_notified = L->op == PLR_OP_REDUCE ? 1 : 2;
+    L->run_notified = L->op == PLR_OP_REDUCE || L->tile_bytes >= 4096 ? 1 : 2;
 
   // tile and chunk tables; a chunk is a whole number of tiles of one segment
   if (L->op == PLR_OP_ALLREDUCE) {  // tiles of the W slices; one flag per tile
@@ -354,11 +367,12 @@ extern "C" int plr_layout_create(const plr_layout_desc* d, plr_layout** out) {
       L->nchunks = (uint32_t)chunks;
     }
   }
-  // copies: runs of 2 tiles once a call has 4096 tiles, as in check mode (measured
-  // without notification on 8 sources: AllGather and AllToAll of 8 x 64 MiB 166 us
-  // with runs of 2 against 184-189 us with 1, AllGatherV of 1 GiB 350 against 382 us;
-  // at 256 KiB per source one tile per workgroup is as fast or faster)
-  if (L->op == PLR_OP_COPY && L->datapath != PLR_PATH_LDS) L->run = L->ntiles >= 4096 ? 2 : 1;
+  // copies of 2 KiB tiles: runs of 2 once a call has 4096 tiles, as in check mode
+  // (measured without notification on 8 sources: AllGather and AllToAll of 8 x 64 MiB
+  // 166 us with runs of 2 against 184-189 us with 1, AllGatherV of 1 GiB 350 against
+  // 382 us; at 256 KiB per source one tile per workgroup is as fast or faster)
+  if (L->op == PLR_OP_COPY && L->datapath != PLR_PATH_LDS)
+    L->run = L->ntiles >= 4096 && L->tile_bytes < 4096 ? 2 : 1;
   if (L->op == PLR_OP_COPY) {  // first flag of every source (segments go source by source)
     const size_t nseg = L->segs.size();
     L->src_flag0.assign(W + 1, 0);

@@ -27,6 +27,7 @@ struct plr_layout {
   // with the share length; copy has W or W*W segments of one common length
   std::vector<Seg> segs;
   uint64_t seg_len;
+  uint64_t src_bytes;  // the most bytes any one source contributes: the policy's regime
   uint64_t dst_bytes;
   bool table_fits;  // copy: the table is carried in the kernel arguments
   bool var_segs;    // copy: segments of different lengths (AllGatherV)

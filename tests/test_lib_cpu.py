@@ -120,6 +120,27 @@ def test_policy_overrides(plr):
     assert _code(plr.plr_layout_create, "reduce", "bf16", 8, 64, "packed", "packed", notify_mode=3) == plr.PLR_EINVAL
 
 
+def test_regime_follows_bytes_per_source(plr):
+    # over 2 MiB from some source: check first, and copies take 4 KiB tiles; else in-kernel
+    # waits and 2 KiB tiles. An AllToAll's segments are slices, its sources contribute W of them.
+    def pol(*a, **k):
+        return plr.plr_layout_create(*a, **k).policy()
+    a2a = pol("copy", "bf16", 8, 4 << 20, "scattered", "transposed")  # 512 KiB slices
+    assert a2a["notify_mode"] == plr.PLR_NOTIFY_CHECK and a2a["tile_bytes"] == 4096
+    ag = pol("copy", "bf16", 8, 2 << 20, "packed", "packed")
+    assert ag["notify_mode"] == plr.PLR_NOTIFY_CHUNKS and ag["tile_bytes"] == 2048
+    ag = pol("copy", "bf16", 8, (2 << 20) + 16, "packed", "packed")
+    assert ag["notify_mode"] == plr.PLR_NOTIFY_CHECK and ag["tile_bytes"] == 4096
+    half = pol("copy", "bf16", 8, 16 << 20, "scattered", "scattered")  # 2 MiB per source
+    assert half["notify_mode"] == plr.PLR_NOTIFY_CHUNKS and half["tile_bytes"] == 2048
+    agv = pol("copy", "bf16", 4, 6 << 20, "packed", "packed", part_bytes=[3 << 20, 1 << 20, 1 << 20, 1 << 20])
+    assert agv["notify_mode"] == plr.PLR_NOTIFY_CHECK and agv["tile_bytes"] == 4096
+    red = pol("reduce", "bf16", 8, 2 << 20, "packed", "packed")
+    assert red["notify_mode"] == plr.PLR_NOTIFY_CHUNKS and red["tile_bytes"] == 4096  # decode-size share
+    red = pol("reduce", "bf16", 8, 4 << 20, "packed", "packed")
+    assert red["notify_mode"] == plr.PLR_NOTIFY_CHECK and red["tile_bytes"] == 2048
+
+
 def test_tiles_and_chunks(plr):
     # a chunk is a whole number of tiles of one segment; ragged ends on both levels
     L = plr.plr_layout_create("reduce", "bf16", 2, 10 * 1024 + 32, "packed", "packed",
