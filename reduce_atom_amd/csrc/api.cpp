@@ -157,6 +157,7 @@ extern "C" int plr_copy(plr_layout* L, const void* const* srcs, void* dst, void*
         a.var_tile0[k] = L->seg_tile0[k];
         a.var_chunk0[k] = L->seg_chunk0[k];
         a.var_len[k] = L->segs[k].len;
+        a.var_shift[k] = L->seg_shift[k];
       }
       a.var_tile0[L->segs.size()] = L->seg_tile0[L->segs.size()];
       a.var_chunk0[L->segs.size()] = L->seg_chunk0[L->segs.size()];

@@ -19,8 +19,8 @@ __global__ void __launch_bounds__(512) k_copy_direct(const CopyArgs a) {
   const uint32_t b = logical_block(a.xcd);
   const uint32_t t_end = min(a.ntiles, (b + 1) * a.run);
   for (uint32_t t = b * a.run; t < t_end; ++t) {
-    uint32_t seg, part, c;
-    uint64_t len;
+    uint32_t seg, part, c, c_last;
+    uint64_t len, b0, b1;  // the tile: bytes [b0, b1) of its segment
     if (a.mode == kCopyVar) {
       // the last segment starting at or before t owns it (empty segments share the
       // first tile of the next one; entries past the last segment hold ~0u)
@@ -29,12 +29,19 @@ __global__ void __launch_bounds__(512) k_copy_direct(const CopyArgs a) {
       for (uint32_t k = 1; k < PLR_MAX_WORLD; ++k) seg = t >= a.var_tile0[k] ? k : seg;
       part = t - a.var_tile0[seg];
       len = a.var_len[seg];
-      c = a.var_chunk0[seg] + part / a.tiles_per_chunk;
+      const uint64_t sh = a.var_shift[seg];
+      b0 = part ? (uint64_t)part * a.tile_bytes - sh : 0;
+      b1 = min((uint64_t)(part + 1) * a.tile_bytes - sh, len);
+      const uint64_t cb = (uint64_t)a.tiles_per_chunk * a.tile_bytes;
+      c = a.var_chunk0[seg] + (uint32_t)(b0 / cb);
+      c_last = a.var_chunk0[seg] + (uint32_t)((b1 - 1) / cb);
     } else {
       seg = t / a.tiles_per_seg;
       part = t - seg * a.tiles_per_seg;
       len = a.seg_len;
-      c = seg * a.chunks_per_seg + part / a.tiles_per_chunk;
+      b0 = (uint64_t)part * a.tile_bytes;
+      b1 = min(b0 + a.tile_bytes, len);
+      c = c_last = seg * a.chunks_per_seg + part / a.tiles_per_chunk;
     }
     uint32_t s;
     uint64_t src_off, dst_off;
@@ -48,15 +55,15 @@ __global__ void __launch_bounds__(512) k_copy_direct(const CopyArgs a) {
       src_off = (uint64_t)d * a.slice;
       dst_off = ((uint64_t)d * a.world + s) * a.slice;
     }
-    if (wait) {
-      const uint32_t f = c;  // flags follow the segments, source by source
-      if (f != ready) {
-        if (!wg_wait_flags(a.nt, f, 0, 1)) return;
-        ready = f;
+    if (wait) {  // flags follow the segments, source by source
+      for (uint32_t f = c; f <= c_last; ++f) {
+        if (f != ready) {
+          if (!wg_wait_flags(a.nt, f, 0, 1)) return;
+          ready = f;
+        }
       }
     }
-    const uint64_t b0 = (uint64_t)part * a.tile_bytes;
-    const uint64_t nv = (min(b0 + a.tile_bytes, len) - b0) >> 4;
+    const uint64_t nv = (b1 - b0) >> 4;
     const u32x4* src = reinterpret_cast<const u32x4*>(a.src[s] + src_off + b0);
     u32x4* dst = reinterpret_cast<u32x4*>(a.dst + dst_off + b0);
     uint64_t v = threadIdx.x;

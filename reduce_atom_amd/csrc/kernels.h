@@ -104,10 +104,13 @@ struct CopyArgs {
   uint64_t seg_src_off[kMaxTableSegs];
   uint64_t seg_dst_off[kMaxTableSegs];
   // kCopyVar: first tile and first chunk of every segment (nseg + 1 entries, then
-  // ~0u in var_tile0), lengths
+  // ~0u in var_tile0), lengths, and the shift of each segment's tiles: tile 0 is that
+  // many bytes short, so that every later tile starts on a 128-byte line of the
+  // destination (chunks stay whole multiples of the tile size from the segment start)
   uint32_t var_tile0[PLR_MAX_WORLD + 1];
   uint32_t var_chunk0[PLR_MAX_WORLD + 1];
   uint64_t var_len[PLR_MAX_WORLD];
+  uint32_t var_shift[PLR_MAX_WORLD];
 };
 
 // kernel arguments are limited to 4 KiB

@@ -46,6 +46,7 @@ struct plr_layout {
   // segments k * tiles_per_seg and k * chunks_per_seg), and first flag of every
   // source (W + 1 entries): segments go source by source
   std::vector<uint32_t> seg_tile0, seg_chunk0, src_flag0;
+  std::vector<uint32_t> seg_shift;  // variable-length copy: bytes tile 0 of a segment is short
 
   // resolved policy (section 4.2 "Codesign Policies and Tuning")
   int workgroups;  // explicit grid size, or 0
