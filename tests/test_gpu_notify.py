@@ -207,3 +207,39 @@ def test_check_mode_many_flags(plr, oracle_mod):
     mirror = words[32 + nflags: 32 + 2 * nflags]
     own = nflags // W  # the last source's flags: the last of W equal ranges
     assert (mirror[:nflags - own] == 2).all() and (mirror[nflags - own:] == 0).all()
+
+
+@pytest.mark.parametrize("mode", list(MODES))
+def test_allgatherv_cut_tiles_wait_for_both_chunks(plr, oracle_mod, mode):
+    """AllGatherV with partitions that start inside 128-byte lines of the output: its
+    tiles are cut on the output's lines, so most of them span two notification chunks
+    (chunks stay whole tiles from the segment start) and wait for both. A delayed
+    producer on another stream, as above; the output must be the real data."""
+    W = 4
+    parts = [16112, 13248, 16 * 1234 + 96, 16 * 555]  # later partitions start 112, 48, 48 B into a line
+    real_np = [synth.bits_np(9, 7, w, parts[w]) for w in range(W)]
+    ref = oracle_mod.allgather_v(real_np, parts)
+    real = [to_dev(s) for s in real_np]
+    srcs = [torch.empty_like(r) for r in real]
+    T = sum(parts)
+    L = plr.plr_layout_create("copy", "bf16", W, T, "packed", "packed", part_bytes=parts, tile_bytes=1024,
+                              chunk_bytes=2048, workgroups=3, block=64, spin_limit=1 << 22,
+                              notify_mode=MODES[mode])
+    assert L.ntiles > sum((p + 1023) // 1024 for p in parts)  # the cut added tiles
+    ws = torch.zeros(L.workspace_bytes, dtype=torch.uint8, device="cuda")
+    dst = torch.empty(T, dtype=torch.uint8, device="cuda")
+    torch.cuda.synchronize()
+    producer, consumer = torch.cuda.Stream(), torch.cuda.Stream()
+    with torch.cuda.stream(producer):
+        for s in srcs:
+            s.fill_(0xA5)
+        if hasattr(torch.cuda, "_sleep"):
+            torch.cuda._sleep(20_000_000)
+        for s, r in zip(srcs, real):
+            s.copy_(r)
+        plr.plr_notify(L, -1, ws)
+    with torch.cuda.stream(consumer):
+        plr.plr_copy(L, srcs, dst, ws)
+    torch.cuda.synchronize()
+    assert plr.plr_check(L, ws, consumer) == plr.PLR_OK
+    assert np.array_equal(dst.cpu().numpy(), ref)
