@@ -136,8 +136,8 @@ __global__ void __launch_bounds__(kRankThreads) k_copy_v_rank(const CopyVArgs a)
   if (t == 0) __hip_atomic_store(a.ticket, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// Kernel 2 cuts every row into tiles of kCvTileBytes (the last tile of a row may be
-// shorter); a workgroup of kCvThreads lanes moves kCvRun consecutive tiles of one
+// Kernel 2 cuts every row into tiles of Shape::kTile bytes (the last tile of a row may be
+// shorter); a workgroup of Shape::kThreads lanes moves Shape::kRun consecutive tiles of one
 // source (grid row y = source y), one 16-byte vector per lane per step, so that the
 // chip holds many short workgroups with their loads in flight, as the copy kernel
 // does. A tile's source address and the locations of its row's key and segment table
@@ -145,20 +145,22 @@ __global__ void __launch_bounds__(kRankThreads) k_copy_v_rank(const CopyVArgs a)
 // the keys and tables, computes each output row (the segment table's entry for the
 // key's destination plus the key's rank, with no second dependent load) and stores
 // last.
-#ifndef PLR_CV_TILE_BYTES
-#define PLR_CV_TILE_BYTES 2048
-#endif
-#ifndef PLR_CV_THREADS
-#define PLR_CV_THREADS 128
-#endif
-#ifndef PLR_CV_RUN
-#define PLR_CV_RUN 2
-#endif
-constexpr uint64_t kCvTileBytes = PLR_CV_TILE_BYTES;
-constexpr int kCvThreads = PLR_CV_THREADS;
-constexpr uint32_t kCvRun = PLR_CV_RUN;
-constexpr int kCvVecs = (int)(kCvTileBytes / 16 / kCvThreads);  // vectors per lane per tile
-static_assert(kCvTileBytes % (16 * kCvThreads) == 0, "a tile is whole vectors of every lane");
+// Two shapes, chosen by the row size: rows over 1 KiB take 2 KiB tiles of 128 lanes in
+// runs of 2 (measured on 8 x 4096 rows of 14,336 B: 153-155 us, against 156-158 us for
+// runs of 3 or 4 and 160 us for 4 KiB tiles); rows of at most 1 KiB take 1 KiB tiles of
+// 64 lanes in runs of 4 (8 x 4096 rows of 64 B: 15-17 us against 22-23 us), so that a
+// small row does not leave most lanes of a large workgroup idle.
+template <int THREADS, int TILE, int RUN>
+struct CvShape {
+  static constexpr int kThreads = THREADS;
+  static constexpr uint64_t kTile = TILE;
+  static constexpr uint32_t kRun = RUN;
+  static constexpr int kVecs = TILE / 16 / THREADS;  // vectors per lane per tile
+  static_assert(TILE % (16 * THREADS) == 0, "a tile is whole vectors of every lane");
+};
+using CvLarge = CvShape<128, 2048, 2>;
+using CvSmall = CvShape<64, 1024, 4>;
+constexpr uint64_t kCvSmallRow = 1024;  // rows of at most this many bytes take CvSmall
 
 // Small form (segments x W <= kSmallCounts): kernel 1 stopped after the segment counts.
 // Lane k of every wave keeps CPL of them (counts k*CPL .. k*CPL+CPL-1; count c is
@@ -215,8 +217,12 @@ __device__ void small_counts_and_offsets(const CopyVArgs& a, const int32_t (&my_
 }
 
 // CPL = counts per lane of the small form; 0 = the ticket form (segment table).
-template <int CPL>
-__global__ void __launch_bounds__(kCvThreads) k_copy_v_scatter(const CopyVArgs a) {
+template <int CPL, class Shape>
+__global__ void __launch_bounds__(Shape::kThreads) k_copy_v_scatter(const CopyVArgs a) {
+  constexpr int kCvThreads = Shape::kThreads;
+  constexpr uint64_t kCvTileBytes = Shape::kTile;
+  constexpr uint32_t kCvRun = Shape::kRun;
+  constexpr int kCvVecs = Shape::kVecs;
   constexpr int C = CPL > 0 ? CPL : 1;
   const uint32_t W = a.world;
   int32_t my_cnt[C];
@@ -325,9 +331,29 @@ __global__ void __launch_bounds__(kCvThreads) k_copy_v_scatter(const CopyVArgs a
   }
 }
 
+// The scatter launch of one shape: one workgroup per run of tiles of the longest source
+// in grid row s (source s); huge inputs make every row stride over its tiles. The small
+// forms have one more column: the workgroup that writes counts and offsets.
+template <class Shape>
+static void launch_scatter(const CopyVArgs& a, int cpl, hipStream_t s) {
+  int64_t most = 0;
+  for (uint32_t w = 0; w < a.world; ++w) most = std::max<int64_t>(most, a.row_start[w + 1] - a.row_start[w]);
+  const uint64_t groups = ((uint64_t)most * a.tiles_per_row + Shape::kRun - 1) / Shape::kRun;
+  const uint32_t gx = (uint32_t)(groups < 1 ? 1 : (groups > (1u << 22) ? (1u << 22) : groups));
+  const dim3 b(Shape::kThreads);
+  if (cpl == 1)
+    launch_dp(k_copy_v_scatter<1, Shape>, dim3(gx + 1, a.world), b, s, false, true, a);
+  else if (cpl == 4)
+    launch_dp(k_copy_v_scatter<4, Shape>, dim3(gx + 1, a.world), b, s, false, true, a);
+  else
+    launch_dp(k_copy_v_scatter<0, Shape>, dim3(gx, a.world), b, s, false, true, a);
+}
+
 hipError_t launch_copy_v(const CopyVArgs& args, hipStream_t s) {
   CopyVArgs a = args;
-  a.tiles_per_row = (a.row_bytes + kCvTileBytes - 1) / kCvTileBytes;
+  const bool small_rows = a.row_bytes <= kCvSmallRow;
+  const uint64_t tile = small_rows ? CvSmall::kTile : CvLarge::kTile;
+  a.tiles_per_row = (a.row_bytes + tile - 1) / tile;
   const uint32_t segs = a.seg_start[a.world];
   const uint64_t n = (uint64_t)segs * a.world;
   const int cpl = n <= 64 ? 1 : (n <= kSmallCounts ? 4 : 0);
@@ -336,19 +362,10 @@ hipError_t launch_copy_v(const CopyVArgs& args, hipStream_t s) {
   launch_dp(k_copy_v_rank, dim3(segs ? segs : 1), dim3(kRankThreads), s, true, false, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  // grid row s covers source s: one workgroup per kCvRun tiles of the longest source;
-  // huge inputs make every row stride over its tiles
-  int64_t most = 0;
-  for (uint32_t w = 0; w < a.world; ++w) most = std::max<int64_t>(most, a.row_start[w + 1] - a.row_start[w]);
-  const uint64_t groups = ((uint64_t)most * a.tiles_per_row + kCvRun - 1) / kCvRun;
-  const uint32_t gx = (uint32_t)(groups < 1 ? 1 : (groups > (1u << 22) ? (1u << 22) : groups));
-  // the small forms have one more column: the workgroup that writes counts and offsets
-  if (cpl == 1)
-    launch_dp(k_copy_v_scatter<1>, dim3(gx + 1, a.world), dim3(kCvThreads), s, false, true, a);
-  else if (cpl == 4)
-    launch_dp(k_copy_v_scatter<4>, dim3(gx + 1, a.world), dim3(kCvThreads), s, false, true, a);
+  if (small_rows)
+    launch_scatter<CvSmall>(a, cpl, s);
   else
-    launch_dp(k_copy_v_scatter<0>, dim3(gx, a.world), dim3(kCvThreads), s, false, true, a);
+    launch_scatter<CvLarge>(a, cpl, s);
   return hipGetLastError();
 }
 

@@ -166,3 +166,15 @@ def test_small_and_ticket_forms(plr, oracle_mod, W, rows):
     dests = [synth.categorical_np(W, 9, s, rows[s], p) for s in range(W)]
     srcs = [synth.bits_np(W, 10, s, max(rows[s], 1) * 64) for s in range(W)]
     _check(plr, oracle_mod, srcs, dests, 64)
+
+
+@pytest.mark.parametrize("rb", [16, 1008, 1024, 1040, 2048, 2064, 5 * 1024 + 48])
+def test_row_sizes_both_scatter_shapes(plr, oracle_mod, rb):
+    """Both sides of the scatter's shape switch (rows of at most 1 KiB: 1 KiB tiles of 64
+    lanes in runs of 4; larger: 2 KiB tiles of 128 lanes in runs of 2), with ragged last
+    tiles in each."""
+    W, rows = 8, [300, 0, 129, 1025, 64, 1, 700, 333]
+    p = synth.zipf_weights(1.1, W)
+    dests = [synth.categorical_np(W, 11, s, rows[s], p) for s in range(W)]
+    srcs = [synth.bits_np(W, 12, s, max(rows[s], 1) * rb) for s in range(W)]
+    _check(plr, oracle_mod, srcs, dests, rb)
