@@ -4,7 +4,9 @@ TEST INFRASTRUCTURE ONLY. Only ``tests/``, ``__graft_entry__.smoke()`` and the
 CPU-baseline leg of ``bench.py`` may import this package. The library in
 ``reduce_atom_amd/`` never imports it and shares no code with it.
 
-The arithmetic lives in ``oracle.c`` (plain C, one element at a time). This module
+The arithmetic lives in ``oracle.c`` (plain C, one element at a time; threaded
+variants split the same per-element code over host threads, for comparing full-size
+outputs in seconds and for timing the oracle on every core). This module
 marshals numpy arrays into it and holds the oracle's own reading of the layouts
 (Purlin paper, section 3.1 "Layouts": a collective is a naming of an input and an
 output layout plus a copy or a reduction; the layout kinds are packed, scattered
@@ -41,7 +43,7 @@ DTYPES = {"bf16": 0, "f16": 1, "f32": 2}
 ELEM_BYTES = {"bf16": 2, "f16": 2, "f32": 4}
 PACKED, SCATTERED, TRANSPOSED = "packed", "scattered", "transposed"
 
-CFLAGS = ["-O2", "-std=c11", "-ffp-contract=off", "-fno-fast-math", "-fPIC", "-shared",
+CFLAGS = ["-O2", "-std=c11", "-ffp-contract=off", "-fno-fast-math", "-fPIC", "-shared", "-pthread",
           "-Wall", "-Wextra", "-Werror"]
 
 
@@ -73,8 +75,31 @@ def lib():
         L.oracle_copy.restype = i32
         L.oracle_copy_v.argtypes = [i32, vp, vp, vp, i64, vp, vp, vp]
         L.oracle_copy_v.restype = i64
+        L.oracle_reduce_mt.argtypes = [i32, i32, vp, vp, vp, i64, i32]
+        L.oracle_reduce_mt.restype = i32
+        L.oracle_copy_mt.argtypes = [i32, vp, vp, vp, vp, vp, vp, i32]
+        L.oracle_copy_mt.restype = i32
+        L.oracle_copy_v_mt.argtypes = [i32, vp, vp, vp, i64, vp, vp, vp, i32]
+        L.oracle_copy_v_mt.restype = i64
+        L.oracle_hardware_threads.argtypes = []
+        L.oracle_hardware_threads.restype = i32
         _lib = L
     return _lib
+
+
+def hardware_threads() -> int:
+    """Logical CPUs online on this host (sysconf, as std::thread::hardware_concurrency)."""
+    return lib().oracle_hardware_threads()
+
+
+def default_threads() -> int:
+    """Threads the threaded variants use by default: the CPUs this process may run on,
+    at most 16."""
+    try:
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:
+        n = os.cpu_count() or 1
+    return max(1, min(16, n))
 
 
 def _ptr(a: np.ndarray) -> int:
@@ -147,8 +172,9 @@ def copy_segments(in_kind: str, out_kind: str, world: int, bytes_per_src: int):
 
 
 # ------------------------------------------------------------------ reduce
-def reduce(dtype: str, srcs, src_off=None, n=None) -> np.ndarray:
-    """Rank-order fp32 reduction of W sources into one share (element bits out)."""
+def reduce(dtype: str, srcs, src_off=None, n=None, threads: int = 1) -> np.ndarray:
+    """Rank-order fp32 reduction of W sources into one share (element bits out).
+    threads > 1 splits the elements over that many host threads (same results)."""
     raws = [_raw(s, dtype).reshape(-1) for s in srcs]
     W = len(raws)
     if src_off is None:
@@ -160,24 +186,27 @@ def reduce(dtype: str, srcs, src_off=None, n=None) -> np.ndarray:
             raise ValueError("share out of bounds")
     out = np.empty(n, dtype=np.float32 if dtype == "f32" else np.uint16)
     offs = np.asarray(src_off, dtype=np.int64)
-    rc = lib().oracle_reduce(DTYPES[dtype], W, _ptr_array(raws), _ptr(offs), _ptr(out), n)
+    if threads > 1:
+        rc = lib().oracle_reduce_mt(DTYPES[dtype], W, _ptr_array(raws), _ptr(offs), _ptr(out), n, threads)
+    else:
+        rc = lib().oracle_reduce(DTYPES[dtype], W, _ptr_array(raws), _ptr(offs), _ptr(out), n)
     if rc:
         raise ValueError("oracle_reduce rejected its arguments")
     return out
 
 
-def reduce_layout(dtype: str, in_kind: str, rank: int, srcs) -> np.ndarray:
+def reduce_layout(dtype: str, in_kind: str, rank: int, srcs, threads: int = 1) -> np.ndarray:
     W = len(srcs)
     offs, n = reduce_share(in_kind, W, rank, _raw(srcs[0], dtype).size)
-    return reduce(dtype, srcs, offs, n)
+    return reduce(dtype, srcs, offs, n, threads)
 
 
-def allreduce(dtype: str, srcs):
+def allreduce(dtype: str, srcs, threads: int = 1):
     """AllReduce of W contributions (Purlin paper, section 2.1: every rank ends with the
     reduction of all contributions): W outputs, each the rank-order reduction of the
     W sources. Written from that definition; the composition ReduceScatter then
     AllGather (section 3.1) is checked against it in the tests."""
-    out = reduce(dtype, srcs)
+    out = reduce(dtype, srcs, threads=threads)
     return [out.copy() for _ in srcs]
 
 
@@ -199,8 +228,9 @@ def unpack(packets: np.ndarray, epoch: int):
 
 
 # ------------------------------------------------------------------ copy
-def copy(srcs, segments, dst_bytes: int, fill: int = 0) -> np.ndarray:
-    """Apply byte segments (src, src_off, dst_off, len) to a fresh output buffer."""
+def copy(srcs, segments, dst_bytes: int, fill: int = 0, threads: int = 1) -> np.ndarray:
+    """Apply byte segments (src, src_off, dst_off, len) to a fresh output buffer.
+    threads > 1 splits every segment over that many host threads (same bytes)."""
     raws = [np.ascontiguousarray(s).reshape(-1).view(np.uint8) for s in srcs]
     out = np.full(dst_bytes, fill, dtype=np.uint8)
     for (s, so, do, ln) in segments:
@@ -211,14 +241,18 @@ def copy(srcs, segments, dst_bytes: int, fill: int = 0) -> np.ndarray:
     so = np.array([g[1] for g in segments], dtype=np.int64)
     do = np.array([g[2] for g in segments], dtype=np.int64)
     ln = np.array([g[3] for g in segments], dtype=np.int64)
-    lib().oracle_copy(k, _ptr_array(raws), _ptr(seg_src), _ptr(so), _ptr(do), _ptr(ln), _ptr(out))
+    if threads > 1:
+        lib().oracle_copy_mt(k, _ptr_array(raws), _ptr(seg_src), _ptr(so), _ptr(do), _ptr(ln), _ptr(out),
+                             threads)
+    else:
+        lib().oracle_copy(k, _ptr_array(raws), _ptr(seg_src), _ptr(so), _ptr(do), _ptr(ln), _ptr(out))
     return out
 
 
-def copy_layout(in_kind: str, out_kind: str, srcs) -> np.ndarray:
+def copy_layout(in_kind: str, out_kind: str, srcs, threads: int = 1) -> np.ndarray:
     B = np.ascontiguousarray(srcs[0]).nbytes
     segs, total = copy_segments(in_kind, out_kind, len(srcs), B)
-    return copy(srcs, segs, total)
+    return copy(srcs, segs, total, threads=threads)
 
 
 # ------------------------------------------------------------------ variable length
@@ -232,16 +266,16 @@ def part_offsets(parts):
     return offs
 
 
-def allgather_v(srcs, parts) -> np.ndarray:
+def allgather_v(srcs, parts, threads: int = 1) -> np.ndarray:
     """AllGatherV (section 2.1 and appendix C.4: a contribution of its own size per
     rank; every rank receives all of them in rank order): source w contributes its
     first parts[w] bytes, placed at the sum of the sizes before it."""
     offs = part_offsets(parts)
     segs = [(w, 0, offs[w], int(parts[w])) for w in range(len(srcs))]
-    return copy(srcs, segs, sum(int(p) for p in parts))
+    return copy(srcs, segs, sum(int(p) for p in parts), threads=threads)
 
 
-def reduce_scatter_v(dtype: str, srcs, parts, rank: int) -> np.ndarray:
+def reduce_scatter_v(dtype: str, srcs, parts, rank: int, threads: int = 1) -> np.ndarray:
     """ReduceScatterV share of `rank` (appendix C.4: the rank's assigned partition is
     its output): every source holds all partitions back to back; the share is the
     rank-order reduction of partition `rank` of every source."""
@@ -250,13 +284,14 @@ def reduce_scatter_v(dtype: str, srcs, parts, rank: int) -> np.ndarray:
     if off % eb or int(parts[rank]) % eb:
         raise ValueError("partition not a whole number of elements")
     W = len(srcs)
-    return reduce(dtype, srcs, [off // eb] * W, int(parts[rank]) // eb)
+    return reduce(dtype, srcs, [off // eb] * W, int(parts[rank]) // eb, threads)
 
 
 # ------------------------------------------------------------------ copy_v
-def copy_v(srcs, dests, row_bytes: int):
+def copy_v(srcs, dests, row_bytes: int, threads: int = 1):
     """Variable-length AllToAll packing. srcs[s]: rows of source s (any dtype, C order);
-    dests[s]: int32 destination per row. Returns (out bytes, counts[s][d], offsets[d][s])."""
+    dests[s]: int32 destination per row. Returns (out bytes, counts[s][d], offsets[d][s]).
+    threads > 1 moves the rows on that many host threads (same bytes)."""
     W = len(srcs)
     raws = [np.ascontiguousarray(s).reshape(-1).view(np.uint8) for s in srcs]
     ds = [np.ascontiguousarray(d, dtype=np.int32).reshape(-1) for d in dests]
@@ -268,8 +303,12 @@ def copy_v(srcs, dests, row_bytes: int):
     out = np.zeros(total * row_bytes, dtype=np.uint8)
     counts = np.zeros((W, W), dtype=np.int64)
     offsets = np.zeros((W, W), dtype=np.int64)
-    got = lib().oracle_copy_v(W, _ptr_array(raws), _ptr(rows), _ptr_array(ds), row_bytes,
-                              _ptr(out), _ptr(counts), _ptr(offsets))
+    if threads > 1:
+        got = lib().oracle_copy_v_mt(W, _ptr_array(raws), _ptr(rows), _ptr_array(ds), row_bytes,
+                                     _ptr(out), _ptr(counts), _ptr(offsets), threads)
+    else:
+        got = lib().oracle_copy_v(W, _ptr_array(raws), _ptr(rows), _ptr_array(ds), row_bytes,
+                                  _ptr(out), _ptr(counts), _ptr(offsets))
     if got < 0:
         raise ValueError("destination out of range")
     assert got == total

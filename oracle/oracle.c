@@ -157,16 +157,22 @@ float oracle_add_f32(float a, float b) {
  * srcs[w] points at source w's buffer; src_off[w] is the element offset of the
  * share inside it (0 for a packed contribution, rank * n for a scattered one).
  */
-int oracle_reduce(int dtype, int W, const void* const* srcs, const int64_t* src_off,
-                  void* dst, int64_t n) {
-  if (W < 1 || dtype < 0 || dtype > 2 || n < 0) return -1;
+/* elements [i0, i1) of the definition above */
+static void reduce_range(int dtype, int W, const void* const* srcs, const int64_t* src_off,
+                         void* dst, int64_t i0, int64_t i1) {
   unsigned int m = ieee_enter();
-  for (int64_t i = 0; i < n; ++i) {
+  for (int64_t i = i0; i < i1; ++i) {
     float a = widen(dtype, srcs[0], src_off[0] + i);
     for (int w = 1; w < W; ++w) a = a + widen(dtype, srcs[w], src_off[w] + i);
     narrow_store(dtype, dst, i, a);
   }
   ieee_leave(m);
+}
+
+int oracle_reduce(int dtype, int W, const void* const* srcs, const int64_t* src_off,
+                  void* dst, int64_t n) {
+  if (W < 1 || dtype < 0 || dtype > 2 || n < 0) return -1;
+  reduce_range(dtype, W, srcs, src_off, dst, 0, n);
   return 0;
 }
 
@@ -189,10 +195,10 @@ int oracle_copy(int nseg, const void* const* srcs, const int32_t* seg_src,
  *                      sources
  * Row i of source s lands at offsets[d*W + s] + (number of rows i' < i of source s
  * bound for the same d). Returns the total row count, or -1 on a bad destination. */
-int64_t oracle_copy_v(int W, const void* const* srcs, const int64_t* rows,
-                      const int32_t* const* dest, int64_t row_bytes, void* dst,
-                      int64_t* counts, int64_t* offsets) {
-  if (W < 1 || W > 64) return -1;
+
+/* counts and offsets as defined above; returns the total row count or -1 */
+static int64_t copy_v_counts_offsets(int W, const int64_t* rows, const int32_t* const* dest,
+                                     int64_t* counts, int64_t* offsets) {
   for (int s = 0; s < W; ++s)
     for (int d = 0; d < W; ++d) counts[s * W + d] = 0;
   for (int s = 0; s < W; ++s)
@@ -210,16 +216,170 @@ int64_t oracle_copy_v(int W, const void* const* srcs, const int64_t* rows,
     }
     base = off;
   }
-  for (int s = 0; s < W; ++s) {
-    int64_t seen[64];
-    for (int d = 0; d < W; ++d) seen[d] = 0;
-    for (int64_t i = 0; i < rows[s]; ++i) {
-      int32_t d = dest[s][i];
-      int64_t out_row = offsets[d * W + s] + seen[d];
-      seen[d] += 1;
-      memcpy((char*)dst + out_row * row_bytes, (const char*)srcs[s] + i * row_bytes,
-             (size_t)row_bytes);
-    }
-  }
   return base;
+}
+
+/* Rows [i0, i1) of source s, in row order. A row's rank among the rows of its source
+ * bound for the same destination is the number of earlier such rows, counted from
+ * row 0 of the source. */
+static void place_rows(int W, int s, const void* const* srcs, const int32_t* const* dest,
+                       int64_t row_bytes, void* dst, const int64_t* offsets, int64_t i0, int64_t i1) {
+  int64_t seen[64];
+  for (int d = 0; d < W; ++d) seen[d] = 0;
+  for (int64_t i = 0; i < i0; ++i) seen[dest[s][i]] += 1;
+  for (int64_t i = i0; i < i1; ++i) {
+    int32_t d = dest[s][i];
+    int64_t out_row = offsets[d * W + s] + seen[d];
+    seen[d] += 1;
+    memcpy((char*)dst + out_row * row_bytes, (const char*)srcs[s] + i * row_bytes, (size_t)row_bytes);
+  }
+}
+
+int64_t oracle_copy_v(int W, const void* const* srcs, const int64_t* rows,
+                      const int32_t* const* dest, int64_t row_bytes, void* dst,
+                      int64_t* counts, int64_t* offsets) {
+  if (W < 1 || W > 64) return -1;
+  int64_t total = copy_v_counts_offsets(W, rows, dest, counts, offsets);
+  if (total < 0) return -1;
+  for (int s = 0; s < W; ++s) place_rows(W, s, srcs, dest, row_bytes, dst, offsets, 0, rows[s]);
+  return total;
+}
+
+/* ------------------------------------------------------- threaded variants
+ * The same definitions with the work split over POSIX threads, only so that the
+ * oracle can be timed on every host core. No element's arithmetic changes: each
+ * output element, byte or row is produced by exactly one thread running the code of
+ * the single-threaded function (reduce: reduce_range over a contiguous range of i;
+ * copy: memcpy of a contiguous part of every segment; copy_v: counts and offsets on
+ * the calling thread as oracle_copy_v computes them, then place_rows over contiguous
+ * row ranges of one source). The results are those of the single-threaded calls bit
+ * for bit; the tests check that. MXCSR is per thread, and reduce_range sets it in
+ * the thread that runs it. */
+#include <pthread.h>
+#include <stdlib.h>
+#include <unistd.h>
+
+/* Logical CPUs online on this host (what std::thread::hardware_concurrency reports). */
+int oracle_hardware_threads(void) {
+  long n = sysconf(_SC_NPROCESSORS_ONLN);
+  return n > 0 ? (int)n : 1;
+}
+
+/* part k of [0, n) cut into `parts` contiguous ranges of nearly equal length */
+static int64_t part_start(int64_t n, int parts, int k) { return (int64_t)((__int128)n * k / parts); }
+
+/* Runs f on nparts argument blocks of `size` bytes, at most nthreads at a time (the
+ * calling thread runs one of each group; a part whose thread cannot start runs here). */
+static void run_parts(void* (*f)(void*), char* parts, size_t size, int nparts, int nthreads) {
+  pthread_t th[256];
+  if (nthreads > 256) nthreads = 256;
+  for (int k0 = 0; k0 < nparts; k0 += nthreads) {
+    int n = nparts - k0 < nthreads ? nparts - k0 : nthreads;
+    int made[256];
+    for (int k = 1; k < n; ++k) {
+      made[k] = pthread_create(&th[k], NULL, f, parts + (size_t)(k0 + k) * size) == 0;
+      if (!made[k]) f(parts + (size_t)(k0 + k) * size);
+    }
+    f(parts + (size_t)k0 * size);
+    for (int k = 1; k < n; ++k)
+      if (made[k]) pthread_join(th[k], NULL);
+  }
+}
+
+typedef struct {
+  int dtype, W;
+  const void* const* srcs;
+  const int64_t* src_off;
+  void* dst;
+  int64_t i0, i1;
+} reduce_part;
+
+static void* reduce_part_run(void* p) {
+  const reduce_part* r = (const reduce_part*)p;
+  reduce_range(r->dtype, r->W, r->srcs, r->src_off, r->dst, r->i0, r->i1);
+  return NULL;
+}
+
+int oracle_reduce_mt(int dtype, int W, const void* const* srcs, const int64_t* src_off,
+                     void* dst, int64_t n, int nthreads) {
+  if (W < 1 || dtype < 0 || dtype > 2 || n < 0 || nthreads < 1) return -1;
+  reduce_part* parts = (reduce_part*)calloc((size_t)nthreads, sizeof(reduce_part));
+  if (!parts) return -1;
+  for (int k = 0; k < nthreads; ++k) {
+    reduce_part r = {dtype, W, srcs, src_off, dst, part_start(n, nthreads, k), part_start(n, nthreads, k + 1)};
+    parts[k] = r;
+  }
+  run_parts(reduce_part_run, (char*)parts, sizeof(reduce_part), nthreads, nthreads);
+  free(parts);
+  return 0;
+}
+
+typedef struct {
+  int nseg;
+  const void* const* srcs;
+  const int32_t* seg_src;
+  const int64_t *src_off, *dst_off, *len;
+  void* dst;
+  int k, parts;
+} copy_part;
+
+static void* copy_part_run(void* p) {
+  const copy_part* c = (const copy_part*)p;
+  for (int s = 0; s < c->nseg; ++s) {
+    int64_t a = part_start(c->len[s], c->parts, c->k), b = part_start(c->len[s], c->parts, c->k + 1);
+    memcpy((char*)c->dst + c->dst_off[s] + a, (const char*)c->srcs[c->seg_src[s]] + c->src_off[s] + a,
+           (size_t)(b - a));
+  }
+  return NULL;
+}
+
+int oracle_copy_mt(int nseg, const void* const* srcs, const int32_t* seg_src,
+                   const int64_t* src_off, const int64_t* dst_off, const int64_t* len, void* dst,
+                   int nthreads) {
+  if (nthreads < 1) return -1;
+  copy_part* parts = (copy_part*)calloc((size_t)nthreads, sizeof(copy_part));
+  if (!parts) return -1;
+  for (int k = 0; k < nthreads; ++k) {
+    copy_part c = {nseg, srcs, seg_src, src_off, dst_off, len, dst, k, nthreads};
+    parts[k] = c;
+  }
+  run_parts(copy_part_run, (char*)parts, sizeof(copy_part), nthreads, nthreads);
+  free(parts);
+  return 0;
+}
+
+typedef struct {
+  int W, s;
+  const void* const* srcs;
+  const int32_t* const* dest;
+  int64_t row_bytes;
+  void* dst;
+  const int64_t* offsets;
+  int64_t i0, i1;
+} copy_v_part;
+
+static void* copy_v_part_run(void* p) {
+  const copy_v_part* c = (const copy_v_part*)p;
+  place_rows(c->W, c->s, c->srcs, c->dest, c->row_bytes, c->dst, c->offsets, c->i0, c->i1);
+  return NULL;
+}
+
+int64_t oracle_copy_v_mt(int W, const void* const* srcs, const int64_t* rows,
+                         const int32_t* const* dest, int64_t row_bytes, void* dst,
+                         int64_t* counts, int64_t* offsets, int nthreads) {
+  if (W < 1 || W > 64 || nthreads < 1) return -1;
+  int64_t total = copy_v_counts_offsets(W, rows, dest, counts, offsets);
+  if (total < 0) return -1;
+  const int nparts = W * nthreads; /* nthreads row ranges of every source */
+  copy_v_part* parts = (copy_v_part*)calloc((size_t)nparts, sizeof(copy_v_part));
+  if (!parts) return -1;
+  for (int s = 0; s < W; ++s)
+    for (int k = 0; k < nthreads; ++k) {
+      copy_v_part c = {W, s, srcs, dest, row_bytes, dst, offsets,
+                       part_start(rows[s], nthreads, k), part_start(rows[s], nthreads, k + 1)};
+      parts[s * nthreads + k] = c;
+    }
+  run_parts(copy_v_part_run, (char*)parts, sizeof(copy_v_part), nparts, nthreads);
+  free(parts);
+  return total;
 }
