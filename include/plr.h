@@ -175,13 +175,19 @@ int plr_layout_create(const plr_layout_desc* desc, plr_layout** out);
 void plr_layout_destroy(plr_layout* L);
 
 /* Bytes of workspace a notified call needs: a 256-byte header (u64 error word at
- * byte 0, u64 ready word at byte 8), the chunk flags uint64_t flags[F] and their
+ * byte 0, u64 ready word at byte 8, u64 late counter at byte 16), the chunk flags
+ * uint64_t flags[F] and their
  * check-time mirror uint64_t mirror[F]. Reduce: F = W * nchunks, flags[w][c] for source
  * w and chunk c of the share. Copy: F = nchunks, one flag per chunk of every segment in
  * segment order (segment k's chunk j at k * nchunks / nsegments + j); segments go source
  * by source, so source s owns the s-th of W equal ranges. The caller allocates it in device
  * memory, ZEROED, once; it is never reset between calls (the epoch only grows,
- * section 4.3 "Epoch Bookkeeping"). One workspace belongs to one layout. */
+ * section 4.3 "Epoch Bookkeeping"). One workspace belongs to one layout.
+ * Diagnostics the caller may read: the ready word holds the epoch of the last call whose
+ * check found every flag already set (0 if some were missing), mirror[i] that epoch if
+ * flag i was set at check time (else 0), and the late counter grows by one for every
+ * wait of a workgroup (or, for the composed AllReduce, a wave) that found a chunk flag
+ * below its epoch and had to poll; the library never resets it. */
 size_t plr_layout_workspace_bytes(const plr_layout* L);
 
 /* Bytes the call writes into dst: the share for a reduce, the whole output for a copy. */

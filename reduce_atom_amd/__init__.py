@@ -172,11 +172,23 @@ def _ptrs(xs):
     return (_vp * len(xs))(*[_addr(x) for x in xs])
 
 
+def _check_len(xs, n: int, what: str) -> None:
+    if xs is not None and len(xs) != n:
+        raise ValueError(f"{what}: {len(xs)} entries, the layout reads {n}")
+
+
+def _world_ptrs(layout: "Layout", xs, what: str):
+    """One device pointer per source of the layout (the C side reads exactly W)."""
+    _check_len(xs, layout.world, what)
+    return _ptrs(xs)
+
+
 class Layout:
     """A compiled collective specification (host object owning a plr_layout*)."""
 
-    def __init__(self, handle: int):
+    def __init__(self, handle: int, world: int = 0):
         self._h = _vp(handle)
+        self.world = world
 
     @property
     def handle(self):
@@ -237,7 +249,17 @@ def plr_layout_create(op, dtype, world, bytes_per_src, in_kind, out_kind, rank=0
     """Compile a layout. op/dtype/kinds accept the C enum values or their names.
     part_bytes: W partition sizes of a variable-length layout (AllGatherV, ReduceScatterV)."""
     d = plr_layout_desc()
-    d.op = OP_CODES.get(op, op)
+    op_c, in_c, out_c = OP_CODES.get(op, op), KIND_CODES.get(in_kind, in_kind), KIND_CODES.get(out_kind, out_kind)
+    # the C side reads exactly this many entries of every list it is given
+    if isinstance(world, int) and 1 <= world <= PLR_MAX_WORLD:
+        # (a reduce rejects out_offsets and an AllReduce both lists without reading them)
+        nseg = world * world if (op_c, in_c, out_c) == (PLR_OP_COPY, PLR_SCATTERED, PLR_TRANSPOSED) else world
+        if op_c in (PLR_OP_REDUCE, PLR_OP_COPY):
+            _check_len(in_offsets, nseg, "in_offsets")
+        if op_c == PLR_OP_COPY:
+            _check_len(out_offsets, nseg, "out_offsets")
+        _check_len(part_bytes, world, "part_bytes")
+    d.op = op_c
     d.dtype = DTYPE_CODES.get(dtype, dtype)
     d.world, d.rank, d.bytes_per_src = world, rank, bytes_per_src
     d.in_kind = KIND_CODES.get(in_kind, in_kind)
@@ -261,7 +283,7 @@ def plr_layout_create(op, dtype, world, bytes_per_src, in_kind, out_kind, rank=0
         d.part_bytes = _c.cast(a, _c.POINTER(_sz))
     h = _vp()
     _ok(_lib.plr_layout_create(_c.byref(d), _c.byref(h)), "plr_layout_create")
-    return Layout(h.value)
+    return Layout(h.value, world)
 
 
 def plr_layout_destroy(layout: Layout) -> None:
@@ -269,38 +291,50 @@ def plr_layout_destroy(layout: Layout) -> None:
 
 
 def plr_reduce(layout: Layout, srcs, dst, workspace=None, stream=None) -> None:
-    _ok(_lib.plr_reduce(layout.handle, _ptrs(srcs), _addr(dst), _addr(workspace), _stream(stream)),
-        "plr_reduce")
+    _ok(_lib.plr_reduce(layout.handle, _world_ptrs(layout, srcs, "srcs"), _addr(dst), _addr(workspace),
+                        _stream(stream)), "plr_reduce")
 
 
 def plr_copy(layout: Layout, srcs, dst, workspace=None, stream=None) -> None:
-    _ok(_lib.plr_copy(layout.handle, _ptrs(srcs), _addr(dst), _addr(workspace), _stream(stream)),
-        "plr_copy")
+    _ok(_lib.plr_copy(layout.handle, _world_ptrs(layout, srcs, "srcs"), _addr(dst), _addr(workspace),
+                      _stream(stream)), "plr_copy")
 
 
 def plr_allreduce(layout: Layout, srcs, dsts, workspace=None, stream=None) -> None:
-    _ok(_lib.plr_allreduce(layout.handle, _ptrs(srcs), _ptrs(dsts), _addr(workspace), _stream(stream)),
-        "plr_allreduce")
+    _ok(_lib.plr_allreduce(layout.handle, _world_ptrs(layout, srcs, "srcs"), _world_ptrs(layout, dsts, "dsts"),
+                           _addr(workspace), _stream(stream)), "plr_allreduce")
 
 
 def plr_pack(layout: Layout, src: int, data, packets, stream=None) -> None:
-    _ok(_lib.plr_pack(layout.handle, src, _ptrs(data), _ptrs(packets), _stream(stream)), "plr_pack")
+    _ok(_lib.plr_pack(layout.handle, src, _world_ptrs(layout, data, "data"), _world_ptrs(layout, packets, "packets"),
+                      _stream(stream)), "plr_pack")
 
 
 def plr_reduce_packets(layout: Layout, packets, dst, workspace, stream=None) -> None:
-    _ok(_lib.plr_reduce_packets(layout.handle, _ptrs(packets), _addr(dst), _addr(workspace), _stream(stream)),
-        "plr_reduce_packets")
+    _ok(_lib.plr_reduce_packets(layout.handle, _world_ptrs(layout, packets, "packets"), _addr(dst),
+                                _addr(workspace), _stream(stream)), "plr_reduce_packets")
 
 
 def plr_copy_v_scratch_bytes(world: int, rows_per_src) -> int:
+    _check_len(rows_per_src, world, "rows_per_src")
     rows = (_c.c_int64 * world)(*rows_per_src)
     return _lib.plr_copy_v_scratch_bytes(world, rows)
 
 
+def _copy_v_lists(srcs, rows_per_src, dest_of_row):
+    W = len(srcs)
+    _check_len(rows_per_src, W, "rows_per_src")
+    _check_len(dest_of_row, W, "dest_of_row")
+    for d in dest_of_row:
+        dt = getattr(d, "dtype", None)
+        if dt is not None and str(dt) != "torch.int32":
+            raise ValueError(f"dest_of_row: int32 tensors expected, got {dt}")
+    return W, (_c.c_int64 * W)(*rows_per_src)
+
+
 def plr_copy_v(srcs, rows_per_src, dest_of_row, row_bytes, dst, counts, offsets, scratch,
                stream=None) -> None:
-    W = len(srcs)
-    rows = (_c.c_int64 * W)(*rows_per_src)
+    W, rows = _copy_v_lists(srcs, rows_per_src, dest_of_row)
     _ok(_lib.plr_copy_v(W, _ptrs(srcs), rows, _ptrs(dest_of_row), row_bytes, _addr(dst),
                         _addr(counts), _addr(offsets), _addr(scratch), _stream(stream)), "plr_copy_v")
 

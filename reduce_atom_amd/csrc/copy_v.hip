@@ -19,6 +19,7 @@
 // from every such call.
 #include <algorithm>
 
+#include "copy_v_grid.h"
 #include "device_common.h"
 
 namespace plr {
@@ -257,8 +258,9 @@ __global__ void __launch_bounds__(Shape::kThreads) k_copy_v_scatter(const CopyVA
   const uint64_t ntiles = (uint64_t)(a.row_start[s + 1] - r0) * a.tiles_per_row;
   const uint8_t* src_s = a.src[s];
   const uint32_t seg0 = a.seg_start[s];
-  const uint64_t stride = (uint64_t)gridDim.x * kCvRun;
-  for (uint64_t t0 = (uint64_t)logical_block(a.xcd) * kCvRun; t0 < ntiles; t0 += stride) {
+  // the small form's last column moved no tile and is not part of the stride
+  const uint64_t stride = cv_tile_stride(gridDim.x, CPL > 0, kCvRun);
+  for (uint64_t t0 = cv_first_tile(logical_block(a.xcd), kCvRun); t0 < ntiles; t0 += stride) {
     const uint32_t m = (uint32_t)min<uint64_t>(kCvRun, ntiles - t0);  // tiles of this run
     // Every data load of the run is issued first, then every key and segment table, and
     // the stores come last: no store of one tile sits between the next tile's loads or
@@ -324,7 +326,7 @@ __global__ void __launch_bounds__(Shape::kThreads) k_copy_v_scatter(const CopyVA
         if (v < nv[k]) st16(dst + v, x[k][u]);
       }
     }
-    // Only calls of more than 2^22 runs per source take another turn of this loop; the
+    // Only calls of more than kCvMaxColumns runs per source take another turn of this loop; the
     // wait keeps its stores from holding registers the next turn's loads and arithmetic
     // reuse (which would put waits for the whole memory queue between them).
     wait_vmem<0>();
@@ -338,13 +340,13 @@ template <class Shape>
 static void launch_scatter(const CopyVArgs& a, int cpl, hipStream_t s) {
   int64_t most = 0;
   for (uint32_t w = 0; w < a.world; ++w) most = std::max<int64_t>(most, a.row_start[w + 1] - a.row_start[w]);
-  const uint64_t groups = ((uint64_t)most * a.tiles_per_row + Shape::kRun - 1) / Shape::kRun;
-  const uint32_t gx = (uint32_t)(groups < 1 ? 1 : (groups > (1u << 22) ? (1u << 22) : groups));
+  const uint32_t gx = cv_grid_columns(cv_tile_columns((uint64_t)most * a.tiles_per_row, Shape::kRun, kCvMaxColumns),
+                                      cpl > 0);
   const dim3 b(Shape::kThreads);
   if (cpl == 1)
-    launch_dp(k_copy_v_scatter<1, Shape>, dim3(gx + 1, a.world), b, s, false, true, a);
+    launch_dp(k_copy_v_scatter<1, Shape>, dim3(gx, a.world), b, s, false, true, a);
   else if (cpl == 4)
-    launch_dp(k_copy_v_scatter<4, Shape>, dim3(gx + 1, a.world), b, s, false, true, a);
+    launch_dp(k_copy_v_scatter<4, Shape>, dim3(gx, a.world), b, s, false, true, a);
   else
     launch_dp(k_copy_v_scatter<0, Shape>, dim3(gx, a.world), b, s, false, true, a);
 }

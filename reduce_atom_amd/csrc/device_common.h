@@ -59,11 +59,14 @@ __device__ __forceinline__ uint32_t logical_block(int xcd) {
 // this kernel after the producer. Otherwise the lane polls the flag until it reaches
 // nt.epoch, within a bounded number of polls, and the wave then executes one
 // agent-scope acquire fence. On a timeout one lane records PLR_ETIMEOUT in the sticky
-// error word; if another wave already recorded an error the wave gives up too.
-// Returns true when every flag has arrived. All lanes of the wave call this together.
+// error word; if another wave already recorded an error the wave gives up too. A wait
+// that found some flag below the epoch at its first poll adds one to the workspace's
+// late counter (header word 2), so that a caller can tell consumers that waited from
+// those that found their data announced. Returns true when every flag has arrived. All
+// lanes of the wave call this together.
 __device__ __forceinline__ bool wait_flags(const Notify& nt, uint64_t first, uint64_t stride, int n) {
   const int lane = __lane_id();
-  int bad = 0, polled = 0;
+  int bad = 0, polled = 0, late = 0;
   if (lane < n) {
     const uint64_t i = first + (uint64_t)lane * stride;
     if (!(nt.mirror && nt.mirror[i] == nt.epoch)) {
@@ -71,6 +74,7 @@ __device__ __forceinline__ bool wait_flags(const Notify& nt, uint64_t first, uin
       const uint64_t* f = nt.flags + i;
       uint64_t polls = 0;
       while (__hip_atomic_load(f, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < nt.epoch) {
+        late = 1;
         if (++polls >= nt.spin_limit) {
           bad = 1;
           break;
@@ -86,6 +90,9 @@ __device__ __forceinline__ bool wait_flags(const Notify& nt, uint64_t first, uin
   }
   const uint64_t timed_out = __ballot(bad == 1);
   const uint64_t failed = __ballot(bad != 0);
+  const uint64_t waited = __ballot(late);
+  if (waited && lane == __builtin_ctzll(waited))
+    __hip_atomic_fetch_add(nt.err + kLateWord, (uint64_t)1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   if (failed) {
     if (timed_out && lane == __builtin_ctzll(timed_out)) {
       uint64_t expect = 0;

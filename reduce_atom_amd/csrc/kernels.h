@@ -24,6 +24,7 @@ constexpr int kCopyStages = 8;
 // Workspace: u64 error word at byte 0, u64 ready word at byte 8, then
 // uint64 flags[W][nchunks] and their check-time mirror uint64 mirror[W][nchunks].
 constexpr size_t kWorkspaceHeader = 256;
+constexpr int kLateWord = 2;  // u64 header word: count of chunk waits that found a flag missing
 constexpr uint64_t kDefaultSpinLimit = 1ull << 20;
 
 // Datapath variants of one launch.

@@ -76,18 +76,18 @@ def test_copy_lds(plr, oracle_mod, kind, W):
         assert np.array_equal(from_dev(dst)[:L.dst_bytes], ref), (kind, W, kw, notify)
 
 
-def test_reduce_lds_prefill_share_sampled(plr, oracle_mod):
+def test_reduce_lds_prefill_share_full(plr, oracle_mod):
+    """The prefill share (8 x [8192, 7168] bf16) on the LDS-staged path: every element
+    against the oracle."""
     W, R, C = 8, 8192, 7168
     srcs = [synth.normal_t(0, 3, w, R * C, 0.5, device="cuda") for w in range(W)]
-    dst = torch.empty(R * C, dtype=torch.bfloat16, device="cuda")
+    dst = torch.full((R * C,), float("nan"), dtype=torch.bfloat16, device="cuda")
     L = plr.plr_layout_create("reduce", "bf16", W, R * C * 2, "packed", "packed", datapath=plr.PLR_PATH_LDS)
     plr.plr_reduce(L, srcs, dst)
     torch.cuda.synchronize()
-    rows = np.unique(np.concatenate([[0, R - 1], np.random.default_rng(1).integers(0, R, 62)]))
-    idx = torch.from_numpy(rows).cuda()
-    got = dst.view(R, C)[idx].view(torch.int16).cpu().numpy().view(np.uint16)
-    ref = oracle_mod.reduce("bf16", [s.view(R, C)[idx].view(torch.int16).cpu().numpy().view(np.uint16)
-                                     for s in srcs])
+    got = dst.view(torch.int16).cpu().numpy().view(np.uint16)
+    ref = oracle_mod.reduce("bf16", [s.view(torch.int16).cpu().numpy().view(np.uint16) for s in srcs],
+                            threads=oracle_mod.default_threads())
     assert_same("bf16", got, ref)
 
 

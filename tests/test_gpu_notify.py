@@ -22,6 +22,26 @@ def plr():
 MODES = {"chunks": 1, "check": 2}
 
 
+def _diag(L, ws, op):
+    """(ready word, late counter, check-time mirror of every flag) of a workspace."""
+    words = ws.view(torch.int64).cpu().numpy()
+    nflags = L.nchunks if op == "copy" else L.world * L.nchunks
+    return int(words[1]), int(words[2]), words[32 + nflags: 32 + 2 * nflags]
+
+
+def _assert_waited(L, ws, op, mode, missing=None):
+    """The consumer really found flags missing and polled for them (the late counter
+    grew); in check mode the check kernel saw them missing too (ready word 0, mirror 0
+    for those flags). `missing`: the flags that must have been missing at check time."""
+    ready, late, mirror = _diag(L, ws, op)
+    assert late > 0, "the consumer never had to wait: the producer's stream did not overlap it"
+    if mode == "check":
+        assert ready == 0, ready
+        assert (mirror == 0).any()
+        if missing is not None:
+            assert (mirror[missing] == 0).all()
+
+
 @pytest.mark.parametrize("mode", list(MODES))
 def test_many_calls_without_reset(plr, oracle_mod, mode):
     W, n = 4, 8192
@@ -41,6 +61,10 @@ def test_many_calls_without_reset(plr, oracle_mod, mode):
     assert_same("bf16", dst.cpu().numpy().view(np.uint16), ref)
     flags = ws[256:256 + 8 * W * L.nchunks].view(torch.int64).cpu().numpy()
     assert (flags == 1000).all()
+    ready, late, _ = _diag(L, ws, "reduce")
+    assert late == 0  # every flag was set before its call: no wait ever polled
+    if mode == "check":
+        assert ready == 1000
 
 
 @pytest.mark.parametrize("mode", list(MODES))
@@ -67,12 +91,12 @@ def test_withheld_notify_times_out(plr, op, mode):
 @pytest.mark.parametrize("mode", list(MODES))
 def test_delayed_producer_on_another_stream(plr, oracle_mod, mode):
     """The producer writes poison, sleeps, writes the real data and notifies, all on its
-    own stream; the consumer is queued right after on another stream. Where the two
-    streams run concurrently the consumer reaches the flags long before they are set and
-    must wait for them; its output must be the reduction of the real data, never of the
-    poison. (HIP may also run the streams one after the other; the result must be the
-    same, so the producer is queued first: a consumer queued first on a hardware queue
-    it shares with the producer could only time out.)"""
+    own stream; the consumer is queued right after on another stream, so it reaches the
+    flags long before they are set and must wait for them; its output must be the
+    reduction of the real data, never of the poison. The workspace's diagnostics prove
+    that the wait happened (the late counter grew; in check mode the check found the
+    flags missing). The producer is queued first: a consumer queued first on a hardware
+    queue it shares with the producer could only time out."""
     W, n = 8, 1 << 16
     real_np = [synth.normal_np(2, 2, w, n) for w in range(W)]
     ref = oracle_mod.reduce("bf16", real_np)
@@ -98,6 +122,7 @@ def test_delayed_producer_on_another_stream(plr, oracle_mod, mode):
     torch.cuda.synchronize()
     assert plr.plr_check(L, ws, consumer) == plr.PLR_OK
     assert_same("bf16", dst.cpu().numpy().view(np.uint16), ref)
+    _assert_waited(L, ws, "reduce", mode)
 
 
 @pytest.mark.parametrize("mode", list(MODES))
@@ -134,9 +159,9 @@ def test_tiles_crossing_chunks(plr, oracle_mod, op, mode):
 @pytest.mark.parametrize("op", ["reduce", "copy"])
 def test_check_mode_partial_arrival(plr, oracle_mod, op):
     """Check mode where half the sources are notified before the call and half by a
-    delayed producer on a second stream: when the streams overlap the check finds flags
-    missing and the consumer takes the per-chunk path; the late sources are still waited
-    for."""
+    delayed producer on a second stream: the check finds the late sources' flags missing
+    (and only those) and the consumer takes the per-chunk path and waits for them, which
+    the workspace's diagnostics confirm."""
     W, nbytes = 4, 64 * 1024
     real_np = [synth.bits_np(7, 4, s, nbytes) for s in range(W)]
     if op == "reduce":
@@ -173,6 +198,11 @@ def test_check_mode_partial_arrival(plr, oracle_mod, op):
         assert np.array_equal(dst.cpu().numpy().view(np.uint16), ref)
     else:
         assert_same("bf16", dst.cpu().numpy().view(np.uint16), ref)
+    # the late sources' flags were missing at check time, the early ones were not
+    nflags = L.nchunks if op == "copy" else W * L.nchunks
+    late_flags = np.arange(nflags // 2, nflags)  # sources 2 and 3: the second half
+    _assert_waited(L, ws, op, "check", missing=late_flags)
+    assert (_diag(L, ws, op)[2][: nflags // 2] == 1).all()
 
 
 def test_check_mode_many_flags(plr, oracle_mod):
@@ -243,3 +273,4 @@ def test_allgatherv_cut_tiles_wait_for_both_chunks(plr, oracle_mod, mode):
     torch.cuda.synchronize()
     assert plr.plr_check(L, ws, consumer) == plr.PLR_OK
     assert np.array_equal(dst.cpu().numpy(), ref)
+    _assert_waited(L, ws, "copy", mode)

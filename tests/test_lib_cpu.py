@@ -402,3 +402,50 @@ def test_reduce_unroll_fits_the_registers(plr):
         assert L.policy()["unroll"] == want, W
     C = plr.plr_layout_create("copy", "bf16", 16, 16 * 64, "packed", "packed", unroll=4)
     assert C.policy()["unroll"] == 4
+
+
+def test_copy_v_scatter_covers_every_tile(tmp_path):
+    """The row scatter's run-to-workgroup mapping (reduce_atom_amd/csrc/copy_v_grid.h, the
+    functions its launcher and kernel use) moves every tile exactly once, also when the
+    column cap makes columns stride and in the small form, whose last column moves no
+    tile. Built and run on the host with a lowered cap."""
+    exe = tmp_path / "cv_grid_check"
+    subprocess.run(["g++", "-std=c++17", "-O1", "-Wall", "-Werror",
+                    "-I", os.path.join(ROOT, "reduce_atom_amd", "csrc"),
+                    os.path.join(ROOT, "tests", "host", "cv_grid_check.cpp"), "-o", str(exe)], check=True)
+    r = subprocess.run([str(exe)], capture_output=True, text=True)
+    assert r.returncode == 0, r.stdout + r.stderr
+    assert r.stdout.startswith("ok")
+
+
+def test_binding_checks_list_lengths(plr):
+    """The binding refuses lists whose length differs from what the C side reads (it
+    would read past a short array and hand the kernels garbage addresses), and
+    destination tensors that are not int32. Integer addresses: nothing is launched."""
+    import torch
+
+    L = plr.plr_layout_create("reduce", "bf16", 4, 4096, "packed", "packed")
+    with pytest.raises(ValueError, match="srcs"):
+        plr.plr_reduce(L, [16, 32, 48], 4096 * 16)
+    C = plr.plr_layout_create("copy", "bf16", 4, 4096, "packed", "packed")
+    with pytest.raises(ValueError, match="srcs"):
+        plr.plr_copy(C, [16] * 5, 1 << 20)
+    A = plr.plr_layout_create("allreduce", "bf16", 2, 4096, "scattered", "scattered")
+    with pytest.raises(ValueError, match="dsts"):
+        plr.plr_allreduce(A, [16, 32], [64])
+    with pytest.raises(ValueError, match="packets"):
+        plr.plr_reduce_packets(L, [16], 1 << 20, 1 << 21)
+    with pytest.raises(ValueError, match="in_offsets"):
+        plr.plr_layout_create("reduce", "bf16", 4, 4096, "packed", "packed", in_offsets=[0, 0, 0])
+    with pytest.raises(ValueError, match="out_offsets"):
+        plr.plr_layout_create("copy", "bf16", 2, 4096, "scattered", "transposed", out_offsets=[0, 0])
+    with pytest.raises(ValueError, match="part_bytes"):
+        plr.plr_layout_create("copy", "bf16", 3, 4096, "packed", "packed", part_bytes=[2048, 2048])
+    with pytest.raises(ValueError, match="rows_per_src"):
+        plr.plr_copy_v([16, 32], [4], [64, 80], 64, 1 << 20, 1 << 21, 1 << 22, 1 << 23)
+    with pytest.raises(ValueError, match="dest_of_row"):
+        plr.plr_copy_v([16, 32], [4, 4], [64], 64, 1 << 20, 1 << 21, 1 << 22, 1 << 23)
+    with pytest.raises(ValueError, match="int32"):
+        plr.plr_copy_v([16], [4], [torch.zeros(4, dtype=torch.int64)], 64, 1 << 20, 1 << 21, 1 << 22, 1 << 23)
+    with pytest.raises(ValueError, match="rows_per_src"):
+        plr.plr_copy_v_scratch_bytes(3, [1, 2])
