@@ -58,7 +58,8 @@ enum {
   PLR_EALIGN = 2,        /* an address or byte count is not a multiple of 16 */
   PLR_EUNSUPPORTED = 3,  /* W > 16, a non-deterministic reduction mode, too many explicit segments */
   PLR_EHIP = 4,          /* a HIP runtime call or kernel launch failed */
-  PLR_ETIMEOUT = 5       /* device side: a chunk's notification did not arrive in time */
+  PLR_ETIMEOUT = 5,      /* device side: a chunk's notification did not arrive in time */
+  PLR_ETOOLARGE = 6      /* the request exceeds the fixed scratch of an allocation-free entry point */
 };
 
 /* ---- element types (the reduction accumulates in binary32 for all of them) ---- */
@@ -310,6 +311,24 @@ int plr_copy_v(int world, const void* const* srcs, const int64_t* rows_per_src,
  * and 16 int32 first output rows, each region rounded up to 256 bytes. 0 for invalid
  * arguments. */
 size_t plr_copy_v_scratch_bytes(int world, const int64_t* rows_per_src);
+
+/* Allocation-free form of plr_copy_v, for callers that cannot allocate device memory
+ * (code under stream capture, tight serving loops, harnesses that forbid allocation):
+ * the same operation, arguments and results as plr_copy_v, without the scratch
+ * argument. Its scratch is a fixed array of plr_copy_v_noalloc_max_scratch_bytes()
+ * bytes (4 MiB) in the library's device code, one per GPU, held until the process ends;
+ * no call allocates or frees memory. A request whose plr_copy_v_scratch_bytes exceeds
+ * that size (about a million rows in all) returns PLR_ETOOLARGE and launches nothing.
+ * Every call on one GPU shares that GPU's array: calls that overlap on one GPU (on
+ * different streams, or from different threads) race and must not be issued. The
+ * kernels run on the stream's device (the current device for the NULL stream).
+ * Errors: as plr_copy_v, plus PLR_ETOOLARGE. */
+int plr_copy_v_noalloc(int world, const void* const* srcs, const int64_t* rows_per_src,
+                       const int32_t* const* dest_of_row, size_t row_bytes, void* dst,
+                       int64_t* counts, int64_t* offsets, void* stream);
+
+/* Size in bytes of plr_copy_v_noalloc's fixed scratch. */
+size_t plr_copy_v_noalloc_max_scratch_bytes(void);
 
 /* Producer side of notify (section 3.2 "SNAC"; section 4.3: the epoch supplies the
  * notification value): release-stores E+1 into every chunk flag of source `src`

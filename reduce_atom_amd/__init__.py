@@ -31,7 +31,7 @@ import torch  # noqa: E402,F401
 _lib = ctypes.CDLL(LIB_PATH)
 
 # ---- constants (include/plr.h) ----
-PLR_OK, PLR_EINVAL, PLR_EALIGN, PLR_EUNSUPPORTED, PLR_EHIP, PLR_ETIMEOUT = range(6)
+PLR_OK, PLR_EINVAL, PLR_EALIGN, PLR_EUNSUPPORTED, PLR_EHIP, PLR_ETIMEOUT, PLR_ETOOLARGE = range(7)
 PLR_BF16, PLR_F16, PLR_F32 = 0, 1, 2
 PLR_OP_REDUCE, PLR_OP_COPY, PLR_OP_ALLREDUCE = 0, 1, 2
 PLR_PACKED, PLR_SCATTERED, PLR_TRANSPOSED = 0, 1, 2
@@ -97,6 +97,10 @@ _lib.plr_copy_v.argtypes = [_i, _c.POINTER(_vp), _i64p, _c.POINTER(_vp), _sz, _v
 _lib.plr_copy_v.restype = _i
 _lib.plr_copy_v_scratch_bytes.argtypes = [_i, _i64p]
 _lib.plr_copy_v_scratch_bytes.restype = _sz
+_lib.plr_copy_v_noalloc.argtypes = [_i, _c.POINTER(_vp), _i64p, _c.POINTER(_vp), _sz, _vp, _vp, _vp, _vp]
+_lib.plr_copy_v_noalloc.restype = _i
+_lib.plr_copy_v_noalloc_max_scratch_bytes.argtypes = []
+_lib.plr_copy_v_noalloc_max_scratch_bytes.restype = _sz
 _lib.plr_notify.argtypes = [_vp, _i, _vp, _vp]
 _lib.plr_notify.restype = _i
 _lib.plr_check.argtypes = [_vp, _vp, _vp]
@@ -116,6 +120,7 @@ EXPORTS = [
     "plr_layout_create", "plr_layout_destroy", "plr_layout_workspace_bytes", "plr_layout_dst_bytes",
     "plr_layout_nchunks", "plr_layout_ntiles", "plr_layout_nsegments", "plr_layout_segment", "plr_layout_policy",
     "plr_layout_epoch", "plr_reduce", "plr_copy", "plr_allreduce", "plr_copy_v", "plr_copy_v_scratch_bytes",
+    "plr_copy_v_noalloc", "plr_copy_v_noalloc_max_scratch_bytes",
     "plr_layout_packet_bytes", "plr_pack", "plr_reduce_packets",
     "plr_notify", "plr_check", "plr_set_timing_events", "plr_set_timing_events_split", "plr_strerror",
     "plr_last_hip_error",
@@ -337,6 +342,17 @@ def plr_copy_v(srcs, rows_per_src, dest_of_row, row_bytes, dst, counts, offsets,
     W, rows = _copy_v_lists(srcs, rows_per_src, dest_of_row)
     _ok(_lib.plr_copy_v(W, _ptrs(srcs), rows, _ptrs(dest_of_row), row_bytes, _addr(dst),
                         _addr(counts), _addr(offsets), _addr(scratch), _stream(stream)), "plr_copy_v")
+
+
+def plr_copy_v_noalloc(srcs, rows_per_src, dest_of_row, row_bytes, dst, counts, offsets, stream=None) -> None:
+    """plr_copy_v with the library's fixed per-GPU scratch instead of a caller buffer."""
+    W, rows = _copy_v_lists(srcs, rows_per_src, dest_of_row)
+    _ok(_lib.plr_copy_v_noalloc(W, _ptrs(srcs), rows, _ptrs(dest_of_row), row_bytes, _addr(dst),
+                                _addr(counts), _addr(offsets), _stream(stream)), "plr_copy_v_noalloc")
+
+
+def plr_copy_v_noalloc_max_scratch_bytes() -> int:
+    return _lib.plr_copy_v_noalloc_max_scratch_bytes()
 
 
 def plr_notify(layout: Layout, src: int, workspace, stream=None) -> None:

@@ -32,7 +32,7 @@ DEVICE = [f"--offload-arch={ARCH}", "-Xclang", "-target-feature", "-Xclang", "-p
           "-fno-gpu-rdc"]
 
 SOURCES = ["api.cpp", "layout.cpp", "reduce.hip", "copy.hip", "copy_v.hip", "notify.hip", "allreduce.hip",
-           "packets.hip"]
+           "packets.hip", "noalloc.hip"]
 
 
 def _compile(src: str, build_dir: str = BUILD, defines=(), csrc: str = CSRC) -> str:

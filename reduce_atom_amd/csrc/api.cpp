@@ -16,10 +16,7 @@ thread_local int g_last_hip = 0;
 
 thread_local Timing g_timing = {nullptr, nullptr, nullptr, nullptr};
 
-int hip_fail(hipError_t e) {
-  g_last_hip = (int)e;
-  return PLR_EHIP;
-}
+int hip_fail(hipError_t e) { return plr::record_hip_error(e); }
 
 bool a16(const void* p) { return ((uintptr_t)p & 15) == 0; }
 
@@ -90,6 +87,11 @@ hipError_t launch_check_for(const plr_layout* L, const Notify& nt, hipStream_t s
 }  // namespace
 
 const Timing& plr::timing() { return g_timing; }
+
+int plr::record_hip_error(hipError_t e) {
+  g_last_hip = (int)e;
+  return PLR_EHIP;
+}
 
 extern "C" int plr_reduce(plr_layout* L, const void* const* srcs, void* dst, void* workspace,
                           void* stream) {
@@ -436,6 +438,7 @@ extern "C" const char* plr_strerror(int code) {
     case PLR_EUNSUPPORTED: return "unsupported configuration";
     case PLR_EHIP: return "HIP runtime error";
     case PLR_ETIMEOUT: return "chunk notification timed out";
+    case PLR_ETOOLARGE: return "request needs more scratch than the allocation-free entry point holds";
     default: return "unknown error";
   }
 }

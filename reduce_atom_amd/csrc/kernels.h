@@ -197,6 +197,9 @@ struct Timing {
 };
 const Timing& timing();
 
+// Keeps e as the calling thread's last HIP error (plr_last_hip_error); returns PLR_EHIP.
+int record_hip_error(hipError_t e);
+
 // Launchers (defined next to their kernels). Return a hipError_t.
 hipError_t launch_reduce(const ReduceArgs& a, int dtype, const Launch& l, hipStream_t s);
 hipError_t launch_copy(const CopyArgs& a, const Launch& l, hipStream_t s);

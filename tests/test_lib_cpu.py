@@ -237,9 +237,10 @@ def test_scratch_bytes(plr):
 
 
 def test_strerror(plr):
-    for code in range(6):
-        assert plr.plr_strerror(code)
+    for code in range(7):
+        assert plr.plr_strerror(code) != "unknown error"
     assert "timed out" in plr.plr_strerror(plr.PLR_ETIMEOUT)
+    assert "scratch" in plr.plr_strerror(plr.PLR_ETOOLARGE)
     assert plr.plr_version().startswith("plr")
 
 
@@ -449,3 +450,28 @@ def test_binding_checks_list_lengths(plr):
         plr.plr_copy_v([16], [4], [torch.zeros(4, dtype=torch.int64)], 64, 1 << 20, 1 << 21, 1 << 22, 1 << 23)
     with pytest.raises(ValueError, match="rows_per_src"):
         plr.plr_copy_v_scratch_bytes(3, [1, 2])
+
+
+def test_copy_v_noalloc_limits_without_device(plr):
+    """The allocation-free copy_v: its fixed scratch size, and requests beyond it (or
+    with invalid row counts) rejected on the host before any device call."""
+    cap = plr.plr_copy_v_noalloc_max_scratch_bytes()
+    assert cap == 4 << 20
+    lib = ctypes.CDLL(plr.LIB_PATH)
+    fn = lib.plr_copy_v_noalloc
+    fn.restype = ctypes.c_int
+    vp = ctypes.c_void_p
+    fn.argtypes = [ctypes.c_int, ctypes.POINTER(vp), ctypes.POINTER(ctypes.c_int64), ctypes.POINTER(vp),
+                   ctypes.c_size_t, vp, vp, vp, vp]
+    ptrs = (vp * 2)(16, 32)
+
+    def call(rows):
+        r = (ctypes.c_int64 * 2)(*rows)
+        return fn(2, ptrs, r, ptrs, 64, 1 << 30, 1 << 31, 1 << 32, None)
+
+    too_many = cap // 4  # one key of 4 bytes per row alone fills the scratch
+    assert plr.plr_copy_v_scratch_bytes(2, [too_many, 0]) > cap
+    assert call([too_many, 0]) == plr.PLR_ETOOLARGE
+    assert call([-1, 4]) == plr.PLR_EINVAL
+    assert fn(0, ptrs, (ctypes.c_int64 * 2)(1, 1), ptrs, 64, 1, 2, 3, None) == plr.PLR_EINVAL
+    assert fn(17, ptrs, (ctypes.c_int64 * 2)(1, 1), ptrs, 64, 1, 2, 3, None) == plr.PLR_EUNSUPPORTED
