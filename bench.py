@@ -243,6 +243,16 @@ def make_inputs(torch, synth, seed, dev):
     return x
 
 
+def host_inputs(torch, x):
+    """The step's inputs as host numpy arrays (raw element bits), for the oracle."""
+    import numpy as np
+
+    def h(t):
+        return t.view(torch.uint8).cpu().numpy()
+    return {"r_src": [h(t).view(np.uint16) for t in x["r_src"]], "c_src": [h(t) for t in x["c_src"]],
+            "v_src": [h(t) for t in x["v_src"]], "v_dest": [t.cpu().numpy() for t in x["v_dest"]]}
+
+
 def run_bench(args):
     import torch
 
@@ -340,12 +350,16 @@ def run_bench(args):
                   "GB/s": round(BYTES[n] / (per_op_us[n] * 1e-6) / 1e9, 1),
                   "frac": round(BYTES[n] / (per_op_us[n] * 1e-6) / 1e9 / PEAK_HBM_GBS, 4)}
               for n in ops}
+    per_op["target_frac"] = 0.8
+    per_op["meets_target"] = {n: per_op[n]["frac"] >= 0.8 for n in ops}
+    # the oracle's CPU baseline runs on these same input bytes, copied to the host
+    host = None if args.no_cpu_baseline else host_inputs(torch, x)
     del x, ws, scratch
     torch.cuda.empty_cache()
     decode = run_decode(args, torch, plr, synth, dev) if not args.no_decode else None
     if decode is not None:
         decode = {"decode": decode, "local": run_local_reduce(args, torch, plr, synth, dev)}
-    return value, ms_per_step, ms_per_step_events, roofline, per_op, decode
+    return value, ms_per_step, ms_per_step_events, roofline, per_op, decode, host
 
 
 def run_decode(args, torch, plr, synth, dev):
@@ -419,6 +433,138 @@ def run_decode(args, torch, plr, synth, dev):
                          "event_pair_p90_us": round(us[int(len(us) * 0.9)], 2)}
         out[f"T={T}"] = res
     return out
+
+
+DECODE_COLD_BYTES = 512 << 20  # the cold decode runs rotate over this much source memory
+CONSUMERS = ("k_reduce_direct", "k_reduce_packets")
+PRODUCERS = ("k_notify", "k_pack")
+
+
+def run_decode_trace_child(args):
+    """Decode-size reduce calls for a kernel trace (run under rocprofv3 by
+    run_decode_trace): for every T and mode (notify off, notify on, packets), warm (the
+    same sources every call) and cold (each call's sources at another place of a
+    512 MiB region, so that they are not in the L2 or the Infinity Cache), --decode-warmup
+    calls and then --decode-iters calls, each one producer step (notify on: k_notify;
+    packets: k_pack) and one consumer kernel. Prints the schedule as JSON."""
+    import torch
+
+    import reduce_atom_amd as plr
+    import synth
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    big = torch.empty(DECODE_COLD_BYTES, dtype=torch.uint8, device=dev)
+    sched = []
+    for T in (args.decode_t or DECODE_T):
+        n = T * 7168
+        nb = 2 * n
+        srcs = [synth.normal_t(args.seed, 2, w, n, 1.0, device=dev) for w in range(W)]
+        sets = DECODE_COLD_BYTES // (W * nb)
+        cold = big[: sets * W * nb].view(sets, W, nb)
+        cold.copy_(torch.stack([x.view(torch.uint8) for x in srcs]).unsqueeze(0).expand(sets, W, nb))
+        cold_lists = [[cold[k, w] for w in range(W)] for k in range(min(sets, args.decode_warmup + args.decode_iters))]
+        dst = torch.empty(n, dtype=torch.bfloat16, device=dev)
+        for mode in ("notify_off", "notify_on", "packets"):
+            L = plr.plr_layout_create("reduce", "bf16", W, nb, "packed", "packed")
+            ws = torch.zeros(max(L.workspace_bytes, 256), dtype=torch.uint8, device=dev) if mode != "notify_off" else None
+            pk = [torch.zeros(L.packet_bytes, dtype=torch.uint8, device=dev) for _ in range(W)] \
+                if mode == "packets" else None
+            for temp in ("warm", "cold"):
+                for i in range(args.decode_warmup + args.decode_iters):
+                    s_i = srcs if temp == "warm" else cold_lists[i % len(cold_lists)]
+                    if pk is not None:
+                        plr.plr_pack(L, -1, s_i, pk)
+                        plr.plr_reduce_packets(L, pk, dst, ws)
+                    else:
+                        if ws is not None:
+                            plr.plr_notify(L, -1, ws)
+                        plr.plr_reduce(L, s_i, dst, ws)
+                sched.append([T, mode, temp, args.decode_warmup, args.decode_iters])
+            torch.cuda.synchronize()
+            if ws is not None and plr.plr_check(L, ws) != plr.PLR_OK:
+                raise RuntimeError(f"decode trace T={T} {mode}: device error")
+        print(f"decode trace: T={T} done", file=sys.stderr, flush=True)
+    print(json.dumps({"decode_trace_schedule": sched}), flush=True)
+
+
+def _pct(v, q):
+    return v[min(len(v) - 1, int(len(v) * q))]
+
+
+def parse_decode_trace(path, sched):
+    """Per (T, mode, warm / cold) statistics of the consumer kernel's traced duration from
+    a rocprofv3 kernel-trace CSV, walking the dispatches in start order along the child's
+    schedule [T, mode, temp, warmup calls, timed calls]: each call has one consumer
+    dispatch, and one producer dispatch unless the mode is notify_off."""
+    import csv
+
+    cons, prod = [], []
+    with open(path) as f:
+        for row in csv.DictReader(f):
+            name = row["Kernel_Name"]
+            t0 = int(row["Start_Timestamp"])
+            us = (int(row["End_Timestamp"]) - t0) / 1000.0
+            if any(k in name for k in CONSUMERS):
+                cons.append((t0, us))
+            elif any(k in name for k in PRODUCERS):
+                prod.append((t0, us))
+    cons.sort()
+    prod.sort()
+    out, ci, pi = {}, 0, 0
+    for T, mode, temp, nw, ni in sched:
+        c = sorted(us for _, us in cons[ci + nw: ci + nw + ni])
+        ci += nw + ni
+        if len(c) != ni:
+            return {"error": f"trace holds {len(cons)} consumer dispatches, fewer than the schedule"}
+        row = {"p50_us": round(_pct(c, 0.5), 2), "p90_us": round(_pct(c, 0.9), 2),
+               "mean_us": round(statistics.mean(c), 2), "min_us": round(c[0], 2), "calls": len(c)}
+        if mode != "notify_off":
+            p = sorted(us for _, us in prod[pi + nw: pi + nw + ni])
+            pi += nw + ni
+            row["producer_p50_us"] = round(_pct(p, 0.5), 2) if p else None
+        out.setdefault(f"T={T}", {}).setdefault(mode, {})[temp] = row
+    if ci != len(cons) or pi != len(prod):
+        return {"error": f"trace holds {len(cons)} consumer and {len(prod)} producer dispatches, "
+                         f"the schedule {ci} and {pi}"}
+    out["source"] = ("rocprofv3 kernel trace: consumer kernel duration per call (k_reduce_direct; packets: "
+                     "k_reduce_packets), after the warmup calls; producer: k_notify / k_pack")
+    return out
+
+
+def run_decode_trace(args):
+    """Kernel-trace latency of the decode-size reduce: this script's
+    --decode-trace-child under `rocprofv3 --kernel-trace` in a child process (started
+    before this process touches the GPU), then p50 / p90 of the consumer kernel's traced
+    duration (k_reduce_direct, or k_reduce_packets for packets) per T, mode and warm /
+    cold, with the producer kernel's p50 beside it."""
+    import shutil
+    import subprocess
+    import tempfile
+
+    prof = shutil.which("rocprofv3")
+    if prof is None:
+        return {"error": "rocprofv3 not found"}
+    d = tempfile.mkdtemp(prefix="plr_decode_trace_")
+    cmd = [prof, "--kernel-trace", "--output-format", "csv", "-d", d, "-o", "dec", "--", sys.executable,
+           os.path.abspath(__file__), "--decode-trace-child", "--decode-iters", str(args.decode_iters),
+           "--decode-warmup", str(args.decode_warmup), "--seed", str(args.seed)]
+    if args.decode_t:
+        cmd += ["--decode-t", ",".join(str(t) for t in args.decode_t)]
+    try:
+        r = subprocess.run(cmd, stdout=subprocess.PIPE, text=True, timeout=600)
+        sched = None
+        for line in r.stdout.splitlines():
+            if line.startswith('{"decode_trace_schedule"'):
+                sched = json.loads(line)["decode_trace_schedule"]
+        path = os.path.join(d, "dec_kernel_trace.csv")
+        if sched is None or not os.path.exists(path):
+            return {"error": f"trace run ended with status {r.returncode} without its schedule or trace"}
+        return parse_decode_trace(path, sched)
+    except subprocess.TimeoutExpired:
+        return {"error": "trace run timed out"}
+    finally:
+        shutil.rmtree(d, ignore_errors=True)
 
 
 def _time_calls(torch, plr, fn, n=10, warm=3):
@@ -811,40 +957,65 @@ def run_atom_user_kernels(torch, srcs):
     return out
 
 
-def run_cpu_baseline(args):
-    """The oracle, as it stands, on a bounded sample of the same step (a fraction of
-    every op's data), on this host's CPU, single-threaded."""
-    import numpy as np
-    import torch
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
 
+
+def run_cpu_baseline(args, host):
+    """The oracle, as it stands, on this host's CPU, on the same input bytes as the GPU
+    step: on all the cores this process may use (the oracle's threaded form, at most 16
+    threads) over the whole step, and single-threaded over a fraction of every op
+    (--cpu-fraction) to bound the run time; median of --cpu-reps runs after one warmup
+    run each. GB/s from the same algorithmic byte counts as the GPU figures."""
     import oracle
-    import synth
 
     f = args.cpu_fraction
     rr = max(1, int(R3 * f))
-    red = [synth.normal_t(args.seed, 3, w, rr * C3, 0.5).view(torch.int16).numpy().view(np.uint16)
-           for w in range(W)]
     bb = max(16 * W, int(B4 * f) // (16 * W) * (16 * W))
-    cps = [synth.bits_np(args.seed, 4, s, bb) for s in range(W)]
     rv = max(1, int(R5 * f))
-    p = synth.zipf_weights(1.1, W)
-    vs = [synth.bits_np(args.seed, 6, s, rv * RB5) for s in range(W)]
-    vd = [synth.categorical_np(args.seed, 5, s, rv, p) for s in range(W)]
-    sample_bytes = ((W + 1) * rr * C3 * 2 + 2 * (2 * W * bb) + 2 * W * rv * RB5 + W * rv * 4)
-    times = []
-    for _ in range(args.cpu_reps):
-        t = time.perf_counter()
-        oracle.reduce("bf16", red)
-        oracle.copy_layout("packed", "packed", cps)
-        oracle.copy_layout("scattered", "transposed", cps)
-        oracle.copy_v(vs, vd, RB5)
-        times.append(time.perf_counter() - t)
-    tmed = statistics.median(times)
-    return {"value": round(sample_bytes / tmed / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
-            "sample": (f"fraction {f} of every op of one step: reduce {rr} of {R3} rows, "
-                       f"allgather/alltoall {bb} of {B4} bytes per source, alltoallv {rv} of {R5} rows "
-                       f"per source; median of {args.cpu_reps} runs of {tmed:.2f} s"),
-            "seconds": round(tmed, 3)}
+    full_bytes = sum(BYTES.values())
+    part_bytes = (W + 1) * rr * C3 * 2 + 2 * (2 * W * bb) + 2 * W * rv * RB5 + W * rv * 4
+    red_part = [a[: rr * C3] for a in host["r_src"]]
+    cps_part = [a[:bb] for a in host["c_src"]]
+    vs_part = [a[: rv * RB5] for a in host["v_src"]]
+    vd_part = [a[:rv] for a in host["v_dest"]]
+
+    def step(threads, red, cps, vs, vd):
+        oracle.reduce("bf16", red, threads=threads)
+        oracle.copy_layout("packed", "packed", cps, threads=threads)
+        oracle.copy_layout("scattered", "transposed", cps, threads=threads)
+        oracle.copy_v(vs, vd, RB5, threads=threads)
+
+    def timed(fn):
+        fn()  # warmup
+        times = []
+        for _ in range(args.cpu_reps):
+            t = time.perf_counter()
+            fn()
+            times.append(time.perf_counter() - t)
+        return statistics.median(times)
+
+    cores = oracle.default_threads()
+    t_all = timed(lambda: step(cores, host["r_src"], host["c_src"], host["v_src"], host["v_dest"]))
+    t_one = timed(lambda: step(1, red_part, cps_part, vs_part, vd_part))
+    one = {"value": round(part_bytes / t_one / 1e9, 4), "unit": "GB/s", "cores": 1,
+           "sample": (f"fraction {f} of every op of the step (reduce {rr} of {R3} rows, allgather/alltoall "
+                      f"{bb} of {B4} bytes per source, alltoallv {rv} of {R5} rows per source); median of "
+                      f"{args.cpu_reps} runs of {t_one:.2f} s after one warmup run"),
+           "seconds": round(t_one, 3)}
+    return {"value": round(full_bytes / t_all / 1e9, 4), "unit": "GB/s", "cores": cores, "kind": "oracle",
+            "sample": (f"the whole step (all four ops, the GPU step's own input bytes) on {cores} threads; "
+                       f"median of {args.cpu_reps} runs of {t_all:.2f} s after one warmup run"),
+            "seconds": round(t_all, 3), "single_core": one,
+            "host": {"cpu_model": cpu_model(), "hardware_threads": oracle.hardware_threads(),
+                     "threads_available": len(os.sched_getaffinity(0))}}
 
 
 def main():
@@ -861,6 +1032,9 @@ def main():
     ap.add_argument("--decode-t", type=lambda v: [int(x) for x in v.split(",")], default=None,
                     help="decode token counts T (comma separated; default 1,8,32,64)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-decode-trace", action="store_true",
+                    help="skip the kernel-trace run of the decode-size reduce (rocprofv3 child process)")
+    ap.add_argument("--decode-trace-child", action="store_true", help=argparse.SUPPRESS)
     ap.add_argument("--v-sweep", action="store_true",
                     help="only the AllGatherV / ReduceScatterV sweep over T = 1 KiB .. 1 GiB, as JSON")
     ap.add_argument("--collective", choices=COLLECTIVES + ("all",),
@@ -869,8 +1043,9 @@ def main():
     ap.add_argument("--max-bytes", type=int, default=1 << 30)
     ap.add_argument("--graph-launches", type=int, default=10)
     ap.add_argument("--runs", type=int, default=20)
-    ap.add_argument("--cpu-fraction", type=float, default=0.5)
-    ap.add_argument("--cpu-reps", type=int, default=3)
+    ap.add_argument("--cpu-fraction", type=float, default=0.25,
+                    help="fraction of every op the single-threaded oracle baseline runs on")
+    ap.add_argument("--cpu-reps", type=int, default=5)
     ap.add_argument("--summarize-trace", metavar="CSV",
                     help="print per-kernel durations of a rocprofv3 kernel-trace CSV and exit")
     ap.add_argument("--summarize-counters", metavar="CSV",
@@ -918,20 +1093,28 @@ def main():
         print(json.dumps({"collective_sweep": run_collective_sweep(args), "graph_launches": args.graph_launches,
                           "runs": args.runs, "warmup": args.warmup, "seed": args.seed}), flush=True)
         return
+    if args.decode_trace_child:
+        run_decode_trace_child(args)
+        return
+    # before this process touches the GPU: the decode kernel trace runs in a child
+    trace = None if (args.no_decode or args.no_decode_trace) else run_decode_trace(args)
     if args.decode_only:
         import torch
 
         import reduce_atom_amd as plr
         import synth
 
-        print(json.dumps({"decode_reduce_us": run_decode(args, torch, plr, synth, torch.device("cuda:0"))}),
-              flush=True)
+        dec = run_decode(args, torch, plr, synth, torch.device("cuda:0"))
+        print(json.dumps({"decode_reduce_us": {"kernel_trace": trace, **dec}}), flush=True)
         return
-    value, ms, ms_events, roofline, per_op, small = run_bench(args)
+    value, ms, ms_events, roofline, per_op, small, host = run_bench(args)
     decode = small["decode"] if small else None
     local = small["local"] if small else None
     nxt = None if args.no_decode else run_next(args)
-    cpu = None if args.no_cpu_baseline else run_cpu_baseline(args)
+    cpu = None if host is None else run_cpu_baseline(args, host)
+    del host
+    if decode is not None and trace is not None:
+        decode = {"kernel_trace": trace, **decode}
     line = {
         "metric": METRIC, "value": round(value, 1), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": round(ms, 4), "higher_is_better": True, "scaling": "weak",

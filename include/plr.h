@@ -254,7 +254,10 @@ int plr_copy(plr_layout* L, const void* const* srcs, void* dst, void* workspace,
  *             the rank that owns k's slice and releases a per-tile flag, then acquires
  *             the flag of tile k-lag and copies that tile into the other W-1 outputs):
  *             required, plr_layout_workspace_bytes(L) bytes, zeroed once; the layout's
- *             epoch advances per call. Producer-side notification does not apply.
+ *             epoch advances per call. Producer-side notification does not apply. All
+ *             ntiles + 16 workgroups of a composed call must be resident at once (one per
+ *             compute unit, 256): plr_layout_create refuses a composed layout whose tile_bytes
+ *             override needs more with PLR_EUNSUPPORTED.
  * Errors: PLR_EINVAL (wrong op, NULL, overlaps, missing workspace), PLR_EALIGN, PLR_EHIP;
  * a composed call whose flags never arrive reports PLR_ETIMEOUT through plr_check. */
 int plr_allreduce(plr_layout* L, const void* const* srcs, void* const* dsts, void* workspace,

@@ -332,6 +332,12 @@ extern "C" int plr_layout_create(const plr_layout_desc* d, plr_layout** out) {
       L->tiles_per_seg = (uint32_t)tps;  // tiles per slice
       L->tiles_per_chunk = L->chunks_per_seg = 1;
       L->ntiles = L->nchunks = (uint32_t)(tps * W);
+      // The composed kernel's gatherers wait for reducers of lower workgroup ids; with
+      // every workgroup of the call resident at once (one per CU at most) each waited-for
+      // reducer is running, whatever order the workgroups are dispatched in. A caller's
+      // tile size that needs more workgroups than that is refused.
+      if (L->datapath == PLR_PATH_COMPOSED && (uint64_t)L->ntiles + (uint64_t)L->lag > kCus)
+        return fail(PLR_EUNSUPPORTED);
     }
   } else if (L->seg_len == 0) {
     L->tiles_per_seg = L->tiles_per_chunk = L->chunks_per_seg = 0;

@@ -86,3 +86,35 @@ def test_command_line_contract(args, msg):
     r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), *args], capture_output=True, text=True,
                        timeout=120)
     assert r.returncode != 0 and msg in r.stderr, (r.returncode, r.stderr)
+
+
+def test_parse_decode_trace_walks_the_schedule(tmp_path):
+    """The decode kernel trace is cut along the child's schedule: warmup dispatches are
+    skipped, producers count only where the mode has one, and a trace that does not match
+    the schedule is reported, not misattributed."""
+    import bench
+
+    rows = ["Kernel_Name,Start_Timestamp,End_Timestamp"]
+    t = 0
+
+    def add(name, us):
+        nonlocal t
+        rows.append(f"\"{name}\",{t},{t + int(us * 1000)}")
+        t += 100000
+
+    add("at::native::fill_kernel", 1.0)
+    for us in (9.0, 3.0, 3.0, 5.0):  # notify_off warm: 1 warmup + 3 timed
+        add("void plr::k_reduce_direct<0, 8, 1>(plr::ReduceArgs)", us)
+    for us in (9.0, 4.0, 6.0, 4.0):  # notify_on warm
+        add("void plr::k_notify(plr::NotifyArgs)", 2.0)
+        add("void plr::k_reduce_direct<0, 8, 1>(plr::ReduceArgs)", us)
+    path = tmp_path / "dec_kernel_trace.csv"
+    path.write_text("\n".join(rows) + "\n")
+    sched = [[1, "notify_off", "warm", 1, 3], [1, "notify_on", "warm", 1, 3]]
+    out = bench.parse_decode_trace(str(path), sched)
+    assert out["T=1"]["notify_off"]["warm"]["p50_us"] == 3.0
+    assert out["T=1"]["notify_off"]["warm"]["calls"] == 3
+    assert out["T=1"]["notify_on"]["warm"]["p50_us"] == 4.0
+    assert out["T=1"]["notify_on"]["warm"]["producer_p50_us"] == 2.0
+    assert "error" in bench.parse_decode_trace(str(path), sched + [[8, "notify_off", "warm", 1, 3]])
+    assert "error" in bench.parse_decode_trace(str(path), sched[:1])

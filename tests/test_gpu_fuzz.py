@@ -171,6 +171,15 @@ def test_fuzz_allreduce(plr, oracle_mod, seed):
     eb = EB[dtype]
     srcs_np = [synth.normal_np(seed, 14, w, B // eb, 1.0, dtype) for w in range(W)]
     ref = oracle_mod.allreduce(dtype, srcs_np)
+    if path == plr.PLR_PATH_COMPOSED and "tile_bytes" in pol:
+        # composed calls must fit one round of workgroups (ntiles + 16 <= 256 CUs)
+        slice_ = B // W
+        tps = -(-slice_ // min(pol["tile_bytes"], slice_))
+        if W * tps + 16 > 256:
+            with pytest.raises(plr.PlrError) as e:
+                plr.plr_layout_create("allreduce", dtype, W, B, "scattered", "scattered", datapath=path, **pol)
+            assert e.value.code == plr.PLR_EUNSUPPORTED, what
+            return
     L = plr.plr_layout_create("allreduce", dtype, W, B, "scattered", "scattered", datapath=path, **pol)
     ws = torch.zeros(max(L.workspace_bytes, 256), dtype=torch.uint8, device="cuda")
     srcs = [to_dev(x) for x in srcs_np]

@@ -29,17 +29,51 @@ def _diag(L, ws, op):
     return int(words[1]), int(words[2]), words[32 + nflags: 32 + 2 * nflags]
 
 
-def _assert_waited(L, ws, op, mode, missing=None):
-    """The consumer really found flags missing and polled for them (the late counter
-    grew); in check mode the check kernel saw them missing too (ready word 0, mirror 0
-    for those flags). `missing`: the flags that must have been missing at check time."""
-    ready, late, mirror = _diag(L, ws, op)
-    assert late > 0, "the consumer never had to wait: the producer's stream did not overlap it"
-    if mode == "check":
-        assert ready == 0, ready
-        assert (mirror == 0).any()
-        if missing is not None:
-            assert (mirror[missing] == 0).all()
+def _until_waited(plr, L, ws, op, mode, produce_late, consume, check, produce_early=None, missing=None,
+                  attempts=8):
+    """The delayed-producer scenario: the producer's work (poison, a sleep, the real data,
+    its notify) is queued on one fresh stream and the consumer's call on another, so the
+    consumer reaches the flags before they are set and must wait. Whether two streams run
+    concurrently is up to how HIP maps them to hardware queues, so the scenario is run on
+    new stream pairs until the workspace shows that the consumer waited (its late counter
+    grew; in check mode the check also found the flags missing: ready word 0, mirror 0 for
+    `missing`); every attempt's output is checked. Returns the attempts taken."""
+    for attempt in range(1, attempts + 1):
+        torch.cuda.synchronize()
+        before = _diag(L, ws, op)[1]
+        if produce_early is not None:
+            produce_early()
+            torch.cuda.synchronize()
+        producer, consumer = torch.cuda.Stream(), torch.cuda.Stream()
+        with torch.cuda.stream(producer):  # queued first: a consumer queued first on a
+            produce_late()                 # hardware queue it shares could only time out
+        with torch.cuda.stream(consumer):
+            consume()
+        torch.cuda.synchronize()
+        assert plr.plr_check(L, ws, consumer) == plr.PLR_OK
+        check()
+        ready, late, mirror = _diag(L, ws, op)
+        if late > before:
+            if mode == "check":
+                assert ready == 0, ready
+                assert (mirror == 0).any()
+                if missing is not None:
+                    assert (mirror[missing] == 0).all()
+            return attempt
+    pytest.fail(f"the consumer never had to wait in {attempts} attempts: the streams never overlapped")
+
+
+def _poison_then_real(plr, L, ws, srcs, real, poison, notify_srcs):
+    def produce():
+        for x in srcs:
+            x.fill_(poison)
+        if hasattr(torch.cuda, "_sleep"):
+            torch.cuda._sleep(20_000_000)
+        for x, r in zip(srcs, real):
+            x.copy_(r)
+        for w in notify_srcs:
+            plr.plr_notify(L, w, ws)
+    return produce
 
 
 @pytest.mark.parametrize("mode", list(MODES))
@@ -106,23 +140,10 @@ def test_delayed_producer_on_another_stream(plr, oracle_mod, mode):
                               workgroups=4, block=64, spin_limit=1 << 22, notify_mode=MODES[mode])
     ws = torch.zeros(L.workspace_bytes, dtype=torch.uint8, device="cuda")
     dst = torch.empty(2 * n, dtype=torch.uint8, device="cuda")
-    torch.cuda.synchronize()
-    producer = torch.cuda.Stream()
-    consumer = torch.cuda.Stream()
-    with torch.cuda.stream(producer):
-        for s in srcs:
-            s.fill_(0xFF)  # NaN poison
-        if hasattr(torch.cuda, "_sleep"):
-            torch.cuda._sleep(20_000_000)
-        for s, r in zip(srcs, real):
-            s.copy_(r)
-        plr.plr_notify(L, -1, ws)  # epoch 1
-    with torch.cuda.stream(consumer):
-        plr.plr_reduce(L, srcs, dst, ws)  # waits on flags of epoch 1
-    torch.cuda.synchronize()
-    assert plr.plr_check(L, ws, consumer) == plr.PLR_OK
-    assert_same("bf16", dst.cpu().numpy().view(np.uint16), ref)
-    _assert_waited(L, ws, "reduce", mode)
+    _until_waited(plr, L, ws, "reduce", mode,
+                  produce_late=_poison_then_real(plr, L, ws, srcs, real, 0xFF, [-1]),  # NaN poison
+                  consume=lambda: plr.plr_reduce(L, srcs, dst, ws),
+                  check=lambda: assert_same("bf16", dst.cpu().numpy().view(np.uint16), ref))
 
 
 @pytest.mark.parametrize("mode", list(MODES))
@@ -175,34 +196,27 @@ def test_check_mode_partial_arrival(plr, oracle_mod, op):
                               workgroups=4, block=64, spin_limit=1 << 22, notify_mode=MODES["check"])
     ws = torch.zeros(L.workspace_bytes, dtype=torch.uint8, device="cuda")
     dst = torch.empty(L.dst_bytes, dtype=torch.uint8, device="cuda")
-    for s, r in zip(srcs[:2], real[:2]):
-        s.copy_(r)
-    for w in range(2):
-        plr.plr_notify(L, w, ws)
-    torch.cuda.synchronize()
-    producer, consumer = torch.cuda.Stream(), torch.cuda.Stream()
-    with torch.cuda.stream(producer):  # queued first: see test_delayed_producer_on_another_stream
-        for s in srcs[2:]:
-            s.fill_(0xFF)
-        if hasattr(torch.cuda, "_sleep"):
-            torch.cuda._sleep(20_000_000)
-        for s, r in zip(srcs[2:], real[2:]):
-            s.copy_(r)
-        for w in range(2, W):
+
+    def early():  # sources 0 and 1: written and announced before the call
+        for x, r in zip(srcs[:2], real[:2]):
+            x.copy_(r)
+        for w in range(2):
             plr.plr_notify(L, w, ws)
-    with torch.cuda.stream(consumer):
-        (plr.plr_reduce if op == "reduce" else plr.plr_copy)(L, srcs, dst, ws)
-    torch.cuda.synchronize()
-    assert plr.plr_check(L, ws, consumer) == plr.PLR_OK
-    if op == "copy":
-        assert np.array_equal(dst.cpu().numpy().view(np.uint16), ref)
-    else:
-        assert_same("bf16", dst.cpu().numpy().view(np.uint16), ref)
-    # the late sources' flags were missing at check time, the early ones were not
+
+    def check():
+        if op == "copy":
+            assert np.array_equal(dst.cpu().numpy().view(np.uint16), ref)
+        else:
+            assert_same("bf16", dst.cpu().numpy().view(np.uint16), ref)
+
     nflags = L.nchunks if op == "copy" else W * L.nchunks
-    late_flags = np.arange(nflags // 2, nflags)  # sources 2 and 3: the second half
-    _assert_waited(L, ws, op, "check", missing=late_flags)
-    assert (_diag(L, ws, op)[2][: nflags // 2] == 1).all()
+    consume = (lambda: plr.plr_reduce(L, srcs, dst, ws)) if op == "reduce" else (lambda: plr.plr_copy(L, srcs, dst, ws))
+    # the late sources (2 and 3) own the second half of the flags: missing at check time,
+    # while the early ones had arrived
+    _until_waited(plr, L, ws, op, "check", produce_early=early,
+                  produce_late=_poison_then_real(plr, L, ws, srcs[2:], real[2:], 0xFF, range(2, W)),
+                  consume=consume, check=check, missing=np.arange(nflags // 2, nflags))
+    assert (_diag(L, ws, op)[2][: nflags // 2] == L.epoch).all()
 
 
 def test_check_mode_many_flags(plr, oracle_mod):
@@ -258,19 +272,7 @@ def test_allgatherv_cut_tiles_wait_for_both_chunks(plr, oracle_mod, mode):
     assert L.ntiles > sum((p + 1023) // 1024 for p in parts)  # the cut added tiles
     ws = torch.zeros(L.workspace_bytes, dtype=torch.uint8, device="cuda")
     dst = torch.empty(T, dtype=torch.uint8, device="cuda")
-    torch.cuda.synchronize()
-    producer, consumer = torch.cuda.Stream(), torch.cuda.Stream()
-    with torch.cuda.stream(producer):
-        for s in srcs:
-            s.fill_(0xA5)
-        if hasattr(torch.cuda, "_sleep"):
-            torch.cuda._sleep(20_000_000)
-        for s, r in zip(srcs, real):
-            s.copy_(r)
-        plr.plr_notify(L, -1, ws)
-    with torch.cuda.stream(consumer):
-        plr.plr_copy(L, srcs, dst, ws)
-    torch.cuda.synchronize()
-    assert plr.plr_check(L, ws, consumer) == plr.PLR_OK
-    assert np.array_equal(dst.cpu().numpy(), ref)
-    _assert_waited(L, ws, "copy", mode)
+    _until_waited(plr, L, ws, "copy", mode,
+                  produce_late=_poison_then_real(plr, L, ws, srcs, real, 0xA5, [-1]),
+                  consume=lambda: plr.plr_copy(L, srcs, dst, ws),
+                  check=lambda: np.testing.assert_array_equal(dst.cpu().numpy(), ref))

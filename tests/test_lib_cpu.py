@@ -282,6 +282,13 @@ def test_allreduce_layouts(plr):
     assert plr.plr_layout_create("allreduce", "bf16", 8, 8192 * 7168 * 2, "scattered", "scattered",
                                  datapath=plr.PLR_PATH_COMPOSED).ntiles == 240
     mk = plr.plr_layout_create
+    # a caller's tile size whose ntiles + 16 workgroups would not all be resident at once
+    # on 256 CUs is refused for the composed path (the fused path takes any tile size)
+    assert _code(mk, "allreduce", "bf16", 8, 8 * 30 * 1024, "scattered", "scattered",
+                 datapath=plr.PLR_PATH_COMPOSED, tile_bytes=1024) == 0  # 240 tiles + 16
+    assert _code(mk, "allreduce", "bf16", 8, 8 * 31 * 1024, "scattered", "scattered",
+                 datapath=plr.PLR_PATH_COMPOSED, tile_bytes=1024) == plr.PLR_EUNSUPPORTED  # 248 + 16
+    assert _code(mk, "allreduce", "bf16", 8, 8 * 31 * 1024, "scattered", "scattered", tile_bytes=1024) == 0
     assert _code(mk, "allreduce", "bf16", 4, 64, "packed", "packed") == plr.PLR_EINVAL
     assert _code(mk, "allreduce", "bf16", 3, 16 * 4, "scattered", "scattered") == plr.PLR_EALIGN
     assert _code(mk, "allreduce", "bf16", 2, 64, "scattered", "scattered", datapath=plr.PLR_PATH_LDS) == plr.PLR_EINVAL
