@@ -968,6 +968,70 @@ def cpu_model() -> str:
     return "unknown"
 
 
+ONLY_OPS = ("reduce", "allgather", "alltoall", "alltoallv", "reduce_lds", "allgather_lds", "allreduce_fused",
+            "allreduce_composed")
+
+
+def run_only(args):
+    """One op of the step (or one row beside it) alone, --warmup + --steps calls, notified
+    as in the step where it is notified there, and nothing else on the GPU: a short
+    program for rocprofv3 counter passes on one kernel."""
+    import torch
+
+    import reduce_atom_amd as plr
+    import synth
+
+    dev = torch.device("cuda:0")
+    op = args.only
+    lds = plr.PLR_PATH_LDS if op.endswith("_lds") else 0
+    if op.startswith("reduce"):
+        srcs = [synth.normal_t(args.seed, 3, w, R3 * C3, 0.5, device=dev) for w in range(W)]
+        dst = torch.empty(R3 * C3, dtype=torch.bfloat16, device=dev)
+        L = plr.plr_layout_create("reduce", "bf16", W, R3 * C3 * 2, "packed", "packed", datapath=lds)
+        ws = torch.zeros(L.workspace_bytes, dtype=torch.uint8, device=dev)
+
+        def call():
+            plr.plr_notify(L, -1, ws)
+            plr.plr_reduce(L, srcs, dst, ws)
+    elif op.startswith("allgather") or op == "alltoall":
+        srcs = [synth.bits_t(args.seed, 4, s, B4, device=dev) for s in range(W)]
+        dst = torch.empty(W * B4, dtype=torch.uint8, device=dev)
+        kinds = ("scattered", "transposed") if op == "alltoall" else ("packed", "packed")
+        L = plr.plr_layout_create("copy", "bf16", W, B4, *kinds, datapath=lds)
+        ws = torch.zeros(L.workspace_bytes, dtype=torch.uint8, device=dev)
+
+        def call():
+            plr.plr_notify(L, -1, ws)
+            plr.plr_copy(L, srcs, dst, ws)
+    elif op == "alltoallv":
+        p = synth.zipf_weights(1.1, W)
+        srcs = [synth.bits_t(args.seed, 6, s, R5 * RB5, device=dev) for s in range(W)]
+        dest = [synth.categorical_t(args.seed, 5, s, R5, p, device=dev) for s in range(W)]
+        dst = torch.empty(W * R5 * RB5, dtype=torch.uint8, device=dev)
+        counts = torch.empty(W * W, dtype=torch.int64, device=dev)
+        offsets = torch.empty(W * W, dtype=torch.int64, device=dev)
+        scratch = torch.zeros(plr.plr_copy_v_scratch_bytes(W, [R5] * W), dtype=torch.uint8, device=dev)
+        L, ws = None, None
+
+        def call():
+            plr.plr_copy_v(srcs, [R5] * W, dest, RB5, dst, counts, offsets, scratch)
+    else:
+        path = plr.PLR_PATH_COMPOSED if op == "allreduce_composed" else plr.PLR_PATH_DIRECT
+        srcs = [synth.normal_t(args.seed, 3, w, R3 * C3, 0.5, device=dev) for w in range(W)]
+        dsts = [torch.empty(R3 * C3, dtype=torch.bfloat16, device=dev) for _ in range(W)]
+        L = plr.plr_layout_create("allreduce", "bf16", W, R3 * C3 * 2, "scattered", "scattered", datapath=path)
+        ws = torch.zeros(max(L.workspace_bytes, 256), dtype=torch.uint8, device=dev)
+
+        def call():
+            plr.plr_allreduce(L, srcs, dsts, ws)
+    for _ in range(args.warmup + args.steps):
+        call()
+    torch.cuda.synchronize()
+    if ws is not None and plr.plr_check(L, ws) != plr.PLR_OK:
+        raise RuntimeError(f"{op}: device error")
+    print(json.dumps({"only": op, "calls": args.warmup + args.steps}), flush=True)
+
+
 def run_cpu_baseline(args, host):
     """The oracle, as it stands, on this host's CPU, on the same input bytes as the GPU
     step: on all the cores this process may use (the oracle's threaded form, at most 16
@@ -1035,6 +1099,8 @@ def main():
     ap.add_argument("--no-decode-trace", action="store_true",
                     help="skip the kernel-trace run of the decode-size reduce (rocprofv3 child process)")
     ap.add_argument("--decode-trace-child", action="store_true", help=argparse.SUPPRESS)
+    ap.add_argument("--only", choices=ONLY_OPS,
+                    help="run one op alone (--warmup + --steps calls, no timing), for counter passes")
     ap.add_argument("--v-sweep", action="store_true",
                     help="only the AllGatherV / ReduceScatterV sweep over T = 1 KiB .. 1 GiB, as JSON")
     ap.add_argument("--collective", choices=COLLECTIVES + ("all",),
@@ -1095,6 +1161,9 @@ def main():
         return
     if args.decode_trace_child:
         run_decode_trace_child(args)
+        return
+    if args.only:
+        run_only(args)
         return
     # before this process touches the GPU: the decode kernel trace runs in a child
     trace = None if (args.no_decode or args.no_decode_trace) else run_decode_trace(args)

@@ -17,10 +17,11 @@ constexpr int kMaxTableSegs = 64;   // explicit segment table carried in kernarg
 enum { kXcdOff = 0, kXcdOn = 1 };
 
 // LDS-staged path: depth of each wave's ring of 4 KiB slabs (1 KiB per wave and
-// source). The reduce keeps W KiB per stage per wave, so 4 waves x S x W KiB stay
-// within the 160 KiB of LDS of a compute unit; the copy keeps 1 KiB per stage.
-constexpr int lds_reduce_stages(int w) { return w <= 4 ? 4 : (w <= 8 ? 3 : 2); }
-constexpr int kCopyStages = 8;
+// source). The reduce keeps W KiB per stage per wave (4 waves x S x W KiB per
+// workgroup: for W = 8, 64 KiB, two workgroups per compute unit's 160 KiB of LDS);
+// the copy keeps 1 KiB per stage (16 KiB per workgroup).
+constexpr int lds_reduce_stages(int w) { return w <= 4 ? 4 : 2; }
+constexpr int kCopyStages = 4;
 // Workspace: u64 error word at byte 0, u64 ready word at byte 8, then
 // uint64 flags[W][nchunks] and their check-time mirror uint64 mirror[W][nchunks].
 constexpr size_t kWorkspaceHeader = 256;

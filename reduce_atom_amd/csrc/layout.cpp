@@ -277,17 +277,20 @@ extern "C" int plr_layout_create(const plr_layout_desc* d, plr_layout** out) {
   }
   if (L->var_segs && L->datapath == PLR_PATH_LDS) return fail(PLR_EUNSUPPORTED);
   if (L->datapath == PLR_PATH_LDS) {
-    // the staged pipeline runs 256-thread workgroups over 4 KiB slabs per source, and a
-    // ring only pipelines across the slabs of one workgroup. Measured on the 8 x 117 MB
-    // reduce and the 8 x 64 MiB AllGather, runs of about one ring are fastest: the
-    // reduce (3 stages) at 4 slabs per workgroup, 184 us against 196 us at 8 workgroups
-    // per CU (14 slabs) and 190 us at 3 slabs; the copy (8 stages) at 8 slabs, 178 us
-    // against 209 us at 8 workgroups per CU (64 slabs), 194 us at 4 and 200 us at 16
+    // the staged pipeline runs 256-thread workgroups over 4 KiB slabs per source. Measured
+    // on the 8 x 117 MB reduce and the 8 x 64 MiB AllGather (ring depth x slabs per
+    // workgroup): the reduce is fastest with 2 stages and one slab per workgroup (two
+    // workgroups per CU by their 64 KiB of LDS), 170.6-171.7 us against 177-180 us at 2
+    // slabs, 184-186 us for the earlier 3 stages x 4 slabs and 165-166 us on the
+    // register-staged path; one stage (32 KiB: 3 to 5 workgroups per CU) took 175-187 us.
+    // The copy is fastest with 4 stages and 2 slabs per workgroup, 165-169 us against
+    // 178-182 us for the earlier 8 stages x 8 slabs and 159-160 us register-staged; fewer
+    // workgroups per CU (LDS padded to 2-5 per CU) took 200-300 us
     if (d->block && d->block != 256) return fail(PLR_EINVAL);
     L->block = 256;
     if (!d->tile_bytes && L->tile_bytes % 4096) L->tile_bytes = 4096;
     L->stages = op == PLR_OP_REDUCE ? lds_reduce_stages(W) : kCopyStages;
-    const int slabs = op == PLR_OP_REDUCE ? L->stages + 1 : L->stages;
+    const int slabs = op == PLR_OP_REDUCE ? (W <= 4 ? L->stages + 1 : 1) : 2;
     const uint64_t per_tile = L->tile_bytes / 4096 ? L->tile_bytes / 4096 : 1;
     L->run = L->run_notified = (int)std::max<uint64_t>(1, (uint64_t)slabs / per_tile);
   }

@@ -108,11 +108,11 @@ def test_policy_overrides(plr):
     assert L.policy() == dict(tile_bytes=2048, chunk_bytes=4096, workgroups=33, block=128, unroll=4,
                               stages=0, datapath=plr.PLR_PATH_DIRECT, notify_mode=plr.PLR_NOTIFY_CHECK)
     # the LDS path reports its ring depth: W KiB per stage per wave for a reduce
-    for w, depth in ((1, 4), (4, 4), (5, 3), (8, 3), (9, 2), (16, 2)):
+    for w, depth in ((1, 4), (4, 4), (5, 2), (8, 2), (9, 2), (16, 2)):
         R = plr.plr_layout_create("reduce", "bf16", w, 1 << 20, "packed", "packed", datapath=plr.PLR_PATH_LDS)
         assert R.policy()["stages"] == depth and R.policy()["block"] == 256
     C = plr.plr_layout_create("copy", "bf16", 8, 1 << 20, "packed", "packed", datapath=plr.PLR_PATH_LDS)
-    assert C.policy()["stages"] == 8 and C.policy()["tile_bytes"] == 4096
+    assert C.policy()["stages"] == 4 and C.policy()["tile_bytes"] == 4096
     S = plr.plr_layout_create("reduce", "bf16", 8, 7168 * 2, "packed", "packed")
     assert S.policy()["notify_mode"] == plr.PLR_NOTIFY_CHUNKS  # decode-size share
     M = plr.plr_layout_create("reduce", "bf16", 8, 7168 * 2, "packed", "packed", notify_mode=plr.PLR_NOTIFY_CHECK)
