@@ -133,59 +133,162 @@ def summarize_counters(path: str) -> str:
     return "\n".join(lines)
 
 
-COUNTER_CMD = ("rocprofv3 --pmc {c} -f csv -d <dir> -o b -- python3 bench.py --steps 3 --warmup 1 "
+# HBM traffic from the L2's memory-side request counters, each pass a run of its own
+# (at most 4 TCC counters per pass): read requests by size, write requests by size, and
+# the derived FETCH_SIZE / WRITE_SIZE beside them for comparison
+TRAFFIC_PASSES = {
+    "rd": "TCC_EA0_RDREQ_32B_sum TCC_EA0_RDREQ_64B_sum TCC_EA0_RDREQ_128B_sum TCC_EA0_RDREQ_sum",
+    "wr": "TCC_EA0_WRREQ_sum TCC_EA0_WRREQ_64B_sum",
+    "fetch": "FETCH_SIZE",
+    "write": "WRITE_SIZE",
+}
+COUNTER_CMD = ("rocprofv3 --pmc {c} -f csv -d <dir>/{p} -o b -- python3 bench.py --steps 3 --warmup 1 "
                "--no-decode --no-cpu-baseline")
-CALIB_CMD = "rocprofv3 --pmc {c} -f csv -d <dir> -o c -- python3 bench.py --calibrate"
+CALIB_CMD = "rocprofv3 --pmc {c} -f csv -d <dir>/cal_{p} -o c -- python3 bench.py --calibrate"
+CALIB_KERNEL = "__amd_rocclr_copyBuffer"
 # counters are taken per kernel; allgather and alltoall share the copy kernel and
 # move the same bytes, so their dispatches are averaged together
 OP_KERNELS = {"reduce": ("plr::k_reduce_direct", None), "allgather": ("plr::k_copy_direct", None),
               "alltoall": ("plr::k_copy_direct", None), "alltoallv": ("plr::k_copy_v_scatter", None)}
 
 
-def _mean_counter(path, name_part, grid=None):
+def _kernel_counters(path, name_part):
+    """{counter: (mean over the kernel's dispatches, dispatches)} from a rocprofv3 counter CSV."""
     import csv
 
-    vals = []
+    vals = {}
     with open(path) as f:
         for r in csv.DictReader(f):
-            if name_part in r["Kernel_Name"] and (grid is None or int(r["Grid_Size"]) == grid):
-                vals.append(float(r["Counter_Value"]))
+            if name_part in r["Kernel_Name"]:
+                vals.setdefault(r["Counter_Name"], []).append(float(r["Counter_Value"]))
     if not vals:
         raise ValueError(f"no dispatch of {name_part} in {path}")
-    return statistics.mean(vals), len(vals)
+    return {c: (statistics.mean(v), len(v)) for c, v in vals.items()}
 
 
-def write_counter_profiles(fetch_csv, write_csv, cal_fetch_csv, cal_write_csv, out_dir):
-    """Turn rocprofv3 FETCH_SIZE / WRITE_SIZE runs into per-op HBM traffic summaries.
-    Both counters are scaled by what they read for the runtime's plain device copy of
-    1 GiB (`__amd_rocclr_copyBuffer`, known to read and write 1 GiB)."""
-    cal_f, _ = _mean_counter(cal_fetch_csv, "__amd_rocclr_copyBuffer")
-    cal_w, _ = _mean_counter(cal_write_csv, "__amd_rocclr_copyBuffer")
-    known_kib = (1 << 30) / 1024
-    sf, sw = known_kib / cal_f, known_kib / cal_w
+def request_bytes(rd: dict, wr: dict):
+    """(read bytes, write bytes) from the L2's memory-side request counts by size."""
+    read = (32 * rd["TCC_EA0_RDREQ_32B_sum"][0] + 64 * rd["TCC_EA0_RDREQ_64B_sum"][0]
+            + 128 * rd["TCC_EA0_RDREQ_128B_sum"][0])
+    w64 = wr["TCC_EA0_WRREQ_64B_sum"][0]
+    write = 64 * w64 + 32 * (wr["TCC_EA0_WRREQ_sum"][0] - w64)
+    return read, write
+
+
+def _pass_csv(d, name, prefix):
+    return os.path.join(d, name, f"{prefix}_counter_collection.csv")
+
+
+def write_counter_profiles(d, out_dir):
+    """Per-op HBM traffic summaries from the counter passes under directory d (TRAFFIC_PASSES
+    over the bench step in d/<pass>, over the calibration copy in d/cal_<pass>). Traffic is
+    the read and write request counts times their sizes, with no scaling; FETCH_SIZE and
+    WRITE_SIZE are reported beside it, and the calibration copy of 1 GiB (the HIP
+    runtime's copy kernel) shows what each reads for a copy of known size."""
+    cal = {p: _kernel_counters(_pass_csv(d, f"cal_{p}", "c"), CALIB_KERNEL) for p in TRAFFIC_PASSES}
+    cal_r, cal_w = request_bytes(cal["rd"], cal["wr"])
+    cal_fetch, cal_write = cal["fetch"]["FETCH_SIZE"][0] * 1024, cal["write"]["WRITE_SIZE"][0] * 1024
+    cmds = [COUNTER_CMD.format(c=c, p=p) for p, c in TRAFFIC_PASSES.items()]
+    cmds += [CALIB_CMD.format(c=c, p=p) for p, c in TRAFFIC_PASSES.items()]
     for op, (kname, _) in OP_KERNELS.items():
-        h = source_hash(op)
-        f_kib, nf = _mean_counter(fetch_csv, kname)
-        w_kib, nw = _mean_counter(write_csv, kname)
-        traffic = (f_kib * sf + w_kib * sw) * 1024
+        k = {p: _kernel_counters(_pass_csv(d, p, "b"), kname) for p in TRAFFIC_PASSES}
+        read, write = request_bytes(k["rd"], k["wr"])
+        fetch, wsize = k["fetch"]["FETCH_SIZE"][0] * 1024, k["write"]["WRITE_SIZE"][0] * 1024
+        traffic = read + write
         path = os.path.join(out_dir, f"{op}_counters.txt")
         with open(path, "w") as out:
-            out.write(f"# HBM traffic per launch of {kname} ({op}) in the bench step, MI355X\n")
-            out.write(f"# commands: {COUNTER_CMD.format(c='FETCH_SIZE')}\n")
-            out.write(f"#           {COUNTER_CMD.format(c='WRITE_SIZE')}\n")
-            out.write(f"#           {CALIB_CMD.format(c='FETCH_SIZE')}   (and WRITE_SIZE)\n")
-            out.write("# then: python bench.py --counters-profile <fetch.csv> <write.csv> <cal_fetch.csv> "
-                      "<cal_write.csv>\n")
+            out.write(f"# HBM traffic per launch of {kname} ({op}) in the bench step, MI355X (gfx950)\n")
+            out.write("# commands (one counter pass per run, <dir> any scratch directory):\n")
+            for c in cmds:
+                out.write(f"#   {c}\n")
+            out.write("# then: python bench.py --counters-profile <dir>\n")
+            out.write("# read bytes = 32 x RDREQ_32B + 64 x RDREQ_64B + 128 x RDREQ_128B; write bytes = 64 x WRREQ_64B\n"
+                      "# + 32 x (WRREQ - WRREQ_64B) (TCC_EA0_* sums over all L2 channels of all XCDs).\n"
+                      "# FETCH_SIZE counts every read request that is neither 32-byte nor a 'bubble' as 64 bytes;\n"
+                      "# gfx950's reads here are 128-byte requests, so it reports half the bytes read.\n")
             out.write(f"kernel: {kname}\n")
-            out.write(f"dispatches_fetch: {nf}\ndispatches_write: {nw}\n")
-            out.write(f"fetch_size_kib_mean: {f_kib:.1f}\nwrite_size_kib_mean: {w_kib:.1f}\n")
-            out.write(f"calibration_copy_fetch_kib: {cal_f:.1f}\ncalibration_copy_write_kib: {cal_w:.1f}\n")
-            out.write(f"fetch_scale: {sf:.5f}\nwrite_scale: {sw:.5f}\n")
+            out.write(f"dispatches: {k['rd']['TCC_EA0_RDREQ_sum'][1]}\n")
+            for p in ("rd", "wr"):
+                for c, (m, _) in sorted(k[p].items()):
+                    out.write(f"{c}: {m:.1f}\n")
+            out.write(f"read_bytes_per_launch: {read:.0f}\nwrite_bytes_per_launch: {write:.0f}\n")
+            out.write(f"fetch_size_bytes: {fetch:.0f}\nwrite_size_bytes: {wsize:.0f}\n")
+            out.write(f"fetch_size_over_read_bytes: {fetch / read:.4f}\n")
+            out.write(f"calibration_copy_1GiB_read_bytes: {cal_r:.0f}\ncalibration_copy_1GiB_write_bytes: {cal_w:.0f}\n")
+            out.write(f"calibration_copy_1GiB_fetch_size_bytes: {cal_fetch:.0f}\n"
+                      f"calibration_copy_1GiB_write_size_bytes: {cal_write:.0f}\n")
             out.write(f"traffic_bytes_per_launch: {traffic:.0f}\n")
             out.write(f"algorithmic_bytes_per_launch: {BYTES[op]}\n")
             out.write(f"traffic_over_algorithmic: {traffic / BYTES[op]:.4f}\n")
-            out.write(f"source_hash: {h}\n")
+            out.write(f"source_hash: {source_hash(op)}\n")
         print(path, f"{traffic / BYTES[op]:.4f}")
+
+
+# What bounds each streaming kernel: counter passes over one op run alone (bench.py --only)
+BOUND_PASSES = {
+    "lvl": "TCC_EA0_RDREQ_LEVEL_sum TCC_EA0_WRREQ_LEVEL_sum TCC_EA0_RDREQ_DRAM_CREDIT_STALL_sum "
+           "TCC_EA0_WRREQ_DRAM_CREDIT_STALL_sum GRBM_GUI_ACTIVE",
+    "req": "TCC_EA0_RDREQ_128B_sum TCC_EA0_WRREQ_64B_sum TCC_EA0_WRREQ_sum TCC_EA0_RDREQ_sum",
+    "sq": "SQ_WAVES SQ_BUSY_CYCLES SQ_WAVE_CYCLES SQ_WAIT_INST_ANY SQ_INSTS_VMEM_RD SQ_INSTS_VMEM_WR GRBM_GUI_ACTIVE",
+    "tcp": "TCP_TCC_READ_REQ_LATENCY_sum TCP_TCC_READ_REQ_sum TCP_UTCL1_TRANSLATION_MISS_sum "
+           "TCP_UTCL1_TRANSLATION_HIT_sum",
+}
+BOUND_OPS = {"reduce": "plr::k_reduce_direct", "allgather": "plr::k_copy_direct",
+             "alltoallv": "plr::k_copy_v_scatter", "reduce_lds": "plr::k_reduce_lds",
+             "allgather_lds": "plr::k_copy_lds", "allreduce_fused": "plr::k_allreduce_fused"}
+BOUND_CMD = ("rocprofv3 --pmc {c} -f csv -d <dir>/{op}_{p} -o p -- python3 bench.py --only {op} --steps 5 "
+             "--warmup 1")
+XCDS = 8
+
+
+def write_bound_profile(d, out_path):
+    """Derived per-kernel figures from the BOUND_PASSES runs under d (d/<op>_<pass>):
+    GPU cycles per XCD (GRBM_GUI_ACTIVE over the 8 XCDs), the mean number of read and
+    write requests outstanding at the L2's memory interface (the _LEVEL sums over those
+    cycles), the mean time a read request spends there (Little's law: outstanding /
+    issue rate), the L1-to-L2 read latency, the share of cycles an L2 channel's DRAM
+    request queue was full (credit stalls per channel), waves and their waiting."""
+    rows = []
+    for op, kname in BOUND_OPS.items():
+        k = {}
+        for p in BOUND_PASSES:
+            k.update(_kernel_counters(_pass_csv(d, f"{op}_{p}", "p"), kname))
+        v = {c: m for c, (m, _) in k.items()}
+        cyc = v["GRBM_GUI_ACTIVE"] / XCDS
+        chans = 16 * XCDS  # L2 channels
+        rd_rate = v["TCC_EA0_RDREQ_sum"] / cyc
+        rows.append((op, kname, {
+            "cycles_per_xcd": cyc,
+            "read_bytes": 128 * v["TCC_EA0_RDREQ_128B_sum"],
+            "write_bytes": 64 * v["TCC_EA0_WRREQ_64B_sum"] + 32 * (v["TCC_EA0_WRREQ_sum"] - v["TCC_EA0_WRREQ_64B_sum"]),
+            "reads_outstanding": v["TCC_EA0_RDREQ_LEVEL_sum"] / cyc,
+            "writes_outstanding": v["TCC_EA0_WRREQ_LEVEL_sum"] / cyc,
+            "read_requests_per_cycle": rd_rate,
+            "read_residency_cycles": (v["TCC_EA0_RDREQ_LEVEL_sum"] / cyc) / rd_rate if rd_rate else 0.0,
+            "l1_to_l2_read_latency_cycles": v["TCP_TCC_READ_REQ_LATENCY_sum"] / max(1.0, v["TCP_TCC_READ_REQ_sum"]),
+            "dram_read_credit_stall_share": v["TCC_EA0_RDREQ_DRAM_CREDIT_STALL_sum"] / chans / cyc,
+            "dram_write_credit_stall_share": v["TCC_EA0_WRREQ_DRAM_CREDIT_STALL_sum"] / chans / cyc,
+            "waves": v["SQ_WAVES"],
+            "wave_cycles_per_wave": v["SQ_WAVE_CYCLES"] / max(1.0, v["SQ_WAVES"]),
+            "wait_share_of_wave_cycles": v["SQ_WAIT_INST_ANY"] / max(1.0, v["SQ_WAVE_CYCLES"]),
+            "utcl1_miss_share": v["TCP_UTCL1_TRANSLATION_MISS_sum"] / max(
+                1.0, v["TCP_UTCL1_TRANSLATION_MISS_sum"] + v["TCP_UTCL1_TRANSLATION_HIT_sum"]),
+        }))
+    with open(out_path, "w") as out:
+        out.write("# What bounds the streaming kernels: rocprofv3 counters of each op run alone, MI355X (gfx950)\n")
+        out.write("# commands (one pass per run; <op> in " + ", ".join(BOUND_OPS) + "):\n")
+        for p, c in BOUND_PASSES.items():
+            out.write(f"#   {BOUND_CMD.format(c=c, op='<op>', p=p)}\n")
+        out.write("# then: python bench.py --bound-profile <dir>\n")
+        out.write(write_bound_profile.__doc__.replace("\n    ", "\n# ").replace('    """', "# ") + "\n")
+        keys = list(rows[0][2])
+        out.write(f"{'':34s}" + "".join(f"{op:>16s}" for op, _, _ in rows) + "\n")
+        for key in keys:
+            out.write(f"{key:34s}" + "".join(
+                f"{r[key]:16.4f}" if r[key] < 10 else f"{r[key]:16.0f}" for _, _, r in rows) + "\n")
+        for op, kname, _ in rows:
+            out.write(f"# {op}: {kname}\n")
+    print(open(out_path).read())
 
 
 class TimingEvents:
@@ -1116,9 +1219,12 @@ def main():
                     help="print per-kernel durations of a rocprofv3 kernel-trace CSV and exit")
     ap.add_argument("--summarize-counters", metavar="CSV",
                     help="print per-kernel mean counters of a rocprofv3 counter CSV and exit")
-    ap.add_argument("--counters-profile", nargs=4, metavar="CSV",
-                    help="FETCH_SIZE, WRITE_SIZE, calibration FETCH_SIZE, calibration WRITE_SIZE "
-                         "counter CSVs: write profiles/<op>_counters.txt and exit")
+    ap.add_argument("--counters-profile", metavar="DIR",
+                    help="directory of the traffic counter passes (TRAFFIC_PASSES): write "
+                         "profiles/<op>_counters.txt and exit")
+    ap.add_argument("--bound-profile", metavar="DIR",
+                    help="directory of the bound counter passes (BOUND_PASSES): write "
+                         "profiles/bounds_counters.txt and exit")
     ap.add_argument("--calibrate", action="store_true",
                     help="only run torch's plain device copy of 1 GiB five times (the reference "
                          "for scaling HBM byte counters)")
@@ -1133,7 +1239,10 @@ def main():
         print(summarize_trace(args.summarize_trace))
         return
     if args.counters_profile:
-        write_counter_profiles(*args.counters_profile, os.path.join(ROOT, "profiles"))
+        write_counter_profiles(args.counters_profile, os.path.join(ROOT, "profiles"))
+        return
+    if args.bound_profile:
+        write_bound_profile(args.bound_profile, os.path.join(ROOT, "profiles", "bounds_counters.txt"))
         return
     if args.summarize_counters:
         print(summarize_counters(args.summarize_counters))

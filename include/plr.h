@@ -269,8 +269,13 @@ int plr_allreduce(plr_layout* L, const void* const* srcs, void* const* dsts, voi
  * are reduced one output element per thread in source order). On gfx950 a packet is
  * one 8-byte atomic: a 4-byte payload word in the low half and the low 32 bits of the
  * epoch in the high half. Only for reduce layouts.
- * plr_layout_packet_bytes: bytes of one source's packet buffer (2 x the share); the
- * caller allocates W of them in device memory, zeroed once, never reset. */
+ * plr_layout_packet_bytes: bytes of one source's packet buffer (4 x the share: two slots
+ * of 2 x the share; epoch e packs into and is reduced from slot e & 1, section 4.3 "Epoch
+ * Bookkeeping": the epoch's parity selects one of two staging buffers); the caller
+ * allocates W of them in device memory, zeroed once, never reset.
+ * Ordering: a producer may run one epoch ahead of the consumer (pack epoch e + 1 while
+ * the consumer of epoch e still reads, the other slot), not two: packing epoch e + 2
+ * reuses epoch e's slot, so it must wait until the consumer of epoch e has finished. */
 size_t plr_layout_packet_bytes(const plr_layout* L);
 
 /* Producer: stamp source src's share (src = -1: every source's, in one launch) with

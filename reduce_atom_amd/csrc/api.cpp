@@ -315,8 +315,13 @@ extern "C" int plr_allreduce(plr_layout* L, const void* const* srcs, void* const
   return PLR_OK;
 }
 
+// Packet buffers hold two slots of 2 x the share each; epoch e uses slot e & 1 (section 4.3
+// "Epoch Bookkeeping": the epoch's parity selects one of two staging buffers), so a
+// producer may pack epoch e + 1 while the consumer of epoch e still reads its packets.
+static uint64_t packet_slot_bytes(const plr_layout* L) { return 2 * L->seg_len; }
+
 extern "C" size_t plr_layout_packet_bytes(const plr_layout* L) {
-  return (L && L->op == PLR_OP_REDUCE) ? 2 * (size_t)L->seg_len : 0;
+  return (L && L->op == PLR_OP_REDUCE) ? 2 * (size_t)packet_slot_bytes(L) : 0;
 }
 
 extern "C" int plr_pack(plr_layout* L, int src, const void* const* data, void* const* packets,
@@ -329,19 +334,23 @@ extern "C" int plr_pack(plr_layout* L, int src, const void* const* data, void* c
     if (!data[s] || !packets[s]) return PLR_EINVAL;
     if (!a16(data[s]) || !a16(packets[s])) return PLR_EALIGN;
     const char* share = static_cast<const char*>(data[s]) + L->segs[s].src_off;
+    const uint64_t pb = plr_layout_packet_bytes(L);
     for (int t = s0; t < s1; ++t) {  // a packet buffer overlaps no share and no other buffer
       const char* other = static_cast<const char*>(data[t]) + L->segs[t].src_off;
-      if (overlaps((uintptr_t)packets[s], 2 * L->seg_len, (uintptr_t)other, L->seg_len)) return PLR_EINVAL;
-      if (t != s && overlaps((uintptr_t)packets[s], 2 * L->seg_len, (uintptr_t)packets[t], 2 * L->seg_len))
-        return PLR_EINVAL;
+      if (overlaps((uintptr_t)packets[s], pb, (uintptr_t)other, L->seg_len)) return PLR_EINVAL;
+      if (t != s && overlaps((uintptr_t)packets[s], pb, (uintptr_t)packets[t], pb)) return PLR_EINVAL;
     }
     a.data[s] = reinterpret_cast<const uint32_t*>(share);
     a.packets[s] = static_cast<uint64_t*>(packets[s]);
   }
   if (!L->seg_len) return PLR_OK;
+  const uint64_t epoch = L->epoch + 1;
+  for (int s = s0; s < s1; ++s)  // this epoch's slot
+    a.packets[s] = reinterpret_cast<uint64_t*>(reinterpret_cast<char*>(a.packets[s]) +
+                                               (epoch & 1) * packet_slot_bytes(L));
   a.nwords = L->seg_len / 4;
   a.first = (uint32_t)s0;
-  a.stamp = (uint32_t)(L->epoch + 1);
+  a.stamp = (uint32_t)epoch;
   hipError_t e = launch_pack(a, (uint32_t)(s1 - s0), static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e);
   return PLR_OK;
@@ -354,12 +363,14 @@ extern "C" int plr_reduce_packets(plr_layout* L, const void* const* packets, voi
   for (int w = 0; w < L->world; ++w) {
     if (!packets[w]) return PLR_EINVAL;
     if (!a16(packets[w])) return PLR_EALIGN;
-    if (overlaps((uintptr_t)dst, L->seg_len, (uintptr_t)packets[w], 2 * L->seg_len)) return PLR_EINVAL;
+    if (overlaps((uintptr_t)dst, L->seg_len, (uintptr_t)packets[w], plr_layout_packet_bytes(L))) return PLR_EINVAL;
   }
   const uint64_t epoch = L->epoch + 1;
   if (L->seg_len) {
     PacketReduceArgs a{};
-    for (int w = 0; w < L->world; ++w) a.pk[w] = static_cast<const uint64_t*>(packets[w]);
+    for (int w = 0; w < L->world; ++w)  // this epoch's slot
+      a.pk[w] = reinterpret_cast<const uint64_t*>(static_cast<const char*>(packets[w]) +
+                                                  (epoch & 1) * packet_slot_bytes(L));
     a.dst = static_cast<uint32_t*>(dst);
     a.nwords = L->seg_len / 4;
     a.world = (uint32_t)L->world;

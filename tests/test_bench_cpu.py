@@ -1,9 +1,10 @@
 """Host-side checks of the measurement code in bench.py (no GPU): the kernel-trace and
-counter summaries it writes into profiles/, the HBM-traffic scaling against the
-calibration copy, the source hash that voids a stale counter summary, and the
+counter summaries it writes into profiles/, the HBM traffic from request counts, the
+source hash that voids a stale counter summary, and the
 command-line contract."""
 import csv
 import os
+import statistics
 import subprocess
 import sys
 
@@ -42,31 +43,49 @@ def test_summarize_trace_groups_by_kernel_and_shape(tmp_path):
     assert lines[2].split()[-4] == "5.00"
 
 
-def test_counter_profiles_scale_by_the_calibration_copy(tmp_path, monkeypatch):
+def test_counter_profiles_count_request_bytes(tmp_path, monkeypatch):
+    """Traffic is request counts times request sizes, unscaled: 128-byte reads count 128
+    bytes, 64-byte writes 64 (other writes 32); FETCH_SIZE, which weighs such reads at 64
+    bytes, is reported beside it; ops that launch the same kernel share its mean."""
     fields = ["Kernel_Name", "Grid_Size", "Counter_Name", "Counter_Value"]
     names = {op: k for op, (k, _) in bench.OP_KERNELS.items()}
-    fetch, write = tmp_path / "f.csv", tmp_path / "w.csv"
-    _write_csv(fetch, fields, [{"Kernel_Name": names[op] + "(x)", "Grid_Size": 1, "Counter_Name": "FETCH_SIZE",
-                                "Counter_Value": 1000.0 * (i + 1)} for i, op in enumerate(names)])
-    _write_csv(write, fields, [{"Kernel_Name": names[op] + "(x)", "Grid_Size": 1, "Counter_Name": "WRITE_SIZE",
-                                "Counter_Value": 100.0 * (i + 1)} for i, op in enumerate(names)])
-    cal_f, cal_w = tmp_path / "cf.csv", tmp_path / "cw.csv"
-    kib = (1 << 30) // 1024
-    _write_csv(cal_f, fields, [{"Kernel_Name": "__amd_rocclr_copyBuffer", "Grid_Size": 1, "Counter_Name": "FETCH_SIZE",
-                                "Counter_Value": kib / 2}])
-    _write_csv(cal_w, fields, [{"Kernel_Name": "__amd_rocclr_copyBuffer", "Grid_Size": 1, "Counter_Name": "WRITE_SIZE",
-                                "Counter_Value": kib}])
+    rows = {p: [] for p in bench.TRAFFIC_PASSES}
+    for i, op in enumerate(names):
+        k = names[op] + "(x)"
+        r128, r64, r32, w64, wall = 1000 * (i + 1), 10 * (i + 1), i, 500 * (i + 1), 500 * (i + 1) + 3
+        for c, v in (("TCC_EA0_RDREQ_128B_sum", r128), ("TCC_EA0_RDREQ_64B_sum", r64),
+                     ("TCC_EA0_RDREQ_32B_sum", r32), ("TCC_EA0_RDREQ_sum", r128 + r64 + r32)):
+            rows["rd"].append({"Kernel_Name": k, "Grid_Size": 1, "Counter_Name": c, "Counter_Value": v})
+        for c, v in (("TCC_EA0_WRREQ_64B_sum", w64), ("TCC_EA0_WRREQ_sum", wall)):
+            rows["wr"].append({"Kernel_Name": k, "Grid_Size": 1, "Counter_Name": c, "Counter_Value": v})
+        rows["fetch"].append({"Kernel_Name": k, "Grid_Size": 1, "Counter_Name": "FETCH_SIZE",
+                              "Counter_Value": (64 * (r128 + r64) + 32 * r32) / 1024})
+        rows["write"].append({"Kernel_Name": k, "Grid_Size": 1, "Counter_Name": "WRITE_SIZE",
+                              "Counter_Value": (64 * w64 + 32 * (wall - w64)) / 1024})
+    for p, rr in rows.items():
+        (tmp_path / p).mkdir()
+        _write_csv(tmp_path / p / "b_counter_collection.csv", fields, rr)
+    cal = {"rd": [("TCC_EA0_RDREQ_128B_sum", 1 << 23), ("TCC_EA0_RDREQ_64B_sum", 0), ("TCC_EA0_RDREQ_32B_sum", 0),
+                  ("TCC_EA0_RDREQ_sum", 1 << 23)],
+           "wr": [("TCC_EA0_WRREQ_64B_sum", 1 << 24), ("TCC_EA0_WRREQ_sum", 1 << 24)],
+           "fetch": [("FETCH_SIZE", (1 << 29) / 1024)], "write": [("WRITE_SIZE", (1 << 30) / 1024)]}
+    for p, cv in cal.items():
+        (tmp_path / f"cal_{p}").mkdir()
+        _write_csv(tmp_path / f"cal_{p}" / "c_counter_collection.csv", fields,
+                   [{"Kernel_Name": "__amd_rocclr_copyBuffer", "Grid_Size": 1, "Counter_Name": c, "Counter_Value": v}
+                    for c, v in cv])
     out = tmp_path / "profiles"
     out.mkdir()
-    bench.write_counter_profiles(str(fetch), str(write), str(cal_f), str(cal_w), str(out))
+    bench.write_counter_profiles(str(tmp_path), str(out))
     monkeypatch.setattr(bench, "ROOT", str(tmp_path))
     for op in names:
-        # fetch counts half of a copy's reads (scale 2), write counts all of its writes (scale
-        # 1); ops that launch the same kernel (allgather, alltoall) share its mean
         same = [i for i, o in enumerate(names) if names[o] == names[op]]
-        f = sum(1000.0 * (i + 1) for i in same) / len(same)
-        w = sum(100.0 * (i + 1) for i in same) / len(same)
-        assert bench.counters_traffic(op) == pytest.approx((2 * f + w) * 1024), op
+        want = statistics.mean(128 * 1000 * (i + 1) + 64 * 10 * (i + 1) + 32 * i + 64 * 500 * (i + 1) + 32 * 3
+                               for i in same)
+        assert bench.counters_traffic(op) == pytest.approx(want), op
+    text = (out / "reduce_counters.txt").read_text()
+    assert "calibration_copy_1GiB_read_bytes: 1073741824" in text
+    assert "calibration_copy_1GiB_fetch_size_bytes: 536870912" in text
     # a summary taken on other sources is void
     p = out / "reduce_counters.txt"
     p.write_text(p.read_text().replace(bench.source_hash("reduce"), "0" * 16))

@@ -48,9 +48,10 @@ def test_pack_matches_oracle_encoding(plr, oracle_mod, W):
         else:
             plr.plr_pack(L, -1, srcs, pk)  # every source in one launch
         torch.cuda.synchronize()
+        nw = share // 4  # packets per slot; epoch e uses slot e & 1
         for w in range(W):
-            want = oracle_mod.pack(srcs_np[w][(W - 1) * share:], epoch)[: share // 4]
-            got = pk[w].cpu().numpy().view(np.uint64)
+            want = oracle_mod.pack(srcs_np[w][(W - 1) * share:], epoch)[:nw]
+            got = pk[w].cpu().numpy().view(np.uint64)[(epoch & 1) * nw:(epoch & 1) * nw + nw]
             assert np.array_equal(got, want), (epoch, w)
         plr.plr_reduce_packets(L, pk, dst, ws)
         assert plr.plr_check(L, ws) == plr.PLR_OK
@@ -123,8 +124,8 @@ def test_many_epochs_without_reset(plr, oracle_mod):
             assert_same("bf16", dst.cpu().numpy().view(np.uint16), ra if i % 2 else rb, f"call {i}")
     assert plr.plr_check(L, ws) == plr.PLR_OK
     assert L.epoch == 500
-    stamps = pk[0].cpu().numpy().view(np.uint64) >> np.uint64(32)
-    assert (stamps == 500).all()
+    stamps = (pk[0].cpu().numpy().view(np.uint64) >> np.uint64(32)).reshape(2, -1)
+    assert (stamps[0] == 500).all() and (stamps[1] == 499).all()  # slot = epoch parity
 
 
 def test_stale_packets_time_out(plr, oracle_mod):
@@ -180,3 +181,37 @@ def test_delayed_producer_on_another_stream(plr, oracle_mod):
     torch.cuda.synchronize()
     assert plr.plr_check(L, ws, consumer) == plr.PLR_OK
     assert_same("bf16", dst.cpu().numpy().view(np.uint16), ref)
+
+
+def test_producer_one_epoch_ahead(plr, oracle_mod):
+    """The producer packs epoch 2 while the consumer of epoch 1 may not have read its
+    packets yet (the consumer's stream is held by a sleep; the producer's is not): the two
+    epochs use the two slots of the packet buffers (epoch parity), so both reductions are
+    the oracle's. With one slot the second pack would overwrite the first epoch's packets
+    and the first consumer would see the wrong stamp."""
+    W, n = 8, 1 << 14
+    a_np = [synth.normal_np(18, 2, w, n) for w in range(W)]
+    b_np = [synth.normal_np(18, 3, w, n) for w in range(W)]
+    a, b = [to_dev(s) for s in a_np], [to_dev(s) for s in b_np]
+    L, pk, ws, dst1 = _setup(plr, "bf16", W, 2 * n, spin_limit=1 << 22)
+    dst2 = torch.empty_like(dst1)
+    torch.cuda.synchronize()
+    producer, consumer = torch.cuda.Stream(), torch.cuda.Stream()
+    with torch.cuda.stream(consumer):
+        if hasattr(torch.cuda, "_sleep"):
+            torch.cuda._sleep(20_000_000)
+    with torch.cuda.stream(producer):
+        plr.plr_pack(L, -1, a, pk)  # epoch 1 (slot 1)
+    ev = torch.cuda.Event()
+    ev.record(producer)
+    with torch.cuda.stream(consumer):
+        consumer.wait_event(ev)
+        plr.plr_reduce_packets(L, pk, dst1, ws)  # epoch 1
+    with torch.cuda.stream(producer):
+        plr.plr_pack(L, -1, b, pk)  # epoch 2 (slot 0), possibly before the epoch-1 consumer ran
+    with torch.cuda.stream(consumer):
+        plr.plr_reduce_packets(L, pk, dst2, ws)  # epoch 2
+    torch.cuda.synchronize()
+    assert plr.plr_check(L, ws, consumer) == plr.PLR_OK
+    assert_same("bf16", dst1.cpu().numpy().view(np.uint16), oracle_mod.reduce("bf16", a_np), "epoch 1")
+    assert_same("bf16", dst2.cpu().numpy().view(np.uint16), oracle_mod.reduce("bf16", b_np), "epoch 2")

@@ -302,11 +302,11 @@ def test_allreduce_layouts(plr):
 
 def test_packet_layouts_and_validation(plr):
     L = plr.plr_layout_create("reduce", "bf16", 4, 4 * 4096, "scattered", "packed", rank=1)
-    assert L.packet_bytes == 2 * 4096
+    assert L.packet_bytes == 4 * 4096  # two slots of 2 x the 4096-byte share
     C = plr.plr_layout_create("copy", "bf16", 2, 4096, "packed", "packed")
     assert C.packet_bytes == 0
     A, P, D, WS = 1 << 40, (1 << 40) + (1 << 24), (1 << 40) + (2 << 24), (1 << 40) + (3 << 24)
-    pk = [P + k * 8192 for k in range(4)]
+    pk = [P + k * L.packet_bytes for k in range(4)]
     src = [A + k * (1 << 20) for k in range(4)]
     assert _code(plr.plr_pack, C, 0, src[:2], pk[:2]) == plr.PLR_EINVAL  # copy layouts have no packets
     assert _code(plr.plr_pack, L, 4, src, pk) == plr.PLR_EINVAL  # no source 4
@@ -316,6 +316,7 @@ def test_packet_layouts_and_validation(plr):
     # source 1's share of a scattered layout at rank 1 starts 4096 bytes into its buffer
     assert _code(plr.plr_pack, L, 1, src, pk[:1] + [src[1] + 4096 + 16] + pk[2:]) == plr.PLR_EINVAL
     assert _code(plr.plr_pack, L, -1, src, pk[:3] + [pk[2] + 4096]) == plr.PLR_EINVAL  # packets overlap
+    assert _code(plr.plr_pack, L, -1, src, pk[:3] + [pk[2] + 12288]) == plr.PLR_EINVAL  # in the second slot
     assert _code(plr.plr_reduce_packets, L, pk, D, 0) == plr.PLR_EINVAL  # workspace required
     assert _code(plr.plr_reduce_packets, L, pk, D, WS + 8) == plr.PLR_EALIGN
     assert _code(plr.plr_reduce_packets, L, pk, pk[2] + 16, WS) == plr.PLR_EINVAL  # dst inside packets
