@@ -280,7 +280,8 @@ def write_bound_profile(d, out_path):
         for p, c in BOUND_PASSES.items():
             out.write(f"#   {BOUND_CMD.format(c=c, op='<op>', p=p)}\n")
         out.write("# then: python bench.py --bound-profile <dir>\n")
-        out.write(write_bound_profile.__doc__.replace("\n    ", "\n# ").replace('    """', "# ") + "\n")
+        for line in write_bound_profile.__doc__.strip().splitlines():
+            out.write("# " + line.strip() + "\n")
         keys = list(rows[0][2])
         out.write(f"{'':34s}" + "".join(f"{op:>16s}" for op, _, _ in rows) + "\n")
         for key in keys:
@@ -633,6 +634,27 @@ def parse_decode_trace(path, sched):
     out["source"] = ("rocprofv3 kernel trace: consumer kernel duration per call (k_reduce_direct; packets: "
                      "k_reduce_packets), after the warmup calls; producer: k_notify / k_pack")
     return out
+
+
+def summarize_decode(path: str) -> str:
+    """The decode-size latency rows of a bench JSON line (the last line of the file): the
+    kernel-trace p50 / p90 of the consumer kernel per T, mode and warm / cold, the
+    producer kernel's p50, and the per-call time in replayed graphs."""
+    with open(path) as f:
+        line = [x for x in f.read().splitlines() if x.startswith("{")][-1]
+    dec = json.loads(line)["decode_reduce_us"]
+    kt = dec["kernel_trace"]
+    out = [f"{'T':>4s} {'mode':11s} {'temp':5s} {'p50_us':>7s} {'p90_us':>7s} {'mean_us':>8s} {'min_us':>7s} "
+           f"{'calls':>6s} {'producer_p50_us':>16s} {'graph_us_per_call':>18s}"]
+    for T in (k for k in kt if k.startswith("T=")):
+        for mode, temps in kt[T].items():
+            for temp, r in temps.items():
+                prod = r.get("producer_p50_us")
+                graph = dec[T][mode]["us_per_call_graph"] if temp == "warm" else None
+                out.append(f"{T[2:]:>4s} {mode:11s} {temp:5s} {r['p50_us']:7.2f} {r['p90_us']:7.2f} "
+                           f"{r['mean_us']:8.2f} {r['min_us']:7.2f} {r['calls']:6d} "
+                           f"{'' if prod is None else f'{prod:.2f}':>16s} {'' if graph is None else f'{graph:.2f}':>18s}")
+    return "\n".join(out)
 
 
 def run_decode_trace(args):
@@ -1217,6 +1239,8 @@ def main():
     ap.add_argument("--cpu-reps", type=int, default=5)
     ap.add_argument("--summarize-trace", metavar="CSV",
                     help="print per-kernel durations of a rocprofv3 kernel-trace CSV and exit")
+    ap.add_argument("--summarize-decode", metavar="JSON",
+                    help="print the decode latency table of a bench JSON line and exit")
     ap.add_argument("--summarize-counters", metavar="CSV",
                     help="print per-kernel mean counters of a rocprofv3 counter CSV and exit")
     ap.add_argument("--counters-profile", metavar="DIR",
@@ -1246,6 +1270,9 @@ def main():
         return
     if args.summarize_counters:
         print(summarize_counters(args.summarize_counters))
+        return
+    if args.summarize_decode:
+        print(summarize_decode(args.summarize_decode))
         return
     if args.calibrate:
         import torch
