@@ -657,6 +657,34 @@ def summarize_decode(path: str) -> str:
     return "\n".join(out)
 
 
+def summarize_sweep(path: str) -> str:
+    """Tables of a --collective or --v-sweep JSON output: time per call, HBM GB/s and (for
+    the collectives) the pages' algbw, one row per size."""
+    with open(path) as f:
+        line = [x for x in f.read().splitlines() if x.startswith("{")][-1]
+    d = json.loads(line)
+    out = []
+    if "collective_sweep" in d:
+        cs = d["collective_sweep"]
+        names = list(cs)
+        sizes = [r["bytes"] for r in cs[names[0]]]
+        for title, key, fmt in (("time per call, us", "us", "{:10.2f}"),
+                                ("HBM GB/s (algorithmic bytes / time)", "hbm_GB/s", "{:10.1f}"),
+                                ("algbw GB/s (page-convention bytes / time)", "algbw_GB/s", "{:10.1f}")):
+            out.append(title)
+            out.append(f"{'S_bytes':>12s}" + "".join(f"{n:>10s}" for n in names))
+            for i, size in enumerate(sizes):
+                out.append(f"{size:12d}" + "".join(fmt.format(cs[n][i][key]) for n in names))
+            out.append("")
+    else:
+        out.append(f"{'T_bytes':>12s} {'largest_part':>12s} {'agv_us':>9s} {'agv_GB/s':>9s} {'rsv0_us':>9s} "
+                   f"{'rsv0_GB/s':>9s}")
+        for r in d["v_sweep"]:
+            out.append(f"{r['T']:12d} {r['largest_part']:12d} {r['allgatherv_us']:9.2f} {r['allgatherv_GB/s']:9.1f} "
+                       f"{r['reducescatterv_rank0_us']:9.2f} {r['reducescatterv_rank0_GB/s']:9.1f}")
+    return "\n".join(out)
+
+
 def run_decode_trace(args):
     """Kernel-trace latency of the decode-size reduce: this script's
     --decode-trace-child under `rocprofv3 --kernel-trace` in a child process (started
@@ -1239,6 +1267,8 @@ def main():
     ap.add_argument("--cpu-reps", type=int, default=5)
     ap.add_argument("--summarize-trace", metavar="CSV",
                     help="print per-kernel durations of a rocprofv3 kernel-trace CSV and exit")
+    ap.add_argument("--summarize-sweep", metavar="JSON",
+                    help="print the tables of a --collective / --v-sweep JSON output and exit")
     ap.add_argument("--summarize-decode", metavar="JSON",
                     help="print the decode latency table of a bench JSON line and exit")
     ap.add_argument("--summarize-counters", metavar="CSV",
@@ -1270,6 +1300,9 @@ def main():
         return
     if args.summarize_counters:
         print(summarize_counters(args.summarize_counters))
+        return
+    if args.summarize_sweep:
+        print(summarize_sweep(args.summarize_sweep))
         return
     if args.summarize_decode:
         print(summarize_decode(args.summarize_decode))
