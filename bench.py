@@ -1192,6 +1192,7 @@ def run_cpu_baseline(args, host):
     (--cpu-fraction) to bound the run time; median of --cpu-reps runs after one warmup
     run each. GB/s from the same algorithmic byte counts as the GPU figures."""
     import oracle
+    import synth
 
     f = args.cpu_fraction
     rr = max(1, int(R3 * f))
@@ -1204,24 +1205,52 @@ def run_cpu_baseline(args, host):
     vs_part = [a[: rv * RB5] for a in host["v_src"]]
     vd_part = [a[:rv] for a in host["v_dest"]]
 
-    def step(threads, red, cps, vs, vd):
-        oracle.reduce("bf16", red, threads=threads)
-        oracle.copy_layout("packed", "packed", cps, threads=threads)
-        oracle.copy_layout("scattered", "transposed", cps, threads=threads)
-        oracle.copy_v(vs, vd, RB5, threads=threads)
+    op_times = {}  # (threads, op) -> seconds of each timed run
+
+    def step(threads, red, cps, vs, vd, record=False):
+        for name, fn in (("reduce", lambda: oracle.reduce("bf16", red, threads=threads)),
+                         ("allgather", lambda: oracle.copy_layout("packed", "packed", cps, threads=threads)),
+                         ("alltoall", lambda: oracle.copy_layout("scattered", "transposed", cps, threads=threads)),
+                         ("alltoallv", lambda: oracle.copy_v(vs, vd, RB5, threads=threads))):
+            t = time.perf_counter()
+            fn()
+            if record:
+                op_times.setdefault((threads, name), []).append(time.perf_counter() - t)
 
     def timed(fn):
-        fn()  # warmup
+        fn(False)  # warmup
         times = []
         for _ in range(args.cpu_reps):
             t = time.perf_counter()
-            fn()
+            fn(True)
             times.append(time.perf_counter() - t)
         return statistics.median(times)
 
     cores = oracle.default_threads()
-    t_all = timed(lambda: step(cores, host["r_src"], host["c_src"], host["v_src"], host["v_dest"]))
-    t_one = timed(lambda: step(1, red_part, cps_part, vs_part, vd_part))
+    t_all = timed(lambda rec: step(cores, host["r_src"], host["c_src"], host["v_src"], host["v_dest"], rec))
+    t_one = timed(lambda rec: step(1, red_part, cps_part, vs_part, vd_part, rec))
+    part = {"reduce": (W + 1) * rr * C3 * 2, "allgather": 2 * W * bb, "alltoall": 2 * W * bb,
+            "alltoallv": 2 * W * rv * RB5 + W * rv * 4}
+    per_op = {n: {"GB/s_all_cores": round(BYTES[n] / statistics.median(op_times[(cores, n)]) / 1e9, 4),
+                  "GB/s_one_core": round(part[n] / statistics.median(op_times[(1, n)]) / 1e9, 4)}
+              for n in BYTES}
+    # the two configs outside the step: the local reduce (8 x 1,048,576 bf16) and the
+    # largest decode share (8 x [64, 7168] bf16), median of --cpu-reps calls each
+    for name, srcs in (("local_reduce_8x1M", [synth.uniform_pm1_np(args.seed, 1, w, 1 << 20) for w in range(W)]),
+                       ("decode_T64", [synth.normal_np(args.seed, 2, w, 64 * 7168, 1.0) for w in range(W)])):
+        nbytes = (W + 1) * srcs[0].nbytes
+        row = {}
+        for tag, th in (("all_cores", cores), ("one_core", 1)):
+            oracle.reduce("bf16", srcs, threads=th)
+            ts = []
+            for _ in range(args.cpu_reps):
+                t = time.perf_counter()
+                oracle.reduce("bf16", srcs, threads=th)
+                ts.append(time.perf_counter() - t)
+            tm = statistics.median(ts)
+            row[f"GB/s_{tag}"] = round(nbytes / tm / 1e9, 4)
+            row[f"us_{tag}"] = round(tm * 1e6, 1)
+        per_op[name] = row
     one = {"value": round(part_bytes / t_one / 1e9, 4), "unit": "GB/s", "cores": 1,
            "sample": (f"fraction {f} of every op of the step (reduce {rr} of {R3} rows, allgather/alltoall "
                       f"{bb} of {B4} bytes per source, alltoallv {rv} of {R5} rows per source); median of "
@@ -1230,7 +1259,7 @@ def run_cpu_baseline(args, host):
     return {"value": round(full_bytes / t_all / 1e9, 4), "unit": "GB/s", "cores": cores, "kind": "oracle",
             "sample": (f"the whole step (all four ops, the GPU step's own input bytes) on {cores} threads; "
                        f"median of {args.cpu_reps} runs of {t_all:.2f} s after one warmup run"),
-            "seconds": round(t_all, 3), "single_core": one,
+            "seconds": round(t_all, 3), "single_core": one, "per_op": per_op,
             "host": {"cpu_model": cpu_model(), "hardware_threads": oracle.hardware_threads(),
                      "threads_available": len(os.sched_getaffinity(0))}}
 

@@ -137,3 +137,34 @@ def test_parse_decode_trace_walks_the_schedule(tmp_path):
     assert out["T=1"]["notify_on"]["warm"]["producer_p50_us"] == 2.0
     assert "error" in bench.parse_decode_trace(str(path), sched + [[8, "notify_off", "warm", 1, 3]])
     assert "error" in bench.parse_decode_trace(str(path), sched[:1])
+
+
+def test_cpu_baseline_on_a_small_step(monkeypatch):
+    """The oracle baseline leg end to end on a miniature step (the same code path, small
+    constants): every op and config is timed on all cores and on one, GB/s are positive."""
+    import argparse
+
+    import numpy as np
+
+    import synth
+
+    W = bench.W
+    monkeypatch.setattr(bench, "R3", 64)
+    monkeypatch.setattr(bench, "C3", 64)
+    monkeypatch.setattr(bench, "B4", 16 * W * 64)
+    monkeypatch.setattr(bench, "R5", 40)
+    monkeypatch.setattr(bench, "RB5", 64)
+    monkeypatch.setattr(bench, "BYTES", {"reduce": (W + 1) * 64 * 64 * 2, "allgather": 2 * W * bench.B4,
+                                         "alltoall": 2 * W * bench.B4, "alltoallv": 2 * W * 40 * 64 + W * 40 * 4})
+    p = synth.zipf_weights(1.1, W)
+    host = {"r_src": [synth.normal_np(0, 3, w, 64 * 64, 0.5) for w in range(W)],
+            "c_src": [synth.bits_np(0, 4, s, bench.B4) for s in range(W)],
+            "v_src": [synth.bits_np(0, 6, s, 40 * 64) for s in range(W)],
+            "v_dest": [synth.categorical_np(0, 5, s, 40, p) for s in range(W)]}
+    args = argparse.Namespace(cpu_fraction=0.5, cpu_reps=1, seed=0)
+    out = bench.run_cpu_baseline(args, host)
+    assert out["kind"] == "oracle" and out["value"] > 0 and out["single_core"]["value"] > 0
+    assert out["cores"] >= 1 and out["host"]["hardware_threads"] >= 1
+    for k in ("reduce", "allgather", "alltoall", "alltoallv", "local_reduce_8x1M", "decode_T64"):
+        assert out["per_op"][k]["GB/s_all_cores"] > 0 and out["per_op"][k]["GB/s_one_core"] > 0, k
+    assert np.isfinite(out["seconds"])
