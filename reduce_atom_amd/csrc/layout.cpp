@@ -48,9 +48,15 @@ static void default_policy(plr_layout* L) {
   L->run_notified = L->op == PLR_OP_REDUCE ? 2 : 4;
   if (L->op == PLR_OP_REDUCE) {
     if (L->src_bytes <= (2u << 20)) {  // latency regime: every tile in one dispatch wave
-      L->block = 256;
+      // 4 KiB tiles of 256 threads; over 512 KiB per source 8 KiB tiles of 512 threads
+      // (16 KiB chunks either way). Measured per call (notify + reduce, replayed graph) on
+      // 8 x [T, 7168] bf16: T = 64, 5.84 us against 6.67 us for 4 KiB tiles (un-notified
+      // 2.69 against 2.77 us); T = 32, 5.31 against 5.43 us notified but 2.52 against
+      // 2.29 us un-notified, and T = 8 slower both ways, so the smaller shares keep 4 KiB
+      const bool big = L->src_bytes > (512u << 10);
+      L->block = big ? 512 : 256;
       L->unroll = 1;
-      L->tile_bytes = 4u << 10;
+      L->tile_bytes = big ? 8u << 10 : 4u << 10;
       L->chunk_bytes = 16u << 10;
       L->run_notified = 1;
     } else {

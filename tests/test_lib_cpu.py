@@ -136,7 +136,12 @@ def test_regime_follows_bytes_per_source(plr):
     agv = pol("copy", "bf16", 4, 6 << 20, "packed", "packed", part_bytes=[3 << 20, 1 << 20, 1 << 20, 1 << 20])
     assert agv["notify_mode"] == plr.PLR_NOTIFY_CHECK and agv["tile_bytes"] == 4096
     red = pol("reduce", "bf16", 8, 2 << 20, "packed", "packed")
-    assert red["notify_mode"] == plr.PLR_NOTIFY_CHUNKS and red["tile_bytes"] == 4096  # decode-size share
+    assert red["notify_mode"] == plr.PLR_NOTIFY_CHUNKS and red["tile_bytes"] == 8192  # decode-size share
+    assert red["block"] == 512 and red["chunk_bytes"] == 16384
+    small = pol("reduce", "bf16", 8, 512 << 10, "packed", "packed")  # at most 512 KiB: 4 KiB tiles
+    assert small["tile_bytes"] == 4096 and small["block"] == 256 and small["chunk_bytes"] == 16384
+    t64 = pol("reduce", "bf16", 8, 64 * 7168 * 2, "packed", "packed")
+    assert t64["tile_bytes"] == 8192 and t64["block"] == 512
     red = pol("reduce", "bf16", 8, 4 << 20, "packed", "packed")
     assert red["notify_mode"] == plr.PLR_NOTIFY_CHECK and red["tile_bytes"] == 2048
 
