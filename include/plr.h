@@ -212,6 +212,15 @@ int plr_layout_policy(const plr_layout* L, size_t* tile_bytes, size_t* chunk_byt
                       int* workgroups, int* block, int* unroll, int* stages, int* datapath,
                       int* notify_mode);
 
+/* The launch shape of un-notified calls (plr_reduce / plr_copy with a NULL workspace):
+ * bytes per tile, threads per workgroup and the tile count. They wait for no chunk, so a
+ * reduce of at most 2 MiB per source on the direct datapath, with no tile, chunk or block
+ * override, launches them with 4 KiB tiles of 256 threads whatever the notified shape;
+ * every other layout reports its plr_layout_policy tile and block and plr_layout_ntiles.
+ * The results are bitwise the same either way. Any output pointer may be NULL;
+ * PLR_EINVAL for a NULL layout. */
+int plr_layout_plain_shape(const plr_layout* L, size_t* tile_bytes, int* block, int* ntiles);
+
 /* Current epoch E of the layout: the last notified call consumed flags >= E. */
 uint64_t plr_layout_epoch(const plr_layout* L);
 

@@ -81,6 +81,8 @@ _lib.plr_layout_segment.argtypes = [_vp, _i, _c.POINTER(_i), _c.POINTER(_sz), _c
 _lib.plr_layout_segment.restype = _i
 _lib.plr_layout_policy.argtypes = [_vp, _c.POINTER(_sz), _c.POINTER(_sz)] + [_c.POINTER(_i)] * 6
 _lib.plr_layout_policy.restype = _i
+_lib.plr_layout_plain_shape.argtypes = [_vp, _c.POINTER(_sz), _c.POINTER(_i), _c.POINTER(_i)]
+_lib.plr_layout_plain_shape.restype = _i
 _lib.plr_reduce.argtypes = [_vp, _c.POINTER(_vp), _vp, _vp, _vp]
 _lib.plr_reduce.restype = _i
 _lib.plr_copy.argtypes = [_vp, _c.POINTER(_vp), _vp, _vp, _vp]
@@ -119,6 +121,7 @@ _lib.plr_version.restype = _c.c_char_p
 EXPORTS = [
     "plr_layout_create", "plr_layout_destroy", "plr_layout_workspace_bytes", "plr_layout_dst_bytes",
     "plr_layout_nchunks", "plr_layout_ntiles", "plr_layout_nsegments", "plr_layout_segment", "plr_layout_policy",
+    "plr_layout_plain_shape",
     "plr_layout_epoch", "plr_reduce", "plr_copy", "plr_allreduce", "plr_copy_v", "plr_copy_v_scratch_bytes",
     "plr_copy_v_noalloc", "plr_copy_v_noalloc_max_scratch_bytes",
     "plr_layout_packet_bytes", "plr_pack", "plr_reduce_packets",
@@ -243,8 +246,12 @@ class Layout:
         _ok(_lib.plr_layout_policy(self._h, _c.byref(tb), _c.byref(cb), _c.byref(wg), _c.byref(bl),
                                    _c.byref(un), _c.byref(st), _c.byref(dp), _c.byref(nm)),
             "plr_layout_policy")
+        pt, pb, pn = _sz(), _i(), _i()
+        _ok(_lib.plr_layout_plain_shape(self._h, _c.byref(pt), _c.byref(pb), _c.byref(pn)),
+            "plr_layout_plain_shape")
         return dict(tile_bytes=tb.value, chunk_bytes=cb.value, workgroups=wg.value, block=bl.value,
-                    unroll=un.value, stages=st.value, datapath=dp.value, notify_mode=nm.value)
+                    unroll=un.value, stages=st.value, datapath=dp.value, notify_mode=nm.value,
+                    plain_tile_bytes=pt.value, plain_block=pb.value, plain_ntiles=pn.value)
 
 
 def plr_layout_create(op, dtype, world, bytes_per_src, in_kind, out_kind, rank=0,

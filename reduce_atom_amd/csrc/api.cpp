@@ -24,20 +24,27 @@ bool overlaps(uintptr_t a0, uint64_t alen, uintptr_t b0, uint64_t blen) {
   return alen && blen && a0 < b0 + blen && b0 < a0 + alen;
 }
 
+// Tiles of a call: notified calls use the chunk-aligned shape, un-notified ones the
+// layout's plain shape (the same except for latency-regime reduces).
+uint64_t tiles_of(const plr_layout* L, bool notified) {
+  return notified ? L->ntiles : L->plain_ntiles;
+}
+
 // Tiles per workgroup: the policy's run, or what an explicit workgroup count implies;
 // the grid then covers every tile once.
 uint32_t run_for(const plr_layout* L, bool notified) {
   uint64_t g = 0;
   if (L->workgroups > 0) g = (uint64_t)L->workgroups;
   if (g == 0) return (uint32_t)std::max(1, notified ? L->run_notified : L->run);
-  return (uint32_t)std::max<uint64_t>(1, (L->ntiles + g - 1) / g);
+  return (uint32_t)std::max<uint64_t>(1, (tiles_of(L, notified) + g - 1) / g);
 }
 
 Launch launch_of(const plr_layout* L, bool notified) {
   const uint32_t run = run_for(L, notified);
-  const uint32_t grid = (uint32_t)std::max<uint64_t>(1, ((uint64_t)L->ntiles + run - 1) / run);
+  const uint32_t grid = (uint32_t)std::max<uint64_t>(1, (tiles_of(L, notified) + run - 1) / run);
   const int xcd = L->xcd_order == kXcdOn;
-  return Launch{grid, (uint32_t)L->block, L->unroll, L->stages, L->datapath, run, xcd};
+  const uint32_t block = (uint32_t)(notified ? L->block : L->plain_block);
+  return Launch{grid, block, L->unroll, L->stages, L->datapath, run, xcd};
 }
 
 // Common checks of plr_reduce / plr_copy. Fills the notification block.
@@ -102,15 +109,16 @@ extern "C" int plr_reduce(plr_layout* L, const void* const* srcs, void* dst, voi
     ReduceArgs a{};
     for (int w = 0; w < L->world; ++w)
       a.src[w] = reinterpret_cast<const u32x4*>(static_cast<const char*>(srcs[w]) + L->segs[w].src_off);
+    const bool notified = nt.flags != nullptr;
     a.dst = static_cast<u32x4*>(dst);
     a.nvec = L->seg_len / 16;
-    a.tile_vecs = L->tile_bytes / 16;
-    a.ntiles = L->ntiles;
+    a.tile_vecs = (notified ? L->tile_bytes : L->plain_tile_bytes) / 16;
+    a.ntiles = (uint32_t)tiles_of(L, notified);
     a.tiles_per_chunk = L->tiles_per_chunk;
     a.nchunks = L->nchunks;
     a.world = (uint32_t)L->world;
     a.nt = nt;
-    const Launch l = launch_of(L, nt.flags != nullptr);
+    const Launch l = launch_of(L, notified);
     a.run = l.run;
     a.xcd = (uint32_t)l.xcd;
     const hipStream_t s = static_cast<hipStream_t>(stream);

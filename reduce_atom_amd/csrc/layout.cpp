@@ -48,11 +48,11 @@ static void default_policy(plr_layout* L) {
   L->run_notified = L->op == PLR_OP_REDUCE ? 2 : 4;
   if (L->op == PLR_OP_REDUCE) {
     if (L->src_bytes <= (2u << 20)) {  // latency regime: every tile in one dispatch wave
-      // 4 KiB tiles of 256 threads; over 512 KiB per source 8 KiB tiles of 512 threads
-      // (16 KiB chunks either way). Measured per call (notify + reduce, replayed graph) on
-      // 8 x [T, 7168] bf16: T = 64, 5.84 us against 6.67 us for 4 KiB tiles (un-notified
-      // 2.69 against 2.77 us); T = 32, 5.31 against 5.43 us notified but 2.52 against
-      // 2.29 us un-notified, and T = 8 slower both ways, so the smaller shares keep 4 KiB
+      // 4 KiB tiles of 256 threads; over 512 KiB per source, notified calls take 8 KiB
+      // tiles of 512 threads (16 KiB chunks either way) and un-notified ones keep 4 KiB
+      // of 256 (set after the tables below). Measured per call (notify + reduce, replayed
+      // graph) on 8 x [T, 7168] bf16: T = 64, 5.84 us against 6.67 us for 4 KiB tiles;
+      // T = 8 slower with 8 KiB
       const bool big = L->src_bytes > (512u << 10);
       L->block = big ? 512 : 256;
       L->unroll = 1;
@@ -407,6 +407,21 @@ extern "C" int plr_layout_create(const plr_layout_desc* d, plr_layout** out) {
     }
     for (int s = 1; s <= W; ++s) L->src_flag0[s] = std::max(L->src_flag0[s], L->src_flag0[s - 1]);
   }
+  L->plain_tile_bytes = L->tile_bytes;
+  L->plain_ntiles = L->ntiles;
+  L->plain_block = L->block;
+  // un-notified reduces of the latency regime keep 4 KiB tiles of 256 threads unless the
+  // caller chose a shape. Kernel trace, warm, 8 x [T, 7168] bf16 on one machine: T = 32 /
+  // 64 / 128 took 3.04 / 3.72 / 4.64 us against 3.36 / 4.24 / 4.72 us with 8 KiB tiles of
+  // 512 threads, which the notified calls keep (4.68 / 5.84 / 7.04 against 4.76 / 6.00 /
+  // 8.36 us with 4 KiB tiles)
+  if (L->op == PLR_OP_REDUCE && L->datapath == PLR_PATH_DIRECT && L->src_bytes <= (2u << 20) &&
+      L->seg_len && !d->tile_bytes && !d->chunk_bytes && !d->block) {
+    const uint64_t t = std::min<uint64_t>(4u << 10, L->seg_len);
+    L->plain_tile_bytes = t;
+    L->plain_ntiles = (uint32_t)((L->seg_len + t - 1) / t);
+    L->plain_block = 256;
+  }
   *out = L;
   return PLR_OK;
 }
@@ -448,5 +463,14 @@ extern "C" int plr_layout_policy(const plr_layout* L, size_t* tile_bytes, size_t
   if (stages) *stages = L->stages;
   if (datapath) *datapath = L->datapath;
   if (notify_mode) *notify_mode = L->notify_mode;
+  return PLR_OK;
+}
+
+extern "C" int plr_layout_plain_shape(const plr_layout* L, size_t* tile_bytes, int* block,
+                                      int* ntiles) {
+  if (!L) return PLR_EINVAL;
+  if (tile_bytes) *tile_bytes = L->plain_tile_bytes;
+  if (block) *block = L->plain_block;
+  if (ntiles) *ntiles = (int)L->plain_ntiles;
   return PLR_OK;
 }

@@ -42,6 +42,11 @@ struct plr_layout {
   uint32_t chunks_per_seg;
   uint32_t ntiles;           // reduce: tiles of the share; copy: tiles of all segments
   uint32_t nchunks;          // reduce: chunks of the share; copy: chunks of all segments
+  // un-notified calls wait for no chunk, so a reduce may launch them with a tile and
+  // workgroup size of their own; every other layout uses the shape above for both
+  uint64_t plain_tile_bytes;
+  uint32_t plain_ntiles;
+  int plain_block;
   // copy: first tile and first chunk of every segment (nseg + 1 entries; with equal
   // segments k * tiles_per_seg and k * chunks_per_seg), and first flag of every
   // source (W + 1 entries): segments go source by source

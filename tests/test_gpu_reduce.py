@@ -150,12 +150,17 @@ def test_config1_local_reduce(plr, oracle_mod):
     assert_same("bf16", from_dev(_run(plr, L2, srcs, 2 * n, workspace=True)).view(np.uint16), ref)
 
 
-@pytest.mark.parametrize("T", [1, 8, 32, 64])
+@pytest.mark.parametrize("T", [1, 8, 32, 37, 64, 128])
 def test_config2_decode_share(plr, oracle_mod, T):
-    """8 contributions of [T, 7168] bf16, N(0, 1): the whole output, notify off and on."""
+    """8 contributions of [T, 7168] bf16, N(0, 1): the whole output, notify off and on.
+    From T = 37 (over 512 KiB per source) the two launch with different tiles and
+    workgroups (8 KiB of 512 threads notified, 4 KiB of 256 not); odd T leave a ragged
+    last tile in both."""
     W, n = 8, T * 7168
     srcs = [synth.normal_np(0, 2, w, n, 1.0) for w in range(W)]
     ref = oracle_mod.reduce("bf16", srcs)
+    pol = plr.plr_layout_create("reduce", "bf16", W, 2 * n, "packed", "packed").policy()
+    assert (pol["tile_bytes"] != pol["plain_tile_bytes"]) == (T >= 37)
     for ws in (False, True):
         L = plr.plr_layout_create("reduce", "bf16", W, 2 * n, "packed", "packed")
         assert_same("bf16", from_dev(_run(plr, L, srcs, 2 * n, workspace=ws)).view(np.uint16), ref,

@@ -106,7 +106,8 @@ def test_policy_overrides(plr):
     L = plr.plr_layout_create("reduce", "f16", 4, 1 << 24, "packed", "packed", chunk_bytes=4096,
                               workgroups=33, block=128, unroll=4, datapath=plr.PLR_PATH_DIRECT)
     assert L.policy() == dict(tile_bytes=2048, chunk_bytes=4096, workgroups=33, block=128, unroll=4,
-                              stages=0, datapath=plr.PLR_PATH_DIRECT, notify_mode=plr.PLR_NOTIFY_CHECK)
+                              stages=0, datapath=plr.PLR_PATH_DIRECT, notify_mode=plr.PLR_NOTIFY_CHECK,
+                              plain_tile_bytes=2048, plain_block=128, plain_ntiles=8192)
     # the LDS path reports its ring depth: W KiB per stage per wave for a reduce
     for w, depth in ((1, 4), (4, 4), (5, 2), (8, 2), (9, 2), (16, 2)):
         R = plr.plr_layout_create("reduce", "bf16", w, 1 << 20, "packed", "packed", datapath=plr.PLR_PATH_LDS)
@@ -142,8 +143,24 @@ def test_regime_follows_bytes_per_source(plr):
     assert small["tile_bytes"] == 4096 and small["block"] == 256 and small["chunk_bytes"] == 16384
     t64 = pol("reduce", "bf16", 8, 64 * 7168 * 2, "packed", "packed")
     assert t64["tile_bytes"] == 8192 and t64["block"] == 512
+    # un-notified calls of a decode-size reduce keep 4 KiB tiles of 256 threads (no chunk
+    # to wait for), 224 of them for [64, 7168] bf16; a caller's shape applies to both
+    assert (t64["plain_tile_bytes"], t64["plain_block"], t64["plain_ntiles"]) == (4096, 256, 224)
+    assert (small["plain_tile_bytes"], small["plain_block"], small["plain_ntiles"]) == (4096, 256, 128)
+    tiny = pol("reduce", "bf16", 8, 48, "packed", "packed")  # one short tile
+    assert (tiny["plain_tile_bytes"], tiny["plain_block"], tiny["plain_ntiles"]) == (48, 256, 1)
+    for kw in (dict(tile_bytes=8192), dict(chunk_bytes=32768), dict(block=128)):
+        o = pol("reduce", "bf16", 8, 64 * 7168 * 2, "packed", "packed", **kw)
+        assert (o["plain_tile_bytes"], o["plain_block"]) == (o["tile_bytes"], o["block"]), kw
+    lds = pol("reduce", "bf16", 8, 64 * 7168 * 2, "packed", "packed", datapath=plr.PLR_PATH_LDS)
+    assert (lds["plain_tile_bytes"], lds["plain_block"]) == (lds["tile_bytes"], lds["block"])
     red = pol("reduce", "bf16", 8, 4 << 20, "packed", "packed")
     assert red["notify_mode"] == plr.PLR_NOTIFY_CHECK and red["tile_bytes"] == 2048
+    assert (red["plain_tile_bytes"], red["plain_block"]) == (2048, 128)
+    for L in (plr.plr_layout_create("copy", "bf16", 8, 2 << 20, "packed", "packed"),
+              plr.plr_layout_create("allreduce", "bf16", 8, 1 << 20, "scattered", "scattered")):
+        o = L.policy()
+        assert (o["plain_tile_bytes"], o["plain_block"], o["plain_ntiles"]) == (o["tile_bytes"], o["block"], L.ntiles)
 
 
 def test_tiles_and_chunks(plr):
