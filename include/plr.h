@@ -317,8 +317,8 @@ int plr_reduce_packets(plr_layout* L, const void* const* packets, void* dst, voi
  *   srcs, dest_of_row: host arrays of W device pointers; rows_per_src: host array.
  * A destination id outside [0, W) is a caller error: its row is skipped and its
  * counts and offsets are undefined.
- * Errors: PLR_EINVAL, PLR_EALIGN (row_bytes, srcs, dst), PLR_EUNSUPPORTED (W > 16, or more
- * than 2^31 - 1 rows in all), PLR_EHIP. */
+ * Errors: PLR_EINVAL (also an output of 2^64 bytes or more), PLR_EALIGN (row_bytes, srcs,
+ * dst), PLR_EUNSUPPORTED (W > 16, or more than 2^31 - 1 rows in all), PLR_EHIP. */
 int plr_copy_v(int world, const void* const* srcs, const int64_t* rows_per_src,
                const int32_t* const* dest_of_row, size_t row_bytes, void* dst,
                int64_t* counts, int64_t* offsets, void* scratch, void* stream);
@@ -326,7 +326,8 @@ int plr_copy_v(int world, const void* const* srcs, const int64_t* rows_per_src,
 /* Scratch bytes plr_copy_v needs for these row counts (host only): a 256-byte header,
  * one 32-bit key per row, and for every 1024-row segment of a source W int32 counts
  * and 16 int32 first output rows, each region rounded up to 256 bytes. 0 for invalid
- * arguments. */
+ * arguments (W outside [1, 16], a negative row count) and for more than 2^31 - 1 rows
+ * in all, which plr_copy_v does not support. */
 size_t plr_copy_v_scratch_bytes(int world, const int64_t* rows_per_src);
 
 /* Allocation-free form of plr_copy_v, for callers that cannot allocate device memory

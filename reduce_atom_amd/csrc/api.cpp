@@ -191,6 +191,17 @@ constexpr uint64_t kCopyVScratchHeader = 256;
 
 static uint64_t up256(uint64_t x) { return (x + 255) & ~255ull; }
 
+int plr::copy_v_check_rows(int world, const int64_t* rows_per_src) {
+  if (!rows_per_src) return PLR_EINVAL;
+  int64_t total = 0;
+  for (int s = 0; s < world; ++s) {
+    if (rows_per_src[s] < 0) return PLR_EINVAL;
+    if (rows_per_src[s] > 0x7FFFFFFF) return PLR_EUNSUPPORTED;
+    total += rows_per_src[s];  // at most 16 x (2^31 - 1): no overflow
+  }
+  return total > 0x7FFFFFFF ? PLR_EUNSUPPORTED : PLR_OK;
+}
+
 struct CopyVScratch {
   uint64_t key_off, count_off, out_off, bytes;
 };
@@ -211,9 +222,8 @@ static CopyVScratch copy_v_scratch(int world, const int64_t* rows_per_src) {
 }
 
 extern "C" size_t plr_copy_v_scratch_bytes(int world, const int64_t* rows_per_src) {
-  if (world < 1 || world > PLR_MAX_WORLD || !rows_per_src) return 0;
-  for (int s = 0; s < world; ++s)
-    if (rows_per_src[s] < 0) return 0;
+  if (world < 1 || world > PLR_MAX_WORLD) return 0;
+  if (copy_v_check_rows(world, rows_per_src) != PLR_OK) return 0;
   return (size_t)copy_v_scratch(world, rows_per_src).bytes;
 }
 
@@ -226,10 +236,11 @@ extern "C" int plr_copy_v(int world, const void* const* srcs, const int64_t* row
   if (row_bytes == 0) return PLR_EINVAL;
   if (row_bytes % 16) return PLR_EALIGN;
   if (((uintptr_t)counts & 7) || ((uintptr_t)offsets & 7) || !a16(scratch)) return PLR_EALIGN;
+  const int rows_rc = copy_v_check_rows(world, rows_per_src);
+  if (rows_rc != PLR_OK) return rows_rc;
   CopyVArgs a{};
   a.row_start[0] = 0;
   for (int s = 0; s < world; ++s) {
-    if (rows_per_src[s] < 0) return PLR_EINVAL;
     if (rows_per_src[s] > 0) {
       if (!srcs[s] || !dest_of_row[s] || !dst) return PLR_EINVAL;
       if (!a16(srcs[s])) return PLR_EALIGN;
@@ -241,8 +252,9 @@ extern "C" int plr_copy_v(int world, const void* const* srcs, const int64_t* row
   }
   const int64_t total = a.row_start[world];
   for (int s = world + 1; s <= PLR_MAX_WORLD; ++s) a.row_start[s] = total;
-  if (total > 0x7FFFFFFF) return PLR_EUNSUPPORTED;  // output rows are int32
   if (total > 0) {
+    // an output past 2^64 bytes cannot exist (and would wrap the overlap check)
+    if (row_bytes > UINT64_MAX / (uint64_t)total) return PLR_EINVAL;
     if (!a16(dst)) return PLR_EALIGN;
     const uint64_t out_bytes = (uint64_t)total * row_bytes;
     for (int s = 0; s < world; ++s)

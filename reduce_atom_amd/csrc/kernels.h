@@ -201,6 +201,11 @@ const Timing& timing();
 // Keeps e as the calling thread's last HIP error (plr_last_hip_error); returns PLR_EHIP.
 int record_hip_error(hipError_t e);
 
+// Row counts of a variable-length AllToAll: PLR_EINVAL for a negative count (or a
+// NULL array), PLR_EUNSUPPORTED for more than 2^31 - 1 rows in all (output rows are
+// int32), else PLR_OK. Each count is bounded before it is added, so nothing overflows.
+int copy_v_check_rows(int world, const int64_t* rows_per_src);
+
 // Launchers (defined next to their kernels). Return a hipError_t.
 hipError_t launch_reduce(const ReduceArgs& a, int dtype, const Launch& l, hipStream_t s);
 hipError_t launch_copy(const CopyArgs& a, const Launch& l, hipStream_t s);

@@ -61,9 +61,9 @@ extern "C" int plr_copy_v_noalloc(int world, const void* const* srcs, const int6
                                   int64_t* counts, int64_t* offsets, void* stream) {
   if (world < 1 || !rows_per_src) return PLR_EINVAL;
   if (world > PLR_MAX_WORLD) return PLR_EUNSUPPORTED;
-  const size_t need = plr_copy_v_scratch_bytes(world, rows_per_src);
-  if (need == 0) return PLR_EINVAL;  // a negative row count
-  if (need > plr::kNoAllocScratchBytes) return PLR_ETOOLARGE;
+  const int rows_rc = plr::copy_v_check_rows(world, rows_per_src);
+  if (rows_rc != PLR_OK) return rows_rc;
+  if (plr_copy_v_scratch_bytes(world, rows_per_src) > plr::kNoAllocScratchBytes) return PLR_ETOOLARGE;
   // the device the kernels will run on: the stream's, or the current one
   int dev = -1;
   hipError_t e = stream ? hipStreamGetDevice(static_cast<hipStream_t>(stream), &dev) : hipGetDevice(&dev);

@@ -246,6 +246,13 @@ def test_call_validation_without_device(plr):
     assert _code(cv, [A + 8], [4], [D], 16, B, D, D, D) == plr.PLR_EALIGN
     assert _code(cv, [A], [4], [D], 16, A + 16, D, D, D) == plr.PLR_EINVAL  # dst overlaps source
     assert _code(cv, [A], [-1], [D], 16, B, D, D, D) == plr.PLR_EINVAL
+    # row counts are bounded before they are summed: no signed overflow, no wrapped sizes
+    big = (1 << 31) - 1
+    assert _code(cv, [A, B], [big, 1], [D, D], 16, D, D, D, D) == plr.PLR_EUNSUPPORTED
+    assert _code(cv, [A, B], [(1 << 62), (1 << 62)], [D, D], 16, D, D, D, D) == plr.PLR_EUNSUPPORTED
+    assert _code(cv, [A] * 4, [(1 << 63) - 1] * 4, [D] * 4, 16, D, D, D, D) == plr.PLR_EUNSUPPORTED
+    # an output of 2^64 bytes or more cannot exist; its size would wrap the overlap check
+    assert _code(cv, [A], [2], [D], 1 << 63, 1 << 40, D, D, D) == plr.PLR_EINVAL
 
 
 def test_scratch_bytes(plr):
@@ -256,6 +263,9 @@ def test_scratch_bytes(plr):
     assert plr.plr_copy_v_scratch_bytes(2, [1025, 0]) == 256 + 4352 + 256 + 256
     assert plr.plr_copy_v_scratch_bytes(2, [-1, 0]) == 0
     assert plr.plr_copy_v_scratch_bytes(0, []) == 0
+    assert plr.plr_copy_v_scratch_bytes(2, [(1 << 31) - 1, 1]) == 0  # more than 2^31 - 1 rows
+    assert plr.plr_copy_v_scratch_bytes(4, [(1 << 62)] * 4) == 0  # the sum would wrap
+    assert plr.plr_copy_v_scratch_bytes(1, [(1 << 31) - 1]) > 8 << 30
 
 
 def test_strerror(plr):
@@ -503,5 +513,6 @@ def test_copy_v_noalloc_limits_without_device(plr):
     assert plr.plr_copy_v_scratch_bytes(2, [too_many, 0]) > cap
     assert call([too_many, 0]) == plr.PLR_ETOOLARGE
     assert call([-1, 4]) == plr.PLR_EINVAL
+    assert call([1 << 62, 1 << 62]) == plr.PLR_EUNSUPPORTED  # as plr_copy_v, not a wrapped size
     assert fn(0, ptrs, (ctypes.c_int64 * 2)(1, 1), ptrs, 64, 1, 2, 3, None) == plr.PLR_EINVAL
     assert fn(17, ptrs, (ctypes.c_int64 * 2)(1, 1), ptrs, 64, 1, 2, 3, None) == plr.PLR_EUNSUPPORTED
