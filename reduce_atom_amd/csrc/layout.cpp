@@ -143,6 +143,7 @@ extern "C" int plr_layout_create(const plr_layout_desc* d, plr_layout** out) {
     for (int w = 0; w < W; ++w) {
       part[w] = d->part_bytes[w];
       if (!aligned16(part[w])) return fail(PLR_EALIGN);
+      if (part[w] > B - part0[w]) return fail(PLR_EINVAL);  // past T (and no wrapped sum)
       part0[w + 1] = part0[w] + part[w];
     }
     if (part0[W] != B) return fail(PLR_EINVAL);  // the sizes add up to the message size T

@@ -393,6 +393,10 @@ def test_variable_length_layouts(plr, oracle_mod):
     # errors
     bad = plr.plr_layout_create
     assert _code(bad, "copy", "bf16", 2, 64, "packed", "packed", part_bytes=[32, 16]) == plr.PLR_EINVAL  # sum
+    # sizes whose 64-bit sum wraps around to T are still past T
+    wrap = [1 << 63, 1 << 63, 16]
+    assert _code(bad, "reduce", "bf16", 3, 16, "scattered", "packed", rank=2, part_bytes=wrap) == plr.PLR_EINVAL
+    assert _code(bad, "copy", "bf16", 3, 16, "packed", "packed", part_bytes=wrap) == plr.PLR_EINVAL
     assert _code(bad, "copy", "bf16", 2, 64, "packed", "packed", part_bytes=[40, 24]) == plr.PLR_EALIGN
     assert _code(bad, "copy", "bf16", 2, 64, "scattered", "transposed", part_bytes=[32, 32]) == plr.PLR_EINVAL
     assert _code(bad, "reduce", "bf16", 2, 64, "packed", "packed", part_bytes=[32, 32]) == plr.PLR_EINVAL
