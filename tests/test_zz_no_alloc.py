@@ -2,7 +2,8 @@
 library's fixed per-GPU array) against plr_copy_v with a caller-allocated scratch, bit
 for bit, on calls in a row that shrink (the array keeps the last call's contents), in
 both the small form (at most 256 segment counts) and the ticket form; both are also
-checked against the oracle."""
+checked against the oracle. The call captured in a HIP graph is replayed with new
+inputs, eager calls on the same array in between."""
 import numpy as np
 import pytest
 import torch
@@ -95,3 +96,52 @@ def test_noalloc_rejects_requests_beyond_its_scratch(plr):
     with pytest.raises(plr.PlrError) as e:
         plr.plr_copy_v_noalloc([src, src], rows, [dest, dest], 16, src, src, src)
     assert e.value.code == plr.PLR_ETOOLARGE
+
+
+def _capture(fn):
+    g = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        with torch.cuda.graph(g, stream=side):
+            fn()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    return g
+
+
+@pytest.mark.parametrize("W,R,rb", [(16, 1100, 64), (8, 1000, 1024)], ids=["ticket_form", "small_form"])
+def test_noalloc_replayed_from_a_graph(plr, oracle_mod, W, R, rb):
+    """The callers it is for: the call captured in a HIP graph (it allocates nothing and
+    records kernel launches only), replayed three times with new inputs written by eager
+    work in between and an eager call of another size on the same array before each
+    replay; every replay matches the oracle."""
+    rows = [R - (s % 3) * 7 for s in range(W)]
+    p = synth.zipf_weights(1.1, W)
+    srcs = [torch.empty(rows[s] * rb, dtype=torch.uint8, device="cuda") for s in range(W)]
+    dests = [torch.empty(rows[s], dtype=torch.int32, device="cuda") for s in range(W)]
+    dst = torch.empty(sum(rows) * rb, dtype=torch.uint8, device="cuda")
+    counts = torch.empty(W * W, dtype=torch.int64, device="cuda")
+    offsets = torch.empty(W * W, dtype=torch.int64, device="cuda")
+    o_rows, o_srcs_np, o_dests_np = _case(4, 700, 32, seed=90)  # the other call's shape
+    o_srcs = [torch.from_numpy(s.copy()).cuda() for s in o_srcs_np]
+    o_dests = [torch.from_numpy(d).cuda() for d in o_dests_np]
+    _run(plr, True, o_rows, o_srcs, o_dests, 32)  # an eager call first, as before any capture
+    g = _capture(lambda: plr.plr_copy_v_noalloc(srcs, rows, dests, rb, dst, counts, offsets))
+    for replay in range(3):
+        srcs_np = [synth.bits_np(70 + replay, 62, s, rows[s] * rb) for s in range(W)]
+        dests_np = [synth.categorical_np(70 + replay, 63, s, rows[s], p) for s in range(W)]
+        for t, a in zip(srcs, srcs_np):
+            t.copy_(torch.from_numpy(a))
+        for t, a in zip(dests, dests_np):
+            t.copy_(torch.from_numpy(a))
+        other = _run(plr, True, o_rows, o_srcs, o_dests, 32)
+        g.replay()
+        torch.cuda.synchronize()
+        ref = oracle_mod.copy_v(srcs_np, dests_np, rb)
+        got = (dst.cpu().numpy(), counts.cpu().numpy().reshape(W, W), offsets.cpu().numpy().reshape(W, W))
+        for a, b, what in zip(got, ref, ("rows", "counts", "offsets")):
+            assert np.array_equal(a, b), f"replay {replay}: {what}"
+        o_ref = oracle_mod.copy_v(o_srcs_np, o_dests_np, 32)
+        for a, b, what in zip(other, o_ref, ("rows", "counts", "offsets")):
+            assert np.array_equal(a, b), f"eager call before replay {replay}: {what}"
