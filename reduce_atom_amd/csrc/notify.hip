@@ -21,7 +21,7 @@ __global__ void __launch_bounds__(256) k_notify(const NotifyArgs a) {
 // stream order may read every chunk whose flag was mirrored without waiting or
 // fencing; only the chunks still missing are waited for one by one (section 3.2: a
 // consumer never reads a chunk before its flag). One workgroup does it all, with
-// kCheckUnroll flag loads per lane in flight, so that the verdict needs one round of
+// kCheckUnroll flag loads per lane in flight, so that the outcome needs one round of
 // loads and a workgroup barrier, not a second kernel-wide combining step.
 constexpr int kCheckUnroll = 8;
 
