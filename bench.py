@@ -1111,14 +1111,21 @@ def run_atom_user_kernels(torch, srcs):
 
 
 def cpu_model() -> str:
+    """The host CPU's model name from /proc/cpuinfo, with its family, model and stepping
+    numbers (virtual machines often report a generic name)."""
+    fields = {}
     try:
         with open("/proc/cpuinfo") as f:
             for line in f:
-                if line.startswith("model name"):
-                    return line.split(":", 1)[1].strip()
+                if not line.strip():
+                    break  # the first processor's block is enough
+                k, _, v = line.partition(":")
+                fields[k.strip()] = v.strip()
     except OSError:
         pass
-    return "unknown"
+    name = fields.get("model name", "unknown")
+    ids = [f"{k} {fields[k]}" for k in ("cpu family", "model", "stepping") if k in fields]
+    return f"{name} ({', '.join(ids)})" if ids else name
 
 
 ONLY_OPS = ("reduce", "allgather", "alltoall", "alltoallv", "reduce_lds", "allgather_lds", "allreduce_fused",
