@@ -25,7 +25,8 @@ def plr():
 
 
 def _declared_functions():
-    text = open(os.path.join(ROOT, "include", "plr.h")).read()
+    with open(os.path.join(ROOT, "include", "plr.h")) as f:
+        text = f.read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
     return sorted(set(re.findall(r"\b(plr_\w+)\s*\(", text)))
 
