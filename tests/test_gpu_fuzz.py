@@ -121,6 +121,45 @@ def test_fuzz(plr, oracle_mod, seed):
             assert np.array_equal(got, ref.view(np.uint8)), what
         else:
             assert_same(dtype, got, ref.view(np.uint8), what)
+    if notify != "none":  # the same layout un-notified (its own launch shape where the policy gives one)
+        dst2 = empty_dev(L.dst_bytes, fill=0xA5)
+        call(L, srcs, dst2)
+        torch.cuda.synchronize()
+        got = from_dev(dst2)[:L.dst_bytes]
+        if call is plr.plr_copy:
+            assert np.array_equal(got, ref.view(np.uint8)), what + " un-notified"
+        else:
+            assert_same(dtype, got, ref.view(np.uint8), what + " un-notified")
+
+
+@pytest.mark.parametrize("seed", range(40 * SCALE))
+def test_fuzz_decode_shares(plr, oracle_mod, seed):
+    """Reduce shares of at most 2 MiB per source with the policy's own launch shapes:
+    notified calls and un-notified ones launch differently over 512 KiB per source, and
+    both must give the oracle's bits, ragged ends included."""
+    rng = np.random.default_rng(5000 + seed)
+    W = int(rng.choice([1, 2, 3, 5, 8, 13, 16]))
+    dtype = ["bf16", "f16", "f32"][rng.integers(3)]
+    B = 16 * int(rng.integers(1, 131073))  # up to 2 MiB per source
+    pol = {"workgroups": int(rng.integers(1, 300))} if rng.random() < 0.2 else {}
+    what = f"seed={seed} W={W} dtype={dtype} B={B} pol={pol}"
+    print(what, flush=True)
+    srcs_np = [synth.normal_np(seed, 12, w, B // EB[dtype], 1.0, dtype) for w in range(W)]
+    ref = oracle_mod.reduce(dtype, srcs_np)
+    srcs = [to_dev(x) for x in srcs_np]
+    L = plr.plr_layout_create("reduce", dtype, W, B, "packed", "packed", **pol)
+    p = L.policy()
+    assert (p["plain_tile_bytes"], p["plain_block"]) == ((min(4096, B), 256) if not pol or "workgroups" in pol
+                                                         else (p["tile_bytes"], p["block"])), what
+    ws = torch.zeros(max(L.workspace_bytes, 256), dtype=torch.uint8, device="cuda")
+    for notified in (False, True, False):
+        dst = empty_dev(B, fill=0x5A)
+        if notified:
+            plr.plr_notify(L, -1, ws)
+        plr.plr_reduce(L, srcs, dst, ws if notified else None)
+        torch.cuda.synchronize()
+        assert_same(dtype, from_dev(dst)[:B], ref.view(np.uint8), f"{what} notified={notified}")
+    assert plr.plr_check(L, ws) == plr.PLR_OK, what
 
 
 @pytest.mark.parametrize("seed", range(40 * SCALE))
