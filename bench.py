@@ -462,8 +462,101 @@ def run_bench(args):
     torch.cuda.empty_cache()
     decode = run_decode(args, torch, plr, synth, dev) if not args.no_decode else None
     if decode is not None:
-        decode = {"decode": decode, "local": run_local_reduce(args, torch, plr, synth, dev)}
+        decode = {"decode": decode, "local": run_local_reduce(args, torch, plr, synth, dev),
+                  "producer": run_producer_kernel(args, torch, plr, synth, dev)}
     return value, ms_per_step, ms_per_step_events, roofline, per_op, decode, host
+
+
+def graph_us_per_call(torch, once, iters, per_graph=50):
+    """Mean microseconds per call of `once` with `per_graph` calls captured in one HIP graph
+    and the graph replayed back to back (about `iters` calls in all), so that host-side call
+    overhead does not starve the GPU. The captured launches are kernels only: no memory-set
+    nodes."""
+    graph = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        with torch.cuda.graph(graph, stream=side):
+            for _ in range(per_graph):
+                once()
+    torch.cuda.current_stream().wait_stream(side)
+    graph.replay()
+    a0, b0 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    reps = max(1, iters // per_graph)
+    torch.cuda.synchronize()
+    a0.record()
+    for _ in range(reps):
+        graph.replay()
+    b0.record()
+    torch.cuda.synchronize()
+    us = a0.elapsed_time(b0) * 1e3 / (per_graph * reps)
+    del graph
+    return us
+
+
+def run_producer_kernel(args, torch, plr, synth, dev):
+    """Producer kernels that announce their own chunks (tests/atom_kernels.hip, atom_produce:
+    the producing kernel copies its input into the share, standing for any producing
+    computation; section 3.2 and Figure 7), each followed by the library's consumer, per
+    call in a replayed HIP graph, W = 8 x [T, 7168] bf16, every mode's result checked equal:
+      ordered        plain stores, then the un-notified reduce (stream order alone, which
+                     only a producer on the consumer's own GPU and stream can rely on);
+      notify_kernel  plain stores, plr_notify (a separate release kernel), notified reduce;
+      flags_fused    plain stores and each chunk's flag released by the producing kernel
+                     (signal_flag), notified reduce;
+      packets_fused  the producing kernel writes packets (store_packet), plr_reduce_packets."""
+    path = os.path.join(ROOT, "tests", "libatom_kernels.so")
+    if not os.path.exists(path):
+        return "not built"
+    lib = ctypes.CDLL(path)
+    vp, sz, i, ull = ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int, ctypes.c_ulonglong
+    lib.atom_produce.argtypes = [i, i, ctypes.POINTER(vp), ctypes.POINTER(vp), sz, sz, vp, ull, vp]
+    out = {}
+    for T in (args.decode_t or DECODE_T):
+        n = T * 7168
+        share = 2 * n
+        ins = [synth.normal_t(args.seed, 3, w, n, 1.0, device=dev) for w in range(W)]
+        in_p = (vp * W)(*[t.data_ptr() for t in ins])
+        dst = torch.empty(n, dtype=torch.bfloat16, device=dev)
+        ref, res = None, {}
+        for mode in ("ordered", "notify_kernel", "flags_fused", "packets_fused"):
+            L = plr.plr_layout_create("reduce", "bf16", W, share, "packed", "packed")
+            chunk = L.policy()["chunk_bytes"]
+            if (share + chunk - 1) // chunk != L.nchunks:  # one producer workgroup per flag
+                raise RuntimeError("producer chunks do not match the layout's flags")
+            ws = torch.zeros(max(L.workspace_bytes, 256), dtype=torch.uint8, device=dev)
+            nbytes = L.packet_bytes if mode == "packets_fused" else share
+            outs = [torch.zeros(nbytes, dtype=torch.uint8, device=dev) for _ in range(W)]
+            out_p = (vp * W)(*[t.data_ptr() for t in outs])
+            pmode = {"ordered": 0, "notify_kernel": 0, "flags_fused": 1, "packets_fused": 2}[mode]
+
+            def once():
+                rc = lib.atom_produce(pmode, W, in_p, out_p, share, chunk, ws.data_ptr() + 256, L.epoch + 1,
+                                      torch.cuda.current_stream().cuda_stream)
+                if rc:
+                    raise RuntimeError(f"atom_produce: {rc}")
+                if mode == "ordered":
+                    plr.plr_reduce(L, outs, dst)
+                elif mode == "notify_kernel":
+                    plr.plr_notify(L, -1, ws)
+                    plr.plr_reduce(L, outs, dst, ws)
+                elif mode == "flags_fused":
+                    plr.plr_reduce(L, outs, dst, ws)
+                else:
+                    plr.plr_reduce_packets(L, outs, dst, ws)
+
+            for _ in range(args.decode_warmup):
+                once()
+            torch.cuda.synchronize()
+            if ref is None:
+                ref = dst.clone()
+            elif not torch.equal(dst, ref):
+                raise RuntimeError(f"producer kernel {mode}: result differs from the ordered mode's")
+            res[mode] = {"us_per_call_graph": round(graph_us_per_call(torch, once, args.decode_iters), 2)}
+            if plr.plr_check(L, ws) != plr.PLR_OK:
+                raise RuntimeError("producer kernel: device error")
+        out[f"T={T}"] = res
+    return out
 
 
 def run_decode(args, torch, plr, synth, dev):
@@ -497,27 +590,8 @@ def run_decode(args, torch, plr, synth, dev):
 
             for _ in range(args.decode_warmup):
                 once()
-            # (a) back to back on the GPU: 50 calls captured in one HIP graph, replayed,
-            # so that host-side call overhead does not starve the GPU (the captured
-            # launches are the library's kernels only; no memory-set nodes)
-            graph = torch.cuda.CUDAGraph()
-            side = torch.cuda.Stream()
-            side.wait_stream(torch.cuda.current_stream())
-            with torch.cuda.stream(side):
-                with torch.cuda.graph(graph, stream=side):
-                    for _ in range(50):
-                        once()
-            torch.cuda.current_stream().wait_stream(side)
-            graph.replay()
-            a0, b0 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            torch.cuda.synchronize()
-            a0.record()
-            for _ in range(args.decode_iters // 50):
-                graph.replay()
-            b0.record()
-            torch.cuda.synchronize()
-            per_call = a0.elapsed_time(b0) * 1e3 / (50 * (args.decode_iters // 50))
-            del graph
+            # (a) back to back on the GPU: 50 calls captured in one HIP graph, replayed
+            per_call = graph_us_per_call(torch, once, args.decode_iters)
             # (b) a pair of timing-only events on every reduce kernel
             E = TimingEvents(torch)
             evs = [(E.create(), E.create()) for _ in range(args.decode_iters)]
@@ -1384,6 +1458,7 @@ def main():
     value, ms, ms_events, roofline, per_op, small, host = run_bench(args)
     decode = small["decode"] if small else None
     local = small["local"] if small else None
+    producer = small["producer"] if small else None
     nxt = None if args.no_decode else run_next(args)
     cpu = None if host is None else run_cpu_baseline(args, host)
     del host
@@ -1399,7 +1474,7 @@ def main():
                    "world": W, "notify": True, "seed": args.seed, "step_bytes": sum(BYTES.values())},
         "roofline": roofline, "cpu_baseline": cpu, "per_op": per_op,
         "ms_per_step_with_op_events": round(ms_events, 4), "decode_reduce_us": decode,
-        "local_reduce_8x1M_bf16": local,
+        "local_reduce_8x1M_bf16": local, "decode_producer_kernel_us": producer,
         "beyond_step": nxt,
     }
     print(json.dumps(line), flush=True)

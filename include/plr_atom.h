@@ -29,6 +29,9 @@
  * at agent scope: the workgroup's later loads see the producer's stores). Flags hold
  * a monotonic epoch (section 4.3 "Epoch Bookkeeping"). A wait is bounded: it returns
  * false after spin_limit polls, and a kernel must then give up without reading.
+ * Packets (section 3.2 and Figure 7: payload and notification in one store): a producer
+ * may write its share directly in the packet form plr_reduce_packets reads
+ * (packet_slot, store_packet), so that it needs neither a flag nor a release.
  *
  * Policy (section 4.2 "Codesign Policies and Tuning": applications may define their
  * own): THREADS (64, 128, 256 or 512) and UNROLL (16-byte vectors per lane in flight
@@ -252,6 +255,24 @@ __device__ __forceinline__ bool wait_flag(const uint64_t* flag, uint64_t epoch, 
     if (ok) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
   }
   return __syncthreads_and(ok) != 0;
+}
+
+// ---- packets (section 3.2 and Figure 7) ----
+// The form plr_reduce_packets reads (include/plr.h): a source's packet buffer holds two
+// slots of 2 x the share's bytes; the consuming call of epoch e reads slot e & 1, where
+// payload word i (4 bytes) of the share is the 8-byte packet at index i, the word in the
+// low half and the low 32 bits of e in the high half. e is the layout's epoch plus one
+// at the consuming call (plr_layout_epoch(L) + 1).
+__host__ __device__ inline uint64_t* packet_slot(void* buffer, uint64_t share_bytes, uint64_t epoch) {
+  return reinterpret_cast<uint64_t*>(static_cast<char*>(buffer) + (epoch & 1) * 2 * share_bytes);
+}
+
+// Write payload word i of a share into its epoch's slot: one 8-byte atomic store, so the
+// consumer never sees the word without its stamp or the stamp without its word. No fence
+// is needed: each packet announces only itself.
+__device__ __forceinline__ void store_packet(uint64_t* slot, uint64_t i, uint32_t word, uint64_t epoch) {
+  __hip_atomic_store(slot + i, ((uint64_t)(uint32_t)epoch << 32) | word, __ATOMIC_RELAXED,
+                     __HIP_MEMORY_SCOPE_AGENT);
 }
 
 }  // namespace atom

@@ -30,7 +30,6 @@ __global__ void __launch_bounds__(kPacketBlock) k_pack(const PackArgs a) {
   const uint32_t* data = a.data[s];
   uint64_t* pk = a.packets[s];
   const uint64_t base = wave_base();
-  const uint64_t hi = (uint64_t)a.stamp << 32;
   uint32_t x[4];
 #pragma unroll
   for (int k = 0; k < 4; ++k) {
@@ -40,7 +39,7 @@ __global__ void __launch_bounds__(kPacketBlock) k_pack(const PackArgs a) {
 #pragma unroll
   for (int k = 0; k < 4; ++k) {
     const uint64_t i = base + 64 * k;
-    if (i < a.nwords) __hip_atomic_store(pk + i, hi | x[k], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (i < a.nwords) atom::store_packet(pk, i, x[k], a.stamp);
   }
 }
 

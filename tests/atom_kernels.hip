@@ -17,6 +17,13 @@
 //    dispatched in increasing order, so every wait ends (the tests keep the grid small
 //    enough to be resident at once in any case); a bounded wait that gives up records 1
 //    in *err and copies nothing.
+//  - atom_produce: the producer side of a reduce layout's notified call, written into
+//    the producing kernel itself (section 3.2 and Figure 7): workgroup (c, s) produces
+//    chunk c of source s's share (here a copy of its input, standing for any producing
+//    computation) and either only stores it (mode 0), or stores it and releases the
+//    chunk's flag in the layout's workspace (mode 1, signal_flag on flags[s][c]), or
+//    writes it as packets of the consuming call's epoch (mode 2, store_packet), which
+//    plr_reduce_packets reads with no flag at all.
 #include <hip/hip_runtime.h>
 
 #include "plr_atom.h"
@@ -84,6 +91,40 @@ __global__ void __launch_bounds__(256) k_pipeline(const uint8_t* src, uint8_t* m
       return;
     }
     Atom<256>::copy(dst + (size_t)c * chunk, mid + (size_t)c * chunk, chunk);
+  }
+}
+
+struct ProduceArgs {
+  const uint8_t* in[PLR_MAX_WORLD];
+  void* out[PLR_MAX_WORLD];  // mode 0 / 1: the share; mode 2: the packet buffer
+  uint64_t share, chunk;     // bytes of a share, bytes per chunk (one workgroup each)
+  uint64_t* flags;           // mode 1: flags[s][c], nchunks per source
+  uint32_t nchunks;
+  uint64_t epoch;            // the consuming call's epoch
+};
+
+template <int MODE>
+__global__ void __launch_bounds__(256) k_produce(const ProduceArgs a) {
+  constexpr int T = 256;
+  const uint32_t c = blockIdx.x, s = blockIdx.y;
+  const uint64_t off = (uint64_t)c * a.chunk;
+  const uint64_t len = min(a.chunk, a.share - off);
+  if (MODE < 2) {
+    Atom<T>::copy(static_cast<uint8_t*>(a.out[s]) + off, a.in[s] + off, len);
+    if (MODE == 1) plr::atom::signal_flag(a.flags + (uint64_t)s * a.nchunks + c, a.epoch);
+  } else {
+    uint64_t* slot = plr::atom::packet_slot(a.out[s], a.share, a.epoch);
+    const uint32_t* in = reinterpret_cast<const uint32_t*>(a.in[s] + off);
+    const uint64_t w0 = off / 4, nw = len / 4;
+    uint64_t i = threadIdx.x;
+    for (; i + 3 * T < nw; i += 4 * T) {  // four words per lane in flight
+      uint32_t x[4];
+#pragma unroll
+      for (int k = 0; k < 4; ++k) x[k] = __builtin_nontemporal_load(in + i + k * T);
+#pragma unroll
+      for (int k = 0; k < 4; ++k) plr::atom::store_packet(slot, w0 + i + k * T, x[k], a.epoch);
+    }
+    for (; i < nw; i += T) plr::atom::store_packet(slot, w0 + i, __builtin_nontemporal_load(in + i), a.epoch);
   }
 }
 
@@ -163,5 +204,35 @@ extern "C" int atom_pipeline(const void* src, void* mid, void* dst, size_t chunk
                      static_cast<const uint8_t*>(src), static_cast<uint8_t*>(mid), static_cast<uint8_t*>(dst), chunk,
                      (uint32_t)nchunks, (uint32_t)lag, static_cast<uint64_t*>(flags), (uint64_t)signal_epoch,
                      (uint64_t)wait_epoch, (uint64_t)spin_limit, static_cast<uint32_t*>(err));
+  return (int)hipGetLastError();
+}
+
+// mode 0: store only; 1: store, then release flags[s][c] (flags = the workspace's flag
+// array, nchunks = ceil(share / chunk)); 2: packets into out[s] (packet buffers).
+extern "C" int atom_produce(int mode, int world, const void* const* in, void* const* out, size_t share, size_t chunk,
+                            void* flags, unsigned long long epoch, void* stream) {
+  if (mode < 0 || mode > 2 || !in || !out || world < 1 || world > PLR_MAX_WORLD || !share || !chunk ||
+      (share & 15) || (chunk & 15) || (mode == 1 && (!flags || ((uintptr_t)flags & 7))))
+    return (int)hipErrorInvalidValue;
+  const uint64_t nchunks = (share + chunk - 1) / chunk;
+  if (nchunks > 0x7FFFFFFF) return (int)hipErrorInvalidValue;
+  ProduceArgs a{};
+  for (int w = 0; w < world; ++w) {
+    if (!in[w] || !out[w] || !a16(in[w]) || !a16(out[w])) return (int)hipErrorInvalidValue;
+    a.in[w] = static_cast<const uint8_t*>(in[w]);
+    a.out[w] = out[w];
+  }
+  a.share = share;
+  a.chunk = chunk;
+  a.flags = static_cast<uint64_t*>(flags);
+  a.nchunks = (uint32_t)nchunks;
+  a.epoch = epoch;
+  const dim3 g((uint32_t)nchunks, (uint32_t)world), b(256);
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  switch (mode) {
+    case 0: hipLaunchKernelGGL(k_produce<0>, g, b, 0, st, a); break;
+    case 1: hipLaunchKernelGGL(k_produce<1>, g, b, 0, st, a); break;
+    default: hipLaunchKernelGGL(k_produce<2>, g, b, 0, st, a); break;
+  }
   return (int)hipGetLastError();
 }

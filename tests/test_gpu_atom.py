@@ -1,7 +1,8 @@
 """User kernels built on the device-callable Atom (include/plr_atom.h; Purlin README
 "Device-side": a kernel calls the Atom's copy or reduce on its own slice), checked
 against the oracle: per-workgroup copies, ordered reductions with and without a fused
-residual-add epilogue, and stage / notify / consume inside one kernel."""
+residual-add epilogue, stage / notify / consume inside one kernel, and producer kernels
+that announce their own chunks (flags or packets) to the library's consumers."""
 import ctypes
 import os
 
@@ -28,6 +29,7 @@ def atom():
     lib.atom_block_copy.argtypes = [vp, vp, sz, u, i, vp]
     lib.atom_block_reduce.argtypes = [i, i, ctypes.POINTER(vp), vp, vp, sz, u, i, vp]
     lib.atom_pipeline.argtypes = [vp, vp, vp, sz, u, u, vp, ull, ull, ull, vp, vp]
+    lib.atom_produce.argtypes = [i, i, ctypes.POINTER(vp), ctypes.POINTER(vp), sz, sz, vp, ull, vp]
     return lib
 
 
@@ -111,3 +113,89 @@ def test_pipeline_bounded_wait_gives_up(atom):
     assert int(err[0].item()) == 1
     assert int(dst.sum().item()) == 0
     assert (flags.cpu().numpy() == 1).all()
+
+
+def _produce(atom, mode, ins, outs, share, chunk, flags_ptr, epoch, stream=None):
+    W = len(ins)
+    vp = ctypes.c_void_p
+    rc = atom.atom_produce(mode, W, (vp * W)(*[t.data_ptr() for t in ins]), (vp * W)(*[t.data_ptr() for t in outs]),
+                           share, chunk, flags_ptr, epoch, stream if stream is not None else _stream())
+    assert rc == 0
+
+
+def _producer_setup(L, mode, share):
+    """The producer's chunks are the layout's flags; packet buffers are the layout's size."""
+    chunk = L.policy()["chunk_bytes"]
+    assert (share + chunk - 1) // chunk == L.nchunks
+    ws = torch.zeros(max(L.workspace_bytes, 256), dtype=torch.uint8, device="cuda")
+    W = L.world
+    if mode == "flags":
+        outs = [torch.empty(share, dtype=torch.uint8, device="cuda") for _ in range(W)]
+    else:
+        outs = [torch.zeros(L.packet_bytes, dtype=torch.uint8, device="cuda") for _ in range(W)]
+    return chunk, ws, outs
+
+
+@pytest.mark.parametrize("mode", ["flags", "packets"])
+@pytest.mark.parametrize("T", [1, 37, 64])
+def test_producer_kernel_feeds_the_library_consumer(atom, oracle_mod, T, mode):
+    """A user producer that announces its own chunks (section 3.2, Figure 7): plain stores
+    plus signal_flag on the layout's workspace flags, consumed by the notified plr_reduce;
+    or packets written with store_packet, consumed by plr_reduce_packets. Three epochs on
+    one workspace and one set of packet buffers (both slots), each against the oracle."""
+    import reduce_atom_amd as plr
+
+    W, n = 8, T * 7168
+    share = 2 * n
+    L = plr.plr_layout_create("reduce", "bf16", W, share, "packed", "packed")
+    chunk, ws, outs = _producer_setup(L, mode, share)
+    for e in range(3):
+        ins_np = [synth.normal_np(50 + e, 13, w, n, 1.0) for w in range(W)]
+        ins = [to_dev(x) for x in ins_np]
+        epoch = L.epoch + 1
+        _produce(atom, 1 if mode == "flags" else 2, ins, outs, share, chunk, ws.data_ptr() + 256, epoch)
+        dst = torch.full((share,), 0x5A, dtype=torch.uint8, device="cuda")
+        if mode == "flags":
+            plr.plr_reduce(L, outs, dst, ws)
+        else:
+            plr.plr_reduce_packets(L, outs, dst, ws)
+        torch.cuda.synchronize()
+        assert plr.plr_check(L, ws) == plr.PLR_OK
+        assert L.epoch == epoch
+        assert_same("bf16", from_dev(dst), oracle_mod.reduce("bf16", ins_np).view(np.uint8),
+                    f"T={T} {mode} epoch {epoch}")
+
+
+@pytest.mark.parametrize("mode", ["flags", "packets"])
+def test_producer_kernel_beside_a_waiting_consumer(atom, oracle_mod, mode):
+    """The producer kernel queued on one stream behind a sleep, the consumer on another
+    (queued second: a consumer queued first on a hardware queue it shares with the producer
+    could only time out): where the streams overlap the consumer reaches the chunks before
+    they are announced, and it reads every chunk only once it is."""
+    import reduce_atom_amd as plr
+
+    W, T = 8, 8
+    n = T * 7168
+    share = 2 * n
+    L = plr.plr_layout_create("reduce", "bf16", W, share, "packed", "packed", spin_limit=1 << 22)
+    chunk, ws, outs = _producer_setup(L, mode, share)
+    for e in range(3):
+        ins_np = [synth.normal_np(60 + e, 14, w, n, 1.0) for w in range(W)]
+        ins = [to_dev(x) for x in ins_np]
+        torch.cuda.synchronize()
+        epoch = L.epoch + 1
+        dst = torch.full((share,), 0x5A, dtype=torch.uint8, device="cuda")
+        producer, consumer = torch.cuda.Stream(), torch.cuda.Stream()
+        with torch.cuda.stream(producer):
+            if hasattr(torch.cuda, "_sleep"):
+                torch.cuda._sleep(20_000_000)
+            _produce(atom, 1 if mode == "flags" else 2, ins, outs, share, chunk, ws.data_ptr() + 256, epoch)
+        with torch.cuda.stream(consumer):
+            if mode == "flags":
+                plr.plr_reduce(L, outs, dst, ws)
+            else:
+                plr.plr_reduce_packets(L, outs, dst, ws)
+        torch.cuda.synchronize()
+        assert plr.plr_check(L, ws) == plr.PLR_OK
+        assert_same("bf16", from_dev(dst), oracle_mod.reduce("bf16", ins_np).view(np.uint8),
+                    f"{mode} epoch {epoch}")
