@@ -521,3 +521,16 @@ def test_copy_v_noalloc_limits_without_device(plr):
     assert call([1 << 62, 1 << 62]) == plr.PLR_EUNSUPPORTED  # as plr_copy_v, not a wrapped size
     assert fn(0, ptrs, (ctypes.c_int64 * 2)(1, 1), ptrs, 64, 1, 2, 3, None) == plr.PLR_EINVAL
     assert fn(17, ptrs, (ctypes.c_int64 * 2)(1, 1), ptrs, 64, 1, 2, 3, None) == plr.PLR_EUNSUPPORTED
+
+
+def test_layout_queries_on_null(plr):
+    """Every query on a NULL layout returns its documented error value, not a crash."""
+    lib = plr._lib
+    assert lib.plr_layout_policy(None, None, None, None, None, None, None, None, None) == plr.PLR_EINVAL
+    assert lib.plr_layout_plain_shape(None, None, None, None) == plr.PLR_EINVAL
+    assert lib.plr_layout_ntiles(None) == -1 and lib.plr_layout_nchunks(None) == -1
+    assert lib.plr_layout_nsegments(None) == -1
+    assert lib.plr_layout_workspace_bytes(None) == 0 and lib.plr_layout_dst_bytes(None) == 0
+    assert lib.plr_layout_packet_bytes(None) == 0 and lib.plr_layout_epoch(None) == 0
+    L = plr.plr_layout_create("reduce", "bf16", 2, 4096, "packed", "packed")
+    assert lib.plr_layout_plain_shape(L.handle, None, None, None) == plr.PLR_OK  # outputs may be NULL
