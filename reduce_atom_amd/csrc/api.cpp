@@ -275,10 +275,7 @@ extern "C" int plr_copy_v(int world, const void* const* srcs, const int64_t* row
   for (int s = world + 1; s <= PLR_MAX_WORLD; ++s) a.seg_start[s] = a.seg_start[world];
   a.row_bytes = row_bytes;
   a.world = (uint32_t)world;
-#ifndef PLR_CV_XCD
-#define PLR_CV_XCD 0
-#endif
-  a.xcd = PLR_CV_XCD;  // XCD-contiguous order of the row scatter
+  a.xcd = 0;  // the row scatter runs its workgroups in plain order
   const hipStream_t s = static_cast<hipStream_t>(stream);
   hipError_t e = launch_copy_v(a, s);
   if (e != hipSuccess) return hip_fail(e);
