@@ -22,8 +22,9 @@ enum { kXcdOff = 0, kXcdOn = 1 };
 // the copy keeps 1 KiB per stage (16 KiB per workgroup).
 constexpr int lds_reduce_stages(int w) { return w <= 4 ? 4 : 2; }
 constexpr int kCopyStages = 4;
-// Workspace: u64 error word at byte 0, u64 ready word at byte 8, then
-// uint64 flags[W][nchunks] and their check-time mirror uint64 mirror[W][nchunks].
+// Workspace: a header of kWorkspaceHeader bytes (u64 error word at byte 0, u64 ready
+// word at byte 8, u64 late counter at byte 16), then uint64 flags[W][nchunks] and their
+// check-time mirror uint64 mirror[W][nchunks].
 constexpr size_t kWorkspaceHeader = 256;
 constexpr int kLateWord = 2;  // u64 header word: count of chunk waits that found a flag missing
 constexpr uint64_t kDefaultSpinLimit = 1ull << 20;

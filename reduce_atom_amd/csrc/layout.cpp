@@ -25,12 +25,13 @@ size_t elem_bytes(plr_dtype t) { return t == PLR_F32 ? 4 : 2; }
 // that covers every tile, so the dispatcher walks the whole chip through memory front
 // to back, in plain workgroup order; 16-byte non-temporal loads and stores. Tiles of
 // 128 threads: 2 KiB per source for the reduce (one vector per lane per source), one
-// per workgroup; 4 KiB for copies of segments over 2 MiB, one per workgroup, else
-// 2 KiB, two per workgroup once a call has 4096 tiles (8 MiB) or more. Flags cover 256 KiB chunks (16 KiB for decode-size
-// shares). With in-kernel waits a notified workgroup pays one agent-scope acquire per
-// chunk it enters, and those acquires invalidate L2 lines, so such calls give each
-// workgroup a run of 2 (reduce) or 4 (copy) tiles; decode-size shares (at most 2 MiB)
-// keep one tile per workgroup, where latency rules.
+// per workgroup; 4 KiB for copies of over 2 MiB from some source, one per workgroup, else
+// 2 KiB, two per workgroup once a call has 4096 tiles (8 MiB) or more. Flags cover 256 KiB
+// chunks (16 KiB for decode-size shares). With in-kernel waits a notified workgroup pays
+// one agent-scope acquire per chunk it enters, and those acquires invalidate L2 lines, so
+// such calls give each workgroup a run of 2 (reduce) or 4 (copy) tiles; decode-size reduce
+// shares (at most 2 MiB per source) keep one tile per workgroup, where latency rules: 4 KiB
+// tiles of 256 threads, and for notified calls over 512 KiB per source 8 KiB of 512.
 constexpr uint64_t kCus = 256;  // compute units of an MI355X (the composed AllReduce's tiles)
 
 static void default_policy(plr_layout* L) {
