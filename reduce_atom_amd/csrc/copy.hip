@@ -4,9 +4,8 @@
 // layout) and section 3.3 "The Atom" (copy moves bytes between the regions the
 // orchestration hands it). Segments of one layout share one length (variable-length
 // layouts carry one per segment); each is cut into tiles (one workgroup step) grouped
-// into chunks (the notification granule,
-// section 3.2), and a workgroup moves whole tiles with 16-byte loads and stores,
-// U vectors in flight per lane. Bytes only:
+// into chunks (the notification granule, section 3.2), and a workgroup moves whole
+// tiles with 16-byte loads and stores, U vectors in flight per lane. Bytes only:
 // nothing passes through a float register path, so every bit pattern is preserved.
 #include "device_common.h"
 
