@@ -145,8 +145,8 @@ typedef struct {
                                  with W >= 15 takes at most 2: 4 x W vectors would not fit the
                                  registers; plr_layout_policy reports the value used) */
   int stages;                 /* reserved on input (1..4 accepted); plr_layout_policy reports the
-                                 LDS ring depth: 4, 3 or 2 stages for a reduce (W <= 4, <= 8,
-                                 more), 8 for a copy, 0 on the direct path */
+                                 LDS ring depth: 4 stages for a reduce with W <= 4, 2 for more
+                                 sources, 4 for a copy, 0 on the direct path */
   int datapath;               /* PLR_PATH_POLICY, PLR_PATH_DIRECT or PLR_PATH_LDS; the LDS path
                                  needs 256-thread workgroups and tiles of whole 4 KiB slabs */
   uint64_t spin_limit;        /* polls of a chunk flag before PLR_ETIMEOUT; 0 = default (about a second) */
