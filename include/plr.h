@@ -20,7 +20,8 @@
  *   - Pointers named "device" are HIP device pointers; "host" ones are host memory.
  *   - The caller owns every device buffer (sources, destination, counts, offsets,
  *     workspace, scratch). The library never allocates device memory; it owns only
- *     the host-side plr_layout object.
+ *     the host-side plr_layout object (and the fixed per-GPU scratch array in its
+ *     device code that plr_copy_v_noalloc uses).
  *   - `stream` is a hipStream_t passed as void* (NULL = the null stream). Calls that
  *     take a stream are asynchronous on it; plr_check is the only call that waits.
  *   - Alignment: every device address and every byte count must be a multiple of 16
@@ -191,11 +192,12 @@ void plr_layout_destroy(plr_layout* L);
  * below its epoch and had to poll; the library never resets it. */
 size_t plr_layout_workspace_bytes(const plr_layout* L);
 
-/* Bytes the call writes into dst: the share for a reduce, the whole output for a copy. */
+/* Bytes the call writes into dst: the share for a reduce, the whole output for a copy
+ * (0 for a NULL layout, as for plr_layout_workspace_bytes). */
 size_t plr_layout_dst_bytes(const plr_layout* L);
 
 /* Number of chunks (the notification granules), of tiles (workgroup steps) and of
- * copy segments. */
+ * copy segments; -1 for a NULL layout. */
 int plr_layout_nchunks(const plr_layout* L);
 int plr_layout_ntiles(const plr_layout* L);
 int plr_layout_nsegments(const plr_layout* L);
@@ -221,7 +223,8 @@ int plr_layout_policy(const plr_layout* L, size_t* tile_bytes, size_t* chunk_byt
  * PLR_EINVAL for a NULL layout. */
 int plr_layout_plain_shape(const plr_layout* L, size_t* tile_bytes, int* block, int* ntiles);
 
-/* Current epoch E of the layout: the last notified call consumed flags >= E. */
+/* Current epoch E of the layout: the last notified call consumed flags >= E (0 for a
+ * NULL layout). */
 uint64_t plr_layout_epoch(const plr_layout* L);
 
 /* Reduce (section 3.3 "The Atom", SCORE): for every element i of the share,
@@ -277,7 +280,9 @@ int plr_allreduce(plr_layout* L, const void* const* srcs, void* const* dsts, voi
  * volume, so the consumer needs no separate flag round trip; section 3.3: the packets
  * are reduced one output element per thread in source order). On gfx950 a packet is
  * one 8-byte atomic: a 4-byte payload word in the low half and the low 32 bits of the
- * epoch in the high half. Only for reduce layouts.
+ * epoch in the high half. Only for reduce layouts. plr_pack writes them from data already
+ * in memory; a producing kernel can write them itself (include/plr_atom.h: packet_slot,
+ * store_packet), which needs no separate pack or notify step.
  * plr_layout_packet_bytes: bytes of one source's packet buffer (4 x the share: two slots
  * of 2 x the share; epoch e packs into and is reduced from slot e & 1, section 4.3 "Epoch
  * Bookkeeping": the epoch's parity selects one of two staging buffers); the caller
