@@ -36,7 +36,9 @@ import subprocess
 import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-_SO = os.path.join(_HERE, "liboracle.so")
+# PLR_ORACLE_LIB names another build of oracle.c to load instead: the mutation tests plant
+# a mistake in a copy of the source and check that the pins fail against that copy's build
+_SO = os.environ.get("PLR_ORACLE_LIB") or os.path.join(_HERE, "liboracle.so")
 _SRC = os.path.join(_HERE, "oracle.c")
 
 DTYPES = {"bf16": 0, "f16": 1, "f32": 2}
@@ -47,10 +49,11 @@ CFLAGS = ["-O2", "-std=c11", "-ffp-contract=off", "-fno-fast-math", "-fPIC", "-s
           "-Wall", "-Wextra", "-Werror"]
 
 
-def build(out: str = _SO) -> str:
-    """Compile oracle.c with gcc (plain scalar C, no contraction, no fast math)."""
+def build(out: str = _SO, src: str = _SRC) -> str:
+    """Compile oracle.c (or another copy of it) with gcc (plain scalar C, no contraction,
+    no fast math)."""
     tmp = out + ".tmp"
-    subprocess.run(["gcc", *CFLAGS, _SRC, "-o", tmp, "-lm"], check=True)
+    subprocess.run(["gcc", *CFLAGS, src, "-o", tmp, "-lm"], check=True)
     os.replace(tmp, out)
     return out
 
