@@ -14,7 +14,9 @@ import oracle
 ROOT = os.path.abspath(os.path.join(os.path.dirname(__file__), ".."))
 SRC = os.path.join(ROOT, "oracle", "oracle.c")
 
-# (text in oracle.c, replacement): each a mistake an implementation could plausibly make
+# (text in oracle.c, replacement): each a mistake an implementation could plausibly make,
+# chosen so that the mutated oracle still writes only inside its buffers (a mistake must be
+# caught by a pin, not by a crash of the child process)
 MUTATIONS = {
     "ties_away_from_even": ("else r = (p & 1) ? p + 1 : p;", "else r = (p & 1) ? p : p + 1;"),
     "accumulator_starts_at_zero": ("float a = widen(dtype, srcs[0], src_off[0] + i);\n    for (int w = 1;",
@@ -25,12 +27,13 @@ MUTATIONS = {
     "fp16_exponent_bias": ("ldexp((double)(1024 + f), e - 15 - 10)", "ldexp((double)(1024 + f), e - 14 - 10)"),
     "bf16_subnormal_scale": ("ldexp((double)f, -126 - 7)", "ldexp((double)f, -127 - 7)"),
     "overflow_saturates": ("F->past_max : F->value", "1e300 : F->value"),
-    "offsets_source_major": ("offsets[d * W + s] = off;", "offsets[s * W + d] = off;"),
+    "blocks_packed_source_major": ("for (int d = 0; d < W; ++d) {\n    int64_t off = base;\n    for (int s = 0; s < W; ++s) {",
+                                   "for (int s = 0; s < W; ++s) {\n    int64_t off = base;\n    for (int d = 0; d < W; ++d) {"),
     "rows_reversed_within_a_block": ("for (int64_t i = i0; i < i1; ++i) {\n    int32_t d = dest[s][i];",
                                      "for (int64_t i = i1 - 1; i >= i0; --i) {\n    int32_t d = dest[s][i];"),
     "denormals_flushed": ("_mm_setcsr(old & ~(0x8000u | 0x0040u | 0x6000u));", "_mm_setcsr((old | 0x8040u) & ~0x6000u);"),
-    "gap_between_thread_ranges": ("return (int64_t)((__int128)n * k / parts); }",
-                                  "return (int64_t)((__int128)n * k / parts) + (k > 0 && k < parts); }"),
+    "last_thread_stops_short": ("return (int64_t)((__int128)n * k / parts); }",
+                                "return k == parts ? n - (n > 0) : (int64_t)((__int128)n * k / parts); }"),
     "thread_rank_prefix_short": ("  for (int64_t i = 0; i < i0; ++i) seen[dest[s][i]] += 1;",
                                  "  for (int64_t i = 1; i < i0; ++i) seen[dest[s][i]] += 1;"),
 }
