@@ -162,6 +162,13 @@ typedef struct {
    * another (host work only). Only the two variable pairs above accept it, on the
    * direct datapath; a copy's offsets may still be overridden. */
   const size_t* part_bytes;
+  /* Resident workgroups per compute unit for the layout's direct-path reduce, copy and fused
+   * AllReduce launches, capped by reserving workgroup memory (LDS: 160 KiB per compute unit)
+   * at each launch, for callers that share the GPU with other work: 0 = policy (no cap:
+   * capping measured no faster on this datapath), -1 = no cap, 3..16 = at most that many.
+   * The LDS-staged and composed paths are never capped. plr_layout_occupancy reports the
+   * cap used. */
+  int wgs_per_cu;
 } plr_layout_desc;
 
 typedef struct plr_layout plr_layout; /* opaque, host only */
@@ -222,6 +229,11 @@ int plr_layout_policy(const plr_layout* L, size_t* tile_bytes, size_t* chunk_byt
  * The results are bitwise the same either way. Any output pointer may be NULL;
  * PLR_EINVAL for a NULL layout. */
 int plr_layout_plain_shape(const plr_layout* L, size_t* tile_bytes, int* block, int* ntiles);
+
+/* The resident-workgroup cap of the layout's direct-path launches (0 = none) and the
+ * workgroup memory (LDS) each of those launches reserves for it, in bytes. Any output
+ * pointer may be NULL; PLR_EINVAL for a NULL layout. */
+int plr_layout_occupancy(const plr_layout* L, int* wgs_per_cu, size_t* lds_bytes);
 
 /* Current epoch E of the layout: the last notified call consumed flags >= E (0 for a
  * NULL layout). */

@@ -61,6 +61,7 @@ class plr_layout_desc(_c.Structure):
         ("notify_mode", _i),
         ("xcd_order", _i),
         ("part_bytes", _c.POINTER(_sz)),
+        ("wgs_per_cu", _i),
     ]
 
 
@@ -83,6 +84,8 @@ _lib.plr_layout_policy.argtypes = [_vp, _c.POINTER(_sz), _c.POINTER(_sz)] + [_c.
 _lib.plr_layout_policy.restype = _i
 _lib.plr_layout_plain_shape.argtypes = [_vp, _c.POINTER(_sz), _c.POINTER(_i), _c.POINTER(_i)]
 _lib.plr_layout_plain_shape.restype = _i
+_lib.plr_layout_occupancy.argtypes = [_vp, _c.POINTER(_i), _c.POINTER(_sz)]
+_lib.plr_layout_occupancy.restype = _i
 _lib.plr_reduce.argtypes = [_vp, _c.POINTER(_vp), _vp, _vp, _vp]
 _lib.plr_reduce.restype = _i
 _lib.plr_copy.argtypes = [_vp, _c.POINTER(_vp), _vp, _vp, _vp]
@@ -121,7 +124,7 @@ _lib.plr_version.restype = _c.c_char_p
 EXPORTS = [
     "plr_layout_create", "plr_layout_destroy", "plr_layout_workspace_bytes", "plr_layout_dst_bytes",
     "plr_layout_nchunks", "plr_layout_ntiles", "plr_layout_nsegments", "plr_layout_segment", "plr_layout_policy",
-    "plr_layout_plain_shape",
+    "plr_layout_plain_shape", "plr_layout_occupancy",
     "plr_layout_epoch", "plr_reduce", "plr_copy", "plr_allreduce", "plr_copy_v", "plr_copy_v_scratch_bytes",
     "plr_copy_v_noalloc", "plr_copy_v_noalloc_max_scratch_bytes",
     "plr_layout_packet_bytes", "plr_pack", "plr_reduce_packets",
@@ -249,17 +252,21 @@ class Layout:
         pt, pb, pn = _sz(), _i(), _i()
         _ok(_lib.plr_layout_plain_shape(self._h, _c.byref(pt), _c.byref(pb), _c.byref(pn)),
             "plr_layout_plain_shape")
+        oc, ol = _i(), _sz()
+        _ok(_lib.plr_layout_occupancy(self._h, _c.byref(oc), _c.byref(ol)), "plr_layout_occupancy")
         return dict(tile_bytes=tb.value, chunk_bytes=cb.value, workgroups=wg.value, block=bl.value,
                     unroll=un.value, stages=st.value, datapath=dp.value, notify_mode=nm.value,
-                    plain_tile_bytes=pt.value, plain_block=pb.value, plain_ntiles=pn.value)
+                    plain_tile_bytes=pt.value, plain_block=pb.value, plain_ntiles=pn.value,
+                    wgs_per_cu=oc.value, lds_reserve=ol.value)
 
 
 def plr_layout_create(op, dtype, world, bytes_per_src, in_kind, out_kind, rank=0,
                       in_offsets=None, out_offsets=None, mode=PLR_MODE_DETERMINISTIC,
                       tile_bytes=0, chunk_bytes=0, workgroups=0, block=0, unroll=0, stages=0, datapath=0,
-                      spin_limit=0, notify_mode=0, xcd_order=0, part_bytes=None) -> Layout:
+                      spin_limit=0, notify_mode=0, xcd_order=0, part_bytes=None, wgs_per_cu=0) -> Layout:
     """Compile a layout. op/dtype/kinds accept the C enum values or their names.
-    part_bytes: W partition sizes of a variable-length layout (AllGatherV, ReduceScatterV)."""
+    part_bytes: W partition sizes of a variable-length layout (AllGatherV, ReduceScatterV).
+    wgs_per_cu: resident workgroups per compute unit (0 policy, -1 no cap, 3..16)."""
     d = plr_layout_desc()
     op_c, in_c, out_c = OP_CODES.get(op, op), KIND_CODES.get(in_kind, in_kind), KIND_CODES.get(out_kind, out_kind)
     # the C side reads exactly this many entries of every list it is given
@@ -289,6 +296,7 @@ def plr_layout_create(op, dtype, world, bytes_per_src, in_kind, out_kind, rank=0
     d.block, d.unroll, d.stages, d.datapath, d.spin_limit = block, unroll, stages, datapath, spin_limit
     d.notify_mode = notify_mode
     d.xcd_order = xcd_order
+    d.wgs_per_cu = wgs_per_cu
     if part_bytes is not None:
         a = (_sz * len(part_bytes))(*part_bytes)
         keep.append(a)

@@ -97,9 +97,9 @@ template <int DT, int W>
 static hipError_t launch_ar_w(const AllReduceArgs& a, const Launch& l, hipStream_t s) {
   dim3 g(l.grid), bl(l.block);
   if (l.datapath == PLR_PATH_COMPOSED)
-    launch_dp(k_allreduce_composed<DT, W>, g, bl, s, true, true, a);
+    launch_dp(k_allreduce_composed<DT, W>, g, bl, 0, s, true, true, a);
   else
-    launch_dp(k_allreduce_fused<DT, W>, g, bl, s, true, true, a);
+    launch_dp(k_allreduce_fused<DT, W>, g, bl, l.lds_bytes, s, true, true, a);
   return hipGetLastError();
 }
 

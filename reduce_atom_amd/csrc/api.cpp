@@ -44,7 +44,7 @@ Launch launch_of(const plr_layout* L, bool notified) {
   const uint32_t grid = (uint32_t)std::max<uint64_t>(1, (tiles_of(L, notified) + run - 1) / run);
   const int xcd = L->xcd_order == kXcdOn;
   const uint32_t block = (uint32_t)(notified ? L->block : L->plain_block);
-  return Launch{grid, block, L->unroll, L->stages, L->datapath, run, xcd};
+  return Launch{grid, block, L->unroll, L->stages, L->datapath, run, xcd, L->lds_reserve};
 }
 
 // Common checks of plr_reduce / plr_copy. Fills the notification block.
@@ -315,6 +315,7 @@ extern "C" int plr_allreduce(plr_layout* L, const void* const* srcs, void* const
   Launch l{};
   l.block = (uint32_t)L->block;
   l.datapath = L->datapath;
+  l.lds_bytes = composed ? 0 : L->lds_reserve;
   if (composed) {
     a.nt.err = static_cast<uint64_t*>(workspace);
     a.nt.flags = reinterpret_cast<const uint64_t*>(static_cast<char*>(workspace) + kWorkspaceHeader);

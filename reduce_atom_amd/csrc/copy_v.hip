@@ -344,11 +344,11 @@ static void launch_scatter(const CopyVArgs& a, int cpl, hipStream_t s) {
                                       cpl > 0);
   const dim3 b(Shape::kThreads);
   if (cpl == 1)
-    launch_dp(k_copy_v_scatter<1, Shape>, dim3(gx, a.world), b, s, false, true, a);
+    launch_dp(k_copy_v_scatter<1, Shape>, dim3(gx, a.world), b, 0, s, false, true, a);
   else if (cpl == 4)
-    launch_dp(k_copy_v_scatter<4, Shape>, dim3(gx, a.world), b, s, false, true, a);
+    launch_dp(k_copy_v_scatter<4, Shape>, dim3(gx, a.world), b, 0, s, false, true, a);
   else
-    launch_dp(k_copy_v_scatter<0, Shape>, dim3(gx, a.world), b, s, false, true, a);
+    launch_dp(k_copy_v_scatter<0, Shape>, dim3(gx, a.world), b, 0, s, false, true, a);
 }
 
 hipError_t launch_copy_v(const CopyVArgs& args, hipStream_t s) {
@@ -361,7 +361,7 @@ hipError_t launch_copy_v(const CopyVArgs& args, hipStream_t s) {
   const int cpl = n <= 64 ? 1 : (n <= kSmallCounts ? 4 : 0);
   a.small = cpl > 0;
   if (a.small) a.xcd = 0;  // the extra column must stay the last workgroup of each row
-  launch_dp(k_copy_v_rank, dim3(segs ? segs : 1), dim3(kRankThreads), s, true, false, a);
+  launch_dp(k_copy_v_rank, dim3(segs ? segs : 1), dim3(kRankThreads), 0, s, true, false, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   if (small_rows)

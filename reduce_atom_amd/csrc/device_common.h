@@ -20,13 +20,16 @@ using atom::combine;
 using atom::Elems;
 
 // Launch of a datapath kernel: `first` / `last` say whether it opens / closes the
-// call's datapath, which decides which of the thread's timing events it carries.
+// call's datapath, which decides which of the thread's timing events it carries. `lds`
+// bytes of workgroup memory are reserved per workgroup beyond the kernel's own; no kernel
+// touches them: they only bound how many workgroups a compute unit holds at once.
 template <typename K, typename... A>
-inline void launch_dp(K kernel, dim3 grid, dim3 block, hipStream_t s, bool first, bool last, A... args) {
+inline void launch_dp(K kernel, dim3 grid, dim3 block, uint32_t lds, hipStream_t s, bool first, bool last,
+                      A... args) {
   const Timing& t = timing();
   hipEvent_t a = first ? t.start : (last ? t.last_start : nullptr);
   hipEvent_t b = last ? t.stop : (first ? t.first_stop : nullptr);
-  hipExtLaunchKernelGGL(kernel, grid, block, 0, s, a, b, 0, args...);
+  hipExtLaunchKernelGGL(kernel, grid, block, lds, s, a, b, 0, args...);
 }
 
 // Constant address space: loads through such a pointer that are the same for every

@@ -38,6 +38,7 @@ struct Launch {
   int datapath;  // PLR_PATH_DIRECT or PLR_PATH_LDS
   uint32_t run;  // consecutive tiles per workgroup
   int xcd;       // XCD-aware workgroup order
+  uint32_t lds_bytes;  // LDS reserved per workgroup to cap resident workgroups per CU (0: none)
 };
 
 // Notification state of one consuming launch (section 3.2, SNAC "notify").

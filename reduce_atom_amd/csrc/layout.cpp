@@ -33,6 +33,7 @@ size_t elem_bytes(plr_dtype t) { return t == PLR_F32 ? 4 : 2; }
 // shares (at most 2 MiB per source) keep one tile per workgroup, where latency rules: 4 KiB
 // tiles of 256 threads, and for notified calls over 512 KiB per source 8 KiB of 512.
 constexpr uint64_t kCus = 256;  // compute units of an MI355X (the composed AllReduce's tiles)
+constexpr uint32_t kLdsPerCu = 160u << 10;  // LDS bytes per compute unit of gfx950
 
 static void default_policy(plr_layout* L) {
   L->stages = 0;  // no ring on the direct path
@@ -284,6 +285,20 @@ extern "C" int plr_layout_create(const plr_layout_desc* d, plr_layout** out) {
     }
   }
   if (L->var_segs && L->datapath == PLR_PATH_LDS) return fail(PLR_EUNSUPPORTED);
+  // resident workgroups per CU, capped through an LDS reservation at launch when the
+  // caller asks; the policy leaves every kernel uncapped. Kernel trace of the 8 x 117 MB
+  // bf16 reduce, three interleaved rounds on one machine: uncapped (10 workgroups per CU,
+  // bounded by its registers) 162.2-163.3 us, 6 or 8 per CU the same, 5 or 4 per CU
+  // 173.7-177.1 us and 3 per CU 205-212 us, notified or not; the 512 MiB copy gained
+  // nothing that held either (163.4-165.0 us uncapped, 178 us at 5 or fewer)
+  if (d->wgs_per_cu < -1 || (d->wgs_per_cu > 0 && (d->wgs_per_cu < 3 || d->wgs_per_cu > 16)))
+    return fail(PLR_EINVAL);
+  L->wgs_per_cu = d->wgs_per_cu > 0 ? d->wgs_per_cu : 0;
+  if (L->datapath != PLR_PATH_DIRECT) L->wgs_per_cu = 0;  // LDS-staged and composed: never capped
+  // the reservation leaves 512 bytes of each share for the kernel's own workgroup memory
+  // (the direct reduce and copy use 256 bytes, for the workgroup-wide vote of their chunk
+  // waits), so that exactly wgs_per_cu workgroups fit
+  L->lds_reserve = L->wgs_per_cu ? ((kLdsPerCu / (uint32_t)L->wgs_per_cu) - 512u) & ~511u : 0;
   if (L->datapath == PLR_PATH_LDS) {
     // the staged pipeline runs 256-thread workgroups over 4 KiB slabs per source. Measured
     // on the 8 x 117 MB reduce and the 8 x 64 MiB AllGather (ring depth x slabs per
@@ -465,6 +480,13 @@ extern "C" int plr_layout_policy(const plr_layout* L, size_t* tile_bytes, size_t
   if (stages) *stages = L->stages;
   if (datapath) *datapath = L->datapath;
   if (notify_mode) *notify_mode = L->notify_mode;
+  return PLR_OK;
+}
+
+extern "C" int plr_layout_occupancy(const plr_layout* L, int* wgs_per_cu, size_t* lds_bytes) {
+  if (!L) return PLR_EINVAL;
+  if (wgs_per_cu) *wgs_per_cu = L->wgs_per_cu;
+  if (lds_bytes) *lds_bytes = L->lds_reserve;
   return PLR_OK;
 }
 

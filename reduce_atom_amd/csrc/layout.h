@@ -64,6 +64,8 @@ struct plr_layout {
   int unroll;
   int stages;
   int datapath;
+  int wgs_per_cu;        // resident-workgroup cap of the direct-path launches, 0 = none
+  uint32_t lds_reserve;  // LDS bytes each such launch reserves for the cap
   uint64_t spin_limit;
 
   uint64_t epoch;  // section 4.3 "Epoch Bookkeeping"

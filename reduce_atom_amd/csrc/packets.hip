@@ -106,7 +106,7 @@ static hipError_t launch_rp_dt(const PacketReduceArgs& a, hipStream_t s) {
   switch (a.world) {
 #define PLR_W(w)                                                         \
   case w:                                                                \
-    launch_dp(k_reduce_packets<DT, w>, g, b, s, true, true, a);        \
+    launch_dp(k_reduce_packets<DT, w>, g, b, 0, s, true, true, a);        \
     return hipGetLastError();
     PLR_W(1) PLR_W(2) PLR_W(3) PLR_W(4) PLR_W(5) PLR_W(6) PLR_W(7) PLR_W(8)
     PLR_W(9) PLR_W(10) PLR_W(11) PLR_W(12) PLR_W(13) PLR_W(14) PLR_W(15) PLR_W(16)

@@ -126,13 +126,13 @@ static hipError_t launch_w(const ReduceArgs& a, const Launch& l, hipStream_t s) 
   dim3 g(l.grid), b(l.block);
   if (l.datapath == PLR_PATH_LDS) {
     if (l.block != 256) return hipErrorInvalidValue;
-    launch_dp(k_reduce_lds<DT, W>, g, b, s, true, true, a);
+    launch_dp(k_reduce_lds<DT, W>, g, b, 0, s, true, true, a);
     return hipGetLastError();
   }
   switch (l.unroll) {
-    case 1: launch_dp(k_reduce_direct<DT, W, 1>, g, b, s, true, true, a); break;
-    case 2: launch_dp(k_reduce_direct<DT, W, 2>, g, b, s, true, true, a); break;
-    case 4: launch_dp(k_reduce_direct<DT, W, 4>, g, b, s, true, true, a); break;
+    case 1: launch_dp(k_reduce_direct<DT, W, 1>, g, b, l.lds_bytes, s, true, true, a); break;
+    case 2: launch_dp(k_reduce_direct<DT, W, 2>, g, b, l.lds_bytes, s, true, true, a); break;
+    case 4: launch_dp(k_reduce_direct<DT, W, 4>, g, b, l.lds_bytes, s, true, true, a); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();

@@ -94,12 +94,13 @@ int main(int argc, char** argv) {
       d.unroll = (int)pick((const int[]){0, 1, 2, 4});
       d.notify_mode = (int)below(3);
       d.xcd_order = (int)below(3);
+      d.wgs_per_cu = (int)pick((const int[]){0, 0, -1, 3, 5, 16});
       if (kind <= 4 && below(3) == 0) d.datapath = 2;  // the LDS path
     }
     if (below(5) == 0) d.in_offsets = in_off.data();
     if (below(5) == 0) d.out_offsets = out_off.data();
     for (int m = (int)below(3) - 1; m > 0 || (m == 0 && below(2)); --m) {  // mutations
-      switch (below(18)) {
+      switch (below(19)) {
         case 0: { int v = (int)pick((const int[]){3, -1, 7}); memcpy(&d.op, &v, 4); break; }
         case 1: { int v = (int)pick((const int[]){3, -1}); memcpy(&d.dtype, &v, 4); break; }
         case 2: d.world = (int)pick((const int[]){0, 17, -3}); break;
@@ -117,6 +118,7 @@ int main(int argc, char** argv) {
         case 14: d.datapath = (int)pick((const int[]){4, 2, 3}); d.notify_mode = 3; break;
         case 15: parts[below(W)] += pick((const size_t[]){8, 16}); d.part_bytes = parts.data(); break;
         case 16: in_off[below(W)] = ~(size_t)15 - 16 * below(4); d.in_offsets = in_off.data(); break;
+        case 17: d.wgs_per_cu = (int)pick((const int[]){1, 2, 17, -2}); break;
         default: out_off[below(W)] = ~(size_t)15 - 16 * below(4); d.out_offsets = out_off.data(); break;
       }
     }
@@ -136,6 +138,14 @@ int main(int argc, char** argv) {
           "nseg %d ntiles %d nchunks %d", nseg, ntiles, nchunks);
     CHECK(plr_layout_workspace_bytes(L) >= 256, "workspace %zu", plr_layout_workspace_bytes(L));
     CHECK(plr_layout_epoch(L) == 0, "epoch");
+    {  // a capped layout reserves exactly what lets that many workgroups share 160 KiB of LDS
+      int cap = -1;
+      size_t lds = 1;
+      CHECK(plr_layout_occupancy(L, &cap, &lds) == PLR_OK, "occupancy");
+      CHECK((cap == 0) == (lds == 0) && cap >= 0 && cap <= 16, "cap %d lds %zu", cap, lds);
+      const size_t share = (lds + 256 + 511) / 512 * 512;  // with 256 bytes of the kernel's own
+      CHECK(cap == 0 || (int)(163840 / share) == cap, "cap %d lds %zu", cap, lds);
+    }
     std::vector<std::pair<size_t, size_t>> outs;
     for (int k = 0; k < nseg; ++k) {
       int src = -1;

@@ -50,6 +50,8 @@ def _draw(rng):
         pol["block"] = 256
         pol["tile_bytes"] = 4096 * int(rng.integers(1, 4))
         pol.pop("chunk_bytes", None)
+    if rng.random() < 0.25:  # resident workgroups per CU (LDS reservation at launch)
+        pol["wgs_per_cu"] = int(rng.choice([-1, 3, 4, 5, 8, 16]))
     notify = ["none", "chunks", "check"][rng.integers(3)]
     if notify != "none":
         pol["notify_mode"] = 1 if notify == "chunks" else 2

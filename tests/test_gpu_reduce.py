@@ -195,6 +195,37 @@ def test_config3_prefill_share_full(plr, oracle_mod, notified):
     assert_same("bf16", got, ref)
 
 
+@pytest.mark.parametrize("cap", [-1, 3, 5, 16])
+def test_resident_workgroup_caps(plr, oracle_mod, cap):
+    """The launch's LDS reservation only bounds how many workgroups share a compute unit:
+    a reduce of 8 x 6 MiB (ragged: not a whole number of tiles), notified and not, a copy
+    and a fused AllReduce under each cap give the oracle's bits."""
+    W, n = 8, 3 * (1 << 20) + 2 * 72
+    srcs_np = [synth.normal_np(7, 30, w, n, 1.0) for w in range(W)]
+    ref = oracle_mod.reduce("bf16", srcs_np, threads=oracle_mod.default_threads())
+    for ws in (False, True):
+        L = plr.plr_layout_create("reduce", "bf16", W, 2 * n, "packed", "packed", wgs_per_cu=cap)
+        assert L.policy()["wgs_per_cu"] == (0 if cap == -1 else cap)
+        assert_same("bf16", from_dev(_run(plr, L, srcs_np, 2 * n, workspace=ws)).view(np.uint16), ref,
+                    f"reduce cap {cap} ws {ws}")
+    B = 4 << 20
+    csrcs = [synth.bits_np(7, 31, s, B) for s in range(W)]
+    C = plr.plr_layout_create("copy", "bf16", W, B, "scattered", "transposed", wgs_per_cu=cap)
+    cdst = torch.empty(C.dst_bytes, dtype=torch.uint8, device="cuda")
+    plr.plr_copy(C, [to_dev(x) for x in csrcs], cdst)
+    torch.cuda.synchronize()
+    assert np.array_equal(from_dev(cdst), oracle_mod.copy_layout("scattered", "transposed", csrcs)), f"copy {cap}"
+    m = W * 16384
+    asrcs_np = [synth.normal_np(7, 32, w, m, 1.0) for w in range(W)]
+    A = plr.plr_layout_create("allreduce", "bf16", W, 2 * m, "scattered", "scattered", wgs_per_cu=cap)
+    adst = [torch.empty(m, dtype=torch.bfloat16, device="cuda") for _ in range(W)]
+    plr.plr_allreduce(A, [to_dev(x) for x in asrcs_np], adst)
+    torch.cuda.synchronize()
+    aref = oracle_mod.reduce("bf16", asrcs_np)
+    for w in range(W):
+        assert_same("bf16", adst[w].view(torch.int16).cpu().numpy().view(np.uint16), aref, f"allreduce {cap} out {w}")
+
+
 def test_repeatable_bits(plr):
     W, n = 8, (1 << 20) + 8
     srcs = [synth.normal_t(0, 4, w, n, 1.0, device="cuda") for w in range(W)]

@@ -108,7 +108,8 @@ def test_policy_overrides(plr):
                               workgroups=33, block=128, unroll=4, datapath=plr.PLR_PATH_DIRECT)
     assert L.policy() == dict(tile_bytes=2048, chunk_bytes=4096, workgroups=33, block=128, unroll=4,
                               stages=0, datapath=plr.PLR_PATH_DIRECT, notify_mode=plr.PLR_NOTIFY_CHECK,
-                              plain_tile_bytes=2048, plain_block=128, plain_ntiles=8192)
+                              plain_tile_bytes=2048, plain_block=128, plain_ntiles=8192,
+                              wgs_per_cu=0, lds_reserve=0)
     # the LDS path reports its ring depth: W KiB per stage per wave for a reduce
     for w, depth in ((1, 4), (4, 4), (5, 2), (8, 2), (9, 2), (16, 2)):
         R = plr.plr_layout_create("reduce", "bf16", w, 1 << 20, "packed", "packed", datapath=plr.PLR_PATH_LDS)
@@ -534,3 +535,31 @@ def test_layout_queries_on_null(plr):
     assert lib.plr_layout_packet_bytes(None) == 0 and lib.plr_layout_epoch(None) == 0
     L = plr.plr_layout_create("reduce", "bf16", 2, 4096, "packed", "packed")
     assert lib.plr_layout_plain_shape(L.handle, None, None, None) == plr.PLR_OK  # outputs may be NULL
+
+
+def test_resident_workgroup_cap(plr):
+    """Resident workgroups per CU are capped through an LDS reservation (leaving 512 bytes
+    for the kernel's own) only when a caller asks; the policy caps nothing; the LDS-staged
+    and composed paths never are capped; bad values are refused."""
+    def occ(*a, **k):
+        p = plr.plr_layout_create(*a, **k).policy()
+        return p["wgs_per_cu"], p["lds_reserve"]
+    big = ("reduce", "bf16", 8, 8192 * 7168 * 2, "packed", "packed")
+    assert occ(*big) == (0, 0)
+    assert occ(*big, wgs_per_cu=-1) == (0, 0)
+    assert occ(*big, wgs_per_cu=5) == (5, 32256)
+    for k in (3, 4, 6, 8, 16):
+        cap, lds = occ(*big, wgs_per_cu=k)
+        assert cap == k and 163840 // ((lds + 256 + 511) // 512 * 512) == k
+    assert occ("reduce", "bf16", 8, 2 << 20, "packed", "packed") == (0, 0)  # decode-size share
+    assert occ("reduce", "bf16", 8, 4 << 20, "scattered", "packed", rank=1) == (0, 0)  # 512 KiB per source
+    assert occ("copy", "bf16", 8, 64 << 20, "packed", "packed") == (0, 0)
+    assert occ("copy", "bf16", 8, 64 << 20, "packed", "packed", wgs_per_cu=8)[0] == 8
+    assert occ("allreduce", "bf16", 8, 1 << 24, "scattered", "scattered") == (0, 0)
+    assert occ("allreduce", "bf16", 8, 1 << 24, "scattered", "scattered", wgs_per_cu=4)[0] == 4
+    assert occ(*big, datapath=plr.PLR_PATH_LDS) == (0, 0)
+    assert occ(*big, datapath=plr.PLR_PATH_LDS, wgs_per_cu=4) == (0, 0)
+    assert occ("allreduce", "bf16", 8, 1 << 24, "scattered", "scattered", datapath=plr.PLR_PATH_COMPOSED,
+               wgs_per_cu=4) == (0, 0)
+    for bad in (1, 2, 17, -2):
+        assert _code(plr.plr_layout_create, *big, wgs_per_cu=bad) == plr.PLR_EINVAL
