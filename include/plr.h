@@ -164,8 +164,9 @@ typedef struct {
   const size_t* part_bytes;
   /* Resident workgroups per compute unit for the layout's direct-path reduce, copy and fused
    * AllReduce launches, capped by reserving workgroup memory (LDS: 160 KiB per compute unit)
-   * at each launch, for callers that share the GPU with other work: 0 = policy (no cap:
-   * capping measured no faster on this datapath), -1 = no cap, 3..16 = at most that many.
+   * at each launch: 0 = policy (3 for the fused AllReduce of more than 2 MiB per source,
+   * whose W output streams per tile are written faster with fewer requests queued; no cap
+   * elsewhere), -1 = no cap, 1..16 = at most that many (one workgroup may hold all 160 KiB).
    * The LDS-staged and composed paths are never capped. plr_layout_occupancy reports the
    * cap used. */
   int wgs_per_cu;

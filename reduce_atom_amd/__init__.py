@@ -266,7 +266,7 @@ def plr_layout_create(op, dtype, world, bytes_per_src, in_kind, out_kind, rank=0
                       spin_limit=0, notify_mode=0, xcd_order=0, part_bytes=None, wgs_per_cu=0) -> Layout:
     """Compile a layout. op/dtype/kinds accept the C enum values or their names.
     part_bytes: W partition sizes of a variable-length layout (AllGatherV, ReduceScatterV).
-    wgs_per_cu: resident workgroups per compute unit (0 policy, -1 no cap, 3..16)."""
+    wgs_per_cu: resident workgroups per compute unit (0 policy, -1 no cap, 1..16)."""
     d = plr_layout_desc()
     op_c, in_c, out_c = OP_CODES.get(op, op), KIND_CODES.get(in_kind, in_kind), KIND_CODES.get(out_kind, out_kind)
     # the C side reads exactly this many entries of every list it is given

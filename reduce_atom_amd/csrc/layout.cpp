@@ -285,15 +285,24 @@ extern "C" int plr_layout_create(const plr_layout_desc* d, plr_layout** out) {
     }
   }
   if (L->var_segs && L->datapath == PLR_PATH_LDS) return fail(PLR_EUNSUPPORTED);
-  // resident workgroups per CU, capped through an LDS reservation at launch when the
-  // caller asks; the policy leaves every kernel uncapped. Kernel trace of the 8 x 117 MB
-  // bf16 reduce, three interleaved rounds on one machine: uncapped (10 workgroups per CU,
-  // bounded by its registers) 162.2-163.3 us, 6 or 8 per CU the same, 5 or 4 per CU
-  // 173.7-177.1 us and 3 per CU 205-212 us, notified or not; the 512 MiB copy gained
-  // nothing that held either (163.4-165.0 us uncapped, 178 us at 5 or fewer)
-  if (d->wgs_per_cu < -1 || (d->wgs_per_cu > 0 && (d->wgs_per_cu < 3 || d->wgs_per_cu > 16)))
+  // resident workgroups per CU, capped through an LDS reservation at launch. The fused
+  // AllReduce of more than 2 MiB per source keeps 3: it writes W output streams per tile,
+  // and with fewer requests queued its DRAM write queues fill less often. Kernel trace, 8
+  // sources, three interleaved rounds on one machine: [8192, 7168] bf16 296-300 us at 2 or
+  // 3 per CU against 322-325 us uncapped (402-404 us at 1); 64 MiB per source 176-180
+  // against 188-190 us; 16 MiB 48.2-48.4 against 49.5-50.8 us; 1 MiB the same either way.
+  // Every other kernel runs uncapped: the 8 x 117 MB reduce took 162.2-163.3 us uncapped,
+  // the same at 6 or 8 per CU and 174-177 us at 4 or 5; the 512 MiB copy gained nothing that
+  // held; the AllToAllV row scatter, which lives on many short workgroups, 150 us uncapped
+  // against 155-440 us at 11 down to 2 per CU.
+  if (d->wgs_per_cu < -1 || d->wgs_per_cu > 16)
     return fail(PLR_EINVAL);
-  L->wgs_per_cu = d->wgs_per_cu > 0 ? d->wgs_per_cu : 0;
+  if (d->wgs_per_cu > 0)
+    L->wgs_per_cu = d->wgs_per_cu;
+  else if (d->wgs_per_cu == 0)
+    L->wgs_per_cu = op == PLR_OP_ALLREDUCE && L->src_bytes > (2u << 20) ? 3 : 0;
+  else
+    L->wgs_per_cu = 0;
   if (L->datapath != PLR_PATH_DIRECT) L->wgs_per_cu = 0;  // LDS-staged and composed: never capped
   // the reservation leaves 512 bytes of each share for the kernel's own workgroup memory
   // (the direct reduce and copy use 256 bytes, for the workgroup-wide vote of their chunk

@@ -94,7 +94,7 @@ int main(int argc, char** argv) {
       d.unroll = (int)pick((const int[]){0, 1, 2, 4});
       d.notify_mode = (int)below(3);
       d.xcd_order = (int)below(3);
-      d.wgs_per_cu = (int)pick((const int[]){0, 0, -1, 3, 5, 16});
+      d.wgs_per_cu = (int)pick((const int[]){0, 0, -1, 1, 2, 3, 5, 16});
       if (kind <= 4 && below(3) == 0) d.datapath = 2;  // the LDS path
     }
     if (below(5) == 0) d.in_offsets = in_off.data();
@@ -118,7 +118,7 @@ int main(int argc, char** argv) {
         case 14: d.datapath = (int)pick((const int[]){4, 2, 3}); d.notify_mode = 3; break;
         case 15: parts[below(W)] += pick((const size_t[]){8, 16}); d.part_bytes = parts.data(); break;
         case 16: in_off[below(W)] = ~(size_t)15 - 16 * below(4); d.in_offsets = in_off.data(); break;
-        case 17: d.wgs_per_cu = (int)pick((const int[]){1, 2, 17, -2}); break;
+        case 17: d.wgs_per_cu = (int)pick((const int[]){17, -2, 1000}); break;
         default: out_off[below(W)] = ~(size_t)15 - 16 * below(4); d.out_offsets = out_off.data(); break;
       }
     }
