@@ -235,7 +235,8 @@ BOUND_PASSES = {
 }
 BOUND_OPS = {"reduce": "plr::k_reduce_direct", "allgather": "plr::k_copy_direct",
              "alltoallv": "plr::k_copy_v_scatter", "reduce_lds": "plr::k_reduce_lds",
-             "allgather_lds": "plr::k_copy_lds", "allreduce_fused": "plr::k_allreduce_fused"}
+             "allgather_lds": "plr::k_copy_lds", "allreduce_fused": "plr::k_allreduce_fused",
+             "allreduce_cap3": "plr::k_allreduce_fused"}
 BOUND_CMD = ("rocprofv3 --pmc {c} -f csv -d <dir>/{op}_{p} -o p -- python3 bench.py --only {op} --steps 5 "
              "--warmup 1")
 XCDS = 8
@@ -851,8 +852,12 @@ def run_next(args):
     srcs = [synth.normal_t(args.seed, 3, w, R3 * C3, 0.5, device=dev) for w in range(W)]
     dsts = [torch.empty(R3 * C3, dtype=torch.bfloat16, device=dev) for _ in range(W)]
     algo = 2 * W * R3 * C3 * 2  # W contributions read, W outputs written
-    for name, path in (("allreduce_fused", plr.PLR_PATH_DIRECT), ("allreduce_composed", plr.PLR_PATH_COMPOSED)):
-        L = plr.plr_layout_create("allreduce", "bf16", W, R3 * C3 * 2, "scattered", "scattered", datapath=path)
+    # the fused kernel at the policy's launch (uncapped) and at 3 workgroups per CU, the
+    # layout option that speeds it on separately allocated buffers such as these
+    for name, path, cap in (("allreduce_fused", plr.PLR_PATH_DIRECT, 0), ("allreduce_cap3", plr.PLR_PATH_DIRECT, 3),
+                            ("allreduce_composed", plr.PLR_PATH_COMPOSED, 0)):
+        L = plr.plr_layout_create("allreduce", "bf16", W, R3 * C3 * 2, "scattered", "scattered", datapath=path,
+                                  wgs_per_cu=cap)
         ws = torch.zeros(max(L.workspace_bytes, 256), dtype=torch.uint8, device=dev)
         us = _time_calls(torch, plr, lambda: plr.plr_allreduce(L, srcs, dsts, ws))
         if plr.plr_check(L, ws) != plr.PLR_OK:
@@ -1203,7 +1208,7 @@ def cpu_model() -> str:
 
 
 ONLY_OPS = ("reduce", "allgather", "alltoall", "alltoallv", "reduce_lds", "allgather_lds", "allreduce_fused",
-            "allreduce_composed")
+            "allreduce_cap3", "allreduce_composed")
 
 
 def run_only(args):
@@ -1253,7 +1258,8 @@ def run_only(args):
         path = plr.PLR_PATH_COMPOSED if op == "allreduce_composed" else plr.PLR_PATH_DIRECT
         srcs = [synth.normal_t(args.seed, 3, w, R3 * C3, 0.5, device=dev) for w in range(W)]
         dsts = [torch.empty(R3 * C3, dtype=torch.bfloat16, device=dev) for _ in range(W)]
-        L = plr.plr_layout_create("allreduce", "bf16", W, R3 * C3 * 2, "scattered", "scattered", datapath=path)
+        L = plr.plr_layout_create("allreduce", "bf16", W, R3 * C3 * 2, "scattered", "scattered", datapath=path,
+                                  wgs_per_cu=3 if op == "allreduce_cap3" else 0)
         ws = torch.zeros(max(L.workspace_bytes, 256), dtype=torch.uint8, device=dev)
 
         def call():
