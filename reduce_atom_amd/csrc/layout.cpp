@@ -290,13 +290,13 @@ extern "C" int plr_layout_create(const plr_layout_desc* d, plr_layout** out) {
   // CU where its 16 streams per tile fall on different places of the HBM address map:
   // [8192, 7168] bf16 in separately allocated tensors 296-308 us against 322-337 us
   // uncapped, 64 MiB per source at spacings of 64-256 MiB 163-178 us against 187-194 us.
-  // Where the streams' start addresses collide in the map (an XOR of address bits that
-  // includes the high ones, so no rule on the addresses predicts it here) the capped launch
-  // lost 10-25%: 219-239 us against 189-194 us with the sources and outputs 512 MiB, 1 GiB
+  // Where the streams' start addresses collide in the map (the pattern an XOR of address
+  // bits that includes the high ones would give; no rule on the addresses predicted it) the
+  // capped launch lost 10-25%: 219-239 us against 189-194 us with the sources and outputs 512 MiB, 1 GiB
   // or 2 GiB apart, 215 us against 193 us in 1 GiB buffers the allocator placed 1 GiB +
   // 2 MiB apart in mixed order, while the same spacing in ascending order gained (170
   // against 188 us). Uncapped, the same placements all took 187-201 us, so the default is
-  // the launch whose time does not depend on where the buffers sit. Every other kernel is
+  // the launch whose time depends least on where the buffers sit. Every other kernel is
   // slower capped: the 8 x 117 MB reduce took 162.2-163.3 us uncapped, the same at 6 or 8
   // per CU and 174-177 us at 4 or 5; the 512 MiB copy gained nothing that held; the
   // AllToAllV row scatter, which lives on many short workgroups, 150 us uncapped against
