@@ -852,7 +852,7 @@ def run_next(args):
     srcs = [synth.normal_t(args.seed, 3, w, R3 * C3, 0.5, device=dev) for w in range(W)]
     dsts = [torch.empty(R3 * C3, dtype=torch.bfloat16, device=dev) for _ in range(W)]
     algo = 2 * W * R3 * C3 * 2  # W contributions read, W outputs written
-    # the fused kernel at the policy's launch (uncapped) and at 3 workgroups per CU, the
+    # the fused kernel at the policy's launch (8 workgroups per CU) and at 3 per CU, the
     # layout option that speeds it on separately allocated buffers such as these
     for name, path, cap in (("allreduce_fused", plr.PLR_PATH_DIRECT, 0), ("allreduce_cap3", plr.PLR_PATH_DIRECT, 3),
                             ("allreduce_composed", plr.PLR_PATH_COMPOSED, 0)):

@@ -164,13 +164,14 @@ typedef struct {
   const size_t* part_bytes;
   /* Resident workgroups per compute unit for the layout's direct-path reduce, copy and fused
    * AllReduce launches, capped by reserving workgroup memory (LDS: 160 KiB per compute unit)
-   * at each launch: 0 = policy (no cap for any layout), -1 = no cap, 1..16 = at most that
-   * many (one workgroup may hold all 160 KiB). The LDS-staged and composed paths are never
-   * capped. 3 speeds the fused AllReduce of large shares by 8-14% when its sources and
-   * outputs fall on different places of the HBM address map (separately allocated tensors
-   * of up to a few hundred MiB) and slows it by 10-25% when they collide there (buffers a
-   * multiple of 512 MiB apart, some large allocations); uncapped, its time moved by under 8%
-   * across the same placements. plr_layout_occupancy reports the cap used. */
+   * at each launch: 0 = policy (8 for the fused AllReduce of more than 2 MiB per source,
+   * 1-4% faster than uncapped wherever its buffers sit; no cap elsewhere), -1 = no cap,
+   * 1..16 = at most that many (one workgroup may hold all 160 KiB). The LDS-staged and
+   * composed paths are never capped. 3 speeds that AllReduce by 8-14% over uncapped when its
+   * sources and outputs fall on different places of the HBM address map (separately
+   * allocated tensors of up to a few hundred MiB) and slows it by 10-25% when they collide
+   * there (buffers a multiple of 512 MiB apart, some large allocations).
+   * plr_layout_occupancy reports the cap used. */
   int wgs_per_cu;
 } plr_layout_desc;
 

@@ -285,25 +285,30 @@ extern "C" int plr_layout_create(const plr_layout_desc* d, plr_layout** out) {
     }
   }
   if (L->var_segs && L->datapath == PLR_PATH_LDS) return fail(PLR_EUNSUPPORTED);
-  // resident workgroups per CU, capped through an LDS reservation at launch when the caller
-  // asks for it; the policy caps nothing. The fused AllReduce of 8 sources gains from 3 per
-  // CU where its 16 streams per tile fall on different places of the HBM address map:
-  // [8192, 7168] bf16 in separately allocated tensors 296-308 us against 322-337 us
-  // uncapped, 64 MiB per source at spacings of 64-256 MiB 163-178 us against 187-194 us.
-  // Where the streams' start addresses collide in the map (the pattern an XOR of address
-  // bits that includes the high ones would give; no rule on the addresses predicted it) the
-  // capped launch lost 10-25%: 219-239 us against 189-194 us with the sources and outputs 512 MiB, 1 GiB
-  // or 2 GiB apart, 215 us against 193 us in 1 GiB buffers the allocator placed 1 GiB +
-  // 2 MiB apart in mixed order, while the same spacing in ascending order gained (170
-  // against 188 us). Uncapped, the same placements all took 187-201 us, so the default is
-  // the launch whose time depends least on where the buffers sit. Every other kernel is
-  // slower capped: the 8 x 117 MB reduce took 162.2-163.3 us uncapped, the same at 6 or 8
-  // per CU and 174-177 us at 4 or 5; the 512 MiB copy gained nothing that held; the
-  // AllToAllV row scatter, which lives on many short workgroups, 150 us uncapped against
-  // 155-440 us at 11 down to 2 per CU.
+  // resident workgroups per CU, capped through an LDS reservation at launch. The fused
+  // AllReduce of more than 2 MiB per source keeps 8: graph replays of 8 sources into 8
+  // outputs, against uncapped on one machine, ran 1-4% faster at every placement tried (64 MiB
+  // per source 64 MiB, 1 GiB + 2 MiB or 2 GiB apart 184-190 us against 188-192 us; in the
+  // collective sweep's 1 GiB buffers 191.8 against 193.6 us; [8192, 7168] bf16 in separate
+  // tensors 326-327 against 334 us) and was never more than 0.4% slower (512 MiB apart: 193.0
+  // against 192.3 us). Fewer workgroups gain more where the 16 streams per tile fall on
+  // different places of the HBM address map (3 per CU: 164-172 us at 64 MiB or 1 GiB + 2 MiB
+  // apart, 308 us for the separate tensors) but lose 10-25% where their start addresses
+  // collide there (the pattern an XOR of address bits that includes the high ones would
+  // give; no rule on the addresses predicted it): 233-239 us at 512 MiB or 2 GiB apart,
+  // 257-260 us at 1 GiB + 4 MiB against 212 us, 214-217 us in the sweep's buffers. So 3 stays
+  // the caller's choice. Every other kernel is slower capped: the 8 x 117 MB reduce took
+  // 162.2-163.3 us uncapped, the same at 6 or 8 per CU and 174-177 us at 4 or 5; the 512 MiB
+  // copy gained nothing that held; the AllToAllV row scatter, which lives on many short
+  // workgroups, 150 us uncapped against 155-440 us at 11 down to 2 per CU.
   if (d->wgs_per_cu < -1 || d->wgs_per_cu > 16)
     return fail(PLR_EINVAL);
-  L->wgs_per_cu = d->wgs_per_cu > 0 ? d->wgs_per_cu : 0;
+  if (d->wgs_per_cu > 0)
+    L->wgs_per_cu = d->wgs_per_cu;
+  else if (d->wgs_per_cu == 0)
+    L->wgs_per_cu = op == PLR_OP_ALLREDUCE && L->src_bytes > (2u << 20) ? 8 : 0;
+  else
+    L->wgs_per_cu = 0;
   if (L->datapath != PLR_PATH_DIRECT) L->wgs_per_cu = 0;  // LDS-staged and composed: never capped
   // the reservation leaves 512 bytes of each share for the kernel's own workgroup memory
   // (the direct reduce and copy use 256 bytes, for the workgroup-wide vote of their chunk

@@ -539,10 +539,9 @@ def test_layout_queries_on_null(plr):
 
 def test_resident_workgroup_cap(plr):
     """Resident workgroups per CU are capped through an LDS reservation (leaving 512 bytes
-    for the kernel's own) when the caller asks: the policy caps nothing (the fused AllReduce
-    included, whose capped time depends on where its buffers sit); callers may cap any
-    direct-path layout; the LDS-staged and composed paths never are capped; bad values are
-    refused."""
+    for the kernel's own): the policy caps the fused AllReduce of more than 2 MiB per source
+    at 8 and nothing else; callers may cap any direct-path layout; the LDS-staged and
+    composed paths never are capped; bad values are refused."""
     def occ(*a, **k):
         p = plr.plr_layout_create(*a, **k).policy()
         return p["wgs_per_cu"], p["lds_reserve"]
@@ -557,7 +556,8 @@ def test_resident_workgroup_cap(plr):
     assert occ("reduce", "bf16", 8, 4 << 20, "scattered", "packed", rank=1) == (0, 0)  # 512 KiB per source
     assert occ("copy", "bf16", 8, 64 << 20, "packed", "packed") == (0, 0)
     assert occ("copy", "bf16", 8, 64 << 20, "packed", "packed", wgs_per_cu=8)[0] == 8
-    assert occ("allreduce", "bf16", 8, 1 << 24, "scattered", "scattered") == (0, 0)
+    assert occ("allreduce", "bf16", 8, 1 << 24, "scattered", "scattered") == (8, 19968)
+    assert occ("allreduce", "bf16", 8, 2 << 20, "scattered", "scattered") == (0, 0)  # 2 MiB: uncapped
     assert occ("allreduce", "bf16", 8, 1 << 24, "scattered", "scattered", wgs_per_cu=3) == (3, 53760)
     assert occ("allreduce", "bf16", 8, 1 << 24, "scattered", "scattered", wgs_per_cu=-1) == (0, 0)
     assert occ("allreduce", "bf16", 8, 1 << 24, "scattered", "scattered", wgs_per_cu=4)[0] == 4
