@@ -49,12 +49,14 @@ def test_allreduce_small(plr, oracle_mod, path, dtype, W):
 
 @pytest.mark.parametrize("path", list(PATHS))
 def test_allreduce_prefill_share_full(plr, oracle_mod, path):
-    """8 contributions of [8192, 7168] bf16 N(0, 0.5) into 8 outputs, default tiles:
-    output 0 whole against the oracle, outputs 1..7 bitwise equal to output 0."""
+    """8 contributions of [8192, 7168] bf16 N(0, 0.5) into 8 outputs, default tiles (and,
+    fused, the policy's 8 resident workgroups per CU): output 0 whole against the oracle,
+    outputs 1..7 bitwise equal to output 0."""
     W, R, C = 8, 8192, 7168
     srcs = [synth.normal_t(0, 3, w, R * C, 0.5, device="cuda") for w in range(W)]
     dsts = [torch.full((R * C,), float("nan"), dtype=torch.bfloat16, device="cuda") for _ in range(W)]
     L = plr.plr_layout_create("allreduce", "bf16", W, R * C * 2, "scattered", "scattered", datapath=PATHS[path])
+    assert L.policy()["wgs_per_cu"] == (8 if PATHS[path] == plr.PLR_PATH_DIRECT else 0)
     ws = torch.zeros(max(L.workspace_bytes, 256), dtype=torch.uint8, device="cuda")
     plr.plr_allreduce(L, srcs, dsts, ws)
     torch.cuda.synchronize()
