@@ -615,6 +615,7 @@ def run_decode(args, torch, plr, synth, dev):
 
 
 DECODE_COLD_BYTES = 512 << 20  # the cold decode runs rotate over this much source memory
+LOCAL_KEY = "local_8x1M"  # the local reduce's entry in the decode trace
 CONSUMERS = ("k_reduce_direct", "k_reduce_packets")
 PRODUCERS = ("k_notify", "k_pack")
 
@@ -625,7 +626,9 @@ def run_decode_trace_child(args):
     same sources every call) and cold (each call's sources at another place of a
     512 MiB region, so that they are not in the L2 or the Infinity Cache), --decode-warmup
     calls and then --decode-iters calls, each one producer step (notify on: k_notify;
-    packets: k_pack) and one consumer kernel. Prints the schedule as JSON."""
+    packets: k_pack) and one consumer kernel. Then the local reduce of 8 x 1,048,576 bf16
+    (uniform[-1, 1]) the same way, notify off, warm and cold (32 sets of 16 MiB). Prints
+    the schedule as JSON."""
     import torch
 
     import reduce_atom_amd as plr
@@ -664,6 +667,20 @@ def run_decode_trace_child(args):
             if ws is not None and plr.plr_check(L, ws) != plr.PLR_OK:
                 raise RuntimeError(f"decode trace T={T} {mode}: device error")
         print(f"decode trace: T={T} done", file=sys.stderr, flush=True)
+    n = 1 << 20
+    srcs = [synth.uniform_pm1_t(args.seed, 1, w, n, device=dev) for w in range(W)]
+    sets = DECODE_COLD_BYTES // (W * 2 * n)
+    cold = big[: sets * W * 2 * n].view(sets, W, 2 * n)
+    cold.copy_(torch.stack([x.view(torch.uint8) for x in srcs]).unsqueeze(0).expand(sets, W, 2 * n))
+    cold_lists = [[cold[k, w] for w in range(W)] for k in range(sets)]
+    dst = torch.empty(n, dtype=torch.bfloat16, device=dev)
+    L = plr.plr_layout_create("reduce", "bf16", W, 2 * n, "packed", "packed")
+    for temp in ("warm", "cold"):
+        for i in range(args.decode_warmup + args.decode_iters):
+            plr.plr_reduce(L, srcs if temp == "warm" else cold_lists[i % sets], dst)
+        sched.append([LOCAL_KEY, "notify_off", temp, args.decode_warmup, args.decode_iters])
+    torch.cuda.synchronize()
+    print("decode trace: local reduce done", file=sys.stderr, flush=True)
     print(json.dumps({"decode_trace_schedule": sched}), flush=True)
 
 
@@ -702,12 +719,13 @@ def parse_decode_trace(path, sched):
             p = sorted(us for _, us in prod[pi + nw: pi + nw + ni])
             pi += nw + ni
             row["producer_p50_us"] = round(_pct(p, 0.5), 2) if p else None
-        out.setdefault(f"T={T}", {}).setdefault(mode, {})[temp] = row
+        out.setdefault(T if T == LOCAL_KEY else f"T={T}", {}).setdefault(mode, {})[temp] = row
     if ci != len(cons) or pi != len(prod):
         return {"error": f"trace holds {len(cons)} consumer and {len(prod)} producer dispatches, "
                          f"the schedule {ci} and {pi}"}
     out["source"] = ("rocprofv3 kernel trace: consumer kernel duration per call (k_reduce_direct; packets: "
-                     "k_reduce_packets), after the warmup calls; producer: k_notify / k_pack")
+                     "k_reduce_packets), after the warmup calls; producer: k_notify / k_pack; "
+                     f"{LOCAL_KEY}: the local reduce of 8 x 1,048,576 bf16, notify off")
     return out
 
 
@@ -717,7 +735,8 @@ def summarize_decode(path: str) -> str:
     producer kernel's p50, and the per-call time in replayed graphs."""
     with open(path) as f:
         line = [x for x in f.read().splitlines() if x.startswith("{")][-1]
-    dec = json.loads(line)["decode_reduce_us"]
+    full = json.loads(line)
+    dec = full["decode_reduce_us"]
     kt = dec["kernel_trace"]
     out = [f"{'T':>4s} {'mode':11s} {'temp':5s} {'p50_us':>7s} {'p90_us':>7s} {'mean_us':>8s} {'min_us':>7s} "
            f"{'calls':>6s} {'producer_p50_us':>16s} {'graph_us_per_call':>18s}"]
@@ -729,6 +748,15 @@ def summarize_decode(path: str) -> str:
                 out.append(f"{T[2:]:>4s} {mode:11s} {temp:5s} {r['p50_us']:7.2f} {r['p90_us']:7.2f} "
                            f"{r['mean_us']:8.2f} {r['min_us']:7.2f} {r['calls']:6d} "
                            f"{'' if prod is None else f'{prod:.2f}':>16s} {'' if graph is None else f'{graph:.2f}':>18s}")
+    local = (full.get("local_reduce_8x1M_bf16") or {}).get("kernel_trace")
+    if local:
+        out.append("")
+        out.append("local reduce, 8 x 1,048,576 bf16 (18,874,368 bytes), notify off")
+        out.append(f"{'temp':5s} {'p50_us':>7s} {'p90_us':>7s} {'mean_us':>8s} {'min_us':>7s} {'calls':>6s} "
+                   f"{'GB/s_at_p50':>12s}")
+        for temp, r in local.items():
+            out.append(f"{temp:5s} {r['p50_us']:7.2f} {r['p90_us']:7.2f} {r['mean_us']:8.2f} {r['min_us']:7.2f} "
+                       f"{r['calls']:6d} {r['GB/s_at_p50']:12.1f}")
     return "\n".join(out)
 
 
@@ -1468,6 +1496,11 @@ def main():
     nxt = None if args.no_decode else run_next(args)
     cpu = None if host is None else run_cpu_baseline(args, host)
     del host
+    if trace is not None and LOCAL_KEY in trace:
+        lt = trace.pop(LOCAL_KEY)["notify_off"]
+        for temp in lt:
+            lt[temp]["GB/s_at_p50"] = round(9 * 2 * (1 << 20) / (lt[temp]["p50_us"] * 1e-6) / 1e9, 1)
+        local = {"kernel_trace": lt, **(local or {})}
     if decode is not None and trace is not None:
         decode = {"kernel_trace": trace, **decode}
     line = {

@@ -127,14 +127,19 @@ def test_parse_decode_trace_walks_the_schedule(tmp_path):
     for us in (9.0, 4.0, 6.0, 4.0):  # notify_on warm
         add("void plr::k_notify(plr::NotifyArgs)", 2.0)
         add("void plr::k_reduce_direct<0, 8, 1>(plr::ReduceArgs)", us)
+    for us in (8.0, 4.5, 4.0, 4.25):  # the local reduce, warm
+        add("void plr::k_reduce_direct<0, 8, 1>(plr::ReduceArgs)", us)
     path = tmp_path / "dec_kernel_trace.csv"
     path.write_text("\n".join(rows) + "\n")
-    sched = [[1, "notify_off", "warm", 1, 3], [1, "notify_on", "warm", 1, 3]]
+    sched = [[1, "notify_off", "warm", 1, 3], [1, "notify_on", "warm", 1, 3],
+             [bench.LOCAL_KEY, "notify_off", "warm", 1, 3]]
     out = bench.parse_decode_trace(str(path), sched)
     assert out["T=1"]["notify_off"]["warm"]["p50_us"] == 3.0
     assert out["T=1"]["notify_off"]["warm"]["calls"] == 3
     assert out["T=1"]["notify_on"]["warm"]["p50_us"] == 4.0
     assert out["T=1"]["notify_on"]["warm"]["producer_p50_us"] == 2.0
+    assert out[bench.LOCAL_KEY]["notify_off"]["warm"]["p50_us"] == 4.25
+    assert "producer_p50_us" not in out[bench.LOCAL_KEY]["notify_off"]["warm"]
     assert "error" in bench.parse_decode_trace(str(path), sched + [[8, "notify_off", "warm", 1, 3]])
     assert "error" in bench.parse_decode_trace(str(path), sched[:1])
 
