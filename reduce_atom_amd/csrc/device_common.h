@@ -130,8 +130,8 @@ namespace plr {
 
 // ---- LDS staging (the Atom pipeline through workgroup-local memory) ----
 // gfx950 global->LDS DMA: each lane's 16 bytes land at lds_base + 16*lane, where
-// lds_base is wave-uniform. The LDS reads that consume a stage are issued as inline
-// ds_read_b128 with explicit waits, so that the compiler does not wait for every
+// lds_base is wave-uniform. The LDS reads that consume a stage are inline ds_read_b128
+// with their own wait (lds_read_wait), so that the compiler does not wait for every
 // DMA in flight (it cannot tell the stages of the ring apart) and the pipeline keeps
 // S-1 stages loading while one is consumed.
 #define PLR_LDS __attribute__((address_space(3)))
@@ -149,12 +149,142 @@ __device__ __forceinline__ void wait_vmem() {
   asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
 }
 
-__device__ __forceinline__ u32x4 lds_read16(const PLR_LDS u32x4* p) {
-  u32x4 v;
-  asm volatile("ds_read_b128 %0, %1" : "=v"(v) : "v"((uint32_t)(uintptr_t)p) : "memory");
-  return v;
-}
+// LDS reads of a ring slab and their wait in one assembly statement: out[k] = the 16-byte
+// vector at `base` + k KiB, k < N, all N reads in flight together, then a wait for them.
+// The compiler takes an assembly statement's outputs as written when the statement
+// ends, so with the reads and the wait in separate statements it may schedule uses of
+// the outputs between them (a reduce's widening was placed right after the read, before
+// the data had arrived). The outputs are early-clobber: none may share a register with
+// the address, which the later reads of the statement still use. Groups of at most 8
+// (the immediate offsets stay under 8 KiB); more than 8 take one statement per group.
+template <int N>
+struct LdsReadWait;
+template <>
+struct LdsReadWait<1> {
+  static __device__ __forceinline__ void run(uint32_t a, u32x4* o) {
+    asm volatile(
+        "ds_read_b128 %0, %1\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(o[0])
+        : "v"(a)
+        : "memory");
+  }
+};
+template <>
+struct LdsReadWait<2> {
+  static __device__ __forceinline__ void run(uint32_t a, u32x4* o) {
+    asm volatile(
+        "ds_read_b128 %0, %2\n\t"
+        "ds_read_b128 %1, %2 offset:1024\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(o[0]), "=&v"(o[1])
+        : "v"(a)
+        : "memory");
+  }
+};
+template <>
+struct LdsReadWait<3> {
+  static __device__ __forceinline__ void run(uint32_t a, u32x4* o) {
+    asm volatile(
+        "ds_read_b128 %0, %3\n\t"
+        "ds_read_b128 %1, %3 offset:1024\n\t"
+        "ds_read_b128 %2, %3 offset:2048\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(o[0]), "=&v"(o[1]), "=&v"(o[2])
+        : "v"(a)
+        : "memory");
+  }
+};
+template <>
+struct LdsReadWait<4> {
+  static __device__ __forceinline__ void run(uint32_t a, u32x4* o) {
+    asm volatile(
+        "ds_read_b128 %0, %4\n\t"
+        "ds_read_b128 %1, %4 offset:1024\n\t"
+        "ds_read_b128 %2, %4 offset:2048\n\t"
+        "ds_read_b128 %3, %4 offset:3072\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(o[0]), "=&v"(o[1]), "=&v"(o[2]), "=&v"(o[3])
+        : "v"(a)
+        : "memory");
+  }
+};
+template <>
+struct LdsReadWait<5> {
+  static __device__ __forceinline__ void run(uint32_t a, u32x4* o) {
+    asm volatile(
+        "ds_read_b128 %0, %5\n\t"
+        "ds_read_b128 %1, %5 offset:1024\n\t"
+        "ds_read_b128 %2, %5 offset:2048\n\t"
+        "ds_read_b128 %3, %5 offset:3072\n\t"
+        "ds_read_b128 %4, %5 offset:4096\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(o[0]), "=&v"(o[1]), "=&v"(o[2]), "=&v"(o[3]), "=&v"(o[4])
+        : "v"(a)
+        : "memory");
+  }
+};
+template <>
+struct LdsReadWait<6> {
+  static __device__ __forceinline__ void run(uint32_t a, u32x4* o) {
+    asm volatile(
+        "ds_read_b128 %0, %6\n\t"
+        "ds_read_b128 %1, %6 offset:1024\n\t"
+        "ds_read_b128 %2, %6 offset:2048\n\t"
+        "ds_read_b128 %3, %6 offset:3072\n\t"
+        "ds_read_b128 %4, %6 offset:4096\n\t"
+        "ds_read_b128 %5, %6 offset:5120\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(o[0]), "=&v"(o[1]), "=&v"(o[2]), "=&v"(o[3]), "=&v"(o[4]), "=&v"(o[5])
+        : "v"(a)
+        : "memory");
+  }
+};
+template <>
+struct LdsReadWait<7> {
+  static __device__ __forceinline__ void run(uint32_t a, u32x4* o) {
+    asm volatile(
+        "ds_read_b128 %0, %7\n\t"
+        "ds_read_b128 %1, %7 offset:1024\n\t"
+        "ds_read_b128 %2, %7 offset:2048\n\t"
+        "ds_read_b128 %3, %7 offset:3072\n\t"
+        "ds_read_b128 %4, %7 offset:4096\n\t"
+        "ds_read_b128 %5, %7 offset:5120\n\t"
+        "ds_read_b128 %6, %7 offset:6144\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(o[0]), "=&v"(o[1]), "=&v"(o[2]), "=&v"(o[3]), "=&v"(o[4]), "=&v"(o[5]), "=&v"(o[6])
+        : "v"(a)
+        : "memory");
+  }
+};
+template <>
+struct LdsReadWait<8> {
+  static __device__ __forceinline__ void run(uint32_t a, u32x4* o) {
+    asm volatile(
+        "ds_read_b128 %0, %8\n\t"
+        "ds_read_b128 %1, %8 offset:1024\n\t"
+        "ds_read_b128 %2, %8 offset:2048\n\t"
+        "ds_read_b128 %3, %8 offset:3072\n\t"
+        "ds_read_b128 %4, %8 offset:4096\n\t"
+        "ds_read_b128 %5, %8 offset:5120\n\t"
+        "ds_read_b128 %6, %8 offset:6144\n\t"
+        "ds_read_b128 %7, %8 offset:7168\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(o[0]), "=&v"(o[1]), "=&v"(o[2]), "=&v"(o[3]), "=&v"(o[4]), "=&v"(o[5]), "=&v"(o[6]), "=&v"(o[7])
+        : "v"(a)
+        : "memory");
+  }
+};
 
-__device__ __forceinline__ void wait_lds_reads() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
+template <int N>
+__device__ __forceinline__ void lds_read_wait(const PLR_LDS u32x4* base, u32x4* out) {
+  static_assert(N >= 1, "at least one vector");
+  if constexpr (N > 8) {
+    LdsReadWait<8>::run((uint32_t)(uintptr_t)base, out);
+    lds_read_wait<N - 8>(base + 8 * 64, out + 8);
+  } else {
+    LdsReadWait<N>::run((uint32_t)(uintptr_t)base, out);
+  }
+}
 
 }  // namespace plr

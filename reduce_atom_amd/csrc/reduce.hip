@@ -112,10 +112,8 @@ __global__ void __launch_bounds__(256) k_reduce_lds(const ReduceArgs a) {
       wait_vmem<0>();
     }
     const int st = (int)(j % S);
-    u32x4 x[W];
-#pragma unroll
-    for (int w = 0; w < W; ++w) x[w] = lds_read16((const PLR_LDS u32x4*)&ring[wave][st][w][lane]);
-    wait_lds_reads();
+    u32x4 x[W];  // ring[wave][st][w][lane] sits 1 KiB after ring[wave][st][w - 1][lane]
+    lds_read_wait<W>((const PLR_LDS u32x4*)&ring[wave][st][0][lane], x);
     const uint64_t v = j * 256 + (uint64_t)wave * 64 + lane;
     if (v < a.nvec) st16(a.dst + v, combine<DT, W>(x));
   }
