@@ -373,6 +373,11 @@ size_t plr_copy_v_noalloc_max_scratch_bytes(void);
  * notification value): release-stores E+1 into every chunk flag of source `src`
  * (or of all sources if src == -1), after all work already queued on `stream`.
  * The next plr_reduce / plr_copy on L consumes epoch E+1.
+ * Ordering: the sources are single-buffered. A consumer accepts any flag >= its epoch,
+ * so a producer must not write a source's next contents (or notify epoch E+2) before the
+ * call consuming E+1 has finished reading it; order that rewrite after the call (stream
+ * order, or an event recorded after it). Packets keep two slots per source so that a
+ * producer may run one epoch ahead (plr_pack).
  * Errors: PLR_EINVAL (src out of range, NULL workspace), PLR_EALIGN, PLR_EHIP. */
 int plr_notify(plr_layout* L, int src, void* workspace, void* stream);
 

@@ -27,7 +27,9 @@
  * Notification (section 3.2 "SNAC"): signal_flag publishes a chunk (release at agent
  * scope, after every store the calling workgroup made), wait_flag consumes it (acquire
  * at agent scope: the workgroup's later loads see the producer's stores). Flags hold
- * a monotonic epoch (section 4.3 "Epoch Bookkeeping"). A wait is bounded: it returns
+ * a monotonic epoch (section 4.3 "Epoch Bookkeeping"), and a wait accepts any value at
+ * or above its epoch, so a chunk's buffer must not be rewritten (or signalled for a later
+ * epoch) before its consumer has finished reading it. A wait is bounded: it returns
  * false after spin_limit polls, and a kernel must then give up without reading.
  * Packets (section 3.2 and Figure 7: payload and notification in one store): a producer
  * may write its share directly in the packet form plr_reduce_packets reads
