@@ -194,6 +194,22 @@ def _world_ptrs(layout: "Layout", xs, what: str):
     return _ptrs(xs)
 
 
+def _need(x, nbytes: int, what: str) -> None:
+    """A tensor argument holds at least the `nbytes` bytes the call reads or writes
+    through it (the C side takes bare pointers and cannot check); raw integer
+    addresses and None are the caller's responsibility."""
+    if x is None or isinstance(x, int):
+        return
+    have = x.numel() * x.element_size()
+    if have < nbytes:
+        raise ValueError(f"{what}: {have} bytes, the call uses {nbytes}")
+
+
+def _need_each(xs, sizes, what: str) -> None:
+    for w, (x, n) in enumerate(zip(xs, sizes)):
+        _need(x, n, f"{what}[{w}]")
+
+
 class Layout:
     """A compiled collective specification (host object owning a plr_layout*)."""
 
@@ -239,6 +255,16 @@ class Layout:
     @property
     def packet_bytes(self) -> int:
         return _lib.plr_layout_packet_bytes(self._h)
+
+    def src_extent(self) -> list:
+        """Bytes of each source the layout's segments reach (its furthest segment end)."""
+        if getattr(self, "_extent", None) is None:
+            ext = [0] * self.world
+            for s, so, _do, ln in self.segments():
+                if ln:
+                    ext[s] = max(ext[s], so + ln)
+            self._extent = ext
+        return self._extent
 
     @property
     def ntiles(self) -> int:
@@ -310,27 +336,51 @@ def plr_layout_destroy(layout: Layout) -> None:
     layout.__del__()
 
 
+def _check_sizes(layout: Layout, srcs, dst, workspace) -> None:
+    if srcs is not None and len(srcs) == layout.world:
+        _need_each(srcs, layout.src_extent(), "srcs")
+    _need(dst, layout.dst_bytes, "dst")
+    if workspace is not None:
+        _need(workspace, layout.workspace_bytes, "workspace")
+
+
 def plr_reduce(layout: Layout, srcs, dst, workspace=None, stream=None) -> None:
+    _check_sizes(layout, srcs, dst, workspace)
     _ok(_lib.plr_reduce(layout.handle, _world_ptrs(layout, srcs, "srcs"), _addr(dst), _addr(workspace),
                         _stream(stream)), "plr_reduce")
 
 
 def plr_copy(layout: Layout, srcs, dst, workspace=None, stream=None) -> None:
+    _check_sizes(layout, srcs, dst, workspace)
     _ok(_lib.plr_copy(layout.handle, _world_ptrs(layout, srcs, "srcs"), _addr(dst), _addr(workspace),
                       _stream(stream)), "plr_copy")
 
 
 def plr_allreduce(layout: Layout, srcs, dsts, workspace=None, stream=None) -> None:
+    # the fused datapath ignores the workspace; the composed one keeps its flags there
+    composed = layout.policy()["datapath"] == PLR_PATH_COMPOSED
+    _check_sizes(layout, srcs, None, workspace if composed else None)
+    if dsts is not None and len(dsts) == layout.world:
+        _need_each(dsts, [layout.dst_bytes] * layout.world, "dsts")
     _ok(_lib.plr_allreduce(layout.handle, _world_ptrs(layout, srcs, "srcs"), _world_ptrs(layout, dsts, "dsts"),
                            _addr(workspace), _stream(stream)), "plr_allreduce")
 
 
 def plr_pack(layout: Layout, src: int, data, packets, stream=None) -> None:
+    if data is not None and packets is not None and len(data) == len(packets) == layout.world:
+        ext = layout.src_extent()
+        for w in range(layout.world) if src == -1 else ([src] if 0 <= src < layout.world else []):
+            _need(data[w], ext[w], f"data[{w}]")
+            _need(packets[w], layout.packet_bytes, f"packets[{w}]")
     _ok(_lib.plr_pack(layout.handle, src, _world_ptrs(layout, data, "data"), _world_ptrs(layout, packets, "packets"),
                       _stream(stream)), "plr_pack")
 
 
 def plr_reduce_packets(layout: Layout, packets, dst, workspace, stream=None) -> None:
+    if packets is not None and len(packets) == layout.world:
+        _need_each(packets, [layout.packet_bytes] * layout.world, "packets")
+    _need(dst, layout.dst_bytes, "dst")
+    _need(workspace, 256, "workspace")
     _ok(_lib.plr_reduce_packets(layout.handle, _world_ptrs(layout, packets, "packets"), _addr(dst),
                                 _addr(workspace), _stream(stream)), "plr_reduce_packets")
 
@@ -352,9 +402,22 @@ def _copy_v_lists(srcs, rows_per_src, dest_of_row):
     return W, (_c.c_int64 * W)(*rows_per_src)
 
 
+def _copy_v_sizes(W, rows_per_src, srcs, dest_of_row, row_bytes, dst, counts, offsets) -> None:
+    if any(r < 0 for r in rows_per_src) or row_bytes < 0:
+        return  # the library rejects these itself
+    _need_each(srcs, [r * row_bytes for r in rows_per_src], "srcs")
+    _need_each(dest_of_row, [4 * r for r in rows_per_src], "dest_of_row")
+    _need(dst, sum(rows_per_src) * row_bytes, "dst")
+    _need(counts, 8 * W * W, "counts")
+    _need(offsets, 8 * W * W, "offsets")
+
+
 def plr_copy_v(srcs, rows_per_src, dest_of_row, row_bytes, dst, counts, offsets, scratch,
                stream=None) -> None:
     W, rows = _copy_v_lists(srcs, rows_per_src, dest_of_row)
+    _copy_v_sizes(W, rows_per_src, srcs, dest_of_row, row_bytes, dst, counts, offsets)
+    if 1 <= W <= PLR_MAX_WORLD:
+        _need(scratch, plr_copy_v_scratch_bytes(W, rows_per_src), "scratch")
     _ok(_lib.plr_copy_v(W, _ptrs(srcs), rows, _ptrs(dest_of_row), row_bytes, _addr(dst),
                         _addr(counts), _addr(offsets), _addr(scratch), _stream(stream)), "plr_copy_v")
 
@@ -362,6 +425,7 @@ def plr_copy_v(srcs, rows_per_src, dest_of_row, row_bytes, dst, counts, offsets,
 def plr_copy_v_noalloc(srcs, rows_per_src, dest_of_row, row_bytes, dst, counts, offsets, stream=None) -> None:
     """plr_copy_v with the library's fixed per-GPU scratch instead of a caller buffer."""
     W, rows = _copy_v_lists(srcs, rows_per_src, dest_of_row)
+    _copy_v_sizes(W, rows_per_src, srcs, dest_of_row, row_bytes, dst, counts, offsets)
     _ok(_lib.plr_copy_v_noalloc(W, _ptrs(srcs), rows, _ptrs(dest_of_row), row_bytes, _addr(dst),
                                 _addr(counts), _addr(offsets), _stream(stream)), "plr_copy_v_noalloc")
 
@@ -371,6 +435,7 @@ def plr_copy_v_noalloc_max_scratch_bytes() -> int:
 
 
 def plr_notify(layout: Layout, src: int, workspace, stream=None) -> None:
+    _need(workspace, layout.workspace_bytes, "workspace")
     _ok(_lib.plr_notify(layout.handle, src, _addr(workspace), _stream(stream)), "plr_notify")
 
 

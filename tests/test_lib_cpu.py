@@ -568,3 +568,51 @@ def test_resident_workgroup_cap(plr):
     for bad in (17, -2, 1000):
         assert _code(plr.plr_layout_create, *big, wgs_per_cu=bad) == plr.PLR_EINVAL
 
+
+
+def test_binding_rejects_tensors_smaller_than_the_call_uses(plr):
+    """The C side takes bare pointers; the binding checks every tensor argument against
+    the bytes the call reads or writes through it before anything reaches the library
+    (CPU tensors here: a call whose sizes pass stops at the device check instead)."""
+    import torch
+
+    W, n = 4, 2048
+    L = plr.plr_layout_create("reduce", "bf16", W, 2 * n, "packed", "packed")
+    ok = [torch.empty(n, dtype=torch.bfloat16) for _ in range(W)]
+    short = ok[:3] + [torch.empty(n - 8, dtype=torch.bfloat16)]
+    with pytest.raises(ValueError, match=r"srcs\[3\]: 4080 bytes, the call uses 4096"):
+        plr.plr_reduce(L, short, torch.empty(n, dtype=torch.bfloat16))
+    with pytest.raises(ValueError, match=r"dst: 4094 bytes"):
+        plr.plr_reduce(L, ok, torch.empty(n - 1, dtype=torch.bfloat16))
+    with pytest.raises(ValueError, match=r"workspace: 8 bytes"):
+        plr.plr_reduce(L, ok, torch.empty(n, dtype=torch.bfloat16), torch.empty(8, dtype=torch.uint8))
+    with pytest.raises(ValueError, match="device tensor expected"):
+        plr.plr_reduce(L, ok, torch.empty(n, dtype=torch.bfloat16))
+    # explicit offsets: a source must reach its segment's end
+    Lo = plr.plr_layout_create("reduce", "bf16", W, 2 * n, "packed", "packed", in_offsets=[0, 0, 0, 4096])
+    assert Lo.src_extent() == [4096, 4096, 4096, 8192]
+    with pytest.raises(ValueError, match=r"srcs\[3\]: 4096 bytes, the call uses 8192"):
+        plr.plr_reduce(Lo, ok, torch.empty(n, dtype=torch.bfloat16))
+    # AllToAll: every source, the whole transposed output
+    A = plr.plr_layout_create("copy", "bf16", W, 4096, "scattered", "transposed")
+    c_ok = [torch.empty(4096, dtype=torch.uint8) for _ in range(W)]
+    with pytest.raises(ValueError, match=r"dst: 16383 bytes, the call uses 16384"):
+        plr.plr_copy(A, c_ok, torch.empty(W * 4096 - 1, dtype=torch.uint8))
+    # variable-length AllToAll: rows, destinations, output, counts and scratch
+    rows, rb = [3, 0, 5, 1], 64
+    srcs = [torch.empty(r * rb, dtype=torch.uint8) for r in rows]
+    dest = [torch.zeros(r, dtype=torch.int32) for r in rows]
+    args = dict(row_bytes=rb, dst=torch.empty(9 * rb, dtype=torch.uint8), counts=torch.empty(16, dtype=torch.int64),
+                offsets=torch.empty(16, dtype=torch.int64),
+                scratch=torch.empty(plr.plr_copy_v_scratch_bytes(W, rows), dtype=torch.uint8))
+    bad_dest = dest[:2] + [torch.zeros(4, dtype=torch.int32)] + dest[3:]
+    with pytest.raises(ValueError, match=r"dest_of_row\[2\]: 16 bytes, the call uses 20"):
+        plr.plr_copy_v(srcs, rows, bad_dest, **args)
+    with pytest.raises(ValueError, match=r"dst: 512 bytes, the call uses 576"):
+        plr.plr_copy_v(srcs, rows, dest, **{**args, "dst": torch.empty(8 * rb, dtype=torch.uint8)})
+    with pytest.raises(ValueError, match=r"counts: 120 bytes"):
+        plr.plr_copy_v(srcs, rows, dest, **{**args, "counts": torch.empty(15, dtype=torch.int64)})
+    with pytest.raises(ValueError, match=r"scratch: 8 bytes"):
+        plr.plr_copy_v(srcs, rows, dest, **{**args, "scratch": torch.empty(8, dtype=torch.uint8)})
+    with pytest.raises(ValueError, match="device tensor expected"):
+        plr.plr_copy_v(srcs, rows, dest, **args)

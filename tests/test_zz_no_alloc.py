@@ -93,8 +93,11 @@ def test_noalloc_rejects_requests_beyond_its_scratch(plr):
     rows = [plr.plr_copy_v_noalloc_max_scratch_bytes() // 4, 16]
     src = torch.empty(16, dtype=torch.uint8, device="cuda")
     dest = torch.zeros(16, dtype=torch.int32, device="cuda")
+    # raw addresses: the library itself must refuse the request before it reads anything
+    # (tensors this small would already be refused by the binding's size checks)
+    s, d = src.data_ptr(), dest.data_ptr()
     with pytest.raises(plr.PlrError) as e:
-        plr.plr_copy_v_noalloc([src, src], rows, [dest, dest], 16, src, src, src)
+        plr.plr_copy_v_noalloc([s, s], rows, [d, d], 16, s, s, s)
     assert e.value.code == plr.PLR_ETOOLARGE
 
 
