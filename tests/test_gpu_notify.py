@@ -221,7 +221,7 @@ def test_check_mode_partial_arrival(plr, oracle_mod, op):
 
 def test_check_mode_many_flags(plr, oracle_mod):
     """More flags (16,384) than the check's lanes hold in one round of loads (8,192): the
-    verdict, the ready word and the mirror cover every flag; a flag still missing in the
+    check's outcome, the ready word and the mirror cover every flag; a flag still missing in the
     second round sends the consumer to wait and, withheld, to PLR_ETIMEOUT."""
     W, nbytes = 8, 1 << 20
     srcs_np = [synth.bits_np(8, 4, s, nbytes) for s in range(W)]
